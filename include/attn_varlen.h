@@ -1,0 +1,153 @@
+/*
+ * attn_varlen.h -- C ABI of the MI355X (gfx950) ragged extreme-GQA attention
+ * library: forward pass and full vector-Jacobian product.
+ *
+ * The operation (page "Noncausal Global Extreme-GQA Ragged Attention Full
+ * VJP", sections "Hard Constraints" and "What You Have"):
+ *
+ *   For every sequence b of a packed ragged batch (query tokens
+ *   [cu_q[b], cu_q[b+1]), key tokens [cu_k[b], cu_k[b+1])), every query head
+ *   h and its K/V head g, with local positions i (query) and j (key),
+ *   Lq = cu_q[b+1]-cu_q[b], Lk = cu_k[b+1]-cu_k[b], D = head_dim:
+ *
+ *     s_ij = (scale_multiplier / sqrt(D)) * <q_ih, k_jg>
+ *     t_ij = softcap * tanh(s_ij / softcap)          (identity when softcap == 0)
+ *     a_ij = t_ij - alibi_slopes[b, h] * |i + Lk - Lq - j|
+ *     P_ij = softmax_j(a_ij) over the Lk keys of sequence b
+ *     out_ih = sum_j P_ij v_jg,     lse_ih = log sum_j exp(a_ij)  (natural log)
+ *
+ *   The soft cap acts on the scaled dot product, before ALiBi.  The backward
+ *   returns dq, dk, dv = the VJP of out against dout; dk and dv are summed over
+ *   every query head that shares the K/V head.  Rows of a sequence with
+ *   Lk == 0 get out = 0, dq = 0 and lse = -inf (page "python-20261012-ragged-
+ *   flash-attention-gradient-recompute", section "Root causes addressed");
+ *   keys of a sequence with Lq == 0 get dk = dv = 0.
+ *
+ * Supported: dtype F16 or BF16 (one dtype for every 16-bit tensor), hkv == 1,
+ * head_dim == 160, causal == 0, window_left == window_right == -1 (the only
+ * case the page defines).  Anything else returns ATTN_UNSUPPORTED.
+ *
+ * Tensors.  Every activation tensor is a strided view [tokens, heads, 160]
+ * with a contiguous feature axis (feature stride 1) and caller-chosen token
+ * and head strides, in elements.  Device pointers and both strides must be
+ * multiples of 16 bytes / 8 elements (ATTN_MISALIGNED otherwise).  Offsets are
+ * computed in 64-bit, so views may span more than 2^31 elements.
+ *
+ * Ownership and threading.  The caller allocates and owns every buffer,
+ * including the workspace, whose size comes from attn_varlen_workspace_size.
+ * The library allocates no device memory, never writes its inputs (padding
+ * included) and keeps no state between calls except a per-device cache of the
+ * compute-unit count.  Outputs must not alias inputs.  All work is enqueued
+ * asynchronously on `stream`; nothing synchronises the host.  Calls on
+ * different streams need different workspaces.
+ *
+ * Determinism.  No atomics are used; every reduction runs in a fixed order, so
+ * repeated calls with identical inputs give bitwise-identical outputs.
+ *
+ * Errors.  Functions return an attn_status; a failed host-side check launches
+ * nothing.  attn_last_error() gives a human-readable detail for the calling
+ * thread.  Inconsistent cu_q / cu_k contents (not monotone, cu[0] != 0,
+ * cu[B] != total) can only be seen on the device: the plan clamps them to
+ * empty sequences and raises a flag that attn_varlen_check_plan() reads
+ * (that call synchronises the stream).
+ */
+#ifndef RAGGED_GQA_ATTN_VARLEN_H
+#define RAGGED_GQA_ATTN_VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_INVALID_ARG = -1,          /* null pointer, bad size, feature stride != 1 */
+  ATTN_UNSUPPORTED = -2,          /* causal/window/head_dim/hkv/dtype outside the supported set */
+  ATTN_MISALIGNED = -3,           /* pointer or stride not a multiple of 16 B */
+  ATTN_WORKSPACE_TOO_SMALL = -4,
+  ATTN_HIP_ERROR = -5,            /* a HIP runtime call or launch failed */
+  ATTN_BAD_SEQLENS = -6           /* device-side cu_q / cu_k check failed */
+} attn_status;
+
+typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+typedef enum {
+  ATTN_ENTRY_FWD = 0,
+  ATTN_ENTRY_BWD = 1,
+  ATTN_ENTRY_FULL_VJP = 2
+} attn_entry;
+
+/* A hipStream_t; NULL is the default stream. */
+typedef void* attn_stream_t;
+
+/* Strided view [tokens, heads, head_dim] of 16-bit elements, feature stride 1. */
+typedef struct {
+  void* data;            /* device pointer to element [0, 0, 0] */
+  int64_t tok_stride;    /* elements between consecutive tokens */
+  int64_t head_stride;   /* elements between consecutive heads */
+} attn_tensor;
+
+typedef struct {
+  int32_t dtype;               /* attn_dtype */
+  int32_t batch;               /* B >= 0 sequences */
+  int32_t hq;                  /* query heads, 1..1024 */
+  int32_t hkv;                 /* K/V heads; must be 1 */
+  int32_t head_dim;            /* must be 160 */
+  int64_t total_q;             /* tokens in the q / dout / out / dq views (= cu_q[B]) */
+  int64_t total_k;             /* tokens in the k / v / dk / dv views (= cu_k[B]) */
+  const int32_t* cu_q;         /* device int32 [B+1], cu_q[0] = 0, nondecreasing */
+  const int32_t* cu_k;         /* device int32 [B+1] */
+  const float* alibi_slopes;   /* device float32 [B, hq], row stride slopes_stride */
+  int64_t slopes_stride;       /* elements between consecutive sequences (>= hq) */
+  int32_t causal;              /* must be 0 */
+  int32_t window_left;         /* must be -1 */
+  int32_t window_right;        /* must be -1 */
+  float softcap;               /* c > 0 caps logits at c*tanh(x/c); 0 = no cap */
+  float scale_multiplier;      /* logit scale = scale_multiplier / sqrt(head_dim) */
+} attn_problem;
+
+/* Bytes of workspace that `entry` (attn_entry) needs for problem `p`.
+ * Depends only on host-visible sizes (batch, hq, total_q, total_k). */
+attn_status attn_varlen_workspace_size(const attn_problem* p, int entry, size_t* bytes);
+
+/* Forward: writes out (strided, dtype of q) and lse (float32 [total_q, hq]
+ * contiguous, natural log, -inf for rows whose sequence has no keys). */
+attn_status attn_varlen_fwd(const attn_problem* p,
+                            const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_tensor* out, float* lse,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Backward from a stored forward: given out and lse from attn_varlen_fwd and
+ * the cotangent dout, writes dq (like q), dk and dv (like k / v). */
+attn_status attn_varlen_bwd(const attn_problem* p,
+                            const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                            const attn_tensor* out, const float* lse, const attn_tensor* dout,
+                            const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Forward plus full VJP in one call: writes out, dq, dk, dv; lse is written
+ * when non-NULL (float32 [total_q, hq]) and kept in the workspace otherwise. */
+attn_status attn_varlen_full_vjp(const attn_problem* p,
+                                 const attn_tensor* q, const attn_tensor* k, const attn_tensor* v,
+                                 const attn_tensor* dout,
+                                 const attn_tensor* out, const attn_tensor* dq,
+                                 const attn_tensor* dk, const attn_tensor* dv, float* lse,
+                                 void* workspace, size_t workspace_bytes, attn_stream_t stream);
+
+/* Synchronises `stream` and reports the device-side cu_q / cu_k check of the
+ * last call that used `workspace`: ATTN_OK or ATTN_BAD_SEQLENS. */
+attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream);
+
+/* Static text for a status code. */
+const char* attn_status_string(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RAGGED_GQA_ATTN_VARLEN_H */

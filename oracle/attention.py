@@ -1,0 +1,224 @@
+"""Plain float64 CPU definition of ragged grouped-query attention and its VJP.
+
+TEST INFRASTRUCTURE ONLY.  This module is the oracle that the HIP path is
+checked against.  Only the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import it; the library never does, and it shares no
+code with the library.
+
+What is computed (sources are the pages' own words, restated):
+
+* Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section
+  "What You Have": packed ragged sequences addressed by cumulative offsets
+  ``cu_q``/``cu_k``; Q has Hq heads, K/V have Hkv heads (one on the page);
+  the logit of query i and key j in a sequence is the dot product scaled by
+  ``scale_multiplier / sqrt(head_dim)`` (0.75 on the page), passed through the
+  soft cap ``c * tanh(x / c)`` (c = 3 on the page), then shifted by the ALiBi
+  term ``-slope[b, h] * |i + Lk - Lq - j|`` with positions local to the
+  sequence, and normalised by a softmax over that sequence's keys.  Every case
+  is noncausal with no window.
+* Same page, section "Hard Constraints": the cap is applied to the scaled dot
+  product before ALiBi and before any masking; the K/V gradients are summed
+  over every query head that shares the K/V head; the function returns
+  (out, dq, dk, dv) in the inputs' packed layouts.
+* Page "python-20261012-ragged-flash-attention-gradient-recompute", section
+  "Root causes addressed": the stored row statistic is L = m + log l
+  (natural log); a row with no keys has L = -inf, output 0 and gradient 0.
+
+Readings taken where the pages are silent (each is listed in the design doc):
+  - ``softcap == 0`` means no cap (identity); the pages always use 3.
+  - head_dim in the scale is the logical feature count D (160), never the
+    padded buffer width.
+  - the query-head to K/V-head map is g = h // (Hq // Hkv).
+  - the backward is the exact chain rule of the forward above:
+        dP = dO V^T,  Delta_i = sum_j P_ij dP_ij,  dA = P * (dP - Delta),
+        dS = dA * (1 - tanh^2(S / c)),  dQ = sigma dS K,
+        dK = sigma sum_h dS^T Q,  dV = sum_h P^T dO.
+
+Everything is dense per (sequence, head): no tiling, no online softmax, no
+fusion.  Rows may be processed in chunks to bound memory; each row's softmax
+still spans all of its sequence's keys, so the arithmetic is unchanged.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = ["sequence_vjp", "forward", "vjp", "rows_vjp"]
+
+
+def _as_f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv):
+    """Forward and VJP for one head of one sequence, rows at query positions ``i_pos``.
+
+    Qh [n, D], dOh [n, D] (or None), K/V [Lk, D]; ``i_pos`` are the local
+    query positions of those n rows.  Returns out, lse, and, when dOh is
+    given, dq, delta and (if ``want_kv``) this head's dK/dV contributions.
+    """
+    n, D = Qh.shape
+    out = np.zeros((n, D))
+    lse = np.full(n, -np.inf)
+    if dOh is None:
+        res = {"out": out, "lse": lse}
+    else:
+        res = {"out": out, "lse": lse, "dq": np.zeros((n, D)), "delta": np.zeros(n)}
+        if want_kv:
+            res["dk"] = np.zeros((Lk, D))
+            res["dv"] = np.zeros((Lk, D))
+    if n == 0 or Lk == 0:
+        # A row with no keys: L = -inf, output and gradients stay exactly zero.
+        return res
+
+    # scaled dot product
+    S = sigma * (Qh @ K.T)                                   # [n, Lk]
+    # soft cap before ALiBi
+    if softcap > 0.0:
+        U = np.tanh(S / softcap)
+        T = softcap * U
+    else:
+        U = None
+        T = S
+    # ALiBi: -slope * |q_position + key_length - query_length - k_position|
+    dist = np.abs(i_pos[:, None] + (Lk - Lq) - np.arange(Lk)[None, :]).astype(np.float64)
+    A = T - slope * dist
+    # softmax over the sequence's keys
+    m = A.max(axis=1, keepdims=True)
+    E = np.exp(A - m)
+    l = E.sum(axis=1, keepdims=True)
+    P = E / l
+    res["out"] = P @ V
+    res["lse"] = (m + np.log(l))[:, 0]
+    if dOh is None:
+        return res
+
+    dP = dOh @ V.T                                           # [n, Lk]
+    delta = (P * dP).sum(axis=1)                             # = rowsum(dO * O)
+    dA = P * (dP - delta[:, None])
+    dS = dA * (1.0 - U * U) if U is not None else dA
+    res["dq"] = sigma * (dS @ K)
+    res["delta"] = delta
+    if want_kv:
+        res["dk"] = sigma * (dS.T @ Qh)
+        res["dv"] = P.T @ dOh
+    return res
+
+
+def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096):
+    """Forward and full VJP of one sequence.
+
+    Q, dO: [Lq, Hq, D]; K, V: [Lk, Hkv, D]; slopes: [Hq].  ``dO`` may be None
+    (forward only).  Returns a dict with out [Lq,Hq,D], lse [Lq,Hq] and, with
+    dO, dq [Lq,Hq,D], delta [Lq,Hq], dk/dv [Lk,Hkv,D].
+    """
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    Lq, Hq, D = Q.shape
+    Lk, Hkv = K.shape[0], K.shape[1]
+    assert Hq % Hkv == 0
+    group = Hq // Hkv
+    sigma = scale_multiplier / math.sqrt(D)
+    out = np.zeros((Lq, Hq, D))
+    lse = np.full((Lq, Hq), -np.inf)
+    res = {"out": out, "lse": lse}
+    if dO is not None:
+        dO = _as_f64(dO)
+        res.update(dq=np.zeros((Lq, Hq, D)), delta=np.zeros((Lq, Hq)),
+                   dk=np.zeros((Lk, Hkv, D)), dv=np.zeros((Lk, Hkv, D)))
+    for h in range(Hq):
+        g = h // group
+        for r0 in range(0, Lq, row_chunk):
+            r1 = min(Lq, r0 + row_chunk)
+            part = _head_rows(Q[r0:r1, h], K[:, g], V[:, g],
+                              None if dO is None else dO[r0:r1, h],
+                              np.arange(r0, r1), Lq, Lk, float(slopes[h]),
+                              softcap, sigma, want_kv=True)
+            out[r0:r1, h] = part["out"]
+            lse[r0:r1, h] = part["lse"]
+            if dO is not None:
+                res["dq"][r0:r1, h] = part["dq"]
+                res["delta"][r0:r1, h] = part["delta"]
+                if "dk" in part:
+                    # K/V gradients sum over every query head sharing K/V head g
+                    res["dk"][:, g] += part["dk"]
+                    res["dv"][:, g] += part["dv"]
+    return res
+
+
+def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
+    q = _as_f64(q)
+    k = _as_f64(k)
+    v = _as_f64(v)
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    slopes = _as_f64(alibi_slopes)
+    Tq, Hq, D = q.shape
+    Tk, Hkv, _ = k.shape
+    B = len(cu_q) - 1
+    assert len(cu_k) == B + 1 and slopes.shape == (B, Hq)
+    res = {"out": np.zeros((Tq, Hq, D)), "lse": np.full((Tq, Hq), -np.inf)}
+    if dout is not None:
+        dout = _as_f64(dout)
+        res.update(dq=np.zeros((Tq, Hq, D)), delta=np.zeros((Tq, Hq)),
+                   dk=np.zeros((Tk, Hkv, D)), dv=np.zeros((Tk, Hkv, D)))
+    for b in range(B):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        part = sequence_vjp(q[q0:q1], k[k0:k1], v[k0:k1],
+                            None if dout is None else dout[q0:q1],
+                            slopes[b], softcap, scale_multiplier)
+        res["out"][q0:q1] = part["out"]
+        res["lse"][q0:q1] = part["lse"]
+        if dout is not None:
+            res["dq"][q0:q1] = part["dq"]
+            res["delta"][q0:q1] = part["delta"]
+            res["dk"][k0:k1] = part["dk"]
+            res["dv"][k0:k1] = part["dv"]
+    return res
+
+
+def forward(q, k, v, cu_q, cu_k, alibi_slopes, softcap, scale_multiplier):
+    """out [Tq,Hq,D] and lse [Tq,Hq] (natural log) for a packed ragged batch."""
+    res = _run(q, k, v, cu_q, cu_k, alibi_slopes, None, softcap, scale_multiplier)
+    return res["out"], res["lse"]
+
+
+def vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
+    """Forward plus full VJP; dict with out, dq, dk, dv, lse, delta (float64)."""
+    return _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier)
+
+
+def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads):
+    """out, lse, dq, delta for selected rows of one sequence.
+
+    Each row's result depends only on its own q/dout row and the sequence's
+    K/V, so a sample of rows can be checked at any sequence length.  ``tokens``
+    and ``heads`` are equal-length integer arrays of local query positions and
+    head indices.  Returns arrays shaped [n, D] / [n].
+    """
+    Q = _as_f64(Q)
+    K = _as_f64(K)
+    V = _as_f64(V)
+    dO = _as_f64(dO)
+    Lq, Hq, D = Q.shape
+    Lk, Hkv = K.shape[0], K.shape[1]
+    group = Hq // Hkv
+    sigma = scale_multiplier / math.sqrt(D)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    heads = np.asarray(heads, dtype=np.int64)
+    n = len(tokens)
+    res = {"out": np.zeros((n, D)), "lse": np.full(n, -np.inf),
+           "dq": np.zeros((n, D)), "delta": np.zeros(n)}
+    for h in np.unique(heads):
+        sel = np.nonzero(heads == h)[0]
+        g = int(h) // group
+        part = _head_rows(Q[tokens[sel], h], K[:, g], V[:, g], dO[tokens[sel], h],
+                          tokens[sel], Lq, Lk, float(slopes[h]), softcap, sigma,
+                          want_kv=False)
+        for key in res:
+            res[key][sel] = part[key]
+    return res
+
