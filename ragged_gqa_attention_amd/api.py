@@ -1,0 +1,207 @@
+"""Python entry points over the C ABI (argument marshalling only).
+
+``attention_varlen_feature_full_vjp`` keeps the signature of page "Noncausal
+Global Extreme-GQA Ragged Attention Full VJP", section "Hard Constraints":
+(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
+softcap, scale_multiplier) -> (out, dq, dk, dv).  Tensors are device tensors;
+torch only provides memory and the current stream.  Every step of the
+computation runs in the HIP library.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+HEAD_DIM = 160
+_DTYPES = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16}
+
+
+def _view(t: torch.Tensor, name: str, dtype, heads=None) -> _lib.AttnTensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.dim() != 3 or t.shape[2] != HEAD_DIM:
+        raise ValueError(f"{name} must be [tokens, heads, {HEAD_DIM}], got {tuple(t.shape)}")
+    if heads is not None and t.shape[1] != heads:
+        raise ValueError(f"{name} has {t.shape[1]} heads, expected {heads}")
+    if t.shape[0] > 0 and t.stride(2) != 1:
+        raise ValueError(f"{name} must have a contiguous feature axis")
+    return _lib.AttnTensor(t.data_ptr(), t.stride(0), t.stride(1))
+
+
+def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
+                 softcap, scale_multiplier) -> _lib.AttnProblem:
+    if q.dtype not in _DTYPES:
+        raise NotImplementedError(f"dtype {q.dtype} is not supported (FP16 / BF16 only)")
+    for name, cu in (("cu_q", cu_q), ("cu_k", cu_k)):
+        if cu.dtype != torch.int32 or cu.dim() != 1 or cu.device.type != "cuda":
+            raise ValueError(f"{name} must be an int32 GPU vector")
+        if not cu.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if cu_q.numel() != cu_k.numel() or cu_q.numel() < 1:
+        raise ValueError("cu_q and cu_k must both hold batch + 1 offsets")
+    batch = cu_q.numel() - 1
+    hq = q.shape[1]
+    if (alibi_slopes.dtype != torch.float32 or alibi_slopes.device.type != "cuda"
+            or alibi_slopes.dim() != 2 or tuple(alibi_slopes.shape) != (batch, hq)
+            or (batch > 0 and alibi_slopes.stride(1) != 1)):
+        raise ValueError(f"alibi_slopes must be a float32 GPU tensor [{batch}, {hq}] "
+                         "with contiguous rows")
+    return _lib.AttnProblem(
+        dtype=_DTYPES[q.dtype], batch=batch, hq=hq, hkv=k.shape[1], head_dim=q.shape[2],
+        total_q=q.shape[0], total_k=k.shape[0],
+        cu_q=cu_q.data_ptr(), cu_k=cu_k.data_ptr(),
+        alibi_slopes=alibi_slopes.data_ptr(),
+        slopes_stride=alibi_slopes.stride(0) if batch > 0 else hq,
+        causal=int(bool(causal)), window_left=int(window_left), window_right=int(window_right),
+        softcap=float(softcap), scale_multiplier=float(scale_multiplier))
+
+
+def workspace_size(problem: _lib.AttnProblem, entry: int) -> int:
+    n = ctypes.c_size_t(0)
+    _lib.raise_for(_lib.load().attn_varlen_workspace_size(ctypes.byref(problem), entry,
+                                                         ctypes.byref(n)),
+                   "attn_varlen_workspace_size")
+    return n.value
+
+
+def _workspace(nbytes: int, device, ws=None) -> torch.Tensor:
+    if ws is not None:
+        if ws.device != device or ws.dtype != torch.uint8 or ws.numel() < nbytes:
+            raise ValueError("workspace tensor is too small or on the wrong device")
+        return ws
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _fptr(t):
+    return ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_float)) if t is not None else None
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_plan(ws, device):
+    _lib.raise_for(_lib.load().attn_varlen_check_plan(ctypes.c_void_p(ws.data_ptr()),
+                                                      _stream(device)),
+                   "cu_q / cu_k check")
+
+
+def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multiplier=0.75,
+                    causal=False, window_left=-1, window_right=-1, *, out=None, lse=None,
+                    workspace=None, check=False):
+    """Forward only: returns (out [Tq,Hq,160] like q, lse float32 [Tq,Hq])."""
+    prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
+                        softcap, scale_multiplier)
+    tq, tk = _view(q, "q", q.dtype), _view(k, "k", q.dtype)
+    tv = _view(v, "v", q.dtype, heads=k.shape[1])
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Tq, Hq] tensor")
+    to = _view(out, "out", q.dtype, heads=q.shape[1])
+    ws = _workspace(workspace_size(prob, _lib.ENTRY_FWD), q.device, workspace)
+    st = _lib.load().attn_varlen_fwd(ctypes.byref(prob), ctypes.byref(tq), ctypes.byref(tk),
+                                     ctypes.byref(tv), ctypes.byref(to), _fptr(lse),
+                                     ctypes.c_void_p(ws.data_ptr()), ws.numel(),
+                                     _stream(q.device))
+    _lib.raise_for(st, "attn_varlen_fwd")
+    if check:
+        _check_plan(ws, q.device)
+    return out, lse
+
+
+def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3.0,
+                    scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1, *,
+                    dq=None, dk=None, dv=None, workspace=None, check=False):
+    """Backward from a saved forward: returns (dq, dk, dv)."""
+    prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
+                        softcap, scale_multiplier)
+    dt = q.dtype
+    tq, tk, tv = _view(q, "q", dt), _view(k, "k", dt), _view(v, "v", dt, heads=k.shape[1])
+    to = _view(out, "out", dt, heads=q.shape[1])
+    tdo = _view(dout, "dout", dt, heads=q.shape[1])
+    if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [Tq, Hq] tensor")
+    dq = torch.empty(q.shape, dtype=dt, device=q.device) if dq is None else dq
+    dk = torch.empty(k.shape, dtype=dt, device=q.device) if dk is None else dk
+    dv = torch.empty(v.shape, dtype=dt, device=q.device) if dv is None else dv
+    tdq = _view(dq, "dq", dt, heads=q.shape[1])
+    tdk = _view(dk, "dk", dt, heads=k.shape[1])
+    tdv = _view(dv, "dv", dt, heads=k.shape[1])
+    ws = _workspace(workspace_size(prob, _lib.ENTRY_BWD), q.device, workspace)
+    st = _lib.load().attn_varlen_bwd(ctypes.byref(prob), ctypes.byref(tq), ctypes.byref(tk),
+                                     ctypes.byref(tv), ctypes.byref(to), _fptr(lse),
+                                     ctypes.byref(tdo), ctypes.byref(tdq), ctypes.byref(tdk),
+                                     ctypes.byref(tdv), ctypes.c_void_p(ws.data_ptr()),
+                                     ws.numel(), _stream(q.device))
+    _lib.raise_for(st, "attn_varlen_bwd")
+    if check:
+        _check_plan(ws, q.device)
+    return dq, dk, dv
+
+
+class FullVJP:
+    """Pre-bound forward + full VJP call with preallocated outputs and workspace.
+
+    Binding once and calling many times keeps the timed region to the library
+    call itself.  Outputs are dense [Tq,Hq,160] / [Tk,1,160] tensors.
+    """
+
+    def __init__(self, q, k, v, cu_q, cu_k, alibi_slopes, dout, causal=False, window_left=-1,
+                 window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False):
+        self.prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left,
+                                 window_right, softcap, scale_multiplier)
+        dt, dev = q.dtype, q.device
+        self.inputs = (q, k, v, dout, cu_q, cu_k, alibi_slopes)   # keep alive
+        self.out = torch.empty(q.shape, dtype=dt, device=dev)
+        self.dq = torch.empty(q.shape, dtype=dt, device=dev)
+        self.dk = torch.empty(k.shape, dtype=dt, device=dev)
+        self.dv = torch.empty(v.shape, dtype=dt, device=dev)
+        self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev) if want_lse else None
+        self.views = [_view(q, "q", dt), _view(k, "k", dt), _view(v, "v", dt, heads=k.shape[1]),
+                      _view(dout, "dout", dt, heads=q.shape[1]),
+                      _view(self.out, "out", dt), _view(self.dq, "dq", dt),
+                      _view(self.dk, "dk", dt), _view(self.dv, "dv", dt)]
+        self.ws = _workspace(workspace_size(self.prob, _lib.ENTRY_FULL_VJP), dev)
+        self.device = dev
+        self._fn = _lib.load().attn_varlen_full_vjp
+
+    def __call__(self, stream=None):
+        s = ctypes.c_void_p(stream if stream is not None
+                            else torch.cuda.current_stream(self.device).cuda_stream)
+        st = self._fn(ctypes.byref(self.prob), *[ctypes.byref(t) for t in self.views],
+                      _fptr(self.lse), ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
+        _lib.raise_for(st, "attn_varlen_full_vjp")
+        return self.out, self.dq, self.dk, self.dv
+
+    def check_plan(self):
+        _check_plan(self.ws, self.device)
+
+
+def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
+                         scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1,
+                         *, want_lse=False, check=False):
+    """Forward + full VJP: returns (out, dq, dk, dv[, lse])."""
+    call = FullVJP(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
+                   softcap, scale_multiplier, want_lse=want_lse)
+    res = call()
+    if check:
+        call.check_plan()
+    return res + ((call.lse,) if want_lse else ())
+
+
+def attention_varlen_feature_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal,
+                                      window_left, window_right, softcap, scale_multiplier):
+    """The page's entry point: returns (out, dq, dk, dv), dense, in the inputs' dtype."""
+    return attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=softcap,
+                                scale_multiplier=scale_multiplier, causal=causal,
+                                window_left=window_left, window_right=window_right)

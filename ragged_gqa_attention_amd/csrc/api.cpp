@@ -1,0 +1,385 @@
+// C ABI of the ragged extreme-GQA attention library (declared in
+// include/attn_varlen.h): argument checks, workspace layout and the launch
+// sequence of each entry point.  Everything is enqueued on the caller's
+// stream; nothing here synchronises except attn_varlen_check_plan.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "attn_varlen.h"
+#include "kernels.hpp"
+
+using namespace rga;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+attn_status fail(attn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+attn_status fail(attn_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t ALIGN = 256;
+constexpr int MIN_CHUNK_ROWS = 512;     // below this a row chunk is not worth its partials
+constexpr int UNITS_PER_CU = 2;         // dK/dV work units aimed at per compute unit
+constexpr int MAX_DEVICES = 64;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+// Compute-unit count per device, read once (the only state the library keeps).
+int device_cus() {
+  static int cache[MAX_DEVICES] = {0};
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+struct Layout {
+  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag;
+  size_t lse, delta, part_dk, part_dv;
+  size_t total;
+  int64_t max_units;
+  int64_t row_tiles;
+};
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+Layout make_layout(const attn_problem* p, int entry, int cus) {
+  Layout L{};
+  const int64_t B = p->batch;
+  const int64_t rows = p->total_q * p->hq;
+  L.row_tiles = ceil_div(rows, ROW_TILE) + B;
+  L.max_units = (int64_t)cus * UNITS_PER_CU + ceil_div(p->total_k, KEY_TILE) + B;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.flag = take(sizeof(int) * 4);   // first, so attn_varlen_check_plan can find it
+  L.seq = take(sizeof(int) * B * SEQ_FIELDS);
+  L.fwd_seq = take(sizeof(int) * B);
+  L.fwd_off = take(sizeof(int) * (B + 1));
+  L.kv_seq = take(sizeof(int) * B);
+  L.kv_off = take(sizeof(int) * (B + 1));
+  L.kv_rank = take(sizeof(int) * B);
+  L.lse = L.delta = L.part_dk = L.part_dv = 0;
+  if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
+  if (entry != ATTN_ENTRY_FWD) {
+    L.delta = take(sizeof(float) * rows);
+    const size_t part = sizeof(float) * (size_t)L.max_units * KEY_TILE * HEAD_DIM;
+    L.part_dk = take(part);
+    L.part_dv = take(part);
+  }
+  L.total = off;
+  return L;
+}
+
+attn_status check_problem(const attn_problem* p) {
+  if (!p) return fail(ATTN_INVALID_ARG, "problem is NULL");
+  if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16)
+    return fail(ATTN_UNSUPPORTED, "dtype %d is neither F16 nor BF16", p->dtype);
+  if (p->head_dim != HEAD_DIM)
+    return fail(ATTN_UNSUPPORTED, "head_dim %d != 160", p->head_dim);
+  if (p->hkv != 1) return fail(ATTN_UNSUPPORTED, "hkv %d != 1", p->hkv);
+  if (p->causal != 0) return fail(ATTN_UNSUPPORTED, "causal masking is not supported");
+  if (p->window_left != -1 || p->window_right != -1)
+    return fail(ATTN_UNSUPPORTED, "sliding windows are not supported (got %d, %d)",
+                p->window_left, p->window_right);
+  if (p->batch < 0) return fail(ATTN_INVALID_ARG, "batch %d < 0", p->batch);
+  if (p->hq < 1 || p->hq > 1024) return fail(ATTN_INVALID_ARG, "hq %d outside 1..1024", p->hq);
+  if (p->total_q < 0 || p->total_k < 0)
+    return fail(ATTN_INVALID_ARG, "negative token count");
+  if (p->total_q > INT32_MAX || p->total_k > INT32_MAX ||
+      p->total_q * (int64_t)p->hq > (int64_t)INT32_MAX - 4 * ROW_TILE)
+    return fail(ATTN_INVALID_ARG, "too many tokens for 32-bit row indices");
+  if (!p->cu_q || !p->cu_k) return fail(ATTN_INVALID_ARG, "cu_q / cu_k is NULL");
+  if (p->batch > 0 && !p->alibi_slopes) return fail(ATTN_INVALID_ARG, "alibi_slopes is NULL");
+  if (p->slopes_stride < p->hq)
+    return fail(ATTN_INVALID_ARG, "slopes_stride %lld < hq", (long long)p->slopes_stride);
+  if (!(p->softcap >= 0.0f) || !std::isfinite(p->softcap))
+    return fail(ATTN_INVALID_ARG, "softcap must be finite and >= 0");
+  if (!std::isfinite(p->scale_multiplier))
+    return fail(ATTN_INVALID_ARG, "scale_multiplier must be finite");
+  return ATTN_OK;
+}
+
+attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens, int heads) {
+  if (!t) return fail(ATTN_INVALID_ARG, "%s is NULL", name);
+  if (tokens > 0 && !t->data) return fail(ATTN_INVALID_ARG, "%s.data is NULL", name);
+  if (t->tok_stride < 0 || t->head_stride < 0)
+    return fail(ATTN_INVALID_ARG, "%s has a negative stride", name);
+  if (tokens > 1 && t->tok_stride < HEAD_DIM)
+    return fail(ATTN_INVALID_ARG, "%s token stride %lld overlaps rows", name,
+                (long long)t->tok_stride);
+  if (heads > 1 && t->head_stride < HEAD_DIM)
+    return fail(ATTN_INVALID_ARG, "%s head stride %lld overlaps rows", name,
+                (long long)t->head_stride);
+  if ((reinterpret_cast<uintptr_t>(t->data) & 15) != 0 || (t->tok_stride & 7) != 0 ||
+      (t->head_stride & 7) != 0)
+    return fail(ATTN_MISALIGNED, "%s pointer or strides are not 16-byte multiples", name);
+  return ATTN_OK;
+}
+
+LogitConsts logit_consts(const attn_problem* p) {
+  LogitConsts lc;
+  const double sigma = (double)p->scale_multiplier / std::sqrt((double)HEAD_DIM);
+  const double l2e = 1.4426950408889634;
+  const double c = p->softcap;
+  lc.sigma = (float)sigma;
+  lc.s_lin = (float)(sigma * l2e);
+  if (c > 0) {
+    lc.k_exp = (float)(2.0 * sigma * l2e / c);
+    lc.t_mul = (float)(-2.0 * c * l2e);
+    lc.t_add = (float)(c * l2e);
+  } else {
+    lc.k_exp = lc.t_mul = lc.t_add = 0.0f;
+  }
+  return lc;
+}
+
+Plan plan_view(void* ws, const Layout& L) {
+  char* base = static_cast<char*>(ws);
+  Plan pl;
+  pl.seq = reinterpret_cast<int*>(base + L.seq);
+  pl.fwd_seq = reinterpret_cast<int*>(base + L.fwd_seq);
+  pl.fwd_off = reinterpret_cast<int*>(base + L.fwd_off);
+  pl.kv_seq = reinterpret_cast<int*>(base + L.kv_seq);
+  pl.kv_off = reinterpret_cast<int*>(base + L.kv_off);
+  pl.kv_rank = reinterpret_cast<int*>(base + L.kv_rank);
+  pl.flag = reinterpret_cast<int*>(base + L.flag);
+  return pl;
+}
+
+attn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ATTN_OK;
+  return fail(ATTN_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define RGA_TRY(expr)                          \
+  do {                                         \
+    const attn_status st__ = (expr);           \
+    if (st__ != ATTN_OK) return st__;          \
+  } while (0)
+
+void set_view(const attn_tensor* t, const uint16_t** data, int64_t* ts, int64_t* hs) {
+  *data = static_cast<const uint16_t*>(t->data);
+  *ts = t->tok_stride;
+  if (hs) *hs = t->head_stride;
+}
+void set_view(const attn_tensor* t, uint16_t** data, int64_t* ts, int64_t* hs) {
+  *data = static_cast<uint16_t*>(t->data);
+  *ts = t->tok_stride;
+  if (hs) *hs = t->head_stride;
+}
+
+// Shared prologue: checks, workspace, plan launch.  Fills `a` and `L`.
+attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes,
+                     hipStream_t s, AttnArgs& a, Layout& L) {
+  RGA_TRY(check_problem(p));
+  const int cus = device_cus();
+  L = make_layout(p, entry, cus);
+  if (!ws && L.total > 0) return fail(ATTN_INVALID_ARG, "workspace is NULL");
+  if (ws_bytes < L.total)
+    return fail(ATTN_WORKSPACE_TOO_SMALL, "workspace %zu B < %zu B needed", ws_bytes, L.total);
+  if ((reinterpret_cast<uintptr_t>(ws) & (ALIGN - 1)) != 0)
+    return fail(ATTN_MISALIGNED, "workspace must be 256-byte aligned");
+  std::memset(&a, 0, sizeof(a));
+  a.slopes = p->alibi_slopes;
+  a.slopes_stride = p->slopes_stride;
+  a.hq = p->hq;
+  a.batch = p->batch;
+  a.total_q = p->total_q;
+  a.total_k = p->total_k;
+  a.lc = logit_consts(p);
+  a.plan = plan_view(ws, L);
+  char* base = static_cast<char*>(ws);
+  if (L.delta) a.delta = reinterpret_cast<float*>(base + L.delta);
+  if (L.part_dk) {
+    a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
+    a.part_dv = reinterpret_cast<float*>(base + L.part_dv);
+  }
+  PlanArgs pa;
+  pa.cu_q = p->cu_q;
+  pa.cu_k = p->cu_k;
+  pa.batch = p->batch;
+  pa.hq = p->hq;
+  pa.total_q = p->total_q;
+  pa.total_k = p->total_k;
+  pa.target_units = cus * UNITS_PER_CU;
+  pa.min_chunk = MIN_CHUNK_ROWS;
+  pa.plan = a.plan;
+  return hip_status(launch_plan(pa, s), "plan launch");
+}
+
+attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
+                         const attn_tensor* v) {
+  RGA_TRY(check_tensor("q", q, p->total_q, p->hq));
+  RGA_TRY(check_tensor("k", k, p->total_k, 1));
+  RGA_TRY(check_tensor("v", v, p->total_k, 1));
+  return ATTN_OK;
+}
+
+// dK/dV, dQ and the partial reduction, after lse and delta are in place.
+attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layout& L,
+                            hipStream_t s) {
+  const bool cap = p->softcap > 0.0f;
+  if (p->batch == 0) return ATTN_OK;
+  RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
+  RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles, s), "dQ launch"));
+  RGA_TRY(hip_status(launch_kv_reduce(a, p->dtype, s), "dK/dV reduce launch"));
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+attn_status attn_varlen_workspace_size(const attn_problem* p, int entry, size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(ATTN_INVALID_ARG, "bytes is NULL");
+  RGA_TRY(check_problem(p));
+  if (entry < ATTN_ENTRY_FWD || entry > ATTN_ENTRY_FULL_VJP)
+    return fail(ATTN_INVALID_ARG, "unknown entry %d", entry);
+  *bytes = make_layout(p, entry, device_cus()).total;
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
+                            const attn_tensor* v, const attn_tensor* out, float* lse,
+                            void* workspace, size_t workspace_bytes, attn_stream_t stream) {
+  g_last_error.clear();
+  RGA_TRY(check_problem(p));
+  RGA_TRY(check_inputs(p, q, k, v));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
+  if (p->total_q > 0 && !lse) return fail(ATTN_INVALID_ARG, "lse is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a;
+  Layout L;
+  RGA_TRY(prologue(p, ATTN_ENTRY_FWD, workspace, workspace_bytes, s, a, L));
+  set_view(q, &a.q, &a.q_ts, &a.q_hs);
+  set_view(k, &a.k, &a.k_ts, nullptr);
+  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(out, &a.out, &a.o_ts, &a.o_hs);
+  a.lse = lse;
+  if (p->batch == 0) return ATTN_OK;
+  return hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, false, (int)L.row_tiles, s),
+                    "forward launch");
+}
+
+attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
+                            const attn_tensor* v, const attn_tensor* out, const float* lse,
+                            const attn_tensor* dout, const attn_tensor* dq,
+                            const attn_tensor* dk, const attn_tensor* dv, void* workspace,
+                            size_t workspace_bytes, attn_stream_t stream) {
+  g_last_error.clear();
+  RGA_TRY(check_problem(p));
+  RGA_TRY(check_inputs(p, q, k, v));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
+  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  if (p->total_q > 0 && !lse) return fail(ATTN_INVALID_ARG, "lse is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a;
+  Layout L;
+  RGA_TRY(prologue(p, ATTN_ENTRY_BWD, workspace, workspace_bytes, s, a, L));
+  set_view(q, &a.q, &a.q_ts, &a.q_hs);
+  set_view(k, &a.k, &a.k_ts, nullptr);
+  set_view(v, &a.v, &a.v_ts, nullptr);
+  a.out = static_cast<uint16_t*>(out->data);
+  a.o_ts = out->tok_stride;
+  a.o_hs = out->head_stride;
+  set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
+  set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
+  set_view(dk, &a.dk, &a.dk_ts, nullptr);
+  set_view(dv, &a.dv, &a.dv_ts, nullptr);
+  a.lse = const_cast<float*>(lse);
+  if (p->batch == 0) return ATTN_OK;
+  RGA_TRY(hip_status(launch_rowdot(a, p->dtype, s), "row-dot launch"));
+  return launch_backward(p, a, L, s);
+}
+
+attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,
+                                 const attn_tensor* k, const attn_tensor* v,
+                                 const attn_tensor* dout, const attn_tensor* out,
+                                 const attn_tensor* dq, const attn_tensor* dk,
+                                 const attn_tensor* dv, float* lse, void* workspace,
+                                 size_t workspace_bytes, attn_stream_t stream) {
+  g_last_error.clear();
+  RGA_TRY(check_problem(p));
+  RGA_TRY(check_inputs(p, q, k, v));
+  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
+  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AttnArgs a;
+  Layout L;
+  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, s, a, L));
+  set_view(q, &a.q, &a.q_ts, &a.q_hs);
+  set_view(k, &a.k, &a.k_ts, nullptr);
+  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
+  set_view(out, &a.out, &a.o_ts, &a.o_hs);
+  set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
+  set_view(dk, &a.dk, &a.dk_ts, nullptr);
+  set_view(dv, &a.dv, &a.dv_ts, nullptr);
+  a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
+  if (p->batch == 0) return ATTN_OK;
+  RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),
+                     "forward launch"));
+  return launch_backward(p, a, L, s);
+}
+
+attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream) {
+  g_last_error.clear();
+  if (!workspace) return fail(ATTN_INVALID_ARG, "workspace is NULL");
+  int flag = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RGA_TRY(hip_status(hipMemcpyAsync(&flag, workspace, sizeof(int), hipMemcpyDeviceToHost, s),
+                     "reading the plan flag"));
+  RGA_TRY(hip_status(hipStreamSynchronize(s), "stream synchronise"));
+  if (flag != 0) return fail(ATTN_BAD_SEQLENS, "cu_q / cu_k are not a valid packing");
+  return ATTN_OK;
+}
+
+const char* attn_status_string(int status) {
+  switch (status) {
+    case ATTN_OK: return "ok";
+    case ATTN_INVALID_ARG: return "invalid argument";
+    case ATTN_UNSUPPORTED: return "unsupported configuration";
+    case ATTN_MISALIGNED: return "misaligned pointer or stride";
+    case ATTN_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case ATTN_HIP_ERROR: return "HIP runtime error";
+    case ATTN_BAD_SEQLENS: return "cu_q / cu_k failed the device-side check";
+    default: return "unknown status";
+  }
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,136 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+//
+// Tile geometry.  Every kernel works with wave64 and the CDNA4 instruction
+// v_mfma_f32_32x32x16_{f16,bf16}: D[32x32] += A[32x16] * B[16x32] with FP32
+// accumulation.  Operand layout (per lane l, l32 = l % 32, g = l / 32):
+//   A: lane holds A[l32][8g .. 8g+7]      (row l32, eight consecutive k)
+//   B: lane holds B[8g .. 8g+7][l32]      (column l32, eight consecutive k)
+//   D: lane holds D[8(r/4) + 4g + r%4][l32] in accumulator register r = 0..15
+// The feature axis (160) is exactly ten k-steps of 16, so no padding of the
+// head dimension is needed.
+//
+// When a result tile D is reused as a B operand of the next product (P or dS
+// feeding PV / dQ / dK / dV), the sixteen k-values a lane owns are not the
+// canonical 8g..8g+7 but {16s + 4g + 0..3, 16s + 8 + 4g + 0..3} for k-step
+// s = 0, 1.  The matching A operand is read with the same permutation from a
+// transposed LDS tile, so the contraction is unchanged.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rga {
+
+constexpr int HEAD_DIM = 160;
+constexpr int KSTEPS = HEAD_DIM / 16;      // k-steps of the QK^T / dO V^T products
+constexpr int DBLK = HEAD_DIM / 32;        // 32-wide feature blocks of O, dQ, dK, dV
+constexpr int CHUNKS = HEAD_DIM / 8;       // 16-byte chunks per 160-element row
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct F16 {};
+struct BF16 {};
+
+template <class T> __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
+
+template <> __device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+template <> __device__ __forceinline__ f32x16 mfma32<BF16>(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Two floats -> two 16-bit values (round to nearest even), lo in bits 0..15.
+template <class T> __device__ __forceinline__ uint32_t pack2(float lo, float hi);
+template <> __device__ __forceinline__ uint32_t pack2<F16>(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+template <> __device__ __forceinline__ uint32_t pack2<BF16>(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16-bit value (low or high half of a word) -> float.
+template <class T> __device__ __forceinline__ float lo_f(uint32_t w);
+template <class T> __device__ __forceinline__ float hi_f(uint32_t w);
+template <> __device__ __forceinline__ float lo_f<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+template <> __device__ __forceinline__ float hi_f<F16>(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+template <> __device__ __forceinline__ float lo_f<BF16>(uint32_t w) {
+  return __builtin_bit_cast(float, w << 16);
+}
+template <> __device__ __forceinline__ float hi_f<BF16>(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of lane (l ^ 32): the other half of a 32x32 accumulator column pair.
+__device__ __forceinline__ float swap_half(float x) { return __shfl_xor(x, 32, 64); }
+
+// Word k of the pair-interleave of two packed 16-bit rows: (a.e, b.e) for
+// element e = 2k + hi.
+__device__ __forceinline__ uint32_t interleave_lo(uint32_t a, uint32_t b) {
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t interleave_hi(uint32_t a, uint32_t b) {
+  return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Constants of the logit pipeline, in base-2 units so the softmax uses exp2:
+//   x = log2(e) * (c * tanh(s / c) - slope * |i + Lk - Lq - j|)
+// with s = sigma * <q, k> and tanh(y) = 1 - 2 / (1 + e^{2y}).
+struct LogitConsts {
+  float k_exp;    // e^{2 s / c} = exp2(k_exp * dot),   k_exp = 2 sigma log2(e) / c
+  float t_mul;    // x_cap = t_mul * 1/(1 + e^{2y}) + t_add
+  float t_add;    //   t_mul = -2 c log2(e),  t_add = c log2(e)
+  float s_lin;    // uncapped: x = s_lin * dot,  s_lin = sigma log2(e)
+  float sigma;    // scale_multiplier / sqrt(head_dim)
+};
+
+// Per-sequence facts written by the planner (int32 each, SEQ_FIELDS per sequence).
+enum SeqField {
+  SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS, SQ_NCHUNK, SQ_CHUNK, SQ_KTILES, SEQ_FIELDS
+};
+
+// Work lists built on the device; all arrays live in the caller's workspace.
+struct Plan {
+  int* seq;        // [B * SEQ_FIELDS]
+  int* fwd_seq;    // [B]    rank -> sequence, row-tile kernels (cost ~ Lk)
+  int* fwd_off;    // [B+1]  exclusive prefix of row tiles over ranks
+  int* kv_seq;     // [B]    rank -> sequence, key-tile kernel (cost ~ rows per chunk)
+  int* kv_off;     // [B+1]  exclusive prefix of (key tile, row chunk) units over ranks
+  int* kv_rank;    // [B]    sequence -> rank in kv order
+  int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation
+};
+
+// Largest rank r with off[r] <= idx, or -1 when idx is past the last item.
+__device__ __forceinline__ int find_rank(const int* off, int nranks, int idx) {
+  if (nranks <= 0 || idx >= off[nranks]) return -1;
+  int lo = 0, hi = nranks - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (off[mid] <= idx) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace rga

@@ -1,0 +1,64 @@
+// Host-visible launchers of the gfx950 kernels and the argument block they share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace rga {
+
+// Row-tile kernels (forward, dQ): one workgroup = 4 waves x 32 folded rows.
+constexpr int ROW_TILE = 128;
+// Key-tile kernel (dK/dV): one workgroup = 4 waves x 32 keys.
+constexpr int KEY_TILE = 128;
+// Folded rows staged per step of the dK/dV kernel.
+constexpr int KV_ROW_STEP = 32;
+// Keys staged per step of the row-tile kernels.
+constexpr int KEY_STEP = 64;
+
+struct AttnArgs {
+  const uint16_t* q;    int64_t q_ts, q_hs;
+  const uint16_t* k;    int64_t k_ts;
+  const uint16_t* v;    int64_t v_ts;
+  const uint16_t* dout; int64_t do_ts, do_hs;
+  uint16_t* out;        int64_t o_ts, o_hs;
+  uint16_t* dq;         int64_t dq_ts, dq_hs;
+  uint16_t* dk;         int64_t dk_ts;
+  uint16_t* dv;         int64_t dv_ts;
+  float* lse;           // [total_q * hq], natural log
+  float* delta;         // [total_q * hq], rowsum(dout * out)
+  float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
+  float* part_dv;
+  const float* slopes;  int64_t slopes_stride;
+  int hq;
+  int batch;
+  int64_t total_q;
+  int64_t total_k;
+  LogitConsts lc;
+  Plan plan;
+};
+
+struct PlanArgs {
+  const int* cu_q;
+  const int* cu_k;
+  int batch;
+  int hq;
+  int64_t total_q;
+  int64_t total_k;
+  int target_units;     // desired number of dK/dV work units
+  int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
+  Plan plan;
+};
+
+enum { DT_F16 = 0, DT_BF16 = 1 };
+
+hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
+                      hipStream_t s);
+hipError_t launch_rowdot(const AttnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
+hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
+hipError_t launch_kv_reduce(const AttnArgs& a, int dtype, hipStream_t s);
+
+}  // namespace rga
