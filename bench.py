@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Forward + full VJP of ragged extreme-GQA attention on one MI355X.
+
+One step = one attn_varlen_full_vjp call (plan, forward with the dO.O row dot,
+dK/dV, dQ, partial reduction) over the resident synthetic batch.  The default
+workload is the Hq=64 Q-short/K-long configuration: 24 sequences, Lq ~ U[16,128],
+Lk ~ U[512,2048], one K/V head, D = 160, BF16 views of width 192 with token step 2.
+
+Prints one JSON line.  `value` is credited TFLOP/s = 14 * sum_b Lq_b Lk_b * Hq * D
+per call / time per call.  `roofline` covers the kernel with the longest average
+duration, timed with HIP events recorded on the library's stream around each
+phase of every timed call.  `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fwd+full-VJP TFLOP/s (% MFMA peak) and ms/call, ragged GQA Hq=64 D=160"
+MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense FP16/BF16 matrix peak
+HEAD_DIM = 160
+# credited flops per score element and head-dim unit, by phase (14 in total)
+PHASE_FLOPS = {"fwd": 4, "dkdv": 8, "dq": 2, "plan": 0, "reduce": 0}
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "ragged_gqa_attention_amd", "csrc", "*"))):
+        if path.endswith((".hip", ".hpp", ".cpp")):
+            with open(path, "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when the summary is missing or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    d = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not m or not d or d.group(1) != kernel_source_digest():
+        return None
+    return float(m.group(1))
+
+
+def cpu_baseline(wl, seconds: float):
+    """The float64 oracle, unchanged, on the first sequences of the workload
+    until about `seconds` of CPU time."""
+    import oracle
+    from ragged_gqa_attention_amd.workloads import oracle_inputs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        threads = os.cpu_count() or 1
+    inp = oracle_inputs(wl)
+    cu_q, cu_k = inp["cu_q"], inp["cu_k"]
+    spent, elems, n = 0.0, 0, 0
+    for b in range(wl.batch):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        t0 = time.perf_counter()
+        oracle.sequence_vjp(inp["q"][q0:q1], inp["k"][k0:k1], inp["v"][k0:k1],
+                            inp["dout"][q0:q1], inp["alibi_slopes"][b], inp["softcap"],
+                            inp["scale_multiplier"])
+        spent += time.perf_counter() - t0
+        elems += (q1 - q0) * (k1 - k0) * wl.hq
+        n += 1
+        if spent >= seconds:
+            break
+    flops = 14.0 * elems * HEAD_DIM
+    return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n} of {wl.batch} sequences of {wl.name} "
+                      f"(sum Lq*Lk*Hq = {elems}), float64 NumPy forward + VJP, "
+                      f"{spent:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload index (1 = the Hq=64 metric configuration)")
+    ap.add_argument("--trial", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the "
+              "path is one GPU's share; multi-GPU sharding is described in DESIGN.md "
+              "and not built.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import ragged_gqa_attention_amd as rga
+    from ragged_gqa_attention_amd import _lib
+    from ragged_gqa_attention_amd.workloads import make_workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    wl = make_workload(args.config, args.trial)
+    g = wl.to(dev)
+    call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
+                       scale_multiplier=g.scale_multiplier)
+    nph = len(_lib.PHASES)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    call.check_plan()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nph + 1)] for _ in range(K)]
+    for row in evs:          # creates the underlying HIP events
+        for e in row:
+            e.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        call(events=evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = start.elapsed_time(end)
+    ms_per_step = ms_total / K
+    per_call = np.array([evs[i][0].elapsed_time(evs[i][nph]) for i in range(K)])
+    phase_ms = {name: float(np.mean([evs[i][p].elapsed_time(evs[i][p + 1]) for i in range(K)]))
+                for p, name in enumerate(_lib.PHASES)}
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    elems = wl.score_elements()
+    flops = wl.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    dom = max(("fwd", "dkdv", "dq"), key=lambda p: phase_ms[p])
+    achieved = PHASE_FLOPS[dom] * elems * HEAD_DIM / (phase_ms[dom] * 1e-3) / 1e12
+    kernel_names = {"fwd": "fwd_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel"}
+    traffic = measured_traffic(kernel_names[dom], wl.name)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == torch.bfloat16 else "f16",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "seed": [args.config, args.trial], "batch": wl.batch,
+            "hq": wl.hq, "hkv": 1, "head_dim": HEAD_DIM, "total_q": wl.total_q,
+            "total_k": wl.total_k, "sum_lq_lk": int((wl.lq * wl.lk).sum()),
+            "view": f"feature width {wl.width}, token step {wl.step}",
+            "softcap": wl.softcap, "scale_multiplier": wl.scale_multiplier,
+        },
+        "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 3),
+        "ms_per_call_median": round(float(np.median(per_call)), 4),
+        "host_wall_ms_per_step": round(1e3 * wall / K, 4),
+        "phase_ms": {k: round(v, 4) for k, v in phase_ms.items()},
+        "roofline": {
+            "kernel": kernel_names[dom],
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_PEAK_TFLOPS, 5),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

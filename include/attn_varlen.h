@@ -136,6 +136,29 @@ attn_status attn_varlen_full_vjp(const attn_problem* p,
                                  const attn_tensor* dk, const attn_tensor* dv, float* lse,
                                  void* workspace, size_t workspace_bytes, attn_stream_t stream);
 
+/* Phases of attn_varlen_full_vjp, in launch order. */
+typedef enum {
+  ATTN_PHASE_PLAN = 0,     /* work lists from cu_q / cu_k */
+  ATTN_PHASE_FWD = 1,      /* forward: out, lse, delta = rowsum(dout * out) */
+  ATTN_PHASE_DKDV = 2,     /* dK, dV over all sharing heads */
+  ATTN_PHASE_DQ = 3,       /* dQ */
+  ATTN_PHASE_REDUCE = 4,   /* fixed-order sum of split dK / dV partials */
+  ATTN_PHASES = 5
+} attn_phase;
+
+/* attn_varlen_full_vjp with per-phase timing.  `events` is NULL or holds
+ * ATTN_PHASES + 1 hipEvent_t handles created by the caller; event i is
+ * recorded on `stream` right before phase i is enqueued and event
+ * ATTN_PHASES after the last one, so the elapsed time between events i and
+ * i + 1 is phase i.  The computation is identical to attn_varlen_full_vjp. */
+attn_status attn_varlen_full_vjp_timed(const attn_problem* p,
+                                       const attn_tensor* q, const attn_tensor* k,
+                                       const attn_tensor* v, const attn_tensor* dout,
+                                       const attn_tensor* out, const attn_tensor* dq,
+                                       const attn_tensor* dk, const attn_tensor* dv, float* lse,
+                                       void* workspace, size_t workspace_bytes,
+                                       attn_stream_t stream, void* const* events);
+
 /* Synchronises `stream` and reports the device-side cu_q / cu_k check of the
  * last call that used `workspace`: ATTN_OK or ATTN_BAD_SEQLENS. */
 attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream);

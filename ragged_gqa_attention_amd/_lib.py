@@ -26,11 +26,15 @@ ENTRY_FWD = 0
 ENTRY_BWD = 1
 ENTRY_FULL_VJP = 2
 
+# phases of the full-VJP call, in launch order
+PHASES = ("plan", "fwd", "dkdv", "dq", "reduce")
+
 EXPORTED = (
     "attn_varlen_workspace_size",
     "attn_varlen_fwd",
     "attn_varlen_bwd",
     "attn_varlen_full_vjp",
+    "attn_varlen_full_vjp_timed",
     "attn_varlen_check_plan",
     "attn_status_string",
     "attn_last_error",
@@ -96,13 +100,16 @@ def load() -> ctypes.CDLL:
         lib.attn_varlen_bwd.argtypes = [P(AttnProblem), T, T, T, T, fp, T, T, T, T, vp, sz, vp]
         lib.attn_varlen_full_vjp.argtypes = [P(AttnProblem), T, T, T, T, T, T, T, T, fp,
                                              vp, sz, vp]
+        lib.attn_varlen_full_vjp_timed.argtypes = lib.attn_varlen_full_vjp.argtypes + [
+            P(ctypes.c_void_p)]
         lib.attn_varlen_check_plan.argtypes = [vp, vp]
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
         lib.attn_last_error.restype = ctypes.c_char_p
         for name in ("attn_varlen_workspace_size", "attn_varlen_fwd", "attn_varlen_bwd",
-                     "attn_varlen_full_vjp", "attn_varlen_check_plan"):
+                     "attn_varlen_full_vjp", "attn_varlen_full_vjp_timed",
+                     "attn_varlen_check_plan"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib

@@ -174,12 +174,22 @@ class FullVJP:
         self.ws = _workspace(workspace_size(self.prob, _lib.ENTRY_FULL_VJP), dev)
         self.device = dev
         self._fn = _lib.load().attn_varlen_full_vjp
+        self._fn_timed = _lib.load().attn_varlen_full_vjp_timed
 
-    def __call__(self, stream=None):
+    def __call__(self, stream=None, events=None):
+        """Enqueue one call.  ``events``: optional list of len(PHASES) + 1 recorded
+        torch.cuda.Event(enable_timing=True); event i brackets the start of phase i."""
         s = ctypes.c_void_p(stream if stream is not None
                             else torch.cuda.current_stream(self.device).cuda_stream)
-        st = self._fn(ctypes.byref(self.prob), *[ctypes.byref(t) for t in self.views],
-                      _fptr(self.lse), ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), s)
+        args = [ctypes.byref(self.prob)] + [ctypes.byref(t) for t in self.views] + [
+            _fptr(self.lse), ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel(), s]
+        if events is None:
+            st = self._fn(*args)
+        else:
+            if len(events) != len(_lib.PHASES) + 1:
+                raise ValueError("need one event per phase plus a final one")
+            handles = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+            st = self._fn_timed(*args, handles)
         _lib.raise_for(st, "attn_varlen_full_vjp")
         return self.out, self.dq, self.dk, self.dv
 

@@ -57,7 +57,7 @@ int device_cus() {
 
 struct Layout {
   size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag;
-  size_t lse, delta, part_dk, part_dv;
+  size_t lse, lres, delta, part_dk, part_dv;
   size_t total;
   int64_t max_units;
   int64_t row_tiles;
@@ -84,8 +84,11 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_seq = take(sizeof(int) * B);
   L.kv_off = take(sizeof(int) * (B + 1));
   L.kv_rank = take(sizeof(int) * B);
-  L.lse = L.delta = L.part_dk = L.part_dv = 0;
-  if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
+  L.lse = L.lres = L.delta = L.part_dk = L.part_dv = 0;
+  if (entry == ATTN_ENTRY_FULL_VJP) {
+    L.lse = take(sizeof(float) * rows);
+    L.lres = take(sizeof(float) * rows);
+  }
   if (entry != ATTN_ENTRY_FWD) {
     L.delta = take(sizeof(float) * rows);
     const size_t part = sizeof(float) * (size_t)L.max_units * KEY_TILE * HEAD_DIM;
@@ -195,8 +198,13 @@ void set_view(const attn_tensor* t, uint16_t** data, int64_t* ts, int64_t* hs) {
 }
 
 // Shared prologue: checks, workspace, plan launch.  Fills `a` and `L`.
+attn_status record(const hipEvent_t* ev, int i, hipStream_t s) {
+  if (!ev) return ATTN_OK;
+  return hip_status(hipEventRecord(ev[i], s), "event record");
+}
+
 attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes,
-                     hipStream_t s, AttnArgs& a, Layout& L) {
+                     hipStream_t s, AttnArgs& a, Layout& L, const hipEvent_t* ev = nullptr) {
   RGA_TRY(check_problem(p));
   const int cus = device_cus();
   L = make_layout(p, entry, cus);
@@ -230,6 +238,7 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.target_units = cus * UNITS_PER_CU;
   pa.min_chunk = MIN_CHUNK_ROWS;
   pa.plan = a.plan;
+  RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
   return hip_status(launch_plan(pa, s), "plan launch");
 }
 
@@ -243,12 +252,16 @@ attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn
 
 // dK/dV, dQ and the partial reduction, after lse and delta are in place.
 attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layout& L,
-                            hipStream_t s) {
+                            hipStream_t s, const hipEvent_t* ev = nullptr) {
   const bool cap = p->softcap > 0.0f;
-  if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
-  RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles, s), "dQ launch"));
-  RGA_TRY(hip_status(launch_kv_reduce(a, p->dtype, s), "dK/dV reduce launch"));
+  if (p->batch > 0) {
+    RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
+    RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
+    RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
+    RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles, s), "dQ launch"));
+    RGA_TRY(record(ev, ATTN_PHASE_REDUCE, s));
+    RGA_TRY(hip_status(launch_kv_reduce(a, p->dtype, s), "dK/dV reduce launch"));
+  }
   return ATTN_OK;
 }
 
@@ -322,12 +335,13 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   return launch_backward(p, a, L, s);
 }
 
-attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,
-                                 const attn_tensor* k, const attn_tensor* v,
-                                 const attn_tensor* dout, const attn_tensor* out,
-                                 const attn_tensor* dq, const attn_tensor* dk,
-                                 const attn_tensor* dv, float* lse, void* workspace,
-                                 size_t workspace_bytes, attn_stream_t stream) {
+attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor* q,
+                                       const attn_tensor* k, const attn_tensor* v,
+                                       const attn_tensor* dout, const attn_tensor* out,
+                                       const attn_tensor* dq, const attn_tensor* dk,
+                                       const attn_tensor* dv, float* lse, void* workspace,
+                                       size_t workspace_bytes, attn_stream_t stream,
+                                       void* const* events) {
   g_last_error.clear();
   RGA_TRY(check_problem(p));
   RGA_TRY(check_inputs(p, q, k, v));
@@ -336,10 +350,15 @@ attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,
   RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
   RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
   RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  if (events) {
+    for (int i = 0; i <= ATTN_PHASES; ++i)
+      if (!events[i]) return fail(ATTN_INVALID_ARG, "events[%d] is NULL", i);
+  }
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
   Layout L;
-  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, s, a, L));
+  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, s, a, L, ev));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
   set_view(k, &a.k, &a.k_ts, nullptr);
   set_view(v, &a.v, &a.v_ts, nullptr);
@@ -349,10 +368,28 @@ attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
-  if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),
-                     "forward launch"));
-  return launch_backward(p, a, L, s);
+  a.lres = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lres);
+  RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+  if (p->batch > 0)
+    RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),
+                       "forward launch"));
+  RGA_TRY(launch_backward(p, a, L, s, ev));
+  if (p->batch == 0) {
+    RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
+    RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
+    RGA_TRY(record(ev, ATTN_PHASE_REDUCE, s));
+  }
+  return record(ev, ATTN_PHASES, s);
+}
+
+attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,
+                                 const attn_tensor* k, const attn_tensor* v,
+                                 const attn_tensor* dout, const attn_tensor* out,
+                                 const attn_tensor* dq, const attn_tensor* dk,
+                                 const attn_tensor* dv, float* lse, void* workspace,
+                                 size_t workspace_bytes, attn_stream_t stream) {
+  return attn_varlen_full_vjp_timed(p, q, k, v, dout, out, dq, dk, dv, lse, workspace,
+                                    workspace_bytes, stream, nullptr);
 }
 
 attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream) {

@@ -79,6 +79,17 @@ template <> __device__ __forceinline__ float hi_f<BF16>(uint32_t w) {
   return __builtin_bit_cast(float, w & 0xffff0000u);
 }
 
+// acc + (lo + hi) of a packed pair of 16-bit values, as one v_dot2 with ones.
+template <class T> __device__ __forceinline__ float add_pair(uint32_t w, float acc);
+template <> __device__ __forceinline__ float add_pair<F16>(uint32_t w, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), one, acc, false);
+}
+template <> __device__ __forceinline__ float add_pair<BF16>(uint32_t w, float acc) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), one, acc, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

@@ -1,27 +1,39 @@
-// Forward kernel: online-softmax attention over folded (token, head) rows.
+// Forward kernel: softmax attention over folded (token, head) rows.
 //
 // Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "What
 // You Have": logits are (scale_multiplier / sqrt(D)) q.k, soft-capped to
 // c tanh(x / c), shifted by -slope[b,h] |i + Lk - Lq - j|, then softmax-ed over
 // the sequence's keys.  Page "python-20261012-ragged-flash-attention-gradient-
-// recompute", section "Root causes addressed": keep a running max m and sum l
-// per row, store only O and L = m + log l.
+// recompute", section "Root causes addressed": stream over key tiles and store
+// only O and L = m + log l.
 //
-// Because every query head shares the one K/V head, the Lq x Hq rows of a
-// sequence are folded into one M dimension (row r = token * Hq + head), so a
-// workgroup's 128 rows reuse each staged K/V tile 128 times.  Each wave owns
-// 32 rows and computes S^T = K Q^T (keys x rows) with Q held in registers, so
-// an accumulator lane owns one row: the row max / sum need only the lane pair
-// (l, l ^ 32), and O^T = V^T P^T keeps the rescale per lane.
+// Every query head shares the one K/V head, so the Lq x Hq rows of a sequence
+// are folded into one M dimension (row = token * Hq + head): a workgroup's 256
+// rows reuse each staged K/V tile 256 times.  Each wave owns 32 rows and forms
+// S^T = K Q^T (keys x rows, Q in registers), so an accumulator lane owns one row
+// and O^T = V^T P^T keeps the row scale per lane.
+//
+// Softmax offset.  Distances are measured from the clamped centre
+// c_i = max(i + Lk - Lq, 0): for a row with i + Lk - Lq < 0 every key lies to
+// its right, so |i + Lk - Lq - j| = j + dmin_i with dmin_i = Lq - Lk - i, and the
+// constant slope * dmin_i moves into the row offset
+//   m_i = c - slope * dmin_i   (capped; without a cap, -slope * dmin_i).
+// With a cap every logit of row i is at most m_i, so m_i is used as the softmax
+// offset fixed before the key loop: P = exp(a - m) <= 1, the nearest key keeps
+// P >= e^{-2c}, and no running maximum, rescale or cross-lane max is needed
+// (the normalised result is the same as with the true maximum).  Without a cap
+// a running maximum relative to m_i is kept.  The row statistic is stored as
+// L = m_i + log l (natural log) and, for the backward, as the small residual
+// log2 l relative to m_i, so the backward never subtracts two large numbers.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
 template <class T, bool CAP, bool DELTA>
-__global__ __launch_bounds__(WG_THREADS) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KEY_STEP * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[HEAD_DIM * LDT];
+__global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KEY_STEP * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KEY_STEP * LDV];
 
   const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
   if (rank < 0) return;
@@ -39,96 +51,131 @@ __global__ __launch_bounds__(WG_THREADS) void fwd_kernel(const AttnArgs a) {
   const int ti = rr / a.hq;
   const int hh = rr - ti * a.hq;
 
-  // Q row as B operand: k-step ks covers features 16ks + 8g .. +7.
-  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs;
+  // Q row as B operand: k-step ks covers features 16ks + 8g .. +7
+  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
   u32x4 qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = load16(qrow + ks * 16 + g * 8);
+  for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = load16(qrow + ks * 16);
 
   const float slope2 = a.slopes[(int64_t)b * a.slopes_stride + hh] * LOG2E;
-  // distance of key j is |cpos - j|; this lane's keys in block kb are
-  // kbase + 32 kb + 8 (r/4) + 4 g + r%4.
-  const float cpos = (float)(ti + Lk - Lq) - (float)(4 * g);
-
-  float m = -__builtin_inff();
-  float lsum = 0.0f;
+  // key j of accumulator register r in block kb of the tile at kbase is
+  // kbase + 32 kb + 8 (r/4) + 4 g + r%4; cb0 - (kbase + 32 kb + 8 (r/4) + r%4)
+  // is then j's signed distance from the clamped centre max(i + Lk - Lq, 0)
+  const float cb0 = (float)(max(ti + Lk - Lq, 0) - 4 * g);
+  const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - ti);
+  float m = CAP ? 0.0f : -__builtin_inff();       // log2 units, relative to moff
+  float lsum = 0.0f;     // exact sum of P
+  float lsum_r = 0.0f;   // sum of P rounded to the input dtype
   f32x16 O[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) O[db] = f32x16{};
 
   const int ntiles = (Lk + KEY_STEP - 1) / KEY_STEP;
+  PairStager<ROW_THREADS, KEY_STEP> st;
+  if (ntiles > 0) {
+    st.load_keys(a.k, a.k_ts, a.v, a.v_ts, k0, min(Lk, KEY_STEP));
+    st.template store<LDK, LDV>(Ks[0], Vs[0]);
+  }
+  __syncthreads();
+
   for (int kt = 0; kt < ntiles; ++kt) {
     const int kbase = kt * KEY_STEP;
-    __syncthreads();
-    stage_keys_rowmajor(Ks, a.k, a.k_ts, k0, Lk, kbase);
-    stage_keys_transposed<false>(Vt, nullptr, a.v, a.v_ts, k0, Lk, kbase);
-    __syncthreads();
+    const bool more = kt + 1 < ntiles;
+    if (more)
+      st.load_keys(a.k, a.k_ts, a.v, a.v_ts, (int64_t)k0 + kbase + KEY_STEP,
+                   Lk - kbase - KEY_STEP);
+    const uint16_t* Kb = Ks[kt & 1];
+    const uint16_t* Vb = Vs[kt & 1];
 
     f32x16 S[2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       S[kb] = f32x16{};
-      const uint16_t* kp = Ks + (kb * 32 + l32) * LDK + g * 8;
+      const uint16_t* kp = Kb + (kb * 32 + l32) * LDK + g * 8;
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks)
         S[kb] = mfma32<T>(load16(kp + ks * 16), qf[ks], S[kb]);
     }
 
-    // logits, masked past the sequence end
-    float tmax = -__builtin_inff();
+    const float cb = cb0 - (float)kbase;
+    const bool full = kbase + KEY_STEP <= Lk;
+    const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);       // key offset without 4g
-        float rc;
-        float x = logit2<CAP>(S[kb][r], slope2, cpos - (float)(kbase + jl), a.lc, rc);
-        x = (kbase + jl + 4 * g < Lk) ? x : -__builtin_inff();
+        const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+        float x;
+        if (CAP)
+          x = __builtin_fmaf(a.lc.t_mul, cap_r(S[kb][r], a.lc),
+                             -slope2 * __builtin_fabsf(cb - (float)jl));
+        else
+          x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
+        if (!full) x = jl < kleft ? x : -__builtin_inff();
         S[kb][r] = x;
-        tmax = __builtin_fmaxf(tmax, x);
       }
     }
-    tmax = __builtin_fmaxf(tmax, swap_half(tmax));
-    const float mnew = __builtin_fmaxf(m, tmax);
-    const float alpha = fast_exp2(m - mnew);
-    m = mnew;
+    if (!CAP) {
+      float tmax = -__builtin_inff();
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tmax = __builtin_fmaxf(tmax, S[kb][r]);
+      tmax = __builtin_fmaxf(tmax, swap_half(tmax));
+      const float mnew = __builtin_fmaxf(m, tmax);
+      const float alpha = fast_exp2(m - mnew);
+      m = mnew;
+      lsum *= alpha;
+      lsum_r *= alpha;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) O[db] *= alpha;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[kb][r] -= mnew;
+    }
 
-    float psum = 0.0f;
+    // P rounded to the input dtype feeds the PV product, and O is normalised by
+    // the sum of those same rounded values (lsum_r), so O is an exact convex
+    // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
+    // matches dP.  L and the backward's residual use the exact FP32 sum.
     u32x4 pb[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(S[kb][r] - mnew);
-        psum += p;
+        const float p = fast_exp2(S[kb][r]);
+        lsum += p;
         S[kb][r] = p;
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
+      for (int s = 0; s < 2; ++s) {
         pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
                           pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
                           pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
                           pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
-    }
-    lsum = lsum * alpha + psum;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) O[db] *= alpha;
+        for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
+      }
+    }
 
     // O^T[d][row] += V^T[d][keys] P^T[keys][row]
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
-      const uint16_t* vp = Vt + (db * 32 + l32) * LDT + g * 4;
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          O[db] = mfma32<T>(read_perm_a(vp + kb * 32 + s * 16), pb[kb][s], O[db]);
-    }
+          O[db] = mfma32<T>(read_tr_a<LDV>(Vb, kb * 32 + s * 16, db * 32, lane), pb[kb][s], O[db]);
+
+    if (more) st.template store<LDK, LDV>(Ks[(kt + 1) & 1], Vs[(kt + 1) & 1]);
+    __syncthreads();
   }
 
   // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta
   lsum += swap_half(lsum);
-  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  lsum_r += swap_half(lsum_r);
+  const float inv = lsum_r > 0.0f ? 1.0f / lsum_r : 0.0f;
   uint16_t* orow = a.out + (int64_t)(q0 + ti) * a.o_ts + (int64_t)hh * a.o_hs + g * 4;
   const uint16_t* dorow = nullptr;
   if (DELTA) dorow = a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)hh * a.do_hs + g * 4;
@@ -151,7 +198,9 @@ __global__ __launch_bounds__(WG_THREADS) void fwd_kernel(const AttnArgs a) {
   if (DELTA) dsum += swap_half(dsum);
   if (row_ok && g == 0) {
     const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
-    a.lse[ri] = lsum > 0.0f ? (m + fast_log2(lsum)) * LN2 : -__builtin_inff();
+    const float res = m + fast_log2(lsum);
+    a.lse[ri] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
+    if (a.lres) a.lres[ri] = lsum > 0.0f ? res : 0.0f;
     if (DELTA) a.delta[ri] = dsum;
   }
 }
@@ -160,11 +209,11 @@ template <class T>
 static hipError_t launch_fwd_t(const AttnArgs& a, bool cap, bool with_delta, int grid,
                                hipStream_t s) {
   if (cap) {
-    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, true, true>), grid, WG_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, true, false>), grid, WG_THREADS, 0, s, a);
+    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a);
   } else {
-    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, false, true>), grid, WG_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, false, false>), grid, WG_THREADS, 0, s, a);
+    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((fwd_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a);
   }
   return hipGetLastError();
 }

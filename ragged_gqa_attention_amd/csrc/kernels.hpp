@@ -8,9 +8,13 @@
 
 namespace rga {
 
-// Row-tile kernels (forward, dQ): one workgroup = 4 waves x 32 folded rows.
-constexpr int ROW_TILE = 128;
+// Row-tile kernels (forward, dQ): one workgroup = 8 waves x 32 folded rows,
+// two waves per SIMD so one wave's VALU work overlaps the other's MFMA.
+constexpr int ROW_WAVES = 8;
+constexpr int ROW_THREADS = ROW_WAVES * 64;
+constexpr int ROW_TILE = ROW_WAVES * 32;
 // Key-tile kernel (dK/dV): one workgroup = 4 waves x 32 keys.
+constexpr int KV_THREADS = 256;
 constexpr int KEY_TILE = 128;
 // Folded rows staged per step of the dK/dV kernel.
 constexpr int KV_ROW_STEP = 32;
@@ -27,6 +31,10 @@ struct AttnArgs {
   uint16_t* dk;         int64_t dk_ts;
   uint16_t* dv;         int64_t dv_ts;
   float* lse;           // [total_q * hq], natural log
+  // [total_q * hq] or null: log2 of the row's softmax sum relative to the row
+  // offset m_i (see fwd.hip).  The forward writes it when non-null; the
+  // backward uses it when non-null and derives it from lse otherwise.
+  float* lres;
   float* delta;         // [total_q * hq], rowsum(dout * out)
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;

@@ -15,6 +15,7 @@
 namespace rga {
 
 constexpr int PLAN_THREADS = 256;
+constexpr int WG_THREADS = 256;          // reduce and row-dot kernels
 constexpr int PLAN_SORT_LIMIT = 8192;   // larger batches keep their natural order
 
 __device__ __forceinline__ long long block_sum(long long v, long long* red) {

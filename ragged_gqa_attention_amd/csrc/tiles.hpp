@@ -1,9 +1,15 @@
-// Global -> LDS staging of key tiles for the row-tile kernels (forward, dQ).
+// LDS tiles, operand reads and the logit pipeline shared by the gfx950 kernels.
 //
-// A key tile holds KEY_STEP consecutive keys of one sequence.  Keys at or past
-// the sequence end are written as zeros: the padding of the packed views is
-// arbitrary (NaN in the tests), and 0 * NaN would poison the MFMA sums even
-// where the softmax weight is exactly zero.
+// Every tile lives in LDS row-major (16-byte chunks of a 160-element row).  A
+// product that contracts over the rows of a tile (P^T V, dS^T Q, P^T dO,
+// dS K) reads its A operand with ds_read_b64_tr_b16, the CDNA4 transposing LDS
+// read: inside each group of 16 lanes, lane i receives element i % 4 of the
+// 8-byte words addressed by lanes 4e + i / 4 (e = 0..3).  So no transposed
+// copy of any tile is ever written.
+//
+// Rows at or past a sequence's end are staged as zeros: the padding of the
+// packed views is arbitrary (NaN in the tests) and 0 * NaN would poison MFMA
+// sums even where the softmax weight is exactly zero.
 #pragma once
 
 #include "common.hpp"
@@ -11,86 +17,106 @@
 
 namespace rga {
 
-constexpr int WG_THREADS = 256;
-// Row-major key tile [KEY_STEP][LDK]: +8 halves keeps the 16-byte reads of 32
-// consecutive rows on distinct LDS banks.
+// Row stride of the LDS tiles read with 16-byte row reads (b128): 336 bytes puts
+// the rows of each 8-lane phase on distinct 16-byte bank slots.
 constexpr int LDK = HEAD_DIM + 8;
-// Transposed key tile [HEAD_DIM][LDT]: +4 halves (34 dwords per row) keeps the
-// 8-byte reads of 16 consecutive feature rows on distinct banks.
-constexpr int LDT = KEY_STEP + 4;
+// Row stride of tiles read only through the transposing read: 352 bytes puts
+// the four rows of each 16-lane group on distinct 32-byte bank slots.
+constexpr int LDV = HEAD_DIM + 16;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-// Row-major copy of keys [kbase, kbase + KEY_STEP) of a sequence starting at
-// token k0 with Lk keys.  Consecutive threads take consecutive 16-byte chunks
-// of a row, so each wave reads whole rows.
-__device__ __forceinline__ void stage_keys_rowmajor(uint16_t* __restrict__ dst,
-                                                    const uint16_t* __restrict__ src,
-                                                    int64_t ts, int k0, int Lk, int kbase) {
-  for (int t = threadIdx.x; t < KEY_STEP * CHUNKS; t += WG_THREADS) {
-    const int key = t / CHUNKS;
-    const int c = t - key * CHUNKS;
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (kbase + key < Lk) val = load16(src + (int64_t)(k0 + kbase + key) * ts + c * 8);
-    *reinterpret_cast<u32x4*>(dst + key * LDK + c * 8) = val;
-  }
+__device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
 }
 
-// Transposed copy dst[d][key] (stride LDT), optionally also the row-major copy
-// into rm (stride LDK).  A task is a pair of keys times one 16-byte chunk, so
-// each LDS write of the transposed tile is a full 32-bit word.
-template <bool ALSO_ROWMAJOR>
-__device__ __forceinline__ void stage_keys_transposed(uint16_t* __restrict__ dst,
-                                                      uint16_t* __restrict__ rm,
-                                                      const uint16_t* __restrict__ src,
-                                                      int64_t ts, int k0, int Lk, int kbase) {
-  constexpr int PAIRS = KEY_STEP / 2;
-  for (int t = threadIdx.x; t < PAIRS * CHUNKS; t += WG_THREADS) {
-    const int kp = t % PAIRS;
-    const int c = t / PAIRS;
-    const int key = 2 * kp;
-    u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-    if (kbase + key < Lk) a = load16(src + (int64_t)(k0 + kbase + key) * ts + c * 8);
-    if (kbase + key + 1 < Lk) b = load16(src + (int64_t)(k0 + kbase + key + 1) * ts + c * 8);
-    uint16_t* col = dst + (c * 8) * LDT + key;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      *reinterpret_cast<uint32_t*>(col + (2 * e) * LDT) = interleave_lo(a[e], b[e]);
-      *reinterpret_cast<uint32_t*>(col + (2 * e + 1) * LDT) = interleave_hi(a[e], b[e]);
-    }
-    if (ALSO_ROWMAJOR) {
-      *reinterpret_cast<u32x4*>(rm + key * LDK + c * 8) = a;
-      *reinterpret_cast<u32x4*>(rm + (key + 1) * LDK + c * 8) = b;
-    }
-  }
-}
-
-// A operand of a 32x32x16 product whose k index runs over keys of a transposed
-// tile: lane (row l32 of the block, group g) takes keys {16s + 4g + 0..3,
-// 16s + 8 + 4g + 0..3} of k-step s, matching the k order of an accumulator
-// reused as B operand.
-__device__ __forceinline__ u32x4 read_perm_a(const uint16_t* rowp) {
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(rowp);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(rowp + 8);
+// A operand of a 32x32x16 product that contracts over tile rows: lane
+// (l32, g) receives X[r0 + 4g + 0..3][c0 + l32] and X[r0 + 8 + 4g + 0..3][c0 + l32],
+// the k order of an accumulator (rows 8(r/4) + 4g + r%4) reused as B operand.
+template <int LD>
+__device__ __forceinline__ u32x4 read_tr_a(const uint16_t* X, int r0, int c0, int lane) {
+  const int i = lane & 15;
+  const int G = lane >> 4;
+  const uint16_t* p = X + (r0 + 4 * (G >> 1) + (i >> 2)) * LD + c0 + 16 * (G & 1) + 4 * (i & 3);
+  const u32x2 lo = read_tr(p);
+  const u32x2 hi = read_tr(p + 8 * LD);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
-// Logit x (base-2 units) from a raw dot product; also returns r = 1/(1+e^{2y})
-// needed by the soft-cap derivative 1 - tanh^2 = 4 r (1 - r).
-template <bool CAP>
-__device__ __forceinline__ float logit2(float dot, float slope2, float dist, const LogitConsts& lc,
-                                        float& r) {
-  float t2;
-  if (CAP) {
-    r = fast_rcp(1.0f + fast_exp2(dot * lc.k_exp));
-    t2 = __builtin_fmaf(lc.t_mul, r, lc.t_add);
-  } else {
-    r = 0.5f;
-    t2 = dot * lc.s_lin;
+// Row-major staging of up to two 160-wide sources into LDS through registers:
+// load() issues the global reads for the next tile, store() writes them once
+// the current tile's compute no longer needs the buffer.  Each thread owns
+// PER_THREAD 16-byte chunks; rows [0, ROWS) come from source 0 and rows
+// [ROWS, 2 ROWS) from source 1.
+template <int THREADS, int ROWS>
+struct PairStager {
+  static constexpr int TASKS = 2 * ROWS * CHUNKS;
+  static constexpr int PER_THREAD = TASKS / THREADS;
+  static_assert(TASKS % THREADS == 0, "tile chunks must divide evenly over the threads");
+  u32x4 reg[PER_THREAD];
+
+  // rows of a key tile: row r of source s is token base + r, valid if r < valid
+  __device__ __forceinline__ void load_keys(const uint16_t* s0, int64_t ts0, const uint16_t* s1,
+                                            int64_t ts1, int64_t base, int valid) {
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int t = threadIdx.x + u * THREADS;
+      const int which = t >= ROWS * CHUNKS;
+      const int tt = t - which * ROWS * CHUNKS;
+      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
+      const uint16_t* src = which ? s1 : s0;
+      const int64_t ts = which ? ts1 : ts0;
+      reg[u] = u32x4{0u, 0u, 0u, 0u};
+      if (r < valid) reg[u] = load16(src + (base + r) * ts + c * 8);
+    }
   }
-  return __builtin_fmaf(-slope2, __builtin_fabsf(dist), t2);
+
+  // rows of a folded (token, head) tile: folded row R = row0 + r, token R / hq,
+  // head R % hq; valid if R < row_end
+  __device__ __forceinline__ void load_rows(const uint16_t* s0, int64_t ts0, int64_t hs0,
+                                            const uint16_t* s1, int64_t ts1, int64_t hs1,
+                                            int q0, int hq, int row0, int row_end) {
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int t = threadIdx.x + u * THREADS;
+      const int which = t >= ROWS * CHUNKS;
+      const int tt = t - which * ROWS * CHUNKS;
+      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
+      const int R = row0 + r;
+      reg[u] = u32x4{0u, 0u, 0u, 0u};
+      if (R < row_end) {
+        const int tok = R / hq, h = R - tok * hq;
+        reg[u] = which ? load16(s1 + (int64_t)(q0 + tok) * ts1 + (int64_t)h * hs1 + c * 8)
+                       : load16(s0 + (int64_t)(q0 + tok) * ts0 + (int64_t)h * hs0 + c * 8);
+      }
+    }
+  }
+
+  template <int LD0, int LD1>
+  __device__ __forceinline__ void store(uint16_t* d0, uint16_t* d1) const {
+#pragma unroll
+    for (int u = 0; u < PER_THREAD; ++u) {
+      const int t = threadIdx.x + u * THREADS;
+      const int which = t >= ROWS * CHUNKS;
+      const int tt = t - which * ROWS * CHUNKS;
+      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
+      uint16_t* dst = which ? d1 + r * LD1 : d0 + r * LD0;
+      *reinterpret_cast<u32x4*>(dst + c * 8) = reg[u];
+    }
+  }
+};
+
+// Capped logit pieces from a raw dot product q.k (see LogitConsts):
+//   r = 1 / (1 + e^{2 s / c}),   c tanh(s / c) log2(e) = t_add + t_mul * r,
+// and 1 - tanh^2(s / c) = 4 r (1 - r).
+__device__ __forceinline__ float cap_r(float dot, const LogitConsts& lc) {
+  return fast_rcp(1.0f + fast_exp2(dot * lc.k_exp));
 }
 
 }  // namespace rga
