@@ -62,7 +62,7 @@ def cpu_baseline(wl, seconds: float):
     """The float64 oracle, unchanged, on the first sequences of the workload
     until about `seconds` of CPU time."""
     import oracle
-    from ragged_gqa_attention_amd.workloads import oracle_inputs
+    from workloads import oracle_inputs
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -107,14 +107,14 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for {max(args.gpus, world)}): the "
-              "path is one GPU's share; multi-GPU sharding is described in DESIGN.md "
-              "and not built.", file=sys.stderr)
+              "path is one GPU's share of the batch and no multi-GPU sharding is built.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
     import ragged_gqa_attention_amd as rga
     from ragged_gqa_attention_amd import _lib
-    from ragged_gqa_attention_amd.workloads import make_workload
+    from workloads import make_workload
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

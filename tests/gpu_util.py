@@ -15,7 +15,7 @@ import torch
 
 import oracle
 import ragged_gqa_attention_amd as rga
-from ragged_gqa_attention_amd import workloads as W
+import workloads as W
 
 TOL = {torch.float16: 1e-2, torch.bfloat16: 2e-2}
 

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import ragged_gqa_attention_amd as rga
-from ragged_gqa_attention_amd import workloads as W
+import workloads as W
 from tests.gpu_util import (TOL, assert_close, assert_lse, gpu_full, need_gpu, oracle_full, say,
                             to_np)
 

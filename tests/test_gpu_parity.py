@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from ragged_gqa_attention_amd import workloads as W
+import workloads as W
 from tests.gpu_util import (TOL, assert_close, assert_lse, check_full, gpu_full, need_gpu,
                             say, to_np)
 
