@@ -56,8 +56,8 @@ int device_cus() {
 }
 
 struct Layout {
-  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag;
-  size_t lse, lres, delta, part_dk, part_dv;
+  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero;
+  size_t lse, rowinfo, part_dk, part_dv;
   size_t total;
   int64_t max_units;
   int64_t row_tiles;
@@ -78,19 +78,17 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
     return at;
   };
   L.flag = take(sizeof(int) * 4);   // first, so attn_varlen_check_plan can find it
+  L.zero = take(256);
   L.seq = take(sizeof(int) * B * SEQ_FIELDS);
   L.fwd_seq = take(sizeof(int) * B);
   L.fwd_off = take(sizeof(int) * (B + 1));
   L.kv_seq = take(sizeof(int) * B);
   L.kv_off = take(sizeof(int) * (B + 1));
   L.kv_rank = take(sizeof(int) * B);
-  L.lse = L.lres = L.delta = L.part_dk = L.part_dv = 0;
-  if (entry == ATTN_ENTRY_FULL_VJP) {
-    L.lse = take(sizeof(float) * rows);
-    L.lres = take(sizeof(float) * rows);
-  }
+  L.lse = L.rowinfo = L.part_dk = L.part_dv = 0;
+  if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
-    L.delta = take(sizeof(float) * rows);
+    L.rowinfo = take(sizeof(float) * 4 * rows);
     const size_t part = sizeof(float) * (size_t)L.max_units * KEY_TILE * HEAD_DIM;
     L.part_dk = take(part);
     L.part_dv = take(part);
@@ -143,6 +141,14 @@ attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens,
       (t->head_stride & 7) != 0)
     return fail(ATTN_MISALIGNED, "%s pointer or strides are not 16-byte multiples", name);
   return ATTN_OK;
+}
+
+// Multiplier and shift for n / d with 0 <= n < 2^31 (see fast_div).
+void fast_div_consts(uint32_t d, uint32_t* mul, uint32_t* shift) {
+  uint32_t sh = 0;
+  while ((1ull << sh) < d) ++sh;
+  *shift = sh;
+  *mul = (uint32_t)((((1ull << sh) - d) << 32) / d + 1);
 }
 
 LogitConsts logit_consts(const attn_problem* p) {
@@ -217,13 +223,15 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.slopes = p->alibi_slopes;
   a.slopes_stride = p->slopes_stride;
   a.hq = p->hq;
+  fast_div_consts((uint32_t)p->hq, &a.hq_mul, &a.hq_shift);
   a.batch = p->batch;
   a.total_q = p->total_q;
   a.total_k = p->total_k;
   a.lc = logit_consts(p);
   a.plan = plan_view(ws, L);
   char* base = static_cast<char*>(ws);
-  if (L.delta) a.delta = reinterpret_cast<float*>(base + L.delta);
+  a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
+  if (L.rowinfo) a.rowinfo = reinterpret_cast<float*>(base + L.rowinfo);
   if (L.part_dk) {
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
     a.part_dv = reinterpret_cast<float*>(base + L.part_dv);
@@ -237,6 +245,7 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.total_k = p->total_k;
   pa.target_units = cus * UNITS_PER_CU;
   pa.min_chunk = MIN_CHUNK_ROWS;
+  pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;
   RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
   return hip_status(launch_plan(pa, s), "plan launch");
@@ -250,7 +259,7 @@ attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn
   return ATTN_OK;
 }
 
-// dK/dV, dQ and the partial reduction, after lse and delta are in place.
+// dK/dV, dQ and the partial reduction, after the row records are in place.
 attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layout& L,
                             hipStream_t s, const hipEvent_t* ev = nullptr) {
   const bool cap = p->softcap > 0.0f;
@@ -331,7 +340,7 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = const_cast<float*>(lse);
   if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_rowdot(a, p->dtype, s), "row-dot launch"));
+  RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
   return launch_backward(p, a, L, s);
 }
 
@@ -368,7 +377,6 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
-  a.lres = reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lres);
   RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
   if (p->batch > 0)
     RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),

@@ -133,6 +133,13 @@ struct Plan {
   int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation
 };
 
+// n / d for 0 <= n < 2^31 with a host-computed multiplier (round-up method of
+// Granlund and Montgomery, "Division by invariant integers using
+// multiplication", 1994): shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1.
+__device__ __forceinline__ int fast_div(int n, uint32_t mul, uint32_t shift) {
+  return (int)((__umulhi((uint32_t)n, mul) + (uint32_t)n) >> shift);
+}
+
 // Largest rank r with off[r] <= idx, or -1 when idx is past the last item.
 __device__ __forceinline__ int find_rank(const int* off, int nranks, int idx) {
   if (nranks <= 0 || idx >= off[nranks]) return -1;

@@ -1,0 +1,322 @@
+// dK / dV kernel: recompute P from the stored row record, then
+//   dP = dO V^T,  dS = P * (dP - Delta) * (1 - tanh^2(s / c)),
+//   dV = sum_rows P^T dO,  dK = sigma sum_rows dS^T Q,
+// summed over every folded (token, head) row of the sequence, i.e. over all
+// query heads that share the K/V head.
+//
+// Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "Hard
+// Constraints": the K/V gradients reduce over every query head sharing the K/V
+// head, and the cap sits between the scaled dot product and ALiBi, so its
+// derivative multiplies dP - Delta.  Page "python-20261012-ragged-flash-
+// attention-gradient-recompute", section "Root causes addressed": no
+// probability matrix is stored; each tile is rebuilt from L.
+//
+// With r = 1 / (1 + e^{2s/c}), 1 - tanh^2(s/c) = 4 r (1 - r); the kernel forms
+// r - r^2 and folds the factor 4 into the final sigma scale of dK.
+//
+// Work split.  A workgroup owns 128 keys of one sequence and a chunk of its
+// folded rows.  Its four waves form two pairs; a pair owns 64 keys and keeps
+// their K and V rows in registers (MFMA operands, lane = key).  Rows are
+// streamed 64 at a time through LDS.  In each step the two waves of a pair
+// each form S, dP, P and dS for one half of the rows (32 rows x 64 keys), then
+// trade halves through LDS: the first wave accumulates dV = P^T dO over all 64
+// rows, the second dK = dS^T Q.  Each wave thus holds one 64-key accumulator,
+// and every operand read from LDS feeds two MFMAs (one per 32-key block),
+// which halves LDS traffic per MFMA compared with one wave doing all four
+// products for 32 keys.  The sum over rows happens in registers in a fixed
+// order; sequences split into several row chunks write FP32 partials that a
+// separate pass adds in chunk order.  No atomics anywhere.
+//
+// Pipeline.  Q and dO tiles are copied global -> LDS with direct loads (no
+// staging registers) into three buffers: step n is read by the S/dP products,
+// step n - 1 by the dV/dK products (which run while the VALU forms P and dS of
+// step n) and step n + 1 is in flight.
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace rga {
+
+namespace {
+
+constexpr int KV_NBUF = 3;
+constexpr int STEP_SLOTS = KV_ROW_STEP * CHUNKS;     // 16-byte chunks per tensor per step
+constexpr int LOADS_PER_WAVE = STEP_SLOTS / 256;     // wave loads per tensor per step (5)
+static_assert(STEP_SLOTS % 256 == 0, "each wave load covers 64 slots; 4 waves share a tile");
+constexpr int TILE_ELEMS = KV_ROW_STEP * HEAD_DIM;
+
+struct KvShared {
+  uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (swizzled)
+  f32x4 rinfo[KV_NBUF][KV_ROW_STEP];     // row records of a step
+  u32x4 xch[2][4][4][64];                 // [slot][writer wave][kb * 2 + s][lane]
+};
+
+// What a workgroup works on: rows [row_begin, row_end) of sequence b against
+// keys [key0, key0 + 64) of the wave's pair.
+struct KvUnit {
+  int q0, k0, Lk, row_begin, row_end, key0, nchunk;
+};
+
+// The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
+template <class T, bool CAP, int ROLE>
+__device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const KvUnit& u,
+                                          int wave, int lane) {
+  const int l32 = lane & 31, g = lane >> 5;
+  const int hq = a.hq;
+
+  // K and V rows of the pair's 64 keys as B operands (lane = key); keys past
+  // the sequence end are zero and their results are never stored.
+  u32x4 kf[2][KSTEPS], vf[2][KSTEPS];
+  float keyf[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = u.key0 + kb * 32 + l32;
+    keyf[kb] = (float)key;
+    const bool ok = key < u.Lk;
+    const uint16_t* kr = a.k + (int64_t)(u.k0 + (ok ? key : 0)) * a.k_ts + g * 8;
+    const uint16_t* vr = a.v + (int64_t)(u.k0 + (ok ? key : 0)) * a.v_ts + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const u32x4 kx = load16(kr + ks * 16), vx = load16(vr + ks * 16);
+      kf[kb][ks] = ok ? kx : u32x4{0u, 0u, 0u, 0u};
+      vf[kb][ks] = ok ? vx : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // Direct loads of step rows [r0, r0 + 64): this wave fills slots
+  // (v * 4 + wave) * 64 + lane of the Q and dO tiles; wave 0 also loads the
+  // row records.  Rows past the chunk end read the zero block.
+  auto issue_loads = [&](int r0, int buf) {
+    if (wave == 0) {
+      const int R = r0 + lane;
+      const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, u.row_end - 1)) * 4;
+      load_lds16(R < u.row_end ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
+    }
+#pragma unroll
+    for (int v = 0; v < LOADS_PER_WAVE; ++v) {
+      const int slot0 = (v * 4 + wave) * 64;
+      int trow, tch;
+      swz_slot(slot0 + lane, trow, tch);
+      const int R = r0 + trow;
+      const int Rc = min(R, u.row_end - 1);
+      const int tok = fast_div(Rc, a.hq_mul, a.hq_shift);
+      const int h = Rc - tok * hq;
+      const uint16_t* sq = a.q + (int64_t)(u.q0 + tok) * a.q_ts + (int64_t)h * a.q_hs + tch * 8;
+      const uint16_t* sd = a.dout + (int64_t)(u.q0 + tok) * a.do_ts + (int64_t)h * a.do_hs + tch * 8;
+      const bool ok = R < u.row_end;
+      load_lds16(ok ? sq : a.zero, &sm.qd[buf][0][slot0 * 8]);
+      load_lds16(ok ? sd : a.zero, &sm.qd[buf][1][slot0 * 8]);
+    }
+  };
+
+  // Lane-constant LDS offsets (elements).  Row reads of the S / dP A operand:
+  // row ROLE * 32 + l32, logical chunk 2 ks + g; only ks % 2 changes the XOR.
+  const int arow = ROLE * 32 + l32;
+  const int sx = (l32 >> 2) & 3;
+  const int roff[2] = {arow * HEAD_DIM + 8 * (g ^ sx), arow * HEAD_DIM + 8 * ((2 + g) ^ sx)};
+  // Transposing reads (see read_tr_a): row 4 (G/2) + i/4 (+ 8), feature
+  // 16 (G%2) + 4 (i%4); every 16-row k-step and 32-feature block adds a constant.
+  const int ti = lane & 15, tG = lane >> 4;
+  const int trow0 = 4 * (tG >> 1) + (ti >> 2);
+  const int tcl = 2 * (tG & 1) + ((ti & 3) >> 1);
+  const int tin = 4 * (ti & 1);
+  const int toff_lo = trow0 * HEAD_DIM + 8 * (tcl ^ ((trow0 >> 2) & 3)) + tin;
+  const int toff_hi = (trow0 + 8) * HEAD_DIM + 8 * (tcl ^ (((trow0 + 8) >> 2) & 3)) + tin;
+  // row records of the lane's rows 8 (r/4) + 4 g + r%4 of the wave's half
+  const int rbase = ROLE * 32 + g * 4;
+
+  f32x16 acc[2][DBLK];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) acc[kb][db] = f32x16{};
+  u32x4 mine[2][2];   // own P (ROLE 0) or own dS (ROLE 1) of the previous step
+
+  // S[row][key] = Q K^T and dP[row][key] = dO V^T for this wave's 32 rows
+  auto scores = [&](int buf, f32x16 (&S)[2], f32x16 (&dP)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) { S[kb] = f32x16{}; dP[kb] = f32x16{}; }
+    const uint16_t* Qb = sm.qd[buf][0];
+    const uint16_t* Db = sm.qd[buf][1];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int off = roff[ks & 1] + 32 * (ks >> 1);
+      const u32x4 qa = load16(Qb + off);
+      const u32x4 da = load16(Db + off);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        S[kb] = mfma32<T>(qa, kf[kb][ks], S[kb]);
+        dP[kb] = mfma32<T>(da, vf[kb][ks], dP[kb]);
+      }
+    }
+  };
+
+  // P and dS of the wave's half; the own product's half stays in `mine`, the
+  // other goes to the partner through LDS slot `slot`.
+  auto pointwise_publish = [&](int buf, int slot, f32x16 (&S)[2], f32x16 (&dP)[2]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
+        float p, w;
+        if (CAP) {
+          const float rc = cap_r(S[kb][r], a.lc);
+          p = fast_exp2(__builtin_fmaf(a.lc.t_mul, rc, bias));
+          w = __builtin_fmaf(-rc, rc, rc);
+        } else {
+          p = fast_exp2(__builtin_fmaf(S[kb][r], a.lc.s_lin, bias));
+          w = 1.0f;
+        }
+        S[kb][r] = p;
+        dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4 pb = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
+                               pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
+                               pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
+                               pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
+        const u32x4 sb = u32x4{pack2<T>(dP[kb][8 * s + 0], dP[kb][8 * s + 1]),
+                               pack2<T>(dP[kb][8 * s + 2], dP[kb][8 * s + 3]),
+                               pack2<T>(dP[kb][8 * s + 4], dP[kb][8 * s + 5]),
+                               pack2<T>(dP[kb][8 * s + 6], dP[kb][8 * s + 7])};
+        mine[kb][s] = ROLE ? sb : pb;
+        sm.xch[slot][wave][kb * 2 + s][lane] = ROLE ? pb : sb;
+      }
+  };
+
+  // dV (ROLE 0) or dK (ROLE 1) over the 64 rows of a step: A = dO^T or Q^T
+  // read transposed from LDS; B = P or dS, from `mine` for the own half and
+  // from the partner's slot for the other.  k-step t covers rows 16t .. 16t + 15.
+  auto accumulate = [&](int buf, int slot) {
+    const uint16_t* X = sm.qd[buf][ROLE ? 0 : 1];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u32x4 B[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        B[kb] = (t >> 1) == ROLE ? mine[kb][t & 1] : sm.xch[slot][wave ^ 1][kb * 2 + (t & 1)][lane];
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const int off = 16 * t * HEAD_DIM + 32 * db;
+        const u32x2 lo = read_tr(X + toff_lo + off);
+        const u32x2 hi = read_tr(X + toff_hi + off);
+        const u32x4 A = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) acc[kb][db] = mfma32<T>(A, B[kb], acc[kb][db]);
+      }
+    }
+  };
+
+  const int nsteps = (u.row_end - u.row_begin + KV_ROW_STEP - 1) / KV_ROW_STEP;
+  issue_loads(u.row_begin, 0);
+  wait_vm();
+  __syncthreads();
+  if (nsteps > 1) issue_loads(u.row_begin + KV_ROW_STEP, 1);
+  f32x16 S[2], dP[2];
+  scores(0, S, dP);
+  pointwise_publish(0, 0, S, dP);
+  wait_vm();
+  __syncthreads();
+  int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
+  for (int n = 1; n < nsteps; ++n) {
+    if (n + 1 < nsteps) issue_loads(u.row_begin + (n + 1) * KV_ROW_STEP, next);
+    scores(cur, S, dP);
+    // products of the previous step: its partner half arrived before the barrier
+    accumulate(prev, (n - 1) & 1);
+    pointwise_publish(cur, n & 1, S, dP);
+    wait_vm();
+    __syncthreads();
+    const int t = prev;
+    prev = cur;
+    cur = next;
+    next = t;
+  }
+  accumulate(prev, (nsteps - 1) & 1);
+
+  // lane owns key key0 + 32 kb + l32, features 32 db + 8 (r/4) + 4 g + r%4
+  const float scale = ROLE ? (CAP ? 4.0f * a.lc.sigma : a.lc.sigma) : 1.0f;
+  if (u.nchunk == 1) {
+    uint16_t* base = ROLE ? a.dk : a.dv;
+    const int64_t ts = ROLE ? a.dk_ts : a.dv_ts;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = u.key0 + kb * 32 + l32;
+      if (key >= u.Lk) continue;
+      uint16_t* dst = base + (int64_t)(u.k0 + key) * ts + g * 4;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x16& A = acc[kb][db];
+          *reinterpret_cast<u32x2*>(dst + db * 32 + rq * 8) =
+              u32x2{pack2<T>(scale * A[rq * 4 + 0], scale * A[rq * 4 + 1]),
+                    pack2<T>(scale * A[rq * 4 + 2], scale * A[rq * 4 + 3])};
+        }
+    }
+  } else {
+    float* base = ROLE ? a.part_dk : a.part_dv;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int64_t slot = (int64_t)blockIdx.x * KEY_TILE + (u.key0 % KEY_TILE) + kb * 32 + l32;
+      float* dst = base + slot * HEAD_DIM + g * 4;
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x16& A = acc[kb][db];
+          *reinterpret_cast<f32x4*>(dst + db * 32 + rq * 8) =
+              f32x4{scale * A[rq * 4 + 0], scale * A[rq * 4 + 1], scale * A[rq * 4 + 2],
+                    scale * A[rq * 4 + 3]};
+        }
+    }
+  }
+}
+
+}  // namespace
+
+template <class T, bool CAP>
+__global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) KvShared sm;
+
+  const int rank = find_rank(a.plan.kv_off, a.batch, blockIdx.x);
+  if (rank < 0) return;
+  const int b = a.plan.kv_seq[rank];
+  const int unit = blockIdx.x - a.plan.kv_off[rank];
+  const int* sq = a.plan.seq + b * SEQ_FIELDS;
+  KvUnit u;
+  u.q0 = sq[SQ_Q0];
+  u.k0 = sq[SQ_K0];
+  u.Lk = sq[SQ_LK];
+  u.nchunk = sq[SQ_NCHUNK];
+  const int rows = sq[SQ_ROWS], chunk = sq[SQ_CHUNK];
+  const int ktile = unit / u.nchunk;
+  const int ci = unit - ktile * u.nchunk;
+  u.row_begin = ci * chunk;
+  u.row_end = min(rows, u.row_begin + chunk);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  u.key0 = ktile * KEY_TILE + (wave >> 1) * 64;
+  // every unit has at least one row (the planner never emits empty chunks)
+  if (wave & 1) dkdv_wave<T, CAP, 1>(a, sm, u, wave, lane);
+  else dkdv_wave<T, CAP, 0>(a, sm, u, wave, lane);
+}
+
+template <class T>
+static hipError_t launch_dkdv_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
+  if (cap) hipLaunchKernelGGL((dkdv_kernel<T, true>), grid, KV_THREADS, 0, s, a);
+  else hipLaunchKernelGGL((dkdv_kernel<T, false>), grid, KV_THREADS, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  return dtype == DT_BF16 ? launch_dkdv_t<BF16>(a, cap, grid, s)
+                          : launch_dkdv_t<F16>(a, cap, grid, s);
+}
+
+}  // namespace rga

@@ -1,0 +1,154 @@
+// dQ kernel: recompute P and dP per row tile from the stored row record, then
+//   dS = P * (dP - Delta) * (1 - tanh^2(s / c)),  dQ = sigma dS K.
+//
+// Page "python-20261012-ragged-flash-attention-gradient-recompute", section
+// "Root causes addressed": no probability matrix is stored; the backward
+// rebuilds each tile from L.  Page "Noncausal Global Extreme-GQA Ragged
+// Attention Full VJP", section "Hard Constraints": the cap sits between the
+// scaled dot product and ALiBi, so its derivative multiplies dP - Delta.
+//
+// With r = 1 / (1 + e^{2s/c}), 1 - tanh^2(s/c) = 4 r (1 - r); the kernel forms
+// r - r^2 and folds the factor 4 into the final sigma scale.
+//
+// P is rebuilt exactly as the forward formed it: distances from the clamped
+// centre max(i + Lk - Lq, 0), the large per-row offset kept analytic, and only
+// the small residual log2 l subtracted (see fwd.hip), so no two large numbers
+// are ever subtracted.
+//
+// A workgroup owns 256 folded rows (like the forward) and walks the keys.
+#include "kernels.hpp"
+#include "tiles.hpp"
+
+namespace rga {
+
+template <class T, bool CAP>
+__global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KEY_STEP * LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KEY_STEP * LDK];
+
+  const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
+  if (rank < 0) return;
+  const int b = a.plan.fwd_seq[rank];
+  const int tile = blockIdx.x - a.plan.fwd_off[rank];
+  const int* sq = a.plan.seq + b * SEQ_FIELDS;
+  const int q0 = sq[SQ_Q0], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
+  const int rows = sq[SQ_ROWS];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int row = tile * ROW_TILE + wave * 32 + l32;
+  const bool row_ok = row < rows;
+  const int rr = row_ok ? row : rows - 1;
+  const int ti = rr / a.hq;
+  const int hh = rr - ti * a.hq;
+  const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
+
+  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
+  const uint16_t* dorow = a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)hh * a.do_hs + g * 8;
+  u32x4 qf[KSTEPS], df[KSTEPS];
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    qf[ks] = load16(qrow + ks * 16);
+    df[ks] = load16(dorow + ks * 16);
+  }
+  // row record: slope * log2(e), clamped centre, -residual, Delta
+  const f32x4 info = Lk > 0 ? *reinterpret_cast<const f32x4*>(a.rowinfo + ri * 4)
+                            : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  const float slope2 = info[0];
+  const float cb0 = info[1] - (float)(4 * g);
+  const float boff = info[2];
+  const float dl = info[3];
+
+  f32x16 dQ[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
+
+  const int ntiles = (Lk + KEY_STEP - 1) / KEY_STEP;
+  PairStager<ROW_THREADS, KEY_STEP> st;
+  if (ntiles > 0) {
+    st.load_keys(a.k, a.k_ts, a.v, a.v_ts, k0, min(Lk, KEY_STEP));
+    st.template store<LDK, LDK>(Ks[0], Vs[0]);
+  }
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int kbase = kt * KEY_STEP;
+    const bool more = kt + 1 < ntiles;
+    if (more)
+      st.load_keys(a.k, a.k_ts, a.v, a.v_ts, (int64_t)k0 + kbase + KEY_STEP,
+                   Lk - kbase - KEY_STEP);
+    const uint16_t* Kb = Ks[kt & 1];
+    const uint16_t* Vb = Vs[kt & 1];
+    const float cb = cb0 - (float)kbase;
+    const bool full = kbase + KEY_STEP <= Lk;
+    const int kleft = Lk - kbase - 4 * g;
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      // S^T[key][row] = K Q^T and dP^T[key][row] = V dO^T (lane = row)
+      f32x16 S = f32x16{}, dP = f32x16{};
+      const uint16_t* kp = Kb + (kb * 32 + l32) * LDK + g * 8;
+      const uint16_t* vp = Vb + (kb * 32 + l32) * LDK + g * 8;
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        S = mfma32<T>(load16(kp + ks * 16), qf[ks], S);
+        dP = mfma32<T>(load16(vp + ks * 16), df[ks], dP);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+        const float bias = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), boff);
+        float p, w;
+        if (CAP) {
+          const float rc = cap_r(S[r], a.lc);
+          p = fast_exp2(__builtin_fmaf(a.lc.t_mul, rc, bias));
+          w = __builtin_fmaf(-rc, rc, rc);
+        } else {
+          p = fast_exp2(__builtin_fmaf(S[r], a.lc.s_lin, bias));
+          w = 1.0f;
+        }
+        if (!full) p = jl < kleft ? p : 0.0f;
+        S[r] = p * (dP[r] - dl) * w;
+      }
+      u32x4 sb[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        sb[s] = u32x4{pack2<T>(S[8 * s + 0], S[8 * s + 1]), pack2<T>(S[8 * s + 2], S[8 * s + 3]),
+                      pack2<T>(S[8 * s + 4], S[8 * s + 5]), pack2<T>(S[8 * s + 6], S[8 * s + 7])};
+      // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row]
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          dQ[db] = mfma32<T>(read_tr_a<LDK>(Kb, kb * 32 + s * 16, db * 32, lane), sb[s], dQ[db]);
+    }
+    if (more) st.template store<LDK, LDK>(Ks[(kt + 1) & 1], Vs[(kt + 1) & 1]);
+    __syncthreads();
+  }
+
+  if (!row_ok) return;
+  const float scale = CAP ? 4.0f * a.lc.sigma : a.lc.sigma;
+  uint16_t* dqr = a.dq + (int64_t)(q0 + ti) * a.dq_ts + (int64_t)hh * a.dq_hs + g * 4;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+      *reinterpret_cast<u32x2*>(dqr + db * 32 + rq * 8) =
+          u32x2{pack2<T>(scale * dQ[db][rq * 4 + 0], scale * dQ[db][rq * 4 + 1]),
+                pack2<T>(scale * dQ[db][rq * 4 + 2], scale * dQ[db][rq * 4 + 3])};
+}
+
+template <class T>
+static hipError_t launch_dq_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
+  if (cap) hipLaunchKernelGGL((dq_kernel<T, true>), grid, ROW_THREADS, 0, s, a);
+  else hipLaunchKernelGGL((dq_kernel<T, false>), grid, ROW_THREADS, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  return dtype == DT_BF16 ? launch_dq_t<BF16>(a, cap, grid, s)
+                          : launch_dq_t<F16>(a, cap, grid, s);
+}
+
+}  // namespace rga

@@ -25,6 +25,8 @@
 // a running maximum relative to m_i is kept.  The row statistic is stored as
 // L = m_i + log l (natural log) and, for the backward, as the small residual
 // log2 l relative to m_i, so the backward never subtracts two large numbers.
+// The backward's per-row record (slope, centre, residual, Delta) is written
+// here in the full-VJP call, Delta = rowsum(dO * O) taken from the FP32 O.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -200,8 +202,10 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
     const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
     const float res = m + fast_log2(lsum);
     a.lse[ri] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
-    if (a.lres) a.lres[ri] = lsum > 0.0f ? res : 0.0f;
-    if (DELTA) a.delta[ri] = dsum;
+    if (a.rowinfo)
+      *reinterpret_cast<f32x4*>(a.rowinfo + ri * 4) =
+          f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f,
+                DELTA ? dsum : 0.0f};
   }
 }
 

@@ -13,11 +13,12 @@ namespace rga {
 constexpr int ROW_WAVES = 8;
 constexpr int ROW_THREADS = ROW_WAVES * 64;
 constexpr int ROW_TILE = ROW_WAVES * 32;
-// Key-tile kernel (dK/dV): one workgroup = 4 waves x 32 keys.
+// Key-tile kernel (dK/dV): one workgroup = 4 waves = 2 wave pairs x 64 keys.
 constexpr int KV_THREADS = 256;
 constexpr int KEY_TILE = 128;
-// Folded rows staged per step of the dK/dV kernel.
-constexpr int KV_ROW_STEP = 32;
+// Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
+// P and dS for half of them).
+constexpr int KV_ROW_STEP = 64;
 // Keys staged per step of the row-tile kernels.
 constexpr int KEY_STEP = 64;
 
@@ -31,15 +32,17 @@ struct AttnArgs {
   uint16_t* dk;         int64_t dk_ts;
   uint16_t* dv;         int64_t dv_ts;
   float* lse;           // [total_q * hq], natural log
-  // [total_q * hq] or null: log2 of the row's softmax sum relative to the row
-  // offset m_i (see fwd.hip).  The forward writes it when non-null; the
-  // backward uses it when non-null and derives it from lse otherwise.
-  float* lres;
-  float* delta;         // [total_q * hq], rowsum(dout * out)
+  // [total_q * hq] records of 4 floats per folded row, read by the backward:
+  //   slope * log2(e), clamped ALiBi centre max(i + Lk - Lq, 0),
+  //   minus the base-2 log of the row's softmax sum relative to the row offset
+  //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
+  float* rowinfo;
+  const uint16_t* zero; // >= 256 zero bytes: source of the loads of rows past a tile's end
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
   const float* slopes;  int64_t slopes_stride;
   int hq;
+  uint32_t hq_mul, hq_shift;   // n / hq == (umulhi(n, hq_mul) + n) >> hq_shift for n < 2^31
   int batch;
   int64_t total_q;
   int64_t total_k;
@@ -56,6 +59,7 @@ struct PlanArgs {
   int64_t total_k;
   int target_units;     // desired number of dK/dV work units
   int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
+  uint16_t* zero;       // 256 bytes the planner clears
   Plan plan;
 };
 
@@ -64,7 +68,7 @@ enum { DT_F16 = 0, DT_BF16 = 1 };
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
                       hipStream_t s);
-hipError_t launch_rowdot(const AttnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 hipError_t launch_kv_reduce(const AttnArgs& a, int dtype, hipStream_t s);

@@ -1,4 +1,5 @@
-// Device planner, fixed-order K/V partial reduction, and the dO.O row dot.
+// Device planner, fixed-order K/V partial reduction, and the backward's row
+// records for the standalone backward entry.
 //
 // The planner reads cu_q / cu_k on the device (no host synchronisation) and
 // builds two work lists for the packed ragged batch (page "Noncausal Global
@@ -15,7 +16,7 @@
 namespace rga {
 
 constexpr int PLAN_THREADS = 256;
-constexpr int WG_THREADS = 256;          // reduce and row-dot kernels
+constexpr int WG_THREADS = 256;          // reduce and row-record kernels
 constexpr int PLAN_SORT_LIMIT = 8192;   // larger batches keep their natural order
 
 __device__ __forceinline__ long long block_sum(long long v, long long* red) {
@@ -68,6 +69,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanArgs a) {
   int* seq = a.plan.seq;
 
   if (tid == 0) bad = 0;
+  if (tid < 16) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   for (int b = tid; b <= B; b += PLAN_THREADS) {
     const int cq = a.cu_q[b], ck = a.cu_k[b];
@@ -193,20 +195,22 @@ hipError_t launch_kv_reduce(const AttnArgs& a, int dtype, hipStream_t s) {
   return hipGetLastError();
 }
 
-// delta[row] = sum_d dout[row, d] * out[row, d] over the stored 16-bit output,
-// for the backward entry that starts from a saved forward.  Eight lanes share
-// a row; each reads 16-byte chunks.
-template <class T>
-__global__ __launch_bounds__(WG_THREADS) void rowdot_kernel(const AttnArgs a) {
+// Row records for the backward entry that starts from a saved forward:
+// Delta = sum_d dout[row, d] * out[row, d] over the stored 16-bit output, the
+// slope in base-2 units, the clamped ALiBi centre and the base-2 residual of
+// the stored natural-log L relative to the row offset the forward used (see
+// fwd.hip).  Eight lanes share a row; each reads 16-byte chunks.
+template <class T, bool CAP>
+__global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * WG_THREADS + threadIdx.x;
   const int64_t r = gid >> 3;
   const int sub = (int)(gid & 7);
   const int64_t nrows = a.total_q * a.hq;
   const bool ok = r < nrows;
+  const int64_t t = ok ? r / a.hq : 0;
+  const int h = (int)(r - t * a.hq);
   float acc = 0.0f;
   if (ok) {
-    const int64_t t = r / a.hq;
-    const int h = (int)(r - t * a.hq);
     const uint16_t* o = a.out + t * a.o_ts + (int64_t)h * a.o_hs;
     const uint16_t* d = a.dout + t * a.do_ts + (int64_t)h * a.do_hs;
     for (int c = sub; c < CHUNKS; c += 8) {
@@ -219,15 +223,36 @@ __global__ __launch_bounds__(WG_THREADS) void rowdot_kernel(const AttnArgs a) {
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
   acc += __shfl_xor(acc, 4, 64);
-  if (ok && sub == 0) a.delta[r] = acc;
+  if (!ok || sub != 0) return;
+  // sequence of token t: the last b with q0(b) <= t (never an empty one)
+  const int* seq = a.plan.seq;
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq[mid * SEQ_FIELDS + SQ_Q0] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int* s = seq + lo * SEQ_FIELDS;
+  const int i = (int)(t - s[SQ_Q0]);
+  const int Lq = s[SQ_LQ], Lk = s[SQ_LK];
+  const float slope2 = a.slopes[(int64_t)lo * a.slopes_stride + h] * LOG2E;
+  const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - i);
+  const float L = a.lse[r];
+  const float negres = Lk > 0 ? moff - L * LOG2E : 0.0f;
+  *reinterpret_cast<f32x4*>(a.rowinfo + r * 4) =
+      f32x4{slope2, (float)max(i + Lk - Lq, 0), negres, acc};
 }
 
-hipError_t launch_rowdot(const AttnArgs& a, int dtype, hipStream_t s) {
+hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s) {
   const int64_t n = a.total_q * a.hq * 8;
   if (n <= 0) return hipSuccess;
   const int grid = (int)((n + WG_THREADS - 1) / WG_THREADS);
-  if (dtype == DT_BF16) hipLaunchKernelGGL(rowdot_kernel<BF16>, grid, WG_THREADS, 0, s, a);
-  else hipLaunchKernelGGL(rowdot_kernel<F16>, grid, WG_THREADS, 0, s, a);
+  if (dtype == DT_BF16) {
+    if (cap) hipLaunchKernelGGL((rowinfo_kernel<BF16, true>), grid, WG_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((rowinfo_kernel<BF16, false>), grid, WG_THREADS, 0, s, a);
+  } else {
+    if (cap) hipLaunchKernelGGL((rowinfo_kernel<F16, true>), grid, WG_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((rowinfo_kernel<F16, false>), grid, WG_THREADS, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -112,6 +112,50 @@ struct PairStager {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Swizzled row tiles filled by direct global->LDS loads.
+//
+// A tile of R rows x 160 16-bit features is stored without padding (320-byte
+// rows, 20 chunks of 16 bytes) with the chunk index of row r XOR-ed with
+// (r / 4) % 4.  LDS serves 16 lanes of a 16-byte read per pass from 16 chunk
+// banks; rows r and r + 4k then start on different banks, so the 16 rows of a
+// row read (one chunk each) and the 4 rows x 2 chunks of a transposing read
+// both touch 16 distinct chunk banks.  The XOR only flips the two low bits of
+// the chunk index, so a chunk never leaves its row.
+__device__ __forceinline__ int swz_off(int row, int chunk) {
+  return row * HEAD_DIM + ((chunk ^ ((row >> 2) & 3)) << 3);
+}
+
+// Logical (row, chunk) held by physical 16-byte slot `slot` of a swizzled tile.
+__device__ __forceinline__ void swz_slot(int slot, int& row, int& chunk) {
+  row = slot / CHUNKS;
+  chunk = (slot - row * CHUNKS) ^ ((row >> 2) & 3);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+// One wave-wide direct load: lane l copies the 16 bytes at `src` (its own
+// address) to LDS at wave_dst + 16 l.  wave_dst must be the same for every lane.
+__device__ __forceinline__ void load_lds16(const void* src, void* wave_dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)const_cast<void*>(src), (lds_void_t*)wave_dst,
+                                   16, 0, 0);
+}
+
+// Wait for this wave's outstanding global loads (direct LDS loads included).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// read_tr_a for a swizzled tile.
+__device__ __forceinline__ u32x4 read_tr_swz(const uint16_t* X, int r0, int c0, int lane) {
+  const int i = lane & 15;
+  const int G = lane >> 4;
+  const int row = r0 + 4 * (G >> 1) + (i >> 2);
+  const int col = c0 + 16 * (G & 1) + 4 * (i & 3);
+  const u32x2 lo = read_tr(X + swz_off(row, col >> 3) + (col & 7));
+  const u32x2 hi = read_tr(X + swz_off(row + 8, col >> 3) + (col & 7));
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Capped logit pieces from a raw dot product q.k (see LogitConsts):
 //   r = 1 / (1 + e^{2 s / c}),   c tanh(s / c) log2(e) = t_add + t_mul * r,
 // and 1 - tanh^2(s / c) = 4 r (1 - r).
