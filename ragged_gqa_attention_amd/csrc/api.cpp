@@ -78,7 +78,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
     return at;
   };
   L.flag = take(sizeof(int) * 4);   // first, so attn_varlen_check_plan can find it
-  L.zero = take(256);
+  L.zero = take(512);
   L.seq = take(sizeof(int) * B * SEQ_FIELDS);
   L.fwd_seq = take(sizeof(int) * B);
   L.fwd_off = take(sizeof(int) * (B + 1));
@@ -137,6 +137,8 @@ attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens,
   if (heads > 1 && t->head_stride < HEAD_DIM)
     return fail(ATTN_INVALID_ARG, "%s head stride %lld overlaps rows", name,
                 (long long)t->head_stride);
+  if (t->tok_stride > INT32_MAX || t->head_stride > INT32_MAX)
+    return fail(ATTN_INVALID_ARG, "%s strides must be below 2^31 elements", name);
   if ((reinterpret_cast<uintptr_t>(t->data) & 15) != 0 || (t->tok_stride & 7) != 0 ||
       (t->head_stride & 7) != 0)
     return fail(ATTN_MISALIGNED, "%s pointer or strides are not 16-byte multiples", name);

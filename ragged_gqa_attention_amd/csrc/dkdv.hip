@@ -28,7 +28,7 @@
 // separate pass adds in chunk order.  No atomics anywhere.
 //
 // Pipeline.  Q and dO tiles are copied global -> LDS with direct loads (no
-// staging registers) into three buffers: step n is read by the S/dP products,
+// staging registers) into blocked tiles, three buffers: step n is read by the S/dP products,
 // step n - 1 by the dV/dK products (which run while the VALU forms P and dS of
 // step n) and step n + 1 is in flight.
 #include "kernels.hpp"
@@ -39,13 +39,24 @@ namespace rga {
 namespace {
 
 constexpr int KV_NBUF = 3;
-constexpr int STEP_SLOTS = KV_ROW_STEP * CHUNKS;     // 16-byte chunks per tensor per step
-constexpr int LOADS_PER_WAVE = STEP_SLOTS / 256;     // wave loads per tensor per step (5)
-static_assert(STEP_SLOTS % 256 == 0, "each wave load covers 64 slots; 4 waves share a tile");
+constexpr int LOADS_PER_WAVE = CHUNKS / 4;          // 4-chunk blocks of a 16-row group (5)
+constexpr int BLK_ELEMS = 64 * 8;                    // one block: 16 rows x 4 chunks
 constexpr int TILE_ELEMS = KV_ROW_STEP * HEAD_DIM;
+static_assert(KV_ROW_STEP == 64, "four waves x 16 rows per step");
+
+// Blocked tile of 64 rows x 20 chunks (16 bytes each): block (r / 16, c / 4)
+// holds rows 16 (r/16) .. +15 and chunks 4 (c/4) .. +3 as 64 consecutive
+// slots, row-major inside, with the chunk's two low bits XOR-ed with
+// (r / 4) % 4.  One wave load (64 lanes x 16 bytes) fills one block, reading
+// 64 contiguous bytes from each of 16 rows.  A row read (16 lanes = 16
+// consecutive rows of one chunk) and a transposing read (4 rows x 2 adjacent
+// chunks) both touch 16 distinct 16-byte bank slots.
+__device__ __forceinline__ int blk_off(int r, int c) {
+  return (((r >> 4) * (CHUNKS / 4) + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
+}
 
 struct KvShared {
-  uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (swizzled)
+  uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (blocked)
   f32x4 rinfo[KV_NBUF][KV_ROW_STEP];     // row records of a step
   u32x4 xch[2][4][4][64];                 // [slot][writer wave][kb * 2 + s][lane]
 };
@@ -82,45 +93,52 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   }
 
-  // Direct loads of step rows [r0, r0 + 64): this wave fills slots
-  // (v * 4 + wave) * 64 + lane of the Q and dO tiles; wave 0 also loads the
-  // row records.  Rows past the chunk end read the zero block.
+  // Direct loads of step rows [r0, r0 + 64) into blocked tiles (see blk_off):
+  // wave w copies rows 16 w .. 16 w + 15 of Q and dO, one 4-chunk block per
+  // load, lane l holding row 16 w + l / 4 for all ten loads, so one address
+  // per lane per step.  Rows past the chunk end read the zero block.  Wave 0
+  // also copies the 64 row records.
+  const int lrow = 16 * wave + (lane >> 2);
+  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   auto issue_loads = [&](int r0, int buf) {
     if (wave == 0) {
       const int R = r0 + lane;
       const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, u.row_end - 1)) * 4;
       load_lds16(R < u.row_end ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
     }
+    const int R = r0 + lrow;
+    const int Rc = min(R, u.row_end - 1);
+    const uint32_t tok = (uint32_t)fast_div(Rc, a.hq_mul, a.hq_shift);
+    const uint32_t h = (uint32_t)Rc - tok * (uint32_t)hq;
+    const uint32_t t_abs = (uint32_t)u.q0 + tok;
+    const bool ok = R < u.row_end;
+    const uint16_t* sq = a.q + ((uint64_t)t_abs * (uint32_t)a.q_ts + (uint64_t)h * (uint32_t)a.q_hs);
+    const uint16_t* sd =
+        a.dout + ((uint64_t)t_abs * (uint32_t)a.do_ts + (uint64_t)h * (uint32_t)a.do_hs);
+    sq = (ok ? sq : a.zero) + lchunk * 8;
+    sd = (ok ? sd : a.zero) + lchunk * 8;
 #pragma unroll
-    for (int v = 0; v < LOADS_PER_WAVE; ++v) {
-      const int slot0 = (v * 4 + wave) * 64;
-      int trow, tch;
-      swz_slot(slot0 + lane, trow, tch);
-      const int R = r0 + trow;
-      const int Rc = min(R, u.row_end - 1);
-      const int tok = fast_div(Rc, a.hq_mul, a.hq_shift);
-      const int h = Rc - tok * hq;
-      const uint16_t* sq = a.q + (int64_t)(u.q0 + tok) * a.q_ts + (int64_t)h * a.q_hs + tch * 8;
-      const uint16_t* sd = a.dout + (int64_t)(u.q0 + tok) * a.do_ts + (int64_t)h * a.do_hs + tch * 8;
-      const bool ok = R < u.row_end;
-      load_lds16(ok ? sq : a.zero, &sm.qd[buf][0][slot0 * 8]);
-      load_lds16(ok ? sd : a.zero, &sm.qd[buf][1][slot0 * 8]);
+    for (int p = 0; p < LOADS_PER_WAVE; ++p) {
+      const int blk = (wave * LOADS_PER_WAVE + p) * 64 * 8;
+      load_lds16(sq + p * 32, &sm.qd[buf][0][blk]);
+      load_lds16(sd + p * 32, &sm.qd[buf][1][blk]);
     }
   };
 
   // Lane-constant LDS offsets (elements).  Row reads of the S / dP A operand:
-  // row ROLE * 32 + l32, logical chunk 2 ks + g; only ks % 2 changes the XOR.
+  // row ROLE * 32 + l32, chunk 2 ks + g; ks / 2 selects the block column and
+  // ks % 2 the XOR pattern.
   const int arow = ROLE * 32 + l32;
-  const int sx = (l32 >> 2) & 3;
-  const int roff[2] = {arow * HEAD_DIM + 8 * (g ^ sx), arow * HEAD_DIM + 8 * ((2 + g) ^ sx)};
-  // Transposing reads (see read_tr_a): row 4 (G/2) + i/4 (+ 8), feature
-  // 16 (G%2) + 4 (i%4); every 16-row k-step and 32-feature block adds a constant.
+  const int roff[2] = {blk_off(arow, g), blk_off(arow, 2 + g)};
+  // Transposing reads (see read_tr_a): lane (i, G) reads row 4 (G/2) + i/4
+  // (+ 8) of the 16-row k-step t, features 16 (G%2) + 4 (i%4) of the
+  // 32-feature block db, which is chunk 4 db + 2 (G%2) + (i%4)/2; each (t, db)
+  // is one block further.
   const int ti = lane & 15, tG = lane >> 4;
   const int trow0 = 4 * (tG >> 1) + (ti >> 2);
   const int tcl = 2 * (tG & 1) + ((ti & 3) >> 1);
-  const int tin = 4 * (ti & 1);
-  const int toff_lo = trow0 * HEAD_DIM + 8 * (tcl ^ ((trow0 >> 2) & 3)) + tin;
-  const int toff_hi = (trow0 + 8) * HEAD_DIM + 8 * (tcl ^ (((trow0 + 8) >> 2) & 3)) + tin;
+  const int toff_lo = blk_off(trow0, tcl) + 4 * (ti & 1);
+  const int toff_hi = blk_off(trow0 + 8, tcl) + 4 * (ti & 1);
   // row records of the lane's rows 8 (r/4) + 4 g + r%4 of the wave's half
   const int rbase = ROLE * 32 + g * 4;
 
@@ -137,15 +155,21 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     for (int kb = 0; kb < 2; ++kb) { S[kb] = f32x16{}; dP[kb] = f32x16{}; }
     const uint16_t* Qb = sm.qd[buf][0];
     const uint16_t* Db = sm.qd[buf][1];
+    // operands of k-step ks + 1 are read while the MFMAs of k-step ks run
+    u32x4 qa[2], da[2];
+    qa[0] = load16(Qb + roff[0]);
+    da[0] = load16(Db + roff[0]);
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      const int off = roff[ks & 1] + 32 * (ks >> 1);
-      const u32x4 qa = load16(Qb + off);
-      const u32x4 da = load16(Db + off);
+      if (ks + 1 < KSTEPS) {
+        const int off = roff[(ks + 1) & 1] + BLK_ELEMS * ((ks + 1) >> 1);
+        qa[(ks + 1) & 1] = load16(Qb + off);
+        da[(ks + 1) & 1] = load16(Db + off);
+      }
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        S[kb] = mfma32<T>(qa, kf[kb][ks], S[kb]);
-        dP[kb] = mfma32<T>(da, vf[kb][ks], dP[kb]);
+        S[kb] = mfma32<T>(qa[ks & 1], kf[kb][ks], S[kb]);
+        dP[kb] = mfma32<T>(da[ks & 1], vf[kb][ks], dP[kb]);
       }
     }
   };
@@ -194,21 +218,29 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // from the partner's slot for the other.  k-step t covers rows 16t .. 16t + 15.
   auto accumulate = [&](int buf, int slot) {
     const uint16_t* X = sm.qd[buf][ROLE ? 0 : 1];
+    u32x4 B[2][2];   // B operands of the partner's half, read up front
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 B[2];
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int s = 0; s < 2; ++s) B[kb][s] = sm.xch[slot][wave ^ 1][kb * 2 + s][lane];
+    // the A operand of product i + 1 is read while the MFMAs of product i run
+    auto read_a = [&](int i) {
+      const int t = i / DBLK, db = i - t * DBLK;
+      const int off = (t * (CHUNKS / 4) + db) * BLK_ELEMS;
+      const u32x2 lo = read_tr(X + toff_lo + off);
+      const u32x2 hi = read_tr(X + toff_hi + off);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 A[2];
+    A[0] = read_a(0);
+#pragma unroll
+    for (int i = 0; i < 4 * DBLK; ++i) {
+      if (i + 1 < 4 * DBLK) A[(i + 1) & 1] = read_a(i + 1);
+      const int t = i / DBLK, db = i - t * DBLK;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        B[kb] = (t >> 1) == ROLE ? mine[kb][t & 1] : sm.xch[slot][wave ^ 1][kb * 2 + (t & 1)][lane];
-#pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const int off = 16 * t * HEAD_DIM + 32 * db;
-        const u32x2 lo = read_tr(X + toff_lo + off);
-        const u32x2 hi = read_tr(X + toff_hi + off);
-        const u32x4 A = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) acc[kb][db] = mfma32<T>(A, B[kb], acc[kb][db]);
-      }
+        acc[kb][db] = mfma32<T>(A[i & 1], (t >> 1) == ROLE ? mine[kb][t & 1] : B[kb][t & 1],
+                                acc[kb][db]);
     }
   };
 

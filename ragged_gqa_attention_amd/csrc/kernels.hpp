@@ -37,7 +37,7 @@ struct AttnArgs {
   //   minus the base-2 log of the row's softmax sum relative to the row offset
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;
-  const uint16_t* zero; // >= 256 zero bytes: source of the loads of rows past a tile's end
+  const uint16_t* zero; // 512 zero bytes: source of the loads of rows past a tile's end
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
   const float* slopes;  int64_t slopes_stride;
@@ -59,7 +59,7 @@ struct PlanArgs {
   int64_t total_k;
   int target_units;     // desired number of dK/dV work units
   int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
-  uint16_t* zero;       // 256 bytes the planner clears
+  uint16_t* zero;       // 512 bytes the planner clears
   Plan plan;
 };
 

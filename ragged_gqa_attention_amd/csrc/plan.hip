@@ -69,7 +69,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanArgs a) {
   int* seq = a.plan.seq;
 
   if (tid == 0) bad = 0;
-  if (tid < 16) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
+  if (tid < 32) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
   for (int b = tid; b <= B; b += PLAN_THREADS) {
     const int cq = a.cu_q[b], ck = a.cu_k[b];
