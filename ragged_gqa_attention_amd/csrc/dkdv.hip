@@ -15,22 +15,22 @@
 // r - r^2 and folds the factor 4 into the final sigma scale of dK.
 //
 // Work split.  A workgroup owns 128 keys of one sequence and a chunk of its
-// folded rows.  Its four waves form two pairs; a pair owns 64 keys and keeps
+// folded rows.  Its eight waves form four pairs; a pair owns 32 keys and keeps
 // their K and V rows in registers (MFMA operands, lane = key).  Rows are
 // streamed 64 at a time through LDS.  In each step the two waves of a pair
-// each form S, dP, P and dS for one half of the rows (32 rows x 64 keys), then
+// each form S, dP, P and dS for one half of the rows (32 rows x 32 keys), then
 // trade halves through LDS: the first wave accumulates dV = P^T dO over all 64
-// rows, the second dK = dS^T Q.  Each wave thus holds one 64-key accumulator,
-// and every operand read from LDS feeds two MFMAs (one per 32-key block),
-// which halves LDS traffic per MFMA compared with one wave doing all four
-// products for 32 keys.  The sum over rows happens in registers in a fixed
-// order; sequences split into several row chunks write FP32 partials that a
-// separate pass adds in chunk order.  No atomics anywhere.
+// rows, the second dK = dS^T Q.  Each wave thus holds one accumulator and
+// stays within 256 registers, so two waves share each SIMD; they take the
+// independent products and pointwise work of a step in opposite orders, so
+// one wave's VALU work overlaps the other's MFMAs.  The sum over rows happens
+// in registers in a fixed order; sequences split into several row chunks
+// write FP32 partials that a separate pass adds in chunk order.  No atomics
+// anywhere.
 //
 // Pipeline.  Q and dO tiles are copied global -> LDS with direct loads (no
-// staging registers) into blocked tiles, three buffers: step n is read by the S/dP products,
-// step n - 1 by the dV/dK products (which run while the VALU forms P and dS of
-// step n) and step n + 1 is in flight.
+// staging registers) into blocked tiles, three buffers: step n is read by the
+// S/dP products, step n - 1 by the dV/dK products and step n + 1 is in flight.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -39,10 +39,14 @@ namespace rga {
 namespace {
 
 constexpr int KV_NBUF = 3;
+constexpr int KV_WAVES = KV_THREADS / 64;
+constexpr int PAIR_KEYS = KEY_TILE / (KV_WAVES / 2);  // keys of one wave pair
+constexpr int KB = PAIR_KEYS / 32;                    // 32-key blocks per wave
 constexpr int LOADS_PER_WAVE = CHUNKS / 4;          // 4-chunk blocks of a 16-row group (5)
+static_assert(KV_WAVES == 8 && KB == 1, "eight waves: wave w copies tensor w / 4, row group w % 4");
 constexpr int BLK_ELEMS = 64 * 8;                    // one block: 16 rows x 4 chunks
 constexpr int TILE_ELEMS = KV_ROW_STEP * HEAD_DIM;
-static_assert(KV_ROW_STEP == 64, "four waves x 16 rows per step");
+static_assert(KV_ROW_STEP == 64, "four 16-row groups per step");
 
 // Blocked tile of 64 rows x 20 chunks (16 bytes each): block (r / 16, c / 4)
 // holds rows 16 (r/16) .. +15 and chunks 4 (c/4) .. +3 as 64 consecutive
@@ -58,28 +62,28 @@ __device__ __forceinline__ int blk_off(int r, int c) {
 struct KvShared {
   uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (blocked)
   f32x4 rinfo[KV_NBUF][KV_ROW_STEP];     // row records of a step
-  u32x4 xch[2][4][4][64];                 // [slot][writer wave][kb * 2 + s][lane]
+  u32x4 xch[2][KV_WAVES][KB * 2][64];     // [slot][writer wave][kb * 2 + s][lane]
 };
 
 // What a workgroup works on: rows [row_begin, row_end) of sequence b against
-// keys [key0, key0 + 64) of the wave's pair.
+// keys [key0, key0 + PAIR_KEYS) of the wave's pair.
 struct KvUnit {
   int q0, k0, Lk, row_begin, row_end, key0, nchunk;
 };
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
-template <class T, bool CAP, int ROLE>
+template <class T, bool CAP, int ROLE, bool LATE>
 __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const KvUnit& u,
                                           int wave, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
   const int hq = a.hq;
 
-  // K and V rows of the pair's 64 keys as B operands (lane = key); keys past
+  // K and V rows of the pair's keys as B operands (lane = key); keys past
   // the sequence end are zero and their results are never stored.
-  u32x4 kf[2][KSTEPS], vf[2][KSTEPS];
-  float keyf[2];
+  u32x4 kf[KB][KSTEPS], vf[KB][KSTEPS];
+  float keyf[KB];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
+  for (int kb = 0; kb < KB; ++kb) {
     const int key = u.key0 + kb * 32 + l32;
     keyf[kb] = (float)key;
     const bool ok = key < u.Lk;
@@ -94,11 +98,13 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   }
 
   // Direct loads of step rows [r0, r0 + 64) into blocked tiles (see blk_off):
-  // wave w copies rows 16 w .. 16 w + 15 of Q and dO, one 4-chunk block per
-  // load, lane l holding row 16 w + l / 4 for all ten loads, so one address
-  // per lane per step.  Rows past the chunk end read the zero block.  Wave 0
+  // wave w copies rows 16 (w%4) .. +15 of Q (w < 4) or dO, one 4-chunk block
+  // per load, lane l holding row 16 (w%4) + l / 4 for all five loads, so one
+  // address per lane per step.  Rows past the chunk end read the zero block.  Wave 0
   // also copies the 64 row records.
-  const int lrow = 16 * wave + (lane >> 2);
+  const int lgroup = wave & 3;            // 16-row group this wave copies
+  const int ltensor = wave >> 2;          // 0: Q, 1: dO
+  const int lrow = 16 * lgroup + (lane >> 2);
   const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   auto issue_loads = [&](int r0, int buf) {
     if (wave == 0) {
@@ -112,17 +118,13 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     const uint32_t h = (uint32_t)Rc - tok * (uint32_t)hq;
     const uint32_t t_abs = (uint32_t)u.q0 + tok;
     const bool ok = R < u.row_end;
-    const uint16_t* sq = a.q + ((uint64_t)t_abs * (uint32_t)a.q_ts + (uint64_t)h * (uint32_t)a.q_hs);
-    const uint16_t* sd =
-        a.dout + ((uint64_t)t_abs * (uint32_t)a.do_ts + (uint64_t)h * (uint32_t)a.do_hs);
-    sq = (ok ? sq : a.zero) + lchunk * 8;
-    sd = (ok ? sd : a.zero) + lchunk * 8;
+    const uint16_t* base = ltensor ? a.dout : a.q;
+    const uint32_t ts = (uint32_t)(ltensor ? a.do_ts : a.q_ts);
+    const uint32_t hs = (uint32_t)(ltensor ? a.do_hs : a.q_hs);
+    const uint16_t* src = (ok ? base + ((uint64_t)t_abs * ts + (uint64_t)h * hs) : a.zero) + lchunk * 8;
 #pragma unroll
-    for (int p = 0; p < LOADS_PER_WAVE; ++p) {
-      const int blk = (wave * LOADS_PER_WAVE + p) * 64 * 8;
-      load_lds16(sq + p * 32, &sm.qd[buf][0][blk]);
-      load_lds16(sd + p * 32, &sm.qd[buf][1][blk]);
-    }
+    for (int p = 0; p < LOADS_PER_WAVE; ++p)
+      load_lds16(src + p * 32, &sm.qd[buf][ltensor][(lgroup * LOADS_PER_WAVE + p) * BLK_ELEMS]);
   };
 
   // Lane-constant LDS offsets (elements).  Row reads of the S / dP A operand:
@@ -142,17 +144,17 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // row records of the lane's rows 8 (r/4) + 4 g + r%4 of the wave's half
   const int rbase = ROLE * 32 + g * 4;
 
-  f32x16 acc[2][DBLK];
+  f32x16 acc[KB][DBLK];
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int db = 0; db < DBLK; ++db) acc[kb][db] = f32x16{};
-  u32x4 mine[2][2];   // own P (ROLE 0) or own dS (ROLE 1) of the previous step
+  u32x4 mine[KB][2];   // own P (ROLE 0) or own dS (ROLE 1) of the previous step
 
   // S[row][key] = Q K^T and dP[row][key] = dO V^T for this wave's 32 rows
-  auto scores = [&](int buf, f32x16 (&S)[2], f32x16 (&dP)[2]) {
+  auto scores = [&](int buf, f32x16 (&S)[KB], f32x16 (&dP)[KB]) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) { S[kb] = f32x16{}; dP[kb] = f32x16{}; }
+    for (int kb = 0; kb < KB; ++kb) { S[kb] = f32x16{}; dP[kb] = f32x16{}; }
     const uint16_t* Qb = sm.qd[buf][0];
     const uint16_t* Db = sm.qd[buf][1];
     // operands of k-step ks + 1 are read while the MFMAs of k-step ks run
@@ -167,7 +169,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
         da[(ks + 1) & 1] = load16(Db + off);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         S[kb] = mfma32<T>(qa[ks & 1], kf[kb][ks], S[kb]);
         dP[kb] = mfma32<T>(da[ks & 1], vf[kb][ks], dP[kb]);
       }
@@ -176,12 +178,13 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
-  auto pointwise_publish = [&](int buf, int slot, f32x16 (&S)[2], f32x16 (&dP)[2]) {
+  auto pointwise_publish = [&](int buf, int slot, f32x16 (&S)[KB], f32x16 (&dP)[KB],
+                               u32x4 (&own)[KB][2]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
         float p, w;
         if (CAP) {
@@ -197,7 +200,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
       }
     }
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const u32x4 pb = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
@@ -208,7 +211,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
                                pack2<T>(dP[kb][8 * s + 2], dP[kb][8 * s + 3]),
                                pack2<T>(dP[kb][8 * s + 4], dP[kb][8 * s + 5]),
                                pack2<T>(dP[kb][8 * s + 6], dP[kb][8 * s + 7])};
-        mine[kb][s] = ROLE ? sb : pb;
+        own[kb][s] = ROLE ? sb : pb;
         sm.xch[slot][wave][kb * 2 + s][lane] = ROLE ? pb : sb;
       }
   };
@@ -218,9 +221,9 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // from the partner's slot for the other.  k-step t covers rows 16t .. 16t + 15.
   auto accumulate = [&](int buf, int slot) {
     const uint16_t* X = sm.qd[buf][ROLE ? 0 : 1];
-    u32x4 B[2][2];   // B operands of the partner's half, read up front
+    u32x4 B[KB][2];   // B operands of the partner's half, read up front
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int s = 0; s < 2; ++s) B[kb][s] = sm.xch[slot][wave ^ 1][kb * 2 + s][lane];
     // the A operand of product i + 1 is read while the MFMAs of product i run
@@ -238,7 +241,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
       if (i + 1 < 4 * DBLK) A[(i + 1) & 1] = read_a(i + 1);
       const int t = i / DBLK, db = i - t * DBLK;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
         acc[kb][db] = mfma32<T>(A[i & 1], (t >> 1) == ROLE ? mine[kb][t & 1] : B[kb][t & 1],
                                 acc[kb][db]);
     }
@@ -249,18 +252,29 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   wait_vm();
   __syncthreads();
   if (nsteps > 1) issue_loads(u.row_begin + KV_ROW_STEP, 1);
-  f32x16 S[2], dP[2];
+  f32x16 S[KB], dP[KB];
   scores(0, S, dP);
-  pointwise_publish(0, 0, S, dP);
+  pointwise_publish(0, 0, S, dP, mine);
   wait_vm();
   __syncthreads();
   int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
   for (int n = 1; n < nsteps; ++n) {
     if (n + 1 < nsteps) issue_loads(u.row_begin + (n + 1) * KV_ROW_STEP, next);
     scores(cur, S, dP);
-    // products of the previous step: its partner half arrived before the barrier
-    accumulate(prev, (n - 1) & 1);
-    pointwise_publish(cur, n & 1, S, dP);
+    // products of the previous step (its partner half arrived before the
+    // barrier) and the pointwise work of this one are independent; the two
+    // waves sharing a SIMD take them in opposite orders, so one runs VALU
+    // while the other keeps the matrix core busy
+    if (LATE) {
+      accumulate(prev, (n - 1) & 1);
+      pointwise_publish(cur, n & 1, S, dP, mine);
+    } else {
+      u32x4 own[KB][2];
+      pointwise_publish(cur, n & 1, S, dP, own);
+      accumulate(prev, (n - 1) & 1);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) { mine[kb][0] = own[kb][0]; mine[kb][1] = own[kb][1]; }
+    }
     wait_vm();
     __syncthreads();
     const int t = prev;
@@ -276,7 +290,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     uint16_t* base = ROLE ? a.dk : a.dv;
     const int64_t ts = ROLE ? a.dk_ts : a.dv_ts;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int key = u.key0 + kb * 32 + l32;
       if (key >= u.Lk) continue;
       uint16_t* dst = base + (int64_t)(u.k0 + key) * ts + g * 4;
@@ -293,7 +307,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   } else {
     float* base = ROLE ? a.part_dk : a.part_dv;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < KB; ++kb) {
       const int64_t slot = (int64_t)blockIdx.x * KEY_TILE + (u.key0 % KEY_TILE) + kb * 32 + l32;
       float* dst = base + slot * HEAD_DIM + g * 4;
 #pragma unroll
@@ -332,10 +346,16 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   u.row_end = min(rows, u.row_begin + chunk);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  u.key0 = ktile * KEY_TILE + (wave >> 1) * 64;
+  u.key0 = ktile * KEY_TILE + (wave >> 1) * PAIR_KEYS;
   // every unit has at least one row (the planner never emits empty chunks)
-  if (wave & 1) dkdv_wave<T, CAP, 1>(a, sm, u, wave, lane);
-  else dkdv_wave<T, CAP, 0>(a, sm, u, wave, lane);
+  // waves w and w + 4 share a SIMD
+  if (wave < 4) {
+    if (wave & 1) dkdv_wave<T, CAP, 1, false>(a, sm, u, wave, lane);
+    else dkdv_wave<T, CAP, 0, false>(a, sm, u, wave, lane);
+  } else {
+    if (wave & 1) dkdv_wave<T, CAP, 1, true>(a, sm, u, wave, lane);
+    else dkdv_wave<T, CAP, 0, true>(a, sm, u, wave, lane);
+  }
 }
 
 template <class T>

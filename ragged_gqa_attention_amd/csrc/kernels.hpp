@@ -13,8 +13,8 @@ namespace rga {
 constexpr int ROW_WAVES = 8;
 constexpr int ROW_THREADS = ROW_WAVES * 64;
 constexpr int ROW_TILE = ROW_WAVES * 32;
-// Key-tile kernel (dK/dV): one workgroup = 4 waves = 2 wave pairs x 64 keys.
-constexpr int KV_THREADS = 256;
+// Key-tile kernel (dK/dV): one workgroup = 8 waves = 4 wave pairs x 32 keys.
+constexpr int KV_THREADS = 512;
 constexpr int KEY_TILE = 128;
 // Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
 // P and dS for half of them).
