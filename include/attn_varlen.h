@@ -138,7 +138,7 @@ attn_status attn_varlen_full_vjp(const attn_problem* p,
 
 /* Phases of attn_varlen_full_vjp, in launch order. */
 typedef enum {
-  ATTN_PHASE_PLAN = 0,     /* work lists from cu_q / cu_k */
+  ATTN_PHASE_PLAN = 0,     /* work lists from cu_q / cu_k, transposed K / V key tiles */
   ATTN_PHASE_FWD = 1,      /* forward: out, lse, delta = rowsum(dout * out) */
   ATTN_PHASE_DKDV = 2,     /* dK, dV over all sharing heads */
   ATTN_PHASE_DQ = 3,       /* dQ */

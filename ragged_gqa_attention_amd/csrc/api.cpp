@@ -57,10 +57,11 @@ int device_cus() {
 
 struct Layout {
   size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero;
-  size_t lse, rowinfo, part_dk, part_dv;
+  size_t lse, rowinfo, part_dk, part_dv, kt, vt;
   size_t total;
   int64_t max_units;
   int64_t row_tiles;
+  int64_t key_tiles;    // upper bound of the transposed 64-key tiles
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -71,6 +72,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   const int64_t rows = p->total_q * p->hq;
   L.row_tiles = ceil_div(rows, ROW_TILE) + B;
   L.max_units = (int64_t)cus * UNITS_PER_CU + ceil_div(p->total_k, KEY_TILE) + B;
+  L.key_tiles = ceil_div(p->total_k, TILE_ROWS) + B;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -85,7 +87,10 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_seq = take(sizeof(int) * B);
   L.kv_off = take(sizeof(int) * (B + 1));
   L.kv_rank = take(sizeof(int) * B);
-  L.lse = L.rowinfo = L.part_dk = L.part_dv = 0;
+  L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
+  const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
+  if (entry != ATTN_ENTRY_BWD) L.vt = take(tt_bytes);   // V^T for the forward
+  if (entry != ATTN_ENTRY_FWD) L.kt = take(tt_bytes);   // K^T for dQ
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
     L.rowinfo = take(sizeof(float) * 4 * rows);
@@ -233,6 +238,8 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.plan = plan_view(ws, L);
   char* base = static_cast<char*>(ws);
   a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
+  if (L.kt) a.kt = reinterpret_cast<uint16_t*>(base + L.kt);
+  if (L.vt) a.vt = reinterpret_cast<uint16_t*>(base + L.vt);
   if (L.rowinfo) a.rowinfo = reinterpret_cast<float*>(base + L.rowinfo);
   if (L.part_dk) {
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
@@ -308,6 +315,7 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   set_view(out, &a.out, &a.o_ts, &a.o_hs);
   a.lse = lse;
   if (p->batch == 0) return ATTN_OK;
+  RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
   return hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, false, (int)L.row_tiles, s),
                     "forward launch");
 }
@@ -342,6 +350,7 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = const_cast<float*>(lse);
   if (p->batch == 0) return ATTN_OK;
+  RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
   RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
   return launch_backward(p, a, L, s);
 }
@@ -379,6 +388,8 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
+  if (p->batch > 0)
+    RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
   RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
   if (p->batch > 0)
     RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),

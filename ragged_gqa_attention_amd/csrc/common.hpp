@@ -119,7 +119,9 @@ struct LogitConsts {
 
 // Per-sequence facts written by the planner (int32 each, SEQ_FIELDS per sequence).
 enum SeqField {
-  SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS, SQ_NCHUNK, SQ_CHUNK, SQ_KTILES, SEQ_FIELDS
+  SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS, SQ_NCHUNK, SQ_CHUNK, SQ_KTILES,
+  SQ_TTOFF,   // first 64-key transposed tile of the sequence (prefix of ceil(Lk / 64))
+  SEQ_FIELDS
 };
 
 // Work lists built on the device; all arrays live in the caller's workspace.

@@ -44,20 +44,7 @@ constexpr int PAIR_KEYS = KEY_TILE / (KV_WAVES / 2);  // keys of one wave pair
 constexpr int KB = PAIR_KEYS / 32;                    // 32-key blocks per wave
 constexpr int LOADS_PER_WAVE = CHUNKS / 4;          // 4-chunk blocks of a 16-row group (5)
 static_assert(KV_WAVES == 8 && KB == 1, "eight waves: wave w copies tensor w / 4, row group w % 4");
-constexpr int BLK_ELEMS = 64 * 8;                    // one block: 16 rows x 4 chunks
-constexpr int TILE_ELEMS = KV_ROW_STEP * HEAD_DIM;
-static_assert(KV_ROW_STEP == 64, "four 16-row groups per step");
-
-// Blocked tile of 64 rows x 20 chunks (16 bytes each): block (r / 16, c / 4)
-// holds rows 16 (r/16) .. +15 and chunks 4 (c/4) .. +3 as 64 consecutive
-// slots, row-major inside, with the chunk's two low bits XOR-ed with
-// (r / 4) % 4.  One wave load (64 lanes x 16 bytes) fills one block, reading
-// 64 contiguous bytes from each of 16 rows.  A row read (16 lanes = 16
-// consecutive rows of one chunk) and a transposing read (4 rows x 2 adjacent
-// chunks) both touch 16 distinct 16-byte bank slots.
-__device__ __forceinline__ int blk_off(int r, int c) {
-  return (((r >> 4) * (CHUNKS / 4) + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
-}
+static_assert(KV_ROW_STEP == TILE_ROWS, "a step is one row tile (see blk_off)");
 
 struct KvShared {
   uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (blocked)
@@ -132,7 +119,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // ks % 2 the XOR pattern.
   const int arow = ROLE * 32 + l32;
   const int roff[2] = {blk_off(arow, g), blk_off(arow, 2 + g)};
-  // Transposing reads (see read_tr_a): lane (i, G) reads row 4 (G/2) + i/4
+  // Transposing reads (see read_tr): lane (i, G) reads row 4 (G/2) + i/4
   // (+ 8) of the 16-row k-step t, features 16 (G%2) + 4 (i%4) of the
   // 32-feature block db, which is chunk 4 db + 2 (G%2) + (i%4)/2; each (t, db)
   // is one block further.

@@ -15,16 +15,30 @@
 // the small residual log2 l subtracted (see fwd.hip), so no two large numbers
 // are ever subtracted.
 //
-// A workgroup owns 256 folded rows (like the forward) and walks the keys.
+// A workgroup owns 256 folded rows (like the forward) and walks the keys in
+// steps of 64, copied to LDS with direct loads (double-buffered): K and V as
+// row tiles and K^T as its pre-transposed key tile, so every product reads
+// its LDS operand with one 16-byte read per MFMA.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
+namespace {
+
+// LDS of one key step: K and V rows (row tiles, blk_off) and K^T (transposed
+// key tile, tt_off), double-buffered.
+struct DqShared {
+  uint16_t k[2][TILE_ELEMS];
+  uint16_t v[2][TILE_ELEMS];
+  uint16_t kt[2][TILE_ELEMS];
+};
+
+}  // namespace
+
 template <class T, bool CAP>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KEY_STEP * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KEY_STEP * LDK];
+  __shared__ __attribute__((aligned(16))) DqShared sm;
 
   const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
   if (rank < 0) return;
@@ -35,11 +49,12 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int rows = sq[SQ_ROWS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int row = tile * ROW_TILE + wave * 32 + l32;
   const bool row_ok = row < rows;
   const int rr = row_ok ? row : rows - 1;
-  const int ti = rr / a.hq;
+  const int ti = fast_div(rr, a.hq_mul, a.hq_shift);
   const int hh = rr - ti * a.hq;
   const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
 
@@ -63,36 +78,57 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
 
-  const int ntiles = (Lk + KEY_STEP - 1) / KEY_STEP;
-  PairStager<ROW_THREADS, KEY_STEP> st;
-  if (ntiles > 0) {
-    st.load_keys(a.k, a.k_ts, a.v, a.v_ts, k0, min(Lk, KEY_STEP));
-    st.template store<LDK, LDK>(Ks[0], Vs[0]);
-  }
-  __syncthreads();
+  const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  const uint16_t* kt_seq = a.kt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
+  // copies of key step kt (60 wave loads): waves 0-3 copy a 16-row group of K
+  // and three K^T loads each, waves 4-7 a 16-row group of V and two K^T loads
+  auto issue = [&](int kt, int buf) {
+    const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
+    if (wave < 4) {
+      load_row_tile(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
+                    wave, lane);
+      load_tt_tile<3>(sm.kt[buf], ktt, 3 * wave, lane);
+    } else {
+      load_row_tile(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk, a.zero,
+                    wave - 4, lane);
+      load_tt_tile<2>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
+    }
+  };
 
+  // lane-constant LDS offsets: K / V row reads (row kb * 32 + l32, chunk
+  // 2 ks + g) and K^T reads (feature row 32 db + l32, chunk 2 (2 kb + s) + g)
+  const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
+  int toff[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) toff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
+
+  if (ntiles > 0) issue(0, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int kbase = kt * KEY_STEP;
-    const bool more = kt + 1 < ntiles;
-    if (more)
-      st.load_keys(a.k, a.k_ts, a.v, a.v_ts, (int64_t)k0 + kbase + KEY_STEP,
-                   Lk - kbase - KEY_STEP);
-    const uint16_t* Kb = Ks[kt & 1];
-    const uint16_t* Vb = Vs[kt & 1];
+    const int buf = kt & 1;
+    // tile kt has landed for every wave, and every wave is done with kt - 1
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
+    const int kbase = kt * TILE_ROWS;
+    const uint16_t* Kb = sm.k[buf];
+    const uint16_t* Vb = sm.v[buf];
+    const uint16_t* KTb = sm.kt[buf];
     const float cb = cb0 - (float)kbase;
-    const bool full = kbase + KEY_STEP <= Lk;
+    const bool full = kbase + TILE_ROWS <= Lk;
     const int kleft = Lk - kbase - 4 * g;
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // S^T[key][row] = K Q^T and dP^T[key][row] = V dO^T (lane = row)
       f32x16 S = f32x16{}, dP = f32x16{};
-      const uint16_t* kp = Kb + (kb * 32 + l32) * LDK + g * 8;
-      const uint16_t* vp = Vb + (kb * 32 + l32) * LDK + g * 8;
+      const int rb = kb * 2 * BLK_COLS * BLK_ELEMS;   // rows kb * 32 ..
 #pragma unroll
       for (int ks = 0; ks < KSTEPS; ++ks) {
-        S = mfma32<T>(load16(kp + ks * 16), qf[ks], S);
-        dP = mfma32<T>(load16(vp + ks * 16), df[ks], dP);
+        const int off = koff[ks & 1] + (ks >> 1) * BLK_ELEMS + rb;
+        S = mfma32<T>(load16(Kb + off), qf[ks], S);
+        dP = mfma32<T>(load16(Vb + off), df[ks], dP);
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -115,15 +151,14 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
       for (int s = 0; s < 2; ++s)
         sb[s] = u32x4{pack2<T>(S[8 * s + 0], S[8 * s + 1]), pack2<T>(S[8 * s + 2], S[8 * s + 3]),
                       pack2<T>(S[8 * s + 4], S[8 * s + 5]), pack2<T>(S[8 * s + 6], S[8 * s + 7])};
-      // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row]
+      // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row]; the K^T operand is one
+      // 16-byte read in the key order of sb
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          dQ[db] = mfma32<T>(read_tr_a<LDK>(Kb, kb * 32 + s * 16, db * 32, lane), sb[s], dQ[db]);
+          dQ[db] = mfma32<T>(load16(KTb + toff[kb][s] + db * 32 * TILE_ROWS), sb[s], dQ[db]);
     }
-    if (more) st.template store<LDK, LDK>(Ks[(kt + 1) & 1], Vs[(kt + 1) & 1]);
-    __syncthreads();
   }
 
   if (!row_ok) return;

@@ -11,7 +11,10 @@
 // are folded into one M dimension (row = token * Hq + head): a workgroup's 256
 // rows reuse each staged K/V tile 256 times.  Each wave owns 32 rows and forms
 // S^T = K Q^T (keys x rows, Q in registers), so an accumulator lane owns one row
-// and O^T = V^T P^T keeps the row scale per lane.
+// and O^T = V^T P^T keeps the row scale per lane.  Key steps of 64 are copied
+// to LDS with direct loads (double-buffered): K as a row tile, V as its
+// pre-transposed key tile, so both products read their LDS operand with one
+// 16-byte read per MFMA.
 //
 // Softmax offset.  Distances are measured from the clamped centre
 // c_i = max(i + Lk - Lq, 0): for a row with i + Lk - Lq < 0 every key lies to
@@ -32,10 +35,20 @@
 
 namespace rga {
 
+namespace {
+
+// LDS of one key step: the K rows (row tile, blk_off) and V^T (transposed key
+// tile, tt_off), double-buffered.
+struct FwdShared {
+  uint16_t k[2][TILE_ELEMS];
+  uint16_t vt[2][TILE_ELEMS];
+};
+
+}  // namespace
+
 template <class T, bool CAP, bool DELTA>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][KEY_STEP * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][KEY_STEP * LDV];
+  __shared__ __attribute__((aligned(16))) FwdShared sm;
 
   const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
   if (rank < 0) return;
@@ -46,11 +59,12 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   const int rows = sq[SQ_ROWS];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int row = tile * ROW_TILE + wave * 32 + l32;
   const bool row_ok = row < rows;
   const int rr = row_ok ? row : rows - 1;
-  const int ti = rr / a.hq;
+  const int ti = fast_div(rr, a.hq_mul, a.hq_shift);
   const int hh = rr - ti * a.hq;
 
   // Q row as B operand: k-step ks covers features 16ks + 8g .. +7
@@ -72,35 +86,51 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) O[db] = f32x16{};
 
-  const int ntiles = (Lk + KEY_STEP - 1) / KEY_STEP;
-  PairStager<ROW_THREADS, KEY_STEP> st;
-  if (ntiles > 0) {
-    st.load_keys(a.k, a.k_ts, a.v, a.v_ts, k0, min(Lk, KEY_STEP));
-    st.template store<LDK, LDV>(Ks[0], Vs[0]);
-  }
-  __syncthreads();
+  const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  const uint16_t* vt_seq = a.vt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
+  // copies of key step kt: waves 0-3 the K rows (one 16-row group each),
+  // waves 4-7 V^T (five 8-feature-row loads each)
+  auto issue = [&](int kt, int buf) {
+    if (wave < 4)
+      load_row_tile(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
+                    wave, lane);
+    else
+      load_tt_tile<5>(sm.vt[buf], vt_seq + (int64_t)kt * TILE_ELEMS, 5 * (wave - 4), lane);
+  };
 
+  // lane-constant LDS offsets: K row reads (row kb * 32 + l32, chunk 2 ks + g)
+  // and V^T reads (feature row 32 db + l32, chunk 2 (2 kb + s) + g)
+  const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
+  int voff[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int s = 0; s < 2; ++s) voff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
+
+  if (ntiles > 0) issue(0, 0);
   for (int kt = 0; kt < ntiles; ++kt) {
-    const int kbase = kt * KEY_STEP;
-    const bool more = kt + 1 < ntiles;
-    if (more)
-      st.load_keys(a.k, a.k_ts, a.v, a.v_ts, (int64_t)k0 + kbase + KEY_STEP,
-                   Lk - kbase - KEY_STEP);
-    const uint16_t* Kb = Ks[kt & 1];
-    const uint16_t* Vb = Vs[kt & 1];
+    const int buf = kt & 1;
+    // tile kt has landed for every wave, and every wave is done with kt - 1
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
+    const int kbase = kt * TILE_ROWS;
+    const uint16_t* Kb = sm.k[buf];
+    const uint16_t* Vb = sm.vt[buf];
 
+    // S^T[key][row] = K Q^T (lane = row)
     f32x16 S[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      S[kb] = f32x16{};
-      const uint16_t* kp = Kb + (kb * 32 + l32) * LDK + g * 8;
+    for (int kb = 0; kb < 2; ++kb) S[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        S[kb] = mfma32<T>(load16(kp + ks * 16), qf[ks], S[kb]);
-    }
+    for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        S[kb] = mfma32<T>(load16(Kb + koff[ks & 1] + (ks >> 1) * BLK_ELEMS + kb * 2 * BLK_COLS * BLK_ELEMS),
+                          qf[ks], S[kb]);
 
     const float cb = cb0 - (float)kbase;
-    const bool full = kbase + KEY_STEP <= Lk;
+    const bool full = kbase + TILE_ROWS <= Lk;
     const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -161,17 +191,15 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       }
     }
 
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]
+    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; the V^T operand is one
+    // 16-byte read in the key order of pb
 #pragma unroll
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
-          O[db] = mfma32<T>(read_tr_a<LDV>(Vb, kb * 32 + s * 16, db * 32, lane), pb[kb][s], O[db]);
-
-    if (more) st.template store<LDK, LDV>(Ks[(kt + 1) & 1], Vs[(kt + 1) & 1]);
-    __syncthreads();
+          O[db] = mfma32<T>(load16(Vb + voff[kb][s] + db * 32 * TILE_ROWS), pb[kb][s], O[db]);
   }
 
   // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta

@@ -16,11 +16,13 @@ constexpr int ROW_TILE = ROW_WAVES * 32;
 // Key-tile kernel (dK/dV): one workgroup = 8 waves = 4 wave pairs x 32 keys.
 constexpr int KV_THREADS = 512;
 constexpr int KEY_TILE = 128;
+// Rows or keys of one LDS tile (row tiles and transposed key tiles, see
+// tiles.hpp): the key step of the row-tile kernels and the row step of dK/dV.
+constexpr int TILE_ROWS = 64;
+constexpr int TILE_ELEMS = TILE_ROWS * HEAD_DIM;
 // Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
 // P and dS for half of them).
-constexpr int KV_ROW_STEP = 64;
-// Keys staged per step of the row-tile kernels.
-constexpr int KEY_STEP = 64;
+constexpr int KV_ROW_STEP = TILE_ROWS;
 
 struct AttnArgs {
   const uint16_t* q;    int64_t q_ts, q_hs;
@@ -38,6 +40,10 @@ struct AttnArgs {
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;
   const uint16_t* zero; // 512 zero bytes: source of the loads of rows past a tile's end
+  // Transposed 64-key tiles of K and V (see tt_key_pos), tile i at i * 64 * 160:
+  // [feature][key], written by transpose_keys_kernel; keys past Lk are zero.
+  uint16_t* kt;
+  uint16_t* vt;
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
   const float* slopes;  int64_t slopes_stride;
@@ -66,6 +72,8 @@ struct PlanArgs {
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
+// Writes the transposed key tiles a.kt and / or a.vt (null pointers are skipped).
+hipError_t launch_transpose_keys(const AttnArgs& a, int tiles, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
                       hipStream_t s);
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);

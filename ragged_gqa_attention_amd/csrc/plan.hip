@@ -32,9 +32,9 @@ __device__ __forceinline__ long long block_sum(long long v, long long* red) {
   return r;
 }
 
-// off[r] = sum_{r' < r} cnt(order[r']) for r = 0..B, cnt read through `count`.
-template <class F>
-__device__ __forceinline__ void block_exclusive_scan(int B, int* off, F count, int* part) {
+// put(r, sum_{r' < r} count(r')) for r = 0..B.
+template <class F, class G>
+__device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, int* part) {
   const int tid = threadIdx.x;
   const int seg = (B + PLAN_THREADS - 1) / PLAN_THREADS;
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
@@ -49,12 +49,12 @@ __device__ __forceinline__ void block_exclusive_scan(int B, int* off, F count, i
       part[i] = run;
       run += c;
     }
-    off[B] = run;
+    put(B, run);
   }
   __syncthreads();
   int run = part[tid];
   for (int r = lo; r < hi; ++r) {
-    off[r] = run;
+    put(r, run);
     run += count(r);
   }
   __syncthreads();
@@ -135,18 +135,76 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanArgs a) {
   __syncthreads();
 
   const int hq = a.hq;
-  block_exclusive_scan(B, a.plan.fwd_off, [&](int r) {
+  block_exclusive_scan(B, [&](int r) {
     const int b = a.plan.fwd_seq[r];
     return (seq[b * SEQ_FIELDS + SQ_LQ] * hq + ROW_TILE - 1) / ROW_TILE;
-  }, part);
-  block_exclusive_scan(B, a.plan.kv_off, [&](int r) {
+  }, [&](int r, int v) { a.plan.fwd_off[r] = v; }, part);
+  block_exclusive_scan(B, [&](int r) {
     const int b = a.plan.kv_seq[r];
     return seq[b * SEQ_FIELDS + SQ_KTILES] * seq[b * SEQ_FIELDS + SQ_NCHUNK];
-  }, part);
+  }, [&](int r, int v) { a.plan.kv_off[r] = v; }, part);
+  // transposed 64-key tiles, in sequence order
+  block_exclusive_scan(B, [&](int b) {
+    return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
+  }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
 }
 
 hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(plan_kernel, 1, PLAN_THREADS, 0, s, a);
+  return hipGetLastError();
+}
+
+// Transposed key tiles (see tt_key_pos): workgroup i writes tile i of K and of
+// V, i.e. keys [64 j, 64 j + 64) of the sequence whose tiles start at or
+// before i (j = i - first tile); keys past Lk become zeros.
+__global__ __launch_bounds__(WG_THREADS) void transpose_keys_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint16_t rows[TILE_ROWS][HEAD_DIM + 8];
+  const int tile = blockIdx.x;
+  const int* seq = a.plan.seq;
+  if (a.batch <= 0) return;
+  int lo = 0, hi = a.batch - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seq[mid * SEQ_FIELDS + SQ_TTOFF] <= tile) lo = mid; else hi = mid - 1;
+  }
+  const int* sb = seq + lo * SEQ_FIELDS;
+  const int j = tile - sb[SQ_TTOFF];
+  const int Lk = sb[SQ_LK];
+  if (j < 0 || j * TILE_ROWS >= Lk) return;
+  const int kbase = sb[SQ_K0] + j * TILE_ROWS;
+  const int nkeys = min(TILE_ROWS, Lk - j * TILE_ROWS);
+  const int tid = threadIdx.x;
+  for (int t = 0; t < 2; ++t) {
+    uint16_t* dst = t ? a.vt : a.kt;
+    if (!dst) continue;    // uniform
+    const uint16_t* src = t ? a.v : a.k;
+    const int64_t ts = t ? a.v_ts : a.k_ts;
+    for (int i = tid; i < TILE_ROWS * CHUNKS; i += WG_THREADS) {
+      const int key = i / CHUNKS, c = i - key * CHUNKS;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
+      *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
+    }
+    __syncthreads();
+    dst += (int64_t)tile * TILE_ELEMS;
+    for (int o = tid; o < HEAD_DIM * (TILE_ROWS / 8); o += WG_THREADS) {
+      const int d = o / (TILE_ROWS / 8), c = o - d * (TILE_ROWS / 8);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo16 = rows[tt_key_pos(8 * c + 2 * e)][d];
+        const uint32_t hi16 = rows[tt_key_pos(8 * c + 2 * e + 1)][d];
+        w[e] = lo16 | (hi16 << 16);
+      }
+      *reinterpret_cast<u32x4*>(dst + d * TILE_ROWS + c * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_transpose_keys(const AttnArgs& a, int tiles, hipStream_t s) {
+  if (tiles <= 0 || (!a.kt && !a.vt)) return hipSuccess;
+  hipLaunchKernelGGL(transpose_keys_kernel, tiles, WG_THREADS, 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,15 +1,27 @@
-// LDS tiles, operand reads and the logit pipeline shared by the gfx950 kernels.
+// LDS tile layouts, direct global -> LDS copies, operand reads and the logit
+// pipeline shared by the gfx950 kernels.
 //
-// Every tile lives in LDS row-major (16-byte chunks of a 160-element row).  A
-// product that contracts over the rows of a tile (P^T V, dS^T Q, P^T dO,
-// dS K) reads its A operand with ds_read_b64_tr_b16, the CDNA4 transposing LDS
-// read: inside each group of 16 lanes, lane i receives element i % 4 of the
-// 8-byte words addressed by lanes 4e + i / 4 (e = 0..3).  So no transposed
-// copy of any tile is ever written.
+// Two tile layouts, both filled by direct loads (global_load_lds_dwordx4: one
+// wave instruction copies 64 lanes x 16 bytes into 64 consecutive 16-byte LDS
+// slots, so no staging registers are needed) and both read without LDS bank
+// conflicts.  LDS serves a 16-byte read 16 lanes at a time from 16 bank
+// slots of 16 bytes (measured on gfx950: odd row strides in 16-byte units are
+// conflict-free, a 320-byte stride is 4-way).
 //
-// Rows at or past a sequence's end are staged as zeros: the padding of the
-// packed views is arbitrary (NaN in the tests) and 0 * NaN would poison MFMA
-// sums even where the softmax weight is exactly zero.
+//  * Row tile: 64 rows (keys or folded query rows) x 160 features = 20 chunks
+//    of 16 bytes per row, stored in blocks of 16 rows x 4 chunks (blk_off).
+//    Read one chunk per lane ("row read", the A/B operand of a product that
+//    contracts over features) or with the transposing read (the operand of a
+//    product that contracts over rows).
+//  * Transposed key tile: 160 feature rows x 64 keys, written once per call
+//    into the workspace by transpose_keys_kernel with the keys of each
+//    16-key group permuted (tt_key_pos) so that one 16-byte read gives a lane
+//    exactly the keys that the accumulator layout of P / dS assigns it.  It
+//    replaces the transposing read for K^T (dQ) and V^T (P V).
+//
+// Rows at or past a sequence's end are loaded from a zero block: the padding
+// of the packed views is arbitrary (NaN in the tests) and 0 * NaN would poison
+// MFMA sums even where the softmax weight is exactly zero.
 #pragma once
 
 #include "common.hpp"
@@ -17,123 +29,55 @@
 
 namespace rga {
 
-// Row stride of the LDS tiles read with 16-byte row reads (b128): 336 bytes puts
-// the rows of each 8-lane phase on distinct 16-byte bank slots.
-constexpr int LDK = HEAD_DIM + 8;
-// Row stride of tiles read only through the transposing read: 352 bytes puts
-// the four rows of each 16-lane group on distinct 32-byte bank slots.
-constexpr int LDV = HEAD_DIM + 16;
-
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void gbl_void_t;
+
+constexpr int BLK_ELEMS = 64 * 8;                     // one 16-row x 4-chunk block
+constexpr int BLK_COLS = CHUNKS / 4;                  // blocks across a row (5)
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// ds_read_b64_tr_b16, the CDNA4 transposing LDS read: inside each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte words addressed by lanes
+// 4e + i / 4 (e = 0..3).  Reading rows 4 (G/2) + i/4 and (+ 8) at features
+// c0 + 16 (G%2) + 4 (i%4) (G = lane / 16) gives lane (l32, g) the A operand
+// X^T[c0 + l32][r0 + 4g + 0..3, r0 + 8 + 4g + 0..3] of a 32x32x16 product that
+// contracts over tile rows, in the k order of an accumulator reused as B.
 __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
   return __builtin_bit_cast(u32x2, v);
 }
 
-// A operand of a 32x32x16 product that contracts over tile rows: lane
-// (l32, g) receives X[r0 + 4g + 0..3][c0 + l32] and X[r0 + 8 + 4g + 0..3][c0 + l32],
-// the k order of an accumulator (rows 8(r/4) + 4g + r%4) reused as B operand.
-template <int LD>
-__device__ __forceinline__ u32x4 read_tr_a(const uint16_t* X, int r0, int c0, int lane) {
-  const int i = lane & 15;
-  const int G = lane >> 4;
-  const uint16_t* p = X + (r0 + 4 * (G >> 1) + (i >> 2)) * LD + c0 + 16 * (G & 1) + 4 * (i & 3);
-  const u32x2 lo = read_tr(p);
-  const u32x2 hi = read_tr(p + 8 * LD);
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+// Element offset of chunk c of row r in a row tile: block (r / 16, c / 4)
+// holds 64 consecutive slots, row-major inside, with the chunk's two low bits
+// XOR-ed with (r / 4) % 4.  One wave load fills one block, reading 64
+// contiguous bytes from each of 16 rows; a row read (16 lanes = 16
+// consecutive rows of one chunk) and a transposing read (4 rows x 2 adjacent
+// chunks) both touch 16 distinct bank slots.
+__device__ __forceinline__ int blk_off(int r, int c) {
+  return (((r >> 4) * BLK_COLS + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
 }
 
-// Row-major staging of up to two 160-wide sources into LDS through registers:
-// load() issues the global reads for the next tile, store() writes them once
-// the current tile's compute no longer needs the buffer.  Each thread owns
-// PER_THREAD 16-byte chunks; rows [0, ROWS) come from source 0 and rows
-// [ROWS, 2 ROWS) from source 1.
-template <int THREADS, int ROWS>
-struct PairStager {
-  static constexpr int TASKS = 2 * ROWS * CHUNKS;
-  static constexpr int PER_THREAD = TASKS / THREADS;
-  static_assert(TASKS % THREADS == 0, "tile chunks must divide evenly over the threads");
-  u32x4 reg[PER_THREAD];
-
-  // rows of a key tile: row r of source s is token base + r, valid if r < valid
-  __device__ __forceinline__ void load_keys(const uint16_t* s0, int64_t ts0, const uint16_t* s1,
-                                            int64_t ts1, int64_t base, int valid) {
-#pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int t = threadIdx.x + u * THREADS;
-      const int which = t >= ROWS * CHUNKS;
-      const int tt = t - which * ROWS * CHUNKS;
-      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
-      const uint16_t* src = which ? s1 : s0;
-      const int64_t ts = which ? ts1 : ts0;
-      reg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (r < valid) reg[u] = load16(src + (base + r) * ts + c * 8);
-    }
-  }
-
-  // rows of a folded (token, head) tile: folded row R = row0 + r, token R / hq,
-  // head R % hq; valid if R < row_end
-  __device__ __forceinline__ void load_rows(const uint16_t* s0, int64_t ts0, int64_t hs0,
-                                            const uint16_t* s1, int64_t ts1, int64_t hs1,
-                                            int q0, int hq, int row0, int row_end) {
-#pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int t = threadIdx.x + u * THREADS;
-      const int which = t >= ROWS * CHUNKS;
-      const int tt = t - which * ROWS * CHUNKS;
-      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
-      const int R = row0 + r;
-      reg[u] = u32x4{0u, 0u, 0u, 0u};
-      if (R < row_end) {
-        const int tok = R / hq, h = R - tok * hq;
-        reg[u] = which ? load16(s1 + (int64_t)(q0 + tok) * ts1 + (int64_t)h * hs1 + c * 8)
-                       : load16(s0 + (int64_t)(q0 + tok) * ts0 + (int64_t)h * hs0 + c * 8);
-      }
-    }
-  }
-
-  template <int LD0, int LD1>
-  __device__ __forceinline__ void store(uint16_t* d0, uint16_t* d1) const {
-#pragma unroll
-    for (int u = 0; u < PER_THREAD; ++u) {
-      const int t = threadIdx.x + u * THREADS;
-      const int which = t >= ROWS * CHUNKS;
-      const int tt = t - which * ROWS * CHUNKS;
-      const int r = tt / CHUNKS, c = tt - r * CHUNKS;
-      uint16_t* dst = which ? d1 + r * LD1 : d0 + r * LD0;
-      *reinterpret_cast<u32x4*>(dst + c * 8) = reg[u];
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Swizzled row tiles filled by direct global->LDS loads.
-//
-// A tile of R rows x 160 16-bit features is stored without padding (320-byte
-// rows, 20 chunks of 16 bytes) with the chunk index of row r XOR-ed with
-// (r / 4) % 4.  LDS serves 16 lanes of a 16-byte read per pass from 16 chunk
-// banks; rows r and r + 4k then start on different banks, so the 16 rows of a
-// row read (one chunk each) and the 4 rows x 2 chunks of a transposing read
-// both touch 16 distinct chunk banks.  The XOR only flips the two low bits of
-// the chunk index, so a chunk never leaves its row.
-__device__ __forceinline__ int swz_off(int row, int chunk) {
-  return row * HEAD_DIM + ((chunk ^ ((row >> 2) & 3)) << 3);
+// Position of key k (0..63) inside a feature row of a transposed key tile:
+// the middle two quads of every 16-key group are swapped, so lane half g of a
+// 16-byte read at chunk 2 s + g gets keys 16 s + {4g .. 4g + 3, 8 + 4g .. 8 + 4g + 3}.
+__device__ __forceinline__ int tt_key_pos(int k) {
+  const int j = k & 15;
+  const int q = j >> 2;
+  return (k & ~15) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2) | (j & 3);
 }
 
-// Logical (row, chunk) held by physical 16-byte slot `slot` of a swizzled tile.
-__device__ __forceinline__ void swz_slot(int slot, int& row, int& chunk) {
-  row = slot / CHUNKS;
-  chunk = (slot - row * CHUNKS) ^ ((row >> 2) & 3);
+// Element offset of 16-byte chunk c (keys 8c .. 8c + 7 in tt_key_pos order)
+// of feature row d in a transposed key tile in LDS: the chunk index is XOR-ed
+// with (d / 2) % 8, so 16 consecutive feature rows of one chunk hit 16
+// distinct bank slots.
+__device__ __forceinline__ int tt_off(int d, int c) {
+  return d * TILE_ROWS + ((c ^ ((d >> 1) & 7)) << 3);
 }
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void gbl_void_t;
 
 // One wave-wide direct load: lane l copies the 16 bytes at `src` (its own
 // address) to LDS at wave_dst + 16 l.  wave_dst must be the same for every lane.
@@ -145,15 +89,34 @@ __device__ __forceinline__ void load_lds16(const void* src, void* wave_dst) {
 // Wait for this wave's outstanding global loads (direct LDS loads included).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// read_tr_a for a swizzled tile.
-__device__ __forceinline__ u32x4 read_tr_swz(const uint16_t* X, int r0, int c0, int lane) {
-  const int i = lane & 15;
-  const int G = lane >> 4;
-  const int row = r0 + 4 * (G >> 1) + (i >> 2);
-  const int col = c0 + 16 * (G & 1) + 4 * (i & 3);
-  const u32x2 lo = read_tr(X + swz_off(row, col >> 3) + (col & 7));
-  const u32x2 hi = read_tr(X + swz_off(row + 8, col >> 3) + (col & 7));
-  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+// Copies the blocked row tile of rows [row0, row0 + 64) of a strided
+// [tokens, 160] view (rows past `nrows` read `zero`) with four waves: wave
+// group w (0..3) copies rows 16 w .. 16 w + 15, lane l holding row
+// 16 w + l / 4 for all five of its loads.
+__device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* src, int64_t ts,
+                                              int row0, int nrows, const uint16_t* zero,
+                                              int w, int lane) {
+  const int r = 16 * w + (lane >> 2);
+  const int c = (lane & 3) ^ ((lane >> 4) & 3);
+  const bool ok = row0 + r < nrows;
+  const uint16_t* p = (ok ? src + (int64_t)(row0 + r) * ts : zero) + c * 8;
+#pragma unroll
+  for (int b = 0; b < BLK_COLS; ++b)
+    load_lds16(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
+}
+
+// Copies wave loads [i0, i0 + n) of a transposed key tile (20 loads of 8
+// feature rows each) from its global copy `src` (160 x 64 elements, unswizzled).
+template <int N>
+__device__ __forceinline__ void load_tt_tile(uint16_t* tile, const uint16_t* src, int i0, int lane) {
+  const int dl = lane >> 3, pc = lane & 7;
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int i = i0 + n;
+    const int d = 8 * i + dl;
+    const int c = pc ^ ((d >> 1) & 7);
+    load_lds16(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
+  }
 }
 
 // Capped logit pieces from a raw dot product q.k (see LogitConsts):
