@@ -32,7 +32,7 @@ METRIC = "fwd+full-VJP TFLOP/s (% MFMA peak) and ms/call, ragged GQA Hq=64 D=160
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense FP16/BF16 matrix peak
 HEAD_DIM = 160
 # credited flops per score element and head-dim unit, by phase (14 in total)
-PHASE_FLOPS = {"fwd": 4, "dkdv": 8, "dq": 2, "plan": 0, "reduce": 0}
+PHASE_FLOPS = {"fwd": 4, "dkdv": 8, "dq": 2, "plan": 0}
 
 
 def kernel_source_digest() -> str:

@@ -141,9 +141,8 @@ typedef enum {
   ATTN_PHASE_PLAN = 0,     /* work lists from cu_q / cu_k, transposed K / V key tiles */
   ATTN_PHASE_FWD = 1,      /* forward: out, lse, delta = rowsum(dout * out) */
   ATTN_PHASE_DKDV = 2,     /* dK, dV over all sharing heads */
-  ATTN_PHASE_DQ = 3,       /* dQ */
-  ATTN_PHASE_REDUCE = 4,   /* fixed-order sum of split dK / dV partials */
-  ATTN_PHASES = 5
+  ATTN_PHASE_DQ = 3,       /* dQ, and the fixed-order sum of split dK / dV partials */
+  ATTN_PHASES = 4
 } attn_phase;
 
 /* attn_varlen_full_vjp with per-phase timing.  `events` is NULL or holds

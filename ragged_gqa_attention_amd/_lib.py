@@ -27,7 +27,7 @@ ENTRY_BWD = 1
 ENTRY_FULL_VJP = 2
 
 # phases of the full-VJP call, in launch order
-PHASES = ("plan", "fwd", "dkdv", "dq", "reduce")
+PHASES = ("plan", "fwd", "dkdv", "dq")
 
 EXPORTED = (
     "attn_varlen_workspace_size",

@@ -33,7 +33,10 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 
 constexpr size_t ALIGN = 256;
 constexpr int MIN_CHUNK_ROWS = 512;     // below this a row chunk is not worth its partials
-constexpr int UNITS_PER_CU = 2;         // dK/dV work units aimed at per compute unit
+// dK/dV work units aimed at per compute unit, as a fraction: the dK/dV workgroup fills a
+// compute unit, so units run in about 1.5 rounds; more rounds balance better but write
+// more FP32 partials (modelled on the benchmark workloads, 1.5 was best).
+constexpr int UNITS_PER_CU_NUM = 3, UNITS_PER_CU_DEN = 2;
 constexpr int MAX_DEVICES = 64;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -71,7 +74,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   const int64_t B = p->batch;
   const int64_t rows = p->total_q * p->hq;
   L.row_tiles = ceil_div(rows, ROW_TILE) + B;
-  L.max_units = (int64_t)cus * UNITS_PER_CU + ceil_div(p->total_k, KEY_TILE) + B;
+  L.max_units = (int64_t)cus * UNITS_PER_CU_NUM / UNITS_PER_CU_DEN + ceil_div(p->total_k, KEY_TILE) + B;
   L.key_tiles = ceil_div(p->total_k, TILE_ROWS) + B;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -210,14 +213,15 @@ void set_view(const attn_tensor* t, uint16_t** data, int64_t* ts, int64_t* hs) {
   if (hs) *hs = t->head_stride;
 }
 
-// Shared prologue: checks, workspace, plan launch.  Fills `a` and `L`.
 attn_status record(const hipEvent_t* ev, int i, hipStream_t s) {
   if (!ev) return ATTN_OK;
   return hip_status(hipEventRecord(ev[i], s), "event record");
 }
 
-attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes,
-                     hipStream_t s, AttnArgs& a, Layout& L, const hipEvent_t* ev = nullptr) {
+// Shared prologue: checks and workspace.  Fills `a`, `L` and the planner's
+// arguments `pa`; launches nothing.
+attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes, AttnArgs& a,
+                     Layout& L, PlanArgs& pa) {
   RGA_TRY(check_problem(p));
   const int cus = device_cus();
   L = make_layout(p, entry, cus);
@@ -245,19 +249,24 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
     a.part_dv = reinterpret_cast<float*>(base + L.part_dv);
   }
-  PlanArgs pa;
   pa.cu_q = p->cu_q;
   pa.cu_k = p->cu_k;
   pa.batch = p->batch;
   pa.hq = p->hq;
   pa.total_q = p->total_q;
   pa.total_k = p->total_k;
-  pa.target_units = cus * UNITS_PER_CU;
+  pa.target_units = cus * UNITS_PER_CU_NUM / UNITS_PER_CU_DEN;
   pa.min_chunk = MIN_CHUNK_ROWS;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;
+  return ATTN_OK;
+}
+
+// Planner plus the transposed key tiles the entry needs (after the views are set).
+attn_status launch_prep_phase(const PlanArgs& pa, const AttnArgs& a, const Layout& L,
+                              hipStream_t s, const hipEvent_t* ev = nullptr) {
   RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
-  return hip_status(launch_plan(pa, s), "plan launch");
+  return hip_status(launch_prep(pa, a, (int)L.key_tiles, s), "plan launch");
 }
 
 attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
@@ -268,7 +277,8 @@ attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn
   return ATTN_OK;
 }
 
-// dK/dV, dQ and the partial reduction, after the row records are in place.
+// dK/dV, then dQ (which also sums the split dK/dV partials), after the row
+// records are in place.
 attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layout& L,
                             hipStream_t s, const hipEvent_t* ev = nullptr) {
   const bool cap = p->softcap > 0.0f;
@@ -277,8 +287,6 @@ attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layo
     RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
     RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
     RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles, s), "dQ launch"));
-    RGA_TRY(record(ev, ATTN_PHASE_REDUCE, s));
-    RGA_TRY(hip_status(launch_kv_reduce(a, p->dtype, s), "dK/dV reduce launch"));
   }
   return ATTN_OK;
 }
@@ -308,14 +316,15 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
   Layout L;
-  RGA_TRY(prologue(p, ATTN_ENTRY_FWD, workspace, workspace_bytes, s, a, L));
+  PlanArgs pa;
+  RGA_TRY(prologue(p, ATTN_ENTRY_FWD, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
   set_view(k, &a.k, &a.k_ts, nullptr);
   set_view(v, &a.v, &a.v_ts, nullptr);
   set_view(out, &a.out, &a.o_ts, &a.o_hs);
   a.lse = lse;
+  RGA_TRY(launch_prep_phase(pa, a, L, s));
   if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
   return hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, false, (int)L.row_tiles, s),
                     "forward launch");
 }
@@ -337,7 +346,8 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
   Layout L;
-  RGA_TRY(prologue(p, ATTN_ENTRY_BWD, workspace, workspace_bytes, s, a, L));
+  PlanArgs pa;
+  RGA_TRY(prologue(p, ATTN_ENTRY_BWD, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
   set_view(k, &a.k, &a.k_ts, nullptr);
   set_view(v, &a.v, &a.v_ts, nullptr);
@@ -349,8 +359,8 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = const_cast<float*>(lse);
+  RGA_TRY(launch_prep_phase(pa, a, L, s));
   if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
   RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
   return launch_backward(p, a, L, s);
 }
@@ -378,7 +388,8 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
   Layout L;
-  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, s, a, L, ev));
+  PlanArgs pa;
+  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
   set_view(k, &a.k, &a.k_ts, nullptr);
   set_view(v, &a.v, &a.v_ts, nullptr);
@@ -388,8 +399,7 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
-  if (p->batch > 0)
-    RGA_TRY(hip_status(launch_transpose_keys(a, (int)L.key_tiles, s), "key transpose launch"));
+  RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
   RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
   if (p->batch > 0)
     RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),
@@ -398,7 +408,6 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   if (p->batch == 0) {
     RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
     RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
-    RGA_TRY(record(ev, ATTN_PHASE_REDUCE, s));
   }
   return record(ev, ATTN_PHASES, s);
 }

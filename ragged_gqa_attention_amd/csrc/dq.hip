@@ -34,11 +34,55 @@ struct DqShared {
   uint16_t kt[2][TILE_ELEMS];
 };
 
+// dK / dV of the keys in slice `part` of `parts` (in units of 4 features):
+// sequences whose rows were split over several dK/dV workgroups sum their FP32
+// partials in chunk order and round once; keys of sequences without query
+// rows get exact zeros; unsplit sequences were stored by the dK/dV kernel.
+// The dK/dV kernel has finished (same stream), so its partials are complete.
+template <class T>
+__device__ __forceinline__ void reduce_kv_slice(const AttnArgs& a, int part, int parts) {
+  constexpr int QUADS = HEAD_DIM / 4;
+  const int64_t total = a.total_k * QUADS;
+  const int64_t per = (total + parts - 1) / parts;
+  const int64_t end = min(total, (part + 1) * per);
+  const int* seq = a.plan.seq;
+  for (int64_t idx = part * per + threadIdx.x; idx < end; idx += ROW_THREADS) {
+    const int t = (int)(idx / QUADS);
+    const int c4 = (int)(idx - (int64_t)t * QUADS);
+    int lo = 0, hi = a.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (seq[mid * SEQ_FIELDS + SQ_K0] <= t) lo = mid; else hi = mid - 1;
+    }
+    const int* sb = seq + lo * SEQ_FIELDS;
+    const int lt = t - sb[SQ_K0];
+    const int nchunk = sb[SQ_NCHUNK];
+    if (nchunk == 1 && lt < sb[SQ_LK]) continue;
+    f32x4 sk = {0.0f, 0.0f, 0.0f, 0.0f}, sv = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (lt < sb[SQ_LK] && nchunk > 1) {
+      const int kt = lt / KEY_TILE, kin = lt - kt * KEY_TILE;
+      const int64_t base = (int64_t)a.plan.kv_off[a.plan.kv_rank[lo]] + (int64_t)kt * nchunk;
+      for (int c = 0; c < nchunk; ++c) {
+        const int64_t off = ((base + c) * KEY_TILE + kin) * HEAD_DIM + c4 * 4;
+        sk += *reinterpret_cast<const f32x4*>(a.part_dk + off);
+        sv += *reinterpret_cast<const f32x4*>(a.part_dv + off);
+      }
+    }
+    *reinterpret_cast<u32x2*>(a.dk + (int64_t)t * a.dk_ts + c4 * 4) =
+        u32x2{pack2<T>(sk[0], sk[1]), pack2<T>(sk[2], sk[3])};
+    *reinterpret_cast<u32x2*>(a.dv + (int64_t)t * a.dv_ts + c4 * 4) =
+        u32x2{pack2<T>(sv[0], sv[1]), pack2<T>(sv[2], sv[3])};
+  }
+}
+
 }  // namespace
 
 template <class T, bool CAP>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) DqShared sm;
+
+  // the fixed-order dK / dV partial sums ride along with dQ, a slice per workgroup
+  if (a.total_k > 0) reduce_kv_slice<T>(a, blockIdx.x, gridDim.x);
 
   const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
   if (rank < 0) return;

@@ -71,14 +71,13 @@ struct PlanArgs {
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s);
-// Writes the transposed key tiles a.kt and / or a.vt (null pointers are skipped).
-hipError_t launch_transpose_keys(const AttnArgs& a, int tiles, hipStream_t s);
+// Planner (one workgroup) and, alongside it, the transposed key tiles a.kt and /
+// or a.vt (null pointers are skipped), up to key_tiles tiles each.
+hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
                       hipStream_t s);
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
-hipError_t launch_kv_reduce(const AttnArgs& a, int dtype, hipStream_t s);
 
 }  // namespace rga

@@ -16,43 +16,46 @@
 namespace rga {
 
 constexpr int PLAN_THREADS = 256;
-constexpr int WG_THREADS = 256;          // reduce and row-record kernels
+constexpr int WG_THREADS = 256;          // row-record kernel
 constexpr int PLAN_SORT_LIMIT = 8192;   // larger batches keep their natural order
 
+constexpr int PLAN_WAVES = PLAN_THREADS / 64;
+
+// Sum over the block (wave shuffles, then the four wave totals).
 __device__ __forceinline__ long long block_sum(long long v, long long* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  if (lane == 0) red[wave] = v;
   __syncthreads();
-  for (int s = PLAN_THREADS / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const long long r = red[0];
+  long long r = 0;
+#pragma unroll
+  for (int w = 0; w < PLAN_WAVES; ++w) r += red[w];
   __syncthreads();
   return r;
 }
 
-// put(r, sum_{r' < r} count(r')) for r = 0..B.
+// put(r, sum_{r' < r} count(r')) for r = 0..B.  Thread t owns a contiguous
+// segment of r; segment totals are scanned with wave shuffles.
 template <class F, class G>
 __device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, int* part) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = (B + PLAN_THREADS - 1) / PLAN_THREADS;
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
   int local = 0;
   for (int r = lo; r < hi; ++r) local += count(r);
-  part[tid] = local;
-  __syncthreads();
-  if (tid == 0) {
-    int run = 0;
-    for (int i = 0; i < PLAN_THREADS; ++i) {
-      const int c = part[i];
-      part[i] = run;
-      run += c;
-    }
-    put(B, run);
+  int x = local;   // inclusive scan inside the wave
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
   }
+  if (lane == 63) part[wave] = x;
   __syncthreads();
-  int run = part[tid];
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += part[w];
+  if (tid == PLAN_THREADS - 1) put(B, base + x);
+  int run = base + x - local;
   for (int r = lo; r < hi; ++r) {
     put(r, run);
     run += count(r);
@@ -60,10 +63,10 @@ __device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, int*
   __syncthreads();
 }
 
-__global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanArgs a) {
+__device__ __forceinline__ void plan_block(const PlanArgs& a) {
   __shared__ int bad;
-  __shared__ long long red[PLAN_THREADS];
-  __shared__ int part[PLAN_THREADS];
+  __shared__ long long red[PLAN_WAVES];
+  __shared__ int part[PLAN_WAVES];
   const int tid = threadIdx.x;
   const int B = a.batch;
   int* seq = a.plan.seq;
@@ -149,107 +152,84 @@ __global__ __launch_bounds__(PLAN_THREADS) void plan_kernel(const PlanArgs a) {
   }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
 }
 
-hipError_t launch_plan(const PlanArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(plan_kernel, 1, PLAN_THREADS, 0, s, a);
-  return hipGetLastError();
-}
-
-// Transposed key tiles (see tt_key_pos): workgroup i writes tile i of K and of
-// V, i.e. keys [64 j, 64 j + 64) of the sequence whose tiles start at or
-// before i (j = i - first tile); keys past Lk become zeros.
-__global__ __launch_bounds__(WG_THREADS) void transpose_keys_kernel(const AttnArgs a) {
+// Transposed key tile `tile` of K (t = 0) or V (t = 1) (see tt_key_pos): keys
+// [64 j, 64 j + 64) of the sequence whose tiles start at or before `tile`
+// (j = tile - first tile, tiles counted as in the planner's SQ_TTOFF); keys
+// past Lk become zeros.  The sequence is found from cu_k directly, so this runs
+// alongside the planner; an invalid cu_k (which the planner flags, and which
+// then plans no work) transposes nothing.
+__device__ __forceinline__ void transpose_block(const PlanArgs& pa, const AttnArgs& a, int tile,
+                                                int t) {
   __shared__ __attribute__((aligned(16))) uint16_t rows[TILE_ROWS][HEAD_DIM + 8];
-  const int tile = blockIdx.x;
-  const int* seq = a.plan.seq;
-  if (a.batch <= 0) return;
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (seq[mid * SEQ_FIELDS + SQ_TTOFF] <= tile) lo = mid; else hi = mid - 1;
-  }
-  const int* sb = seq + lo * SEQ_FIELDS;
-  const int j = tile - sb[SQ_TTOFF];
-  const int Lk = sb[SQ_LK];
-  if (j < 0 || j * TILE_ROWS >= Lk) return;
-  const int kbase = sb[SQ_K0] + j * TILE_ROWS;
-  const int nkeys = min(TILE_ROWS, Lk - j * TILE_ROWS);
+  __shared__ int part[PLAN_WAVES];
+  __shared__ int s_bad, s_b, s_j;
+  uint16_t* dst = t ? a.vt : a.kt;
+  const int B = pa.batch;
+  if (!dst || B <= 0) return;
   const int tid = threadIdx.x;
-  for (int t = 0; t < 2; ++t) {
-    uint16_t* dst = t ? a.vt : a.kt;
-    if (!dst) continue;    // uniform
-    const uint16_t* src = t ? a.v : a.k;
-    const int64_t ts = t ? a.v_ts : a.k_ts;
-    for (int i = tid; i < TILE_ROWS * CHUNKS; i += WG_THREADS) {
-      const int key = i / CHUNKS, c = i - key * CHUNKS;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
-      *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
-    }
-    __syncthreads();
-    dst += (int64_t)tile * TILE_ELEMS;
-    for (int o = tid; o < HEAD_DIM * (TILE_ROWS / 8); o += WG_THREADS) {
-      const int d = o / (TILE_ROWS / 8), c = o - d * (TILE_ROWS / 8);
-      uint32_t w[4];
+  if (tid == 0) { s_bad = 0; s_b = -1; s_j = 0; }
+  __syncthreads();
+  for (int b = tid; b <= B; b += PLAN_THREADS) {
+    const int ck = pa.cu_k[b];
+    bool fail = ck < 0 || (int64_t)ck > pa.total_k;
+    if (b == 0) fail |= ck != 0;
+    if (b == B) fail |= (int64_t)ck != pa.total_k;
+    if (b < B) fail |= pa.cu_k[b + 1] < ck;
+    if (fail) s_bad = 1;   // benign race: every writer stores 1
+  }
+  __syncthreads();
+  if (s_bad) return;
+  auto ntiles = [&](int b) { return (pa.cu_k[b + 1] - pa.cu_k[b] + TILE_ROWS - 1) / TILE_ROWS; };
+  block_exclusive_scan(B, ntiles, [&](int b, int off) {
+    if (b < B && off <= tile && tile < off + ntiles(b)) { s_b = b; s_j = tile - off; }
+  }, part);
+  const int b = s_b, j = s_j;
+  if (b < 0) return;
+  const int k0 = pa.cu_k[b];
+  const int Lk = pa.cu_k[b + 1] - k0;
+  const int kbase = k0 + j * TILE_ROWS;
+  const int nkeys = min(TILE_ROWS, Lk - j * TILE_ROWS);
+  const uint16_t* src = t ? a.v : a.k;
+  const int64_t ts = t ? a.v_ts : a.k_ts;
+  for (int i = tid; i < TILE_ROWS * CHUNKS; i += PLAN_THREADS) {
+    const int key = i / CHUNKS, c = i - key * CHUNKS;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
+    *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
+  }
+  __syncthreads();
+  dst += (int64_t)tile * TILE_ELEMS;
+  // task: feature pair (2 dp, 2 dp + 1) x chunk c of 8 keys
+  for (int o = tid; o < (HEAD_DIM / 2) * (TILE_ROWS / 8); o += PLAN_THREADS) {
+    const int dp = o / (TILE_ROWS / 8), c = o - dp * (TILE_ROWS / 8);
+    uint32_t w0[4], w1[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo16 = rows[tt_key_pos(8 * c + 2 * e)][d];
-        const uint32_t hi16 = rows[tt_key_pos(8 * c + 2 * e + 1)][d];
-        w[e] = lo16 | (hi16 << 16);
-      }
-      *reinterpret_cast<u32x4*>(dst + d * TILE_ROWS + c * 8) = u32x4{w[0], w[1], w[2], w[3]};
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t x0 = *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e)][2 * dp]);
+      const uint32_t x1 =
+          *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e + 1)][2 * dp]);
+      w0[e] = (x0 & 0xffffu) | (x1 << 16);
+      w1[e] = (x0 >> 16) | (x1 & 0xffff0000u);
     }
-    __syncthreads();
+    *reinterpret_cast<u32x4*>(dst + (2 * dp) * TILE_ROWS + c * 8) = u32x4{w0[0], w0[1], w0[2], w0[3]};
+    *reinterpret_cast<u32x4*>(dst + (2 * dp + 1) * TILE_ROWS + c * 8) =
+        u32x4{w1[0], w1[1], w1[2], w1[3]};
   }
 }
 
-hipError_t launch_transpose_keys(const AttnArgs& a, int tiles, hipStream_t s) {
-  if (tiles <= 0 || (!a.kt && !a.vt)) return hipSuccess;
-  hipLaunchKernelGGL(transpose_keys_kernel, tiles, WG_THREADS, 0, s, a);
-  return hipGetLastError();
+// Workgroup 0 plans; workgroups 1 + 2 i + t transpose key tile i of K or V.
+__global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(const PlanArgs pa, const AttnArgs a) {
+  if (blockIdx.x == 0) {
+    plan_block(pa);
+  } else {
+    const int i = blockIdx.x - 1;
+    transpose_block(pa, a, i >> 1, i & 1);
+  }
 }
 
-// dK / dV of every key: sequences whose rows were split sum their FP32
-// partials in chunk order; sequences without query rows get exact zeros;
-// unsplit sequences were written by the dK/dV kernel and are skipped.
-template <class T>
-__global__ __launch_bounds__(WG_THREADS) void kv_reduce_kernel(const AttnArgs a) {
-  constexpr int QUADS = HEAD_DIM / 4;
-  const int64_t idx = (int64_t)blockIdx.x * WG_THREADS + threadIdx.x;
-  if (idx >= a.total_k * QUADS) return;
-  const int t = (int)(idx / QUADS);
-  const int c4 = (int)(idx - (int64_t)t * QUADS);
-  const int* seq = a.plan.seq;
-  int lo = 0, hi = a.batch - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (seq[mid * SEQ_FIELDS + SQ_K0] <= t) lo = mid; else hi = mid - 1;
-  }
-  const int* s = seq + lo * SEQ_FIELDS;
-  const int lt = t - s[SQ_K0];
-  const int nchunk = s[SQ_NCHUNK];
-  f32x4 sk = {0.0f, 0.0f, 0.0f, 0.0f}, sv = {0.0f, 0.0f, 0.0f, 0.0f};
-  if (lt < s[SQ_LK] && nchunk > 0) {
-    if (nchunk == 1) return;
-    const int kt = lt / KEY_TILE, kin = lt - kt * KEY_TILE;
-    const int64_t base = (int64_t)a.plan.kv_off[a.plan.kv_rank[lo]] + (int64_t)kt * nchunk;
-    for (int c = 0; c < nchunk; ++c) {
-      const int64_t off = ((base + c) * KEY_TILE + kin) * HEAD_DIM + c4 * 4;
-      sk += *reinterpret_cast<const f32x4*>(a.part_dk + off);
-      sv += *reinterpret_cast<const f32x4*>(a.part_dv + off);
-    }
-  }
-  *reinterpret_cast<u32x2*>(a.dk + (int64_t)t * a.dk_ts + c4 * 4) =
-      u32x2{pack2<T>(sk[0], sk[1]), pack2<T>(sk[2], sk[3])};
-  *reinterpret_cast<u32x2*>(a.dv + (int64_t)t * a.dv_ts + c4 * 4) =
-      u32x2{pack2<T>(sv[0], sv[1]), pack2<T>(sv[2], sv[3])};
-}
-
-hipError_t launch_kv_reduce(const AttnArgs& a, int dtype, hipStream_t s) {
-  const int64_t n = a.total_k * (HEAD_DIM / 4);
-  if (n <= 0) return hipSuccess;
-  const int grid = (int)((n + WG_THREADS - 1) / WG_THREADS);
-  if (dtype == DT_BF16) hipLaunchKernelGGL(kv_reduce_kernel<BF16>, grid, WG_THREADS, 0, s, a);
-  else hipLaunchKernelGGL(kv_reduce_kernel<F16>, grid, WG_THREADS, 0, s, a);
+hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s) {
+  const int transposers = (a.kt || a.vt) ? 2 * key_tiles : 0;
+  hipLaunchKernelGGL(prep_kernel, 1 + transposers, PLAN_THREADS, 0, s, pa, a);
   return hipGetLastError();
 }
 
