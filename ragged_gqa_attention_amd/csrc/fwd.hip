@@ -118,22 +118,21 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
     const uint16_t* Kb = sm.k[buf];
     const uint16_t* Vb = sm.vt[buf];
 
-    // S^T[key][row] = K Q^T (lane = row)
-    f32x16 S[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) S[kb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        S[kb] = mfma32<T>(load16(Kb + koff[ks & 1] + (ks >> 1) * BLK_ELEMS + kb * 2 * BLK_COLS * BLK_ELEMS),
-                          qf[ks], S[kb]);
-
     const float cb = cb0 - (float)kbase;
     const bool full = kbase + TILE_ROWS <= Lk;
     const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
+
+    // S^T[key][row] = K Q^T (lane = row) for key block kb
+    f32x16 S[2];
+    auto scores = [&](int kb) {
+      S[kb] = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+      for (int ks = 0; ks < KSTEPS; ++ks)
+        S[kb] = mfma32<T>(load16(Kb + koff[ks & 1] + (ks >> 1) * BLK_ELEMS + kb * 2 * BLK_COLS * BLK_ELEMS),
+                          qf[ks], S[kb]);
+    };
+    // capped and biased logits (log2 units) of key block kb, masked past Lk
+    auto logits = [&](int kb) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
@@ -146,8 +145,55 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
         if (!full) x = jl < kleft ? x : -__builtin_inff();
         S[kb][r] = x;
       }
-    }
-    if (!CAP) {
+    };
+    // P rounded to the input dtype feeds the PV product, and O is normalised by
+    // the sum of those same rounded values (lsum_r), so O is an exact convex
+    // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
+    // matches dP.  L and the backward's residual use the exact FP32 sum.
+    u32x4 pb[2][2];
+    auto probs = [&](int kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(S[kb][r]);
+        lsum += p;
+        S[kb][r] = p;
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
+                          pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
+                          pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
+                          pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
+      }
+    };
+    // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb; the V^T
+    // operand is one 16-byte read in the key order of pb
+    auto pv = [&](int kb) {
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+          O[db] = mfma32<T>(load16(Vb + voff[kb][s] + db * 32 * TILE_ROWS), pb[kb][s], O[db]);
+    };
+
+    if (CAP) {
+      // the offset is fixed, so the two key blocks are independent: the MFMAs
+      // of one block can run while the VALU works on the other
+      scores(0);
+      scores(1);
+      logits(0);
+      probs(0);
+      pv(0);
+      logits(1);
+      probs(1);
+      pv(1);
+    } else {
+      scores(0);
+      scores(1);
+      logits(0);
+      logits(1);
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -165,41 +211,11 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[kb][r] -= mnew;
+      probs(0);
+      probs(1);
+      pv(0);
+      pv(1);
     }
-
-    // P rounded to the input dtype feeds the PV product, and O is normalised by
-    // the sum of those same rounded values (lsum_r), so O is an exact convex
-    // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
-    // matches dP.  L and the backward's residual use the exact FP32 sum.
-    u32x4 pb[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(S[kb][r]);
-        lsum += p;
-        S[kb][r] = p;
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
-                          pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
-                          pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
-                          pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
-      }
-    }
-
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row]; the V^T operand is one
-    // 16-byte read in the key order of pb
-#pragma unroll
-    for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          O[db] = mfma32<T>(load16(Vb + voff[kb][s] + db * 32 * TILE_ROWS), pb[kb][s], O[db]);
   }
 
   // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta
