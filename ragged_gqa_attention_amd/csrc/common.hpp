@@ -41,6 +41,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 struct F16 {};
 struct BF16 {};
 
+// Compile-time flag passed to generic lambdas (e.g. a masked and an unmasked
+// instance of one loop body).
+template <bool B> struct Flag { static constexpr bool value = B; };
+
 template <class T> __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c);
 
 template <> __device__ __forceinline__ f32x16 mfma32<F16>(u32x4 a, u32x4 b, f32x16 c) {

@@ -148,19 +148,12 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) toff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
 
-  if (ntiles > 0) issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    // tile kt has landed for every wave, and every wave is done with kt - 1
-    wait_vm();
-    __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
-    const int kbase = kt * TILE_ROWS;
+  // one key step on the tiles in LDS buffer buf; masked: keys past Lk get P = 0
+  auto step = [&](int buf, int kbase, auto masked) {
     const uint16_t* Kb = sm.k[buf];
     const uint16_t* Vb = sm.v[buf];
     const uint16_t* KTb = sm.kt[buf];
     const float cb = cb0 - (float)kbase;
-    const bool full = kbase + TILE_ROWS <= Lk;
     const int kleft = Lk - kbase - 4 * g;
 
 #pragma unroll
@@ -187,7 +180,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
           p = fast_exp2(__builtin_fmaf(S[r], a.lc.s_lin, bias));
           w = 1.0f;
         }
-        if (!full) p = jl < kleft ? p : 0.0f;
+        if (decltype(masked)::value) p = jl < kleft ? p : 0.0f;
         S[r] = p * (dP[r] - dl) * w;
       }
       u32x4 sb[2];
@@ -203,6 +196,26 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
         for (int s = 0; s < 2; ++s)
           dQ[db] = mfma32<T>(load16(KTb + toff[kb][s] + db * 32 * TILE_ROWS), sb[s], dQ[db]);
     }
+  };
+
+  // tile kt has landed for every wave, and every wave is done with kt - 1;
+  // then start the copies of kt + 1
+  auto advance = [&](int kt) {
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+  };
+  // the key mask costs a compare and a select per logit, so only a partial
+  // last key step runs the masked instance (after the loop)
+  const int nfull = Lk / TILE_ROWS;
+  if (ntiles > 0) issue(0, 0);
+  for (int kt = 0; kt < nfull; ++kt) {
+    advance(kt);
+    step(kt & 1, kt * TILE_ROWS, Flag<false>{});
+  }
+  if (nfull < ntiles) {
+    advance(nfull);
+    step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
   }
 
   if (!row_ok) return;

@@ -107,29 +107,28 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) voff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
 
-  if (ntiles > 0) issue(0, 0);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    // tile kt has landed for every wave, and every wave is done with kt - 1
-    wait_vm();
-    __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
-    const int kbase = kt * TILE_ROWS;
+  // one key step on the tile in LDS buffer buf; masked: keys past Lk get P = 0
+  auto step = [&](int buf, int kbase, auto masked) {
     const uint16_t* Kb = sm.k[buf];
     const uint16_t* Vb = sm.vt[buf];
-
     const float cb = cb0 - (float)kbase;
-    const bool full = kbase + TILE_ROWS <= Lk;
     const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
 
     // S^T[key][row] = K Q^T (lane = row) for key block kb
     f32x16 S[2];
+    // (LDS operands are read two k-steps ahead of the MFMA that uses them)
     auto scores = [&](int kb) {
+      const uint16_t* Kr = Kb + kb * 2 * BLK_COLS * BLK_ELEMS;
+      auto kop = [&](int ks) { return load16(Kr + koff[ks & 1] + (ks >> 1) * BLK_ELEMS); };
+      u32x4 ka[3];
+      ka[0] = kop(0);
+      ka[1] = kop(1);
       S[kb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks)
-        S[kb] = mfma32<T>(load16(Kb + koff[ks & 1] + (ks >> 1) * BLK_ELEMS + kb * 2 * BLK_COLS * BLK_ELEMS),
-                          qf[ks], S[kb]);
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        if (ks + 2 < KSTEPS) ka[(ks + 2) % 3] = kop(ks + 2);
+        S[kb] = mfma32<T>(ka[ks % 3], qf[ks], S[kb]);
+      }
     };
     // capped and biased logits (log2 units) of key block kb, masked past Lk
     auto logits = [&](int kb) {
@@ -142,7 +141,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
                              -slope2 * __builtin_fabsf(cb - (float)jl));
         else
           x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
-        if (!full) x = jl < kleft ? x : -__builtin_inff();
+        if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
         S[kb][r] = x;
       }
     };
@@ -171,11 +170,15 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
     // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb; the V^T
     // operand is one 16-byte read in the key order of pb
     auto pv = [&](int kb) {
+      auto vop = [&](int i) { return load16(Vb + voff[kb][i & 1] + (i >> 1) * 32 * TILE_ROWS); };
+      u32x4 va[3];
+      va[0] = vop(0);
+      va[1] = vop(1);
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-          O[db] = mfma32<T>(load16(Vb + voff[kb][s] + db * 32 * TILE_ROWS), pb[kb][s], O[db]);
+      for (int i = 0; i < 2 * DBLK; ++i) {
+        if (i + 2 < 2 * DBLK) va[(i + 2) % 3] = vop(i + 2);
+        O[i >> 1] = mfma32<T>(va[i % 3], pb[kb][i & 1], O[i >> 1]);
+      }
     };
 
     if (CAP) {
@@ -216,6 +219,26 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       pv(0);
       pv(1);
     }
+  };
+
+  // tile kt has landed for every wave, and every wave is done with kt - 1;
+  // then start the copies of kt + 1
+  auto advance = [&](int kt) {
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+  };
+  // the key mask costs a compare and a select per logit, so only a partial
+  // last key step runs the masked instance (after the loop)
+  const int nfull = Lk / TILE_ROWS;
+  if (ntiles > 0) issue(0, 0);
+  for (int kt = 0; kt < nfull; ++kt) {
+    advance(kt);
+    step(kt & 1, kt * TILE_ROWS, Flag<false>{});
+  }
+  if (nfull < ntiles) {
+    advance(nfull);
+    step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
   }
 
   // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta
