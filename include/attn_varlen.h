@@ -112,6 +112,29 @@ typedef struct {
  * Depends only on host-visible sizes (batch, hq, total_q, total_k). */
 attn_status attn_varlen_workspace_size(const attn_problem* p, int entry, size_t* bytes);
 
+/* Workspace with room for the stored dS of every sequence.
+ *
+ * The backward entries (ATTN_ENTRY_BWD, ATTN_ENTRY_FULL_VJP) use any workspace
+ * bytes beyond attn_varlen_workspace_size to keep dS = P * (dP - Delta) *
+ * (1 - tanh^2) in the input dtype, as the dK/dV pass forms it, so that dQ is
+ * one product dS K instead of a second recomputation of S, P and dP (page
+ * "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "Hard
+ * Constraints": the cap derivative multiplies dP - Delta).  A sequence needs
+ * ceil(Lq * hq / 256) * ceil(Lk / 64) images of 32 KiB; sequences get room in
+ * batch order while it lasts and the rest recompute, so every workspace size
+ * from the minimum up gives the same results to within rounding (the stored
+ * and the recomputed dS round the same value; a sequence's dQ is bitwise
+ * repeatable for a fixed workspace size).
+ *
+ * This function returns the size at which every sequence is stored, from host
+ * copies of cu_q / cu_k (int32 [batch + 1], the same contents the device
+ * arrays will hold).  Errors: ATTN_BAD_SEQLENS when they do not start at 0,
+ * end at total_q / total_k and never decrease.  For ATTN_ENTRY_FWD it equals
+ * attn_varlen_workspace_size. */
+attn_status attn_varlen_workspace_size_ds(const attn_problem* p, int entry,
+                                          const int32_t* cu_q_host, const int32_t* cu_k_host,
+                                          size_t* bytes);
+
 /* Forward: writes out (strided, dtype of q) and lse (float32 [total_q, hq]
  * contiguous, natural log, -inf for rows whose sequence has no keys). */
 attn_status attn_varlen_fwd(const attn_problem* p,

@@ -31,6 +31,7 @@ PHASES = ("plan", "fwd", "dkdv", "dq")
 
 EXPORTED = (
     "attn_varlen_workspace_size",
+    "attn_varlen_workspace_size_ds",
     "attn_varlen_fwd",
     "attn_varlen_bwd",
     "attn_varlen_full_vjp",
@@ -96,6 +97,9 @@ def load() -> ctypes.CDLL:
         T = P(AttnTensor)
         vp, sz, fp = ctypes.c_void_p, ctypes.c_size_t, P(ctypes.c_float)
         lib.attn_varlen_workspace_size.argtypes = [P(AttnProblem), ctypes.c_int, P(sz)]
+        i32p = P(ctypes.c_int32)
+        lib.attn_varlen_workspace_size_ds.argtypes = [P(AttnProblem), ctypes.c_int, i32p, i32p,
+                                                      P(sz)]
         lib.attn_varlen_fwd.argtypes = [P(AttnProblem), T, T, T, T, fp, vp, sz, vp]
         lib.attn_varlen_bwd.argtypes = [P(AttnProblem), T, T, T, T, fp, T, T, T, T, vp, sz, vp]
         lib.attn_varlen_full_vjp.argtypes = [P(AttnProblem), T, T, T, T, T, T, T, T, fp,
@@ -107,7 +111,8 @@ def load() -> ctypes.CDLL:
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
         lib.attn_last_error.restype = ctypes.c_char_p
-        for name in ("attn_varlen_workspace_size", "attn_varlen_fwd", "attn_varlen_bwd",
+        for name in ("attn_varlen_workspace_size", "attn_varlen_workspace_size_ds",
+                     "attn_varlen_fwd", "attn_varlen_bwd",
                      "attn_varlen_full_vjp", "attn_varlen_full_vjp_timed",
                      "attn_varlen_check_plan"):
             getattr(lib, name).restype = ctypes.c_int

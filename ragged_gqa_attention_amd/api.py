@@ -63,12 +63,38 @@ def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_rig
         softcap=float(softcap), scale_multiplier=float(scale_multiplier))
 
 
-def workspace_size(problem: _lib.AttnProblem, entry: int) -> int:
+def workspace_size(problem: _lib.AttnProblem, entry: int, cu_q=None, cu_k=None) -> int:
+    """Minimum workspace bytes; with cu_q / cu_k (copied to the host, which
+    synchronises) the size at which the backward stores dS for every sequence."""
     n = ctypes.c_size_t(0)
-    _lib.raise_for(_lib.load().attn_varlen_workspace_size(ctypes.byref(problem), entry,
-                                                         ctypes.byref(n)),
-                   "attn_varlen_workspace_size")
+    lib = _lib.load()
+    if cu_q is None:
+        st = lib.attn_varlen_workspace_size(ctypes.byref(problem), entry, ctypes.byref(n))
+        _lib.raise_for(st, "attn_varlen_workspace_size")
+        return n.value
+    hq = cu_q.detach().to("cpu", torch.int32).contiguous()
+    hk = cu_k.detach().to("cpu", torch.int32).contiguous()
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    st = lib.attn_varlen_workspace_size_ds(ctypes.byref(problem), entry,
+                                           ctypes.cast(hq.data_ptr(), i32p),
+                                           ctypes.cast(hk.data_ptr(), i32p), ctypes.byref(n))
+    _lib.raise_for(st, "attn_varlen_workspace_size_ds")
     return n.value
+
+
+# Default cap on the workspace bytes spent on stored dS (see
+# attn_varlen_workspace_size_ds); sequences beyond it recompute dS in dQ.
+DS_DEFAULT_BUDGET = 8 << 30
+
+
+def _bwd_workspace_size(problem, entry, cu_q, cu_k, store_ds) -> int:
+    """store_ds: True (room for every sequence's dS, up to DS_DEFAULT_BUDGET
+    bytes), False (minimum workspace) or a number of extra bytes beyond the
+    minimum."""
+    base = workspace_size(problem, entry)
+    if store_ds is True:
+        return min(workspace_size(problem, entry, cu_q, cu_k), base + DS_DEFAULT_BUDGET)
+    return base + (0 if store_ds is False or store_ds is None else int(store_ds))
 
 
 def _workspace(nbytes: int, device, ws=None) -> torch.Tensor:
@@ -121,8 +147,9 @@ def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multip
 
 def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3.0,
                     scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1, *,
-                    dq=None, dk=None, dv=None, workspace=None, check=False):
-    """Backward from a saved forward: returns (dq, dk, dv)."""
+                    dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=True):
+    """Backward from a saved forward: returns (dq, dk, dv).  ``store_ds``: see
+    _bwd_workspace_size (ignored when ``workspace`` is given: its size decides)."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
                         softcap, scale_multiplier)
     dt = q.dtype
@@ -137,7 +164,10 @@ def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3
     tdq = _view(dq, "dq", dt, heads=q.shape[1])
     tdk = _view(dk, "dk", dt, heads=k.shape[1])
     tdv = _view(dv, "dv", dt, heads=k.shape[1])
-    ws = _workspace(workspace_size(prob, _lib.ENTRY_BWD), q.device, workspace)
+    if workspace is None:
+        ws = _workspace(_bwd_workspace_size(prob, _lib.ENTRY_BWD, cu_q, cu_k, store_ds), q.device)
+    else:
+        ws = _workspace(workspace_size(prob, _lib.ENTRY_BWD), q.device, workspace)
     st = _lib.load().attn_varlen_bwd(ctypes.byref(prob), ctypes.byref(tq), ctypes.byref(tk),
                                      ctypes.byref(tv), ctypes.byref(to), _fptr(lse),
                                      ctypes.byref(tdo), ctypes.byref(tdq), ctypes.byref(tdk),
@@ -154,10 +184,13 @@ class FullVJP:
 
     Binding once and calling many times keeps the timed region to the library
     call itself.  Outputs are dense [Tq,Hq,160] / [Tk,1,160] tensors.
+    ``store_ds`` sizes the workspace (see _bwd_workspace_size); True reads
+    cu_q / cu_k back to the host once, here.
     """
 
     def __init__(self, q, k, v, cu_q, cu_k, alibi_slopes, dout, causal=False, window_left=-1,
-                 window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False):
+                 window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False,
+                 store_ds=True):
         self.prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left,
                                  window_right, softcap, scale_multiplier)
         dt, dev = q.dtype, q.device
@@ -171,7 +204,8 @@ class FullVJP:
                       _view(dout, "dout", dt, heads=q.shape[1]),
                       _view(self.out, "out", dt), _view(self.dq, "dq", dt),
                       _view(self.dk, "dk", dt), _view(self.dv, "dv", dt)]
-        self.ws = _workspace(workspace_size(self.prob, _lib.ENTRY_FULL_VJP), dev)
+        self.ws = _workspace(_bwd_workspace_size(self.prob, _lib.ENTRY_FULL_VJP, cu_q, cu_k,
+                                                 store_ds), dev)
         self.device = dev
         self._fn = _lib.load().attn_varlen_full_vjp
         self._fn_timed = _lib.load().attn_varlen_full_vjp_timed
@@ -199,10 +233,10 @@ class FullVJP:
 
 def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
                          scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1,
-                         *, want_lse=False, check=False):
+                         *, want_lse=False, check=False, store_ds=True):
     """Forward + full VJP: returns (out, dq, dk, dv[, lse])."""
     call = FullVJP(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
-                   softcap, scale_multiplier, want_lse=want_lse)
+                   softcap, scale_multiplier, want_lse=want_lse, store_ds=store_ds)
     res = call()
     if check:
         call.check_plan()

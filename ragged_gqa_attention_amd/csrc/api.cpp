@@ -4,6 +4,7 @@
 // stream; nothing here synchronises except attn_varlen_check_plan.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -259,6 +260,13 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.min_chunk = MIN_CHUNK_ROWS;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;
+  // workspace past the fixed layout holds stored dS images (backward entries)
+  pa.ds_images = 0;
+  if (entry != ATTN_ENTRY_FWD && ws_bytes > L.total) {
+    const size_t n = (ws_bytes - L.total) / DS_IMAGE_BYTES;
+    pa.ds_images = (long long)std::min<size_t>(n, (size_t)INT32_MAX);
+    if (pa.ds_images > 0) a.ds = reinterpret_cast<uint16_t*>(base + L.total);
+  }
   return ATTN_OK;
 }
 
@@ -302,6 +310,32 @@ attn_status attn_varlen_workspace_size(const attn_problem* p, int entry, size_t*
   if (entry < ATTN_ENTRY_FWD || entry > ATTN_ENTRY_FULL_VJP)
     return fail(ATTN_INVALID_ARG, "unknown entry %d", entry);
   *bytes = make_layout(p, entry, device_cus()).total;
+  return ATTN_OK;
+}
+
+attn_status attn_varlen_workspace_size_ds(const attn_problem* p, int entry,
+                                          const int32_t* cu_q_host, const int32_t* cu_k_host,
+                                          size_t* bytes) {
+  g_last_error.clear();
+  if (!bytes) return fail(ATTN_INVALID_ARG, "bytes is NULL");
+  RGA_TRY(check_problem(p));
+  if (entry < ATTN_ENTRY_FWD || entry > ATTN_ENTRY_FULL_VJP)
+    return fail(ATTN_INVALID_ARG, "unknown entry %d", entry);
+  if (!cu_q_host || !cu_k_host) return fail(ATTN_INVALID_ARG, "cu_q_host / cu_k_host is NULL");
+  const int B = p->batch;
+  if (cu_q_host[0] != 0 || cu_k_host[0] != 0 || cu_q_host[B] != p->total_q ||
+      cu_k_host[B] != p->total_k)
+    return fail(ATTN_BAD_SEQLENS, "cu_q / cu_k must start at 0 and end at total_q / total_k");
+  size_t images = 0;
+  for (int b = 0; b < B; ++b) {
+    const int64_t lq = (int64_t)cu_q_host[b + 1] - cu_q_host[b];
+    const int64_t lk = (int64_t)cu_k_host[b + 1] - cu_k_host[b];
+    if (lq < 0 || lk < 0) return fail(ATTN_BAD_SEQLENS, "cu_q / cu_k decrease at %d", b);
+    if (lq > 0 && lk > 0)
+      images += (size_t)ceil_div(lq * p->hq, ROW_TILE) * (size_t)ceil_div(lk, TILE_ROWS);
+  }
+  *bytes = make_layout(p, entry, device_cus()).total;
+  if (entry != ATTN_ENTRY_FWD) *bytes += images * DS_IMAGE_BYTES;
   return ATTN_OK;
 }
 

@@ -56,6 +56,8 @@ struct KvShared {
 // keys [key0, key0 + PAIR_KEYS) of the wave's pair.
 struct KvUnit {
   int q0, k0, Lk, row_begin, row_end, key0, nchunk;
+  int ds;    // first dS image of the sequence, -1 when dS is not stored
+  int nks;   // 64-key steps of the sequence (images per row tile)
 };
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
@@ -163,9 +165,26 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   };
 
+  // Stored dS: each wave writes its 32 x 32 block of a step's dS to the image
+  // of its row tile and key step, lane (key, g) writing chunks 2 s + g of the
+  // block's 32-row column range (see ds_off).  The lane's part of the offset
+  // is ds_off(key, g); chunk 2 s + g differs from chunk g by bit 4 of the
+  // element offset, and the 32-row range (first row hr, a multiple of 32)
+  // selects the block column.
+  // Pairs whose keys lie past the sequence's last image store nothing; keys
+  // past Lk inside it store zeros (K^T is zero there, and 0 * dS must stay 0).
+  const bool ds_on = u.ds >= 0 && u.key0 < u.nks * TILE_ROWS;
+  const bool ds_key_ok = u.key0 + l32 < u.Lk;
+  const int ds_lane = ds_off((u.key0 & (TILE_ROWS - 1)) + l32, g);
+  auto store_ds = [&](int hr, int s, const u32x4& v) {
+    uint16_t* img = a.ds + ((int64_t)u.ds + (int64_t)(hr / ROW_TILE) * u.nks + u.key0 / TILE_ROWS) *
+                               DS_IMAGE_ELEMS + ((hr & (ROW_TILE - 1)) / 32) * BLK_ELEMS;
+    *reinterpret_cast<u32x4*>(img + (ds_lane ^ (16 * s))) = ds_key_ok ? v : u32x4{0u, 0u, 0u, 0u};
+  };
+
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
-  auto pointwise_publish = [&](int buf, int slot, f32x16 (&S)[KB], f32x16 (&dP)[KB],
+  auto pointwise_publish = [&](int buf, int slot, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB],
                                u32x4 (&own)[KB][2]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -200,6 +219,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
                                pack2<T>(dP[kb][8 * s + 6], dP[kb][8 * s + 7])};
         own[kb][s] = ROLE ? sb : pb;
         sm.xch[slot][wave][kb * 2 + s][lane] = ROLE ? pb : sb;
+        if (ds_on) store_ds(r0 + ROLE * 32, s, sb);
       }
   };
 
@@ -241,7 +261,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   if (nsteps > 1) issue_loads(u.row_begin + KV_ROW_STEP, 1);
   f32x16 S[KB], dP[KB];
   scores(0, S, dP);
-  pointwise_publish(0, 0, S, dP, mine);
+  pointwise_publish(0, 0, u.row_begin, S, dP, mine);
   wait_vm();
   __syncthreads();
   int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
@@ -254,10 +274,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     // while the other keeps the matrix core busy
     if (LATE) {
       accumulate(prev, (n - 1) & 1);
-      pointwise_publish(cur, n & 1, S, dP, mine);
+      pointwise_publish(cur, n & 1, u.row_begin + n * KV_ROW_STEP, S, dP, mine);
     } else {
       u32x4 own[KB][2];
-      pointwise_publish(cur, n & 1, S, dP, own);
+      pointwise_publish(cur, n & 1, u.row_begin + n * KV_ROW_STEP, S, dP, own);
       accumulate(prev, (n - 1) & 1);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) { mine[kb][0] = own[kb][0]; mine[kb][1] = own[kb][1]; }
@@ -326,6 +346,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   u.k0 = sq[SQ_K0];
   u.Lk = sq[SQ_LK];
   u.nchunk = sq[SQ_NCHUNK];
+  u.ds = a.ds ? sq[SQ_DSOFF] : -1;
+  u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
   const int rows = sq[SQ_ROWS], chunk = sq[SQ_CHUNK];
   const int ktile = unit / u.nchunk;
   const int ci = unit - ktile * u.nchunk;

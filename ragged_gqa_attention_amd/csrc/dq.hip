@@ -75,11 +75,100 @@ __device__ __forceinline__ void reduce_kv_slice(const AttnArgs& a, int part, int
   }
 }
 
+// LDS of one key step of the stored-dS path: the dS image (64 keys x 256
+// rows, ds_off) and K^T (tt_off), double-buffered.
+struct DqStoredShared {
+  uint16_t ds[2][DS_IMAGE_ELEMS];
+  uint16_t kt[2][TILE_ELEMS];
+};
+
+// dQ of row tile `tile` from the dS images the dK/dV kernel stored:
+// dQ^T[d][row] += K^T[d][keys] dS^T[keys][row], nothing recomputed.  Both
+// operands come from LDS: K^T with one 16-byte read, dS^T with two
+// transposing reads of the image (lane l32 gets row 32 w + tt_key_pos(l32),
+// keys in the order of the K^T read).  Limited by the HBM reads of the images.
+template <class T, bool CAP>
+__device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm, const int* sq,
+                                          int tile) {
+  const int q0 = sq[SQ_Q0], Lk = sq[SQ_LK], rows = sq[SQ_ROWS];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int nks = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  const uint16_t* img0 = a.ds + ((int64_t)sq[SQ_DSOFF] + (int64_t)tile * nks) * DS_IMAGE_ELEMS;
+  const uint16_t* kt_seq = a.kt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
+  // copies of key step kt: each wave four 1 KB blocks of the image, waves 0-3
+  // three and waves 4-7 two of the 20 K^T loads
+  constexpr int IMG_LOADS = DS_IMAGE_ELEMS / BLK_ELEMS / ROW_WAVES;
+  auto issue = [&](int kt, int buf) {
+    const uint16_t* img = img0 + (int64_t)kt * DS_IMAGE_ELEMS;
+#pragma unroll
+    for (int j = 0; j < IMG_LOADS; ++j) {
+      const int blk = IMG_LOADS * wave + j;
+      load_lds16(img + blk * BLK_ELEMS + lane * 8, sm.ds[buf] + blk * BLK_ELEMS);
+    }
+    const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
+    if (wave < 4) load_tt_tile<3>(sm.kt[buf], ktt, 3 * wave, lane);
+    else load_tt_tile<2>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
+  };
+
+  // transposing reads (see read_tr): lane (i, G) addresses key rows
+  // 4 (G/2) + i/4 and + 8 of k-step t, chunk 4 w + 2 (G%2) + (i%4)/2
+  const int ti = lane & 15, tG = lane >> 4;
+  const int krow = 4 * (tG >> 1) + (ti >> 2);
+  const int chunk = 4 * wave + 2 * (tG & 1) + ((ti & 3) >> 1);
+  const int dlo = ds_off(krow, chunk) + 4 * (ti & 1);
+  const int dhi = ds_off(krow + 8, chunk) + 4 * (ti & 1);
+  constexpr int KSTEP_ELEMS = (ROW_TILE / 32) * BLK_ELEMS;   // 16 keys of an image
+  int toff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) toff[t] = tt_off(l32, 2 * t + g);
+
+  f32x16 dQ[DBLK];
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
+  if (nks > 0) issue(0, 0);
+  for (int kt = 0; kt < nks; ++kt) {
+    const int buf = kt & 1;
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < nks) issue(kt + 1, buf ^ 1);
+    const uint16_t* D = sm.ds[buf];
+    const uint16_t* KT = sm.kt[buf];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const u32x2 lo = read_tr(D + dlo + t * KSTEP_ELEMS);
+      const u32x2 hi = read_tr(D + dhi + t * KSTEP_ELEMS);
+      const u32x4 bt = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+        dQ[db] = mfma32<T>(load16(KT + toff[t] + db * 32 * TILE_ROWS), bt, dQ[db]);
+    }
+  }
+
+  const int row = tile * ROW_TILE + wave * 32 + tt_key_pos(l32);
+  if (row >= rows) return;
+  const int ti_ = fast_div(row, a.hq_mul, a.hq_shift);
+  const int hh = row - ti_ * a.hq;
+  const float scale = CAP ? 4.0f * a.lc.sigma : a.lc.sigma;
+  uint16_t* dqr = a.dq + (int64_t)(q0 + ti_) * a.dq_ts + (int64_t)hh * a.dq_hs + g * 4;
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+      *reinterpret_cast<u32x2*>(dqr + db * 32 + rq * 8) =
+          u32x2{pack2<T>(scale * dQ[db][rq * 4 + 0], scale * dQ[db][rq * 4 + 1]),
+                pack2<T>(scale * dQ[db][rq * 4 + 2], scale * dQ[db][rq * 4 + 3])};
+}
+
 }  // namespace
 
 template <class T, bool CAP>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) DqShared sm;
+  __shared__ __attribute__((aligned(16))) union {
+    DqShared r;
+    DqStoredShared d;
+  } sm;
 
   // the fixed-order dK / dV partial sums ride along with dQ, a slice per workgroup
   if (a.total_k > 0) reduce_kv_slice<T>(a, blockIdx.x, gridDim.x);
@@ -89,6 +178,10 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int b = a.plan.fwd_seq[rank];
   const int tile = blockIdx.x - a.plan.fwd_off[rank];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
+  if (a.ds && sq[SQ_DSOFF] >= 0) {
+    dq_stored<T, CAP>(a, sm.d, sq, tile);
+    return;
+  }
   const int q0 = sq[SQ_Q0], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
   const int rows = sq[SQ_ROWS];
 
@@ -129,13 +222,13 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   auto issue = [&](int kt, int buf) {
     const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
     if (wave < 4) {
-      load_row_tile(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
+      load_row_tile(sm.r.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
                     wave, lane);
-      load_tt_tile<3>(sm.kt[buf], ktt, 3 * wave, lane);
+      load_tt_tile<3>(sm.r.kt[buf], ktt, 3 * wave, lane);
     } else {
-      load_row_tile(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk, a.zero,
+      load_row_tile(sm.r.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk, a.zero,
                     wave - 4, lane);
-      load_tt_tile<2>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
+      load_tt_tile<2>(sm.r.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
     }
   };
 
@@ -150,9 +243,9 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
 
   // one key step on the tiles in LDS buffer buf; masked: keys past Lk get P = 0
   auto step = [&](int buf, int kbase, auto masked) {
-    const uint16_t* Kb = sm.k[buf];
-    const uint16_t* Vb = sm.v[buf];
-    const uint16_t* KTb = sm.kt[buf];
+    const uint16_t* Kb = sm.r.k[buf];
+    const uint16_t* Vb = sm.r.v[buf];
+    const uint16_t* KTb = sm.r.kt[buf];
     const float cb = cb0 - (float)kbase;
     const int kleft = Lk - kbase - 4 * g;
 

@@ -23,6 +23,10 @@ constexpr int TILE_ELEMS = TILE_ROWS * HEAD_DIM;
 // Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
 // P and dS for half of them).
 constexpr int KV_ROW_STEP = TILE_ROWS;
+// Stored dS: one image per (row tile of ROW_TILE folded rows, 64-key step),
+// 64 keys x ROW_TILE rows of 16-bit values (layout: ds_off in tiles.hpp).
+constexpr int DS_IMAGE_ELEMS = TILE_ROWS * ROW_TILE;
+constexpr size_t DS_IMAGE_BYTES = sizeof(uint16_t) * DS_IMAGE_ELEMS;
 
 struct AttnArgs {
   const uint16_t* q;    int64_t q_ts, q_hs;
@@ -46,6 +50,10 @@ struct AttnArgs {
   uint16_t* vt;
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
+  // dS images written by dK/dV and read by dQ for the sequences the planner
+  // gave a slot (SQ_DSOFF >= 0); sequence images are row-tile major:
+  // image SQ_DSOFF + row_tile * ceil(Lk / 64) + key_step.
+  uint16_t* ds;
   const float* slopes;  int64_t slopes_stride;
   int hq;
   uint32_t hq_mul, hq_shift;   // n / hq == (umulhi(n, hq_mul) + n) >> hq_shift for n < 2^31
@@ -65,6 +73,7 @@ struct PlanArgs {
   int64_t total_k;
   int target_units;     // desired number of dK/dV work units
   int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
+  long long ds_images;  // dS images that fit the workspace (0: no stored dS)
   uint16_t* zero;       // 512 bytes the planner clears
   Plan plan;
 };

@@ -37,25 +37,25 @@ __device__ __forceinline__ long long block_sum(long long v, long long* red) {
 
 // put(r, sum_{r' < r} count(r')) for r = 0..B.  Thread t owns a contiguous
 // segment of r; segment totals are scanned with wave shuffles.
-template <class F, class G>
-__device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, int* part) {
+template <class V, class F, class G>
+__device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, V* part) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int seg = (B + PLAN_THREADS - 1) / PLAN_THREADS;
   const int lo = min(B, tid * seg), hi = min(B, lo + seg);
-  int local = 0;
+  V local = 0;
   for (int r = lo; r < hi; ++r) local += count(r);
-  int x = local;   // inclusive scan inside the wave
+  V x = local;   // inclusive scan inside the wave
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
+    const V y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
   if (lane == 63) part[wave] = x;
   __syncthreads();
-  int base = 0;
+  V base = 0;
   for (int w = 0; w < wave; ++w) base += part[w];
   if (tid == PLAN_THREADS - 1) put(B, base + x);
-  int run = base + x - local;
+  V run = base + x - local;
   for (int r = lo; r < hi; ++r) {
     put(r, run);
     run += count(r);
@@ -150,6 +150,20 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   block_exclusive_scan(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
   }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
+  // stored dS images, in sequence order, while they fit the workspace (a
+  // sequence that does not fit recomputes dS in the dQ kernel)
+  auto images = [&](int b) -> long long {
+    const int* sb = seq + b * SEQ_FIELDS;
+    if (sb[SQ_ROWS] == 0 || sb[SQ_LK] == 0) return 0;
+    return (long long)((sb[SQ_ROWS] + ROW_TILE - 1) / ROW_TILE) *
+           ((sb[SQ_LK] + TILE_ROWS - 1) / TILE_ROWS);
+  };
+  block_exclusive_scan(B, images, [&](int b, long long off) {
+    if (b < B) {
+      const long long n = images(b);
+      seq[b * SEQ_FIELDS + SQ_DSOFF] = (n > 0 && off + n <= a.ds_images) ? (int)off : -1;
+    }
+  }, red);
 }
 
 // Transposed key tile `tile` of K (t = 0) or V (t = 1) (see tt_key_pos): keys

@@ -79,6 +79,17 @@ __device__ __forceinline__ int tt_off(int d, int c) {
   return d * TILE_ROWS + ((c ^ ((d >> 1) & 7)) << 3);
 }
 
+// Element offset of 16-byte chunk c (c = 0..31) of key k (0..63) in a dS
+// image: the blocked row-tile layout of blk_off with 64 keys as its rows and
+// ROW_TILE folded rows as its columns (eight block columns).  Chunk c holds
+// rows 8c + {0..3, 8..11} or 8c - 4 + {0..3, 8..11}: inside every 16-row group
+// the middle two quads are swapped (tt_key_pos), which is the row order of
+// the dS accumulator registers.  A transposing read returns row
+// 32 w + tt_key_pos(l32) to lane l32 of the wave that reads chunks 4w .. 4w + 3.
+__device__ __forceinline__ int ds_off(int k, int c) {
+  return (((k >> 4) * (ROW_TILE / 32) + (c >> 2)) * 64 + (k & 15) * 4 + ((c & 3) ^ ((k >> 2) & 3))) * 8;
+}
+
 // One wave-wide direct load: lane l copies the 16 bytes at `src` (its own
 // address) to LDS at wave_dst + 16 l.  wave_dst must be the same for every lane.
 __device__ __forceinline__ void load_lds16(const void* src, void* wave_dst) {

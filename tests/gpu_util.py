@@ -34,11 +34,14 @@ def to_np(t):
     return t.detach().float().cpu().double().numpy()
 
 
-def gpu_full(wl_gpu, check=True):
+def gpu_full(wl_gpu, check=True, store_ds=True):
+    """One full-VJP call.  store_ds: True (workspace with room for every
+    sequence's dS), False (minimum workspace: dQ recomputes dS) or a number of
+    extra workspace bytes (room for some sequences)."""
     out, dq, dk, dv, lse = rga.attn_varlen_full_vjp(
         wl_gpu.q, wl_gpu.k, wl_gpu.v, wl_gpu.cu_q, wl_gpu.cu_k, wl_gpu.slopes, wl_gpu.dout,
         softcap=wl_gpu.softcap, scale_multiplier=wl_gpu.scale_multiplier, want_lse=True,
-        check=check)
+        check=check, store_ds=store_ds)
     torch.cuda.synchronize()
     return dict(out=out, dq=dq, dk=dk, dv=dv, lse=lse)
 
@@ -76,14 +79,21 @@ def oracle_full(wl):
                       inp["alibi_slopes"], inp["dout"], inp["softcap"], inp["scale_multiplier"])
 
 
-def check_full(wl, label):
-    """Whole-tensor parity of the full-VJP entry against the full oracle."""
+def check_full(wl, label, modes=(True, False)):
+    """Whole-tensor parity of the full-VJP entry against the full oracle, for
+    each workspace mode in `modes` (see gpu_full)."""
     tol = TOL[wl.dtype]
     say(f"[{label}] B={wl.batch} Hq={wl.hq} {wl.dtype} step={wl.step} W={wl.width} "
         f"Tq={wl.total_q} Tk={wl.total_k} sum LqLk={int((wl.lq * wl.lk).sum())}")
-    got = gpu_full(wl.to("cuda"))
+    g = wl.to("cuda")
     ref = oracle_full(wl)
-    for name in ("out", "dq", "dk", "dv"):
-        assert_close(name, to_np(got[name]), ref[name], tol, label)
-    assert_lse(to_np(got["lse"]), ref["lse"], label)
-    return got, ref
+    results = []
+    for mode in modes:
+        lab = f"{label} store_ds={mode}"
+        say(f"[{lab}]")
+        got = gpu_full(g, store_ds=mode)
+        for name in ("out", "dq", "dk", "dv"):
+            assert_close(name, to_np(got[name]), ref[name], tol, lab)
+        assert_lse(to_np(got["lse"]), ref["lse"], lab)
+        results.append(got)
+    return results, ref

@@ -130,3 +130,29 @@ def test_status_strings():
     for st in range(-6, 1):
         assert lib.attn_status_string(st).decode() not in ("", "unknown status")
     assert lib.attn_status_string(-99).decode() == "unknown status"
+
+
+def test_workspace_size_with_stored_ds():
+    """Room for dS: ceil(Lq hq / 256) ceil(Lk / 64) images of 32 KiB per
+    sequence with rows and keys, on top of the minimum; the forward needs none;
+    malformed host offsets are rejected."""
+    lib = _lib.load()
+    i32 = ctypes.c_int32
+    lq, lk = [3, 0, 9, 5], [70, 4, 0, 64]
+    cq = (i32 * 5)(*[sum(lq[:i]) for i in range(5)])
+    ck = (i32 * 5)(*[sum(lk[:i]) for i in range(5)])
+    prob = _problem(batch=4, total_q=sum(lq), total_k=sum(lk))
+    for entry in (_lib.ENTRY_FWD, _lib.ENTRY_BWD, _lib.ENTRY_FULL_VJP):
+        base, full = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        assert lib.attn_varlen_workspace_size(ctypes.byref(prob), entry, ctypes.byref(base)) == 0
+        assert lib.attn_varlen_workspace_size_ds(ctypes.byref(prob), entry, cq, ck,
+                                                 ctypes.byref(full)) == 0
+        images = (1 * 2) + (2 * 1) if entry != _lib.ENTRY_FWD else 0   # seqs 0 and 3
+        assert full.value - base.value == images * 64 * 256 * 2
+    bad = (i32 * 5)(0, 3, 2, 12, 17)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_varlen_workspace_size_ds(ctypes.byref(prob), _lib.ENTRY_BWD, bad, ck,
+                                             ctypes.byref(n)) == _lib.ATTN_BAD_SEQLENS
+    short = (i32 * 5)(0, 3, 3, 12, 16)
+    assert lib.attn_varlen_workspace_size_ds(ctypes.byref(prob), _lib.ENTRY_BWD, short, ck,
+                                             ctypes.byref(n)) == _lib.ATTN_BAD_SEQLENS

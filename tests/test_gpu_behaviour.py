@@ -20,17 +20,20 @@ from tests.gpu_util import (TOL, assert_close, assert_lse, gpu_full, need_gpu, o
 pytestmark = pytest.mark.gpu
 
 
-def _bind(g):
+def _bind(g, store_ds=True):
     return rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
-                       scale_multiplier=g.scale_multiplier, want_lse=True)
+                       scale_multiplier=g.scale_multiplier, want_lse=True, store_ds=store_ds)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 3])
-def test_bitwise_repeatable(cfg):
+@pytest.mark.parametrize("cfg,store_ds", [(0, True), (1, True), (3, True), (1, False),
+                                          (3, False)])
+def test_bitwise_repeatable(cfg, store_ds):
     """Three calls, outputs pre-filled with different garbage, give identical bits."""
     need_gpu()
     g = W.make_workload(cfg).to("cuda")
-    call = _bind(g)
+    call = _bind(g, store_ds)
+    if store_ds:   # stale dS images from another problem must not leak in
+        call.ws.fill_(0x7f)
     results = []
     for fill in (float("nan"), 12345.0, -0.0):
         for t in (call.out, call.dq, call.dk, call.dv, call.lse):
@@ -54,13 +57,16 @@ def test_forward_and_backward_entries():
         tol = TOL[wl.dtype]
         out, lse = rga.attn_varlen_fwd(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.softcap,
                                        g.scale_multiplier, check=True)
-        dq, dk, dv = rga.attn_varlen_bwd(g.q, g.k, g.v, out, lse, g.dout, g.cu_q, g.cu_k,
-                                         g.slopes, g.softcap, g.scale_multiplier, check=True)
         torch.cuda.synchronize()
         assert_close("out", to_np(out), ref["out"], tol, wl.name + " fwd")
         assert_lse(to_np(lse), ref["lse"], wl.name + " fwd")
-        for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
-            assert_close(name, to_np(t), ref[name], tol, wl.name + " bwd")
+        for store_ds in (True, False):
+            dq, dk, dv = rga.attn_varlen_bwd(g.q, g.k, g.v, out, lse, g.dout, g.cu_q, g.cu_k,
+                                             g.slopes, g.softcap, g.scale_multiplier, check=True,
+                                             store_ds=store_ds)
+            torch.cuda.synchronize()
+            for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+                assert_close(name, to_np(t), ref[name], tol, f"{wl.name} bwd store_ds={store_ds}")
 
 
 def test_special_sequences():

@@ -4,7 +4,9 @@ Small cases (config 0 and 30 seeded fuzz draws with lengths on and around the
 32/64/128 tile edges, empty and single-key sequences, every head count, both
 dtypes, token steps 1-3 and widths 160/176/192) compare every output element.
 The Hq=64 Q-short/K-long configuration that the benchmark times is compared in
-full.  The three larger configurations compare sampled rows of out/dq (each row
+full.  Small and benchmark cases run twice: with a workspace that stores dS
+for dQ and with the minimum workspace (dQ recomputes dS); one case stores dS
+for only some sequences.  The three larger configurations compare sampled rows of out/dq (each row
 depends only on its own inputs and its sequence's K/V), full dk/dv of their
 cheapest sequences, and the identity sum_j dv_j = sum_(i,h) dout_(i,h) for
 every sequence (each softmax row sums to one).
@@ -14,6 +16,7 @@ import pytest
 import torch
 
 import oracle
+import ragged_gqa_attention_amd as rga
 import workloads as W
 from tests.gpu_util import (TOL, assert_close, assert_lse, check_full, gpu_full, need_gpu,
                             say, to_np)
@@ -33,9 +36,31 @@ def test_fuzz_parity(seed):
 
 
 def test_config1_full_parity():
-    """The benchmarked Hq=64 Q-short/K-long configuration, every element."""
+    """The benchmarked Hq=64 Q-short/K-long configuration, every element, with
+    dQ from stored dS and with dQ recomputing dS."""
     need_gpu()
-    check_full(W.make_workload(1), "cfg1")
+    (stored, recomputed), _ = check_full(W.make_workload(1), "cfg1")
+    # storing dS changes nothing before dQ
+    for name in ("out", "lse", "dk", "dv"):
+        assert torch.equal(stored[name], recomputed[name]), name
+
+
+def test_partial_ds_capacity():
+    """A workspace with room for the dS of only some sequences: those use the
+    stored path, the rest recompute, and the result still matches the oracle."""
+    need_gpu()
+    wl = W.make_workload(1)
+    g = wl.to("cuda")
+    prob = rga.api.make_problem(g.q, g.k, g.cu_q, g.cu_k, g.slopes, False, -1, -1, g.softcap,
+                                g.scale_multiplier)
+    full = rga.workspace_size(prob, 2, g.cu_q, g.cu_k)
+    base = rga.workspace_size(prob, 2)
+    assert full > base
+    # room for about 40 % of the images, plus a few bytes that fit no image
+    (part,), ref = check_full(wl, "cfg1 partial", modes=((full - base) * 2 // 5 + 1000,))
+    stored = gpu_full(g, store_ds=True)
+    for name in ("out", "lse", "dk", "dv"):
+        assert torch.equal(part[name], stored[name]), name
 
 
 def _seq_slices(wl, b):
