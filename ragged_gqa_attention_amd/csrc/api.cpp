@@ -294,7 +294,9 @@ attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layo
     RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
     RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
     RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
-    RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles, s), "dQ launch"));
+    // row tiles, then one partial-sum workgroup per compute unit
+    RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles + device_cus(), s),
+                       "dQ launch"));
   }
   return ATTN_OK;
 }

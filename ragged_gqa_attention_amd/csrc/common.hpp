@@ -126,6 +126,7 @@ enum SeqField {
   SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS, SQ_NCHUNK, SQ_CHUNK, SQ_KTILES,
   SQ_TTOFF,   // first 64-key transposed tile of the sequence (prefix of ceil(Lk / 64))
   SQ_DSOFF,   // first stored dS image of the sequence, -1 when its dS is not stored
+  SQ_KTOFF,   // first 128-key tile of the sequence in batch order (prefix of SQ_KTILES)
   SEQ_FIELDS
 };
 

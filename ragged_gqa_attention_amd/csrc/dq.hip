@@ -34,52 +34,70 @@ struct DqShared {
   uint16_t kt[2][TILE_ELEMS];
 };
 
-// dK / dV of the keys in slice `part` of `parts` (in units of 4 features):
+// dK / dV of the 128-key tiles part, part + parts, ... (batch order):
 // sequences whose rows were split over several dK/dV workgroups sum their FP32
 // partials in chunk order and round once; keys of sequences without query
-// rows get exact zeros; unsplit sequences were stored by the dK/dV kernel.
-// The dK/dV kernel has finished (same stream), so its partials are complete.
+// rows get exact zeros; tiles of unsplit sequences were stored by the dK/dV
+// kernel.  The dK/dV kernel has finished (same stream), so its partials are
+// complete.  A tile is 128 x 40 groups of 4 features, ten per thread, whose
+// chunk sums are formed side by side (ten loads per tensor in flight).
 template <class T>
-__device__ __forceinline__ void reduce_kv_slice(const AttnArgs& a, int part, int parts) {
+__device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int parts) {
   constexpr int QUADS = HEAD_DIM / 4;
-  const int64_t total = a.total_k * QUADS;
-  const int64_t per = (total + parts - 1) / parts;
-  const int64_t end = min(total, (part + 1) * per);
+  constexpr int PER_THREAD = KEY_TILE * QUADS / ROW_THREADS;
+  static_assert(PER_THREAD * ROW_THREADS == KEY_TILE * QUADS, "whole tiles per pass");
   const int* seq = a.plan.seq;
-  for (int64_t idx = part * per + threadIdx.x; idx < end; idx += ROW_THREADS) {
-    const int t = (int)(idx / QUADS);
-    const int c4 = (int)(idx - (int64_t)t * QUADS);
-    int lo = 0, hi = a.batch - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (seq[mid * SEQ_FIELDS + SQ_K0] <= t) lo = mid; else hi = mid - 1;
-    }
-    const int* sb = seq + lo * SEQ_FIELDS;
-    const int lt = t - sb[SQ_K0];
+  const int B = a.batch;
+  if (B <= 0) return;
+  const int ntiles = seq[(B - 1) * SEQ_FIELDS + SQ_KTOFF] + seq[(B - 1) * SEQ_FIELDS + SQ_KTILES];
+  int b = 0;
+  for (int gt = part; gt < ntiles; gt += parts) {
+    while (b + 1 < B && seq[(b + 1) * SEQ_FIELDS + SQ_KTOFF] <= gt) ++b;   // gt only grows
+    const int* sb = seq + b * SEQ_FIELDS;
     const int nchunk = sb[SQ_NCHUNK];
-    if (nchunk == 1 && lt < sb[SQ_LK]) continue;
-    f32x4 sk = {0.0f, 0.0f, 0.0f, 0.0f}, sv = {0.0f, 0.0f, 0.0f, 0.0f};
-    if (lt < sb[SQ_LK] && nchunk > 1) {
-      const int kt = lt / KEY_TILE, kin = lt - kt * KEY_TILE;
-      const int64_t base = (int64_t)a.plan.kv_off[a.plan.kv_rank[lo]] + (int64_t)kt * nchunk;
+    if (nchunk == 1) continue;
+    const int kt = gt - sb[SQ_KTOFF];
+    const int k0 = sb[SQ_K0] + kt * KEY_TILE;
+    const int nkeys = min(KEY_TILE, sb[SQ_LK] - kt * KEY_TILE);
+    f32x4 sk[PER_THREAD], sv[PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      sk[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    if (nchunk > 1) {
+      const int64_t base = (int64_t)a.plan.kv_off[a.plan.kv_rank[b]] + (int64_t)kt * nchunk;
       for (int c = 0; c < nchunk; ++c) {
-        const int64_t off = ((base + c) * KEY_TILE + kin) * HEAD_DIM + c4 * 4;
-        sk += *reinterpret_cast<const f32x4*>(a.part_dk + off);
-        sv += *reinterpret_cast<const f32x4*>(a.part_dv + off);
+        const float* pk = a.part_dk + (base + c) * KEY_TILE * HEAD_DIM;
+        const float* pv = a.part_dv + (base + c) * KEY_TILE * HEAD_DIM;
+#pragma unroll
+        for (int j = 0; j < PER_THREAD; ++j) {
+          const int i = threadIdx.x + j * ROW_THREADS;   // key i / 40, features 4 (i % 40)
+          sk[j] += *reinterpret_cast<const f32x4*>(pk + 4 * i);
+          sv[j] += *reinterpret_cast<const f32x4*>(pv + 4 * i);
+        }
       }
     }
-    *reinterpret_cast<u32x2*>(a.dk + (int64_t)t * a.dk_ts + c4 * 4) =
-        u32x2{pack2<T>(sk[0], sk[1]), pack2<T>(sk[2], sk[3])};
-    *reinterpret_cast<u32x2*>(a.dv + (int64_t)t * a.dv_ts + c4 * 4) =
-        u32x2{pack2<T>(sv[0], sv[1]), pack2<T>(sv[2], sv[3])};
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int i = threadIdx.x + j * ROW_THREADS;
+      const int key = i / QUADS, c4 = i - key * QUADS;
+      if (key >= nkeys) continue;
+      const int64_t t = k0 + key;
+      *reinterpret_cast<u32x2*>(a.dk + t * a.dk_ts + c4 * 4) =
+          u32x2{pack2<T>(sk[j][0], sk[j][1]), pack2<T>(sk[j][2], sk[j][3])};
+      *reinterpret_cast<u32x2*>(a.dv + t * a.dv_ts + c4 * 4) =
+          u32x2{pack2<T>(sv[j][0], sv[j][1]), pack2<T>(sv[j][2], sv[j][3])};
+    }
   }
 }
 
-// LDS of one key step of the stored-dS path: the dS image (64 keys x 256
-// rows, ds_off) and K^T (tt_off), double-buffered.
+// LDS of the stored-dS path: the dS image (64 keys x 256 rows, ds_off) and
+// K^T (tt_off) of a key step, three buffers (two steps in flight).
+constexpr int DQS_NBUF = 3;
 struct DqStoredShared {
-  uint16_t ds[2][DS_IMAGE_ELEMS];
-  uint16_t kt[2][TILE_ELEMS];
+  uint16_t ds[DQS_NBUF][DS_IMAGE_ELEMS];
+  uint16_t kt[DQS_NBUF][TILE_ELEMS];
 };
 
 // dQ of row tile `tile` from the dS images the dK/dV kernel stored:
@@ -87,6 +105,8 @@ struct DqStoredShared {
 // operands come from LDS: K^T with one 16-byte read, dS^T with two
 // transposing reads of the image (lane l32 gets row 32 w + tt_key_pos(l32),
 // keys in the order of the K^T read).  Limited by the HBM reads of the images.
+// The first two steps' copies are issued before the workgroup's slice of
+// the dK / dV partial sums, so they land while it runs.
 template <class T, bool CAP>
 __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm, const int* sq,
                                           int tile) {
@@ -98,8 +118,9 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   const uint16_t* img0 = a.ds + ((int64_t)sq[SQ_DSOFF] + (int64_t)tile * nks) * DS_IMAGE_ELEMS;
   const uint16_t* kt_seq = a.kt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
   // copies of key step kt: each wave four 1 KB blocks of the image, waves 0-3
-  // three and waves 4-7 two of the 20 K^T loads
+  // three and waves 4-7 two of the 20 K^T loads (7 or 6 per wave)
   constexpr int IMG_LOADS = DS_IMAGE_ELEMS / BLK_ELEMS / ROW_WAVES;
+  static_assert(IMG_LOADS == 4, "waits below count 4 + 3 or 4 + 2 loads per step");
   auto issue = [&](int kt, int buf) {
     const uint16_t* img = img0 + (int64_t)kt * DS_IMAGE_ELEMS;
 #pragma unroll
@@ -128,11 +149,19 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
   if (nks > 0) issue(0, 0);
+  if (nks > 1) issue(1, 1);
   for (int kt = 0; kt < nks; ++kt) {
-    const int buf = kt & 1;
-    wait_vm();
+    const int buf = kt % DQS_NBUF;
+    // step kt has landed (step kt + 1 may still be in flight) for every wave,
+    // and every wave is done with step kt - 1, whose buffer step kt + 2 takes
+    if (kt + 1 < nks) {
+      if (wave < 4) wait_vm_le<7>();
+      else wait_vm_le<6>();
+    } else {
+      wait_vm();
+    }
     __syncthreads();
-    if (kt + 1 < nks) issue(kt + 1, buf ^ 1);
+    if (kt + 2 < nks) issue(kt + 2, (kt + 2) % DQS_NBUF);
     const uint16_t* D = sm.ds[buf];
     const uint16_t* KT = sm.kt[buf];
 #pragma unroll
@@ -170,11 +199,16 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     DqStoredShared d;
   } sm;
 
-  // the fixed-order dK / dV partial sums ride along with dQ, a slice per workgroup
-  if (a.total_k > 0) reduce_kv_slice<T>(a, blockIdx.x, gridDim.x);
-
+  // Workgroups past the row tiles (the grid's tail) sum the split dK / dV
+  // partials, a slice each: they start as the row tiles drain and fill the
+  // compute units the last row tiles leave idle.
   const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
-  if (rank < 0) return;
+  if (rank < 0) {
+    const int first = a.batch > 0 ? a.plan.fwd_off[a.batch] : 0;
+    if (a.total_k > 0 && (int)blockIdx.x >= first)
+      reduce_kv_tiles<T>(a, blockIdx.x - first, gridDim.x - first);
+    return;
+  }
   const int b = a.plan.fwd_seq[rank];
   const int tile = blockIdx.x - a.plan.fwd_off[rank];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;

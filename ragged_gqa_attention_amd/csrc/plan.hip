@@ -150,6 +150,9 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   block_exclusive_scan(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
   }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
+  // 128-key tiles in batch order (the dK / dV partial sums walk them)
+  block_exclusive_scan(B, [&](int b) { return seq[b * SEQ_FIELDS + SQ_KTILES]; },
+                       [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_KTOFF] = v; }, part);
   // stored dS images, in sequence order, while they fit the workspace (a
   // sequence that does not fit recomputes dS in the dQ kernel)
   auto images = [&](int b) -> long long {

@@ -99,6 +99,13 @@ __device__ __forceinline__ void load_lds16(const void* src, void* wave_dst) {
 
 // Wait for this wave's outstanding global loads (direct LDS loads included).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Wait until at most N of this wave's vector memory operations are
+// outstanding (they complete in issue order for this count).
+template <int N>
+__device__ __forceinline__ void wait_vm_le() {
+  static_assert(N >= 0 && N < 16, "vmcnt field holds 0..15 in its low bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
 
 // Copies the blocked row tile of rows [row0, row0 + 64) of a strided
 // [tokens, 160] view (rows past `nrows` read `zero`) with four waves: wave
