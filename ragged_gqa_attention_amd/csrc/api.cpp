@@ -60,7 +60,7 @@ int device_cus() {
 }
 
 struct Layout {
-  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero;
+  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero, fwd_map, kv_map;
   size_t lse, rowinfo, part_dk, part_dv, kt, vt;
   size_t total;
   int64_t max_units;
@@ -91,6 +91,8 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_seq = take(sizeof(int) * B);
   L.kv_off = take(sizeof(int) * (B + 1));
   L.kv_rank = take(sizeof(int) * B);
+  L.fwd_map = take(sizeof(int) * 2 * (size_t)L.row_tiles);
+  L.kv_map = take(sizeof(int) * 2 * (size_t)L.max_units);
   L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
   const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
   if (entry != ATTN_ENTRY_BWD) L.vt = take(tt_bytes);   // V^T for the forward
@@ -189,6 +191,8 @@ Plan plan_view(void* ws, const Layout& L) {
   pl.kv_off = reinterpret_cast<int*>(base + L.kv_off);
   pl.kv_rank = reinterpret_cast<int*>(base + L.kv_rank);
   pl.flag = reinterpret_cast<int*>(base + L.flag);
+  pl.fwd_map = reinterpret_cast<int*>(base + L.fwd_map);
+  pl.kv_map = reinterpret_cast<int*>(base + L.kv_map);
   return pl;
 }
 
@@ -258,6 +262,9 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.total_k = p->total_k;
   pa.target_units = cus * UNITS_PER_CU_NUM / UNITS_PER_CU_DEN;
   pa.min_chunk = MIN_CHUNK_ROWS;
+  pa.fwd_slots = (int)L.row_tiles;
+  a.fwd_slots = (int)L.row_tiles;
+  pa.kv_slots = (int)L.max_units;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;
   // workspace past the fixed layout holds stored dS images (backward entries)

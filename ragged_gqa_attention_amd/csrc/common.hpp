@@ -139,6 +139,9 @@ struct Plan {
   int* kv_off;     // [B+1]  exclusive prefix of (key tile, row chunk) units over ranks
   int* kv_rank;    // [B]    sequence -> rank in kv order
   int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation
+  // Workgroup -> work item, so a workgroup finds its item with one load:
+  int* fwd_map;    // [fwd_slots * 2]  row tile i: (sequence, tile in sequence), (-1, 0) past the end
+  int* kv_map;     // [kv_slots * 2]   dK/dV unit i: (sequence, unit in sequence), (-1, 0) past the end
 };
 
 // n / d for 0 <= n < 2^31 with a host-computed multiplier (round-up method of

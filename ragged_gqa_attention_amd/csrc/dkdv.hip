@@ -336,10 +336,9 @@ template <class T, bool CAP>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) KvShared sm;
 
-  const int rank = find_rank(a.plan.kv_off, a.batch, blockIdx.x);
-  if (rank < 0) return;
-  const int b = a.plan.kv_seq[rank];
-  const int unit = blockIdx.x - a.plan.kv_off[rank];
+  const int b = a.plan.kv_map[2 * blockIdx.x];
+  if (b < 0) return;
+  const int unit = a.plan.kv_map[2 * blockIdx.x + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   KvUnit u;
   u.q0 = sq[SQ_Q0];

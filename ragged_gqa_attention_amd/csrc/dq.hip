@@ -202,15 +202,14 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   // Workgroups past the row tiles (the grid's tail) sum the split dK / dV
   // partials, a slice each: they start as the row tiles drain and fill the
   // compute units the last row tiles leave idle.
-  const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
-  if (rank < 0) {
+  const int b = (int)blockIdx.x < a.fwd_slots ? a.plan.fwd_map[2 * blockIdx.x] : -1;
+  if (b < 0) {
     const int first = a.batch > 0 ? a.plan.fwd_off[a.batch] : 0;
     if (a.total_k > 0 && (int)blockIdx.x >= first)
       reduce_kv_tiles<T>(a, blockIdx.x - first, gridDim.x - first);
     return;
   }
-  const int b = a.plan.fwd_seq[rank];
-  const int tile = blockIdx.x - a.plan.fwd_off[rank];
+  const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   if (a.ds && sq[SQ_DSOFF] >= 0) {
     dq_stored<T, CAP>(a, sm.d, sq, tile);

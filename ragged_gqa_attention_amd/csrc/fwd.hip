@@ -37,11 +37,13 @@ namespace rga {
 
 namespace {
 
-// LDS of one key step: the K rows (row tile, blk_off) and V^T (transposed key
-// tile, tt_off), double-buffered.
+// LDS of a key step: the K rows (row tile, blk_off) and V^T (transposed key
+// tile, tt_off), three buffers (one step in flight, one being read, and the
+// previous one still read by the deferred half of the lag waves).
+constexpr int FWD_NBUF = 3;
 struct FwdShared {
-  uint16_t k[2][TILE_ELEMS];
-  uint16_t vt[2][TILE_ELEMS];
+  uint16_t k[FWD_NBUF][TILE_ELEMS];
+  uint16_t vt[FWD_NBUF][TILE_ELEMS];
 };
 
 }  // namespace
@@ -50,10 +52,9 @@ template <class T, bool CAP, bool DELTA>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) FwdShared sm;
 
-  const int rank = find_rank(a.plan.fwd_off, a.batch, blockIdx.x);
-  if (rank < 0) return;
-  const int b = a.plan.fwd_seq[rank];
-  const int tile = blockIdx.x - a.plan.fwd_off[rank];
+  const int b = a.plan.fwd_map[2 * blockIdx.x];
+  if (b < 0) return;
+  const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   const int q0 = sq[SQ_Q0], Lq = sq[SQ_LQ], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
   const int rows = sq[SQ_ROWS];
@@ -107,96 +108,147 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) voff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
 
-  // one key step on the tile in LDS buffer buf; masked: keys past Lk get P = 0
-  auto step = [&](int buf, int kbase, auto masked) {
-    const uint16_t* Kb = sm.k[buf];
-    const uint16_t* Vb = sm.vt[buf];
+  // S^T[key][row] = K Q^T (lane = row) for key block kb of the K tile Kb
+  // (LDS operands are read two k-steps ahead of the MFMA that uses them)
+  f32x16 S[2];
+  auto scores = [&](int kb, const uint16_t* Kb) {
+    const uint16_t* Kr = Kb + kb * 2 * BLK_COLS * BLK_ELEMS;
+    auto kop = [&](int ks) { return load16(Kr + koff[ks & 1] + (ks >> 1) * BLK_ELEMS); };
+    u32x4 ka[3];
+    ka[0] = kop(0);
+    ka[1] = kop(1);
+    S[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      if (ks + 2 < KSTEPS) ka[(ks + 2) % 3] = kop(ks + 2);
+      S[kb] = mfma32<T>(ka[ks % 3], qf[ks], S[kb]);
+    }
+  };
+  // capped and biased logits (log2 units) of key block kb of the step at
+  // kbase; masked: keys past Lk get -inf (only a partial last step needs it,
+  // the compare and select cost a VALU pair per logit)
+  auto logits = [&](int kb, int kbase, auto masked) {
     const float cb = cb0 - (float)kbase;
     const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+      float x;
+      if (CAP)
+        x = __builtin_fmaf(a.lc.t_mul, cap_r(S[kb][r], a.lc),
+                           -slope2 * __builtin_fabsf(cb - (float)jl));
+      else
+        x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
+      if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
+      S[kb][r] = x;
+    }
+  };
+  // P rounded to the input dtype feeds the PV product, and O is normalised by
+  // the sum of those same rounded values (lsum_r), so O is an exact convex
+  // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
+  // matches dP.  L and the backward's residual use the exact FP32 sum.
+  u32x4 pb[2][2];
+  auto probs = [&](int kb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(S[kb][r]);
+      lsum += p;
+      S[kb][r] = p;
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
+                        pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
+                        pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
+                        pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
+    }
+  };
+  // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb of the V^T
+  // tile Vb; the V^T operand is one 16-byte read in the key order of pb
+  auto pv = [&](int kb, const uint16_t* Vb) {
+    auto vop = [&](int i) { return load16(Vb + voff[kb][i & 1] + (i >> 1) * 32 * TILE_ROWS); };
+    u32x4 va[3];
+    va[0] = vop(0);
+    va[1] = vop(1);
+#pragma unroll
+    for (int i = 0; i < 2 * DBLK; ++i) {
+      if (i + 2 < 2 * DBLK) va[(i + 2) % 3] = vop(i + 2);
+      O[i >> 1] = mfma32<T>(va[i % 3], pb[kb][i & 1], O[i >> 1]);
+    }
+  };
 
-    // S^T[key][row] = K Q^T (lane = row) for key block kb
-    f32x16 S[2];
-    // (LDS operands are read two k-steps ahead of the MFMA that uses them)
-    auto scores = [&](int kb) {
-      const uint16_t* Kr = Kb + kb * 2 * BLK_COLS * BLK_ELEMS;
-      auto kop = [&](int ks) { return load16(Kr + koff[ks & 1] + (ks >> 1) * BLK_ELEMS); };
-      u32x4 ka[3];
-      ka[0] = kop(0);
-      ka[1] = kop(1);
-      S[kb] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        if (ks + 2 < KSTEPS) ka[(ks + 2) % 3] = kop(ks + 2);
-        S[kb] = mfma32<T>(ka[ks % 3], qf[ks], S[kb]);
-      }
-    };
-    // capped and biased logits (log2 units) of key block kb, masked past Lk
-    auto logits = [&](int kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
-        float x;
-        if (CAP)
-          x = __builtin_fmaf(a.lc.t_mul, cap_r(S[kb][r], a.lc),
-                             -slope2 * __builtin_fabsf(cb - (float)jl));
-        else
-          x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
-        if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
-        S[kb][r] = x;
-      }
-    };
-    // P rounded to the input dtype feeds the PV product, and O is normalised by
-    // the sum of those same rounded values (lsum_r), so O is an exact convex
-    // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
-    // matches dP.  L and the backward's residual use the exact FP32 sum.
-    u32x4 pb[2][2];
-    auto probs = [&](int kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(S[kb][r]);
-        lsum += p;
-        S[kb][r] = p;
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
-                          pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
-                          pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
-                          pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
-      }
-    };
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb; the V^T
-    // operand is one 16-byte read in the key order of pb
-    auto pv = [&](int kb) {
-      auto vop = [&](int i) { return load16(Vb + voff[kb][i & 1] + (i >> 1) * 32 * TILE_ROWS); };
-      u32x4 va[3];
-      va[0] = vop(0);
-      va[1] = vop(1);
-#pragma unroll
-      for (int i = 0; i < 2 * DBLK; ++i) {
-        if (i + 2 < 2 * DBLK) va[(i + 2) % 3] = vop(i + 2);
-        O[i >> 1] = mfma32<T>(va[i % 3], pb[kb][i & 1], O[i >> 1]);
-      }
-    };
+  // tile kt has landed for every wave, and every wave is done with kt - 2;
+  // then start the copies of kt + 1 (three buffers)
+  auto advance = [&](int kt) {
+    wait_vm();
+    __syncthreads();
+    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) % FWD_NBUF);
+  };
+  // the key mask costs a compare and a select per logit, so only a partial
+  // last key step runs the masked instance (after the loop)
+  const int nfull = Lk / TILE_ROWS;
+  const bool partial = nfull < ntiles;
+  constexpr Flag<false> unmasked{};
+  constexpr Flag<true> masked{};
+  if (ntiles > 0) issue(0, 0);
 
-    if (CAP) {
-      // the offset is fixed, so the two key blocks are independent: the MFMAs
-      // of one block can run while the VALU works on the other
-      scores(0);
-      scores(1);
-      logits(0);
-      probs(0);
-      pv(0);
-      logits(1);
-      probs(1);
-      pv(1);
-    } else {
-      scores(0);
-      scores(1);
-      logits(0);
-      logits(1);
+  if (CAP) {
+    // The offset is fixed, so the two 32-key blocks of a step are independent.
+    // Waves w and w + 4 share a SIMD; if both ran the same order they would
+    // want the matrix core and the VALU at the same moments.  Wave w (lead)
+    // takes a step as S0 S1 | logits/P 0 | PV0 | logits/P 1 | PV1; wave w + 4
+    // (lag) defers block 1 of each step into the next one: (logits/P 1 | PV1
+    // of the previous step) S0 S1 | logits/P 0 | PV0, so its VALU work falls on
+    // the lead wave's products and the other way round.  A deferred block reads
+    // the previous step's V^T, hence three LDS buffers.
+    auto run = [&](auto lag) {
+      constexpr bool LAG = decltype(lag)::value;
+      auto step = [&](int kt, auto mk) {
+        const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
+        if (LAG && kt > 0) {   // the previous step is a full one
+          logits(1, kbase - TILE_ROWS, unmasked);
+          probs(1);
+          pv(1, sm.vt[(kt - 1) % FWD_NBUF]);
+        }
+        scores(0, sm.k[buf]);
+        scores(1, sm.k[buf]);
+        logits(0, kbase, mk);
+        probs(0);
+        pv(0, sm.vt[buf]);
+        if (!LAG) {
+          logits(1, kbase, mk);
+          probs(1);
+          pv(1, sm.vt[buf]);
+        }
+      };
+      for (int kt = 0; kt < nfull; ++kt) {
+        advance(kt);
+        step(kt, unmasked);
+      }
+      if (partial) {
+        advance(nfull);
+        step(nfull, masked);
+      }
+      if (LAG && ntiles > 0) {   // block 1 of the last step
+        const int kt = ntiles - 1;
+        if (partial) logits(1, kt * TILE_ROWS, masked);
+        else logits(1, kt * TILE_ROWS, unmasked);
+        probs(1);
+        pv(1, sm.vt[kt % FWD_NBUF]);
+      }
+    };
+    if (wave < 4) run(Flag<false>{});
+    else run(Flag<true>{});
+  } else {
+    // running maximum over both blocks of a step, then rescale
+    auto step = [&](int kt, auto mk) {
+      const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
+      scores(0, sm.k[buf]);
+      scores(1, sm.k[buf]);
+      logits(0, kbase, mk);
+      logits(1, kbase, mk);
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -216,29 +268,17 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
         for (int r = 0; r < 16; ++r) S[kb][r] -= mnew;
       probs(0);
       probs(1);
-      pv(0);
-      pv(1);
+      pv(0, sm.vt[buf]);
+      pv(1, sm.vt[buf]);
+    };
+    for (int kt = 0; kt < nfull; ++kt) {
+      advance(kt);
+      step(kt, unmasked);
     }
-  };
-
-  // tile kt has landed for every wave, and every wave is done with kt - 1;
-  // then start the copies of kt + 1
-  auto advance = [&](int kt) {
-    wait_vm();
-    __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
-  };
-  // the key mask costs a compare and a select per logit, so only a partial
-  // last key step runs the masked instance (after the loop)
-  const int nfull = Lk / TILE_ROWS;
-  if (ntiles > 0) issue(0, 0);
-  for (int kt = 0; kt < nfull; ++kt) {
-    advance(kt);
-    step(kt & 1, kt * TILE_ROWS, Flag<false>{});
-  }
-  if (nfull < ntiles) {
-    advance(nfull);
-    step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
+    if (partial) {
+      advance(nfull);
+      step(nfull, masked);
+    }
   }
 
   // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta

@@ -60,6 +60,7 @@ struct AttnArgs {
   int batch;
   int64_t total_q;
   int64_t total_k;
+  int fwd_slots;        // entries of plan.fwd_map; the dQ grid has more (partial sums)
   LogitConsts lc;
   Plan plan;
 };
@@ -74,6 +75,8 @@ struct PlanArgs {
   int target_units;     // desired number of dK/dV work units
   int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
   long long ds_images;  // dS images that fit the workspace (0: no stored dS)
+  int fwd_slots;        // entries of plan.fwd_map (the row-tile launches' grid)
+  int kv_slots;         // entries of plan.kv_map (the dK/dV launch's grid)
   uint16_t* zero;       // 512 bytes the planner clears
   Plan plan;
 };

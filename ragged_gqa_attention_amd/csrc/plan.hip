@@ -63,13 +63,26 @@ __device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, V* p
   __syncthreads();
 }
 
+// Batches up to this size are planned in LDS and copied out at the end (each
+// planning step re-reads what the previous one wrote; LDS keeps those round
+// trips short); larger ones are planned in place in global memory.
+constexpr int PLAN_LDS_B = 256;
+
 __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   __shared__ int bad;
   __shared__ long long red[PLAN_WAVES];
   __shared__ int part[PLAN_WAVES];
+  __shared__ int l_seq[PLAN_LDS_B * SEQ_FIELDS];
+  __shared__ int l_fseq[PLAN_LDS_B], l_kseq[PLAN_LDS_B];
+  __shared__ int l_foff[PLAN_LDS_B + 1], l_koff[PLAN_LDS_B + 1];
   const int tid = threadIdx.x;
   const int B = a.batch;
-  int* seq = a.plan.seq;
+  const bool in_lds = B <= PLAN_LDS_B;
+  int* seq = in_lds ? l_seq : a.plan.seq;
+  int* fwd_seq = in_lds ? l_fseq : a.plan.fwd_seq;
+  int* kv_seq = in_lds ? l_kseq : a.plan.kv_seq;
+  int* fwd_off = in_lds ? l_foff : a.plan.fwd_off;
+  int* kv_off = in_lds ? l_koff : a.plan.kv_off;
 
   if (tid == 0) bad = 0;
   if (tid < 32) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
@@ -131,21 +144,41 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
         rk += (ko > kb) || (ko == kb && o < b);
       }
     }
-    a.plan.fwd_seq[rf] = b;
-    a.plan.kv_seq[rk] = b;
+    fwd_seq[rf] = b;
+    kv_seq[rk] = b;
     a.plan.kv_rank[b] = rk;
   }
   __syncthreads();
 
   const int hq = a.hq;
   block_exclusive_scan(B, [&](int r) {
-    const int b = a.plan.fwd_seq[r];
+    const int b = fwd_seq[r];
     return (seq[b * SEQ_FIELDS + SQ_LQ] * hq + ROW_TILE - 1) / ROW_TILE;
-  }, [&](int r, int v) { a.plan.fwd_off[r] = v; }, part);
+  }, [&](int r, int v) { fwd_off[r] = v; }, part);
   block_exclusive_scan(B, [&](int r) {
-    const int b = a.plan.kv_seq[r];
+    const int b = kv_seq[r];
     return seq[b * SEQ_FIELDS + SQ_KTILES] * seq[b * SEQ_FIELDS + SQ_NCHUNK];
-  }, [&](int r, int v) { a.plan.kv_off[r] = v; }, part);
+  }, [&](int r, int v) { kv_off[r] = v; }, part);
+  // workgroup -> item maps (entries past the last item get sequence -1)
+  __threadfence_block();
+  __syncthreads();
+  auto fill_map = [&](int* map, int slots, const int* off, const int* order) {
+    for (int i = tid; i < slots; i += PLAN_THREADS) {
+      int r = -1;
+      if (B > 0 && i < off[B]) {
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (off[mid] <= i) lo = mid; else hi = mid - 1;
+        }
+        r = lo;
+      }
+      map[2 * i] = r >= 0 ? order[r] : -1;
+      map[2 * i + 1] = r >= 0 ? i - off[r] : 0;
+    }
+  };
+  fill_map(a.plan.fwd_map, a.fwd_slots, fwd_off, fwd_seq);
+  fill_map(a.plan.kv_map, a.kv_slots, kv_off, kv_seq);
   // transposed 64-key tiles, in sequence order
   block_exclusive_scan(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
@@ -167,85 +200,118 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
       seq[b * SEQ_FIELDS + SQ_DSOFF] = (n > 0 && off + n <= a.ds_images) ? (int)off : -1;
     }
   }, red);
+  if (in_lds) {   // the kernels read the plan from global memory
+    for (int i = tid; i < B * SEQ_FIELDS; i += PLAN_THREADS) a.plan.seq[i] = l_seq[i];
+    for (int i = tid; i < B; i += PLAN_THREADS) {
+      a.plan.fwd_seq[i] = l_fseq[i];
+      a.plan.kv_seq[i] = l_kseq[i];
+    }
+    for (int i = tid; i <= B; i += PLAN_THREADS) {
+      a.plan.fwd_off[i] = l_foff[i];
+      a.plan.kv_off[i] = l_koff[i];
+    }
+  }
 }
 
-// Transposed key tile `tile` of K (t = 0) or V (t = 1) (see tt_key_pos): keys
-// [64 j, 64 j + 64) of the sequence whose tiles start at or before `tile`
-// (j = tile - first tile, tiles counted as in the planner's SQ_TTOFF); keys
-// past Lk become zeros.  The sequence is found from cu_k directly, so this runs
-// alongside the planner; an invalid cu_k (which the planner flags, and which
+// Transposed key tile `tile` of K and of V (see tt_key_pos; null outputs are
+// skipped): keys [64 j, 64 j + 64) of the sequence whose tiles start at or
+// before `tile` (j = tile - first tile, tiles counted as in the planner's
+// SQ_TTOFF); keys past Lk become zeros.  The sequence is found from cu_k
+// directly, so this runs alongside the planner: wave 0 checks cu_k and scans
+// the per-sequence tile counts with lane shuffles (lane l owns a contiguous
+// run of sequences).  An invalid cu_k (which the planner flags, and which
 // then plans no work) transposes nothing.
-__device__ __forceinline__ void transpose_block(const PlanArgs& pa, const AttnArgs& a, int tile,
-                                                int t) {
+__device__ __forceinline__ void transpose_tiles(const PlanArgs& pa, const AttnArgs& a, int tile) {
   __shared__ __attribute__((aligned(16))) uint16_t rows[TILE_ROWS][HEAD_DIM + 8];
-  __shared__ int part[PLAN_WAVES];
-  __shared__ int s_bad, s_b, s_j;
-  uint16_t* dst = t ? a.vt : a.kt;
+  __shared__ int s_b, s_j;
   const int B = pa.batch;
-  if (!dst || B <= 0) return;
+  if ((!a.kt && !a.vt) || B <= 0) return;
   const int tid = threadIdx.x;
-  if (tid == 0) { s_bad = 0; s_b = -1; s_j = 0; }
-  __syncthreads();
-  for (int b = tid; b <= B; b += PLAN_THREADS) {
-    const int ck = pa.cu_k[b];
-    bool fail = ck < 0 || (int64_t)ck > pa.total_k;
-    if (b == 0) fail |= ck != 0;
-    if (b == B) fail |= (int64_t)ck != pa.total_k;
-    if (b < B) fail |= pa.cu_k[b + 1] < ck;
-    if (fail) s_bad = 1;   // benign race: every writer stores 1
+  if (tid < 64) {
+    const int lane = tid;
+    const int seg = (B + 63) / 64;
+    const int lo = min(B, lane * seg), hi = min(B, lo + seg);
+    bool fail = false;
+    int count = 0;
+    int prev = lo <= B ? pa.cu_k[lo] : 0;
+    if (lo == 0) fail |= prev != 0;
+    fail |= prev < 0 || (int64_t)prev > pa.total_k;
+    for (int b = lo; b < hi; ++b) {
+      const int nx = pa.cu_k[b + 1];
+      fail |= nx < prev || (int64_t)nx > pa.total_k;
+      count += (nx - prev + TILE_ROWS - 1) / TILE_ROWS;
+      prev = nx;
+    }
+    if (hi == B && lo < hi) fail |= (int64_t)prev != pa.total_k;
+    if (B <= lane * seg && lane * seg < B + seg) fail |= (int64_t)pa.cu_k[B] != pa.total_k;
+    const bool any_fail = __any(fail);
+    int x = count;   // inclusive scan over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    int run = x - count;   // tiles before this lane's first sequence
+    int fb = -1, fj = 0;
+    if (!any_fail && run <= tile && tile < x) {
+      for (int b = lo; b < hi; ++b) {
+        const int n = (pa.cu_k[b + 1] - pa.cu_k[b] + TILE_ROWS - 1) / TILE_ROWS;
+        if (tile < run + n) { fb = b; fj = tile - run; break; }
+        run += n;
+      }
+    }
+    const unsigned long long who = __ballot(fb >= 0);
+    if (lane == 0) { s_b = -1; s_j = 0; }
+    if (who != 0 && lane == __ffsll((long long)who) - 1) { s_b = fb; s_j = fj; }
   }
   __syncthreads();
-  if (s_bad) return;
-  auto ntiles = [&](int b) { return (pa.cu_k[b + 1] - pa.cu_k[b] + TILE_ROWS - 1) / TILE_ROWS; };
-  block_exclusive_scan(B, ntiles, [&](int b, int off) {
-    if (b < B && off <= tile && tile < off + ntiles(b)) { s_b = b; s_j = tile - off; }
-  }, part);
   const int b = s_b, j = s_j;
   if (b < 0) return;
   const int k0 = pa.cu_k[b];
   const int Lk = pa.cu_k[b + 1] - k0;
   const int kbase = k0 + j * TILE_ROWS;
   const int nkeys = min(TILE_ROWS, Lk - j * TILE_ROWS);
-  const uint16_t* src = t ? a.v : a.k;
-  const int64_t ts = t ? a.v_ts : a.k_ts;
-  for (int i = tid; i < TILE_ROWS * CHUNKS; i += PLAN_THREADS) {
-    const int key = i / CHUNKS, c = i - key * CHUNKS;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
-    *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
-  }
-  __syncthreads();
-  dst += (int64_t)tile * TILE_ELEMS;
-  // task: feature pair (2 dp, 2 dp + 1) x chunk c of 8 keys
-  for (int o = tid; o < (HEAD_DIM / 2) * (TILE_ROWS / 8); o += PLAN_THREADS) {
-    const int dp = o / (TILE_ROWS / 8), c = o - dp * (TILE_ROWS / 8);
-    uint32_t w0[4], w1[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t x0 = *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e)][2 * dp]);
-      const uint32_t x1 =
-          *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e + 1)][2 * dp]);
-      w0[e] = (x0 & 0xffffu) | (x1 << 16);
-      w1[e] = (x0 >> 16) | (x1 & 0xffff0000u);
+  for (int t = 0; t < 2; ++t) {
+    uint16_t* dst = t ? a.vt : a.kt;
+    if (!dst) continue;
+    const uint16_t* src = t ? a.v : a.k;
+    const int64_t ts = t ? a.v_ts : a.k_ts;
+    for (int i = tid; i < TILE_ROWS * CHUNKS; i += PLAN_THREADS) {
+      const int key = i / CHUNKS, c = i - key * CHUNKS;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
+      *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
     }
-    *reinterpret_cast<u32x4*>(dst + (2 * dp) * TILE_ROWS + c * 8) = u32x4{w0[0], w0[1], w0[2], w0[3]};
-    *reinterpret_cast<u32x4*>(dst + (2 * dp + 1) * TILE_ROWS + c * 8) =
-        u32x4{w1[0], w1[1], w1[2], w1[3]};
+    __syncthreads();
+    dst += (int64_t)tile * TILE_ELEMS;
+    // task: feature pair (2 dp, 2 dp + 1) x chunk c of 8 keys
+    for (int o = tid; o < (HEAD_DIM / 2) * (TILE_ROWS / 8); o += PLAN_THREADS) {
+      const int dp = o / (TILE_ROWS / 8), c = o - dp * (TILE_ROWS / 8);
+      uint32_t w0[4], w1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x0 = *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e)][2 * dp]);
+        const uint32_t x1 =
+            *reinterpret_cast<const uint32_t*>(&rows[tt_key_pos(8 * c + 2 * e + 1)][2 * dp]);
+        w0[e] = interleave_lo(x0, x1);
+        w1[e] = interleave_hi(x0, x1);
+      }
+      *reinterpret_cast<u32x4*>(dst + (2 * dp) * TILE_ROWS + c * 8) = u32x4{w0[0], w0[1], w0[2], w0[3]};
+      *reinterpret_cast<u32x4*>(dst + (2 * dp + 1) * TILE_ROWS + c * 8) =
+          u32x4{w1[0], w1[1], w1[2], w1[3]};
+    }
+    __syncthreads();
   }
 }
 
-// Workgroup 0 plans; workgroups 1 + 2 i + t transpose key tile i of K or V.
+// Workgroup 0 plans; workgroup 1 + i transposes key tile i of K and V.
 __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(const PlanArgs pa, const AttnArgs a) {
-  if (blockIdx.x == 0) {
-    plan_block(pa);
-  } else {
-    const int i = blockIdx.x - 1;
-    transpose_block(pa, a, i >> 1, i & 1);
-  }
+  if (blockIdx.x == 0) plan_block(pa);
+  else transpose_tiles(pa, a, blockIdx.x - 1);
 }
 
 hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s) {
-  const int transposers = (a.kt || a.vt) ? 2 * key_tiles : 0;
+  const int transposers = (a.kt || a.vt) ? key_tiles : 0;
   hipLaunchKernelGGL(prep_kernel, 1 + transposers, PLAN_THREADS, 0, s, pa, a);
   return hipGetLastError();
 }
