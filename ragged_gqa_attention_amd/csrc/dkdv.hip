@@ -184,27 +184,28 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
-  auto pointwise_publish = [&](int buf, int slot, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB],
-                               u32x4 (&own)[KB][2]) {
+  // P and dS of accumulator register r (row rbase + 8 (r/4) + r%4)
+  auto pointwise = [&](int buf, int r, f32x16 (&S)[KB], f32x16 (&dP)[KB]) {
+    const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
-        float p, w;
-        if (CAP) {
-          const float rc = cap_r(S[kb][r], a.lc);
-          p = fast_exp2(__builtin_fmaf(a.lc.t_mul, rc, bias));
-          w = __builtin_fmaf(-rc, rc, rc);
-        } else {
-          p = fast_exp2(__builtin_fmaf(S[kb][r], a.lc.s_lin, bias));
-          w = 1.0f;
-        }
-        S[kb][r] = p;
-        dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
+    for (int kb = 0; kb < KB; ++kb) {
+      const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
+      float p, w;
+      if (CAP) {
+        const float rc = cap_r(S[kb][r], a.lc);
+        p = fast_exp2(__builtin_fmaf(a.lc.t_mul, rc, bias));
+        w = __builtin_fmaf(-rc, rc, rc);
+      } else {
+        p = fast_exp2(__builtin_fmaf(S[kb][r], a.lc.s_lin, bias));
+        w = 1.0f;
       }
+      S[kb][r] = p;
+      dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
     }
+  };
+  // packs P and dS; the own product's half goes to `own`, the other to the
+  // partner through LDS slot `slot`; dS also to its image
+  auto publish = [&](int slot, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB], u32x4 (&own)[KB][2]) {
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -221,6 +222,12 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
         sm.xch[slot][wave][kb * 2 + s][lane] = ROLE ? pb : sb;
         if (ds_on) store_ds(r0 + ROLE * 32, s, sb);
       }
+  };
+  auto pointwise_publish = [&](int buf, int slot, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB],
+                               u32x4 (&own)[KB][2]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pointwise(buf, r, S, dP);
+    publish(slot, r0, S, dP, own);
   };
 
   // dV (ROLE 0) or dK (ROLE 1) over the 64 rows of a step: A = dO^T or Q^T

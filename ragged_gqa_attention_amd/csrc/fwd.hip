@@ -45,6 +45,11 @@ struct FwdShared {
   uint16_t k[FWD_NBUF][TILE_ELEMS];
   uint16_t vt[FWD_NBUF][TILE_ELEMS];
 };
+// After the key loop the same LDS holds the normalised O rows (pitch of 168
+// elements) and each row's record.
+constexpr int O_PITCH = HEAD_DIM + 8;
+static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared),
+              "O staging fits the key-tile buffers");
 
 }  // namespace
 
@@ -281,38 +286,66 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
     }
   }
 
-  // epilogue: normalise, store O (feature 32db + 8(r/4) + 4g + r%4), L, and delta
+  // Epilogue.  The normalised O goes through LDS so that global stores (and
+  // the dO loads of Delta) move whole 64-byte pieces of rows: in the
+  // accumulator layout a lane holds 8-byte pieces of one row, which would
+  // touch a new row every lane.  Delta = dO . O uses the rounded O, as the
+  // standalone backward does from the stored output.
   lsum += swap_half(lsum);
   lsum_r += swap_half(lsum_r);
   const float inv = lsum_r > 0.0f ? 1.0f / lsum_r : 0.0f;
-  uint16_t* orow = a.out + (int64_t)(q0 + ti) * a.o_ts + (int64_t)hh * a.o_hs + g * 4;
-  const uint16_t* dorow = nullptr;
-  if (DELTA) dorow = a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)hh * a.do_hs + g * 4;
-  float dsum = 0.0f;
+  const float res = m + fast_log2(lsum);
+  __syncthreads();   // every wave is done with the key tiles
+  uint16_t* obuf = reinterpret_cast<uint16_t*>(&sm);
+  f32x4* sinfo = reinterpret_cast<f32x4*>(obuf + ROW_TILE * O_PITCH);
+  const int lrow = wave * 32 + l32;
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db) {
+  for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      const float o0 = O[db][rq * 4 + 0] * inv, o1 = O[db][rq * 4 + 1] * inv;
-      const float o2 = O[db][rq * 4 + 2] * inv, o3 = O[db][rq * 4 + 3] * inv;
-      const int off = db * 32 + rq * 8;
-      if (row_ok)
-        *reinterpret_cast<u32x2*>(orow + off) = u32x2{pack2<T>(o0, o1), pack2<T>(o2, o3)};
-      if (DELTA) {
-        const u32x2 d = *reinterpret_cast<const u32x2*>(dorow + off);
-        dsum += o0 * lo_f<T>(d[0]) + o1 * hi_f<T>(d[0]) + o2 * lo_f<T>(d[1]) + o3 * hi_f<T>(d[1]);
+    for (int rq = 0; rq < 4; ++rq)
+      *reinterpret_cast<u32x2*>(obuf + lrow * O_PITCH + db * 32 + rq * 8 + g * 4) =
+          u32x2{pack2<T>(O[db][rq * 4 + 0] * inv, O[db][rq * 4 + 1] * inv),
+                pack2<T>(O[db][rq * 4 + 2] * inv, O[db][rq * 4 + 3] * inv)};
+  if (g == 0) {
+    sinfo[lrow] = f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f, 0.0f};
+    if (row_ok)
+      a.lse[(int64_t)(q0 + ti) * a.hq + hh] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
+  }
+  __syncthreads();
+  // lanes 4q .. 4q + 3 take row 32 w + 16 h + q, chunks (lane % 4) + 4 i
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = wave * 32 + 16 * h + (lane >> 2);
+    const int rg = tile * ROW_TILE + r;
+    const bool ok = rg < rows;
+    const int rc = ok ? rg : rows - 1;
+    const int tk = fast_div(rc, a.hq_mul, a.hq_shift);
+    const int hd = rc - tk * a.hq;
+    uint16_t* orow = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
+    const uint16_t* drow = DELTA ? a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs
+                                 : nullptr;
+    float dpart = 0.0f;
+#pragma unroll
+    for (int i = 0; i < CHUNKS / 4; ++i) {
+      const int c = (lane & 3) + 4 * i;
+      const u32x4 o = load16(obuf + r * O_PITCH + c * 8);
+      if (ok) *reinterpret_cast<u32x4*>(orow + c * 8) = o;
+      if (DELTA && ok) {
+        const u32x4 d = load16(drow + c * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dpart += lo_f<T>(o[e]) * lo_f<T>(d[e]) + hi_f<T>(o[e]) * hi_f<T>(d[e]);
       }
     }
-  }
-  if (DELTA) dsum += swap_half(dsum);
-  if (row_ok && g == 0) {
-    const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
-    const float res = m + fast_log2(lsum);
-    a.lse[ri] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
-    if (a.rowinfo)
-      *reinterpret_cast<f32x4*>(a.rowinfo + ri * 4) =
-          f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f,
-                DELTA ? dsum : 0.0f};
+    if (DELTA) {
+      dpart += __shfl_xor(dpart, 1, 64);
+      dpart += __shfl_xor(dpart, 2, 64);
+    }
+    if (ok && (lane & 3) == 0 && a.rowinfo) {
+      f32x4 rec = sinfo[r];
+      rec[3] = DELTA ? dpart : 0.0f;
+      *reinterpret_cast<f32x4*>(a.rowinfo + ((int64_t)q0 * a.hq + rg) * 4) = rec;
+    }
   }
 }
 
