@@ -92,6 +92,42 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
   }
 }
 
+// Stores the dQ accumulators of a 256-row tile.  The rounded values go
+// through LDS (row pitch 168 elements, reusing the tile buffers after a
+// barrier) so that each global store writes 64-byte pieces of rows: lanes
+// 4q .. 4q + 3 of wave w take row 32 w + 16 h + q, chunks (lane % 4) + 4 i.
+// lrow: the tile-local row the lane's accumulator column belongs to.
+template <class T>
+__device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage,
+                                              const f32x16 (&dQ)[DBLK], float scale, int lrow,
+                                              int tile, int q0, int rows, int wave, int lane) {
+  constexpr int PITCH = HEAD_DIM + 8;
+  const int g = lane >> 5;
+  __syncthreads();   // every wave is done with the tile buffers
+#pragma unroll
+  for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq)
+      *reinterpret_cast<u32x2*>(stage + lrow * PITCH + db * 32 + rq * 8 + g * 4) =
+          u32x2{pack2<T>(scale * dQ[db][rq * 4 + 0], scale * dQ[db][rq * 4 + 1]),
+                pack2<T>(scale * dQ[db][rq * 4 + 2], scale * dQ[db][rq * 4 + 3])};
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = wave * 32 + 16 * h + (lane >> 2);
+    const int rg = tile * ROW_TILE + r;
+    if (rg >= rows) continue;
+    const int tk = fast_div(rg, a.hq_mul, a.hq_shift);
+    const int hd = rg - tk * a.hq;
+    uint16_t* drow = a.dq + (int64_t)(q0 + tk) * a.dq_ts + (int64_t)hd * a.dq_hs;
+#pragma unroll
+    for (int i = 0; i < CHUNKS / 4; ++i) {
+      const int c = (lane & 3) + 4 * i;
+      *reinterpret_cast<u32x4*>(drow + c * 8) = load16(stage + r * PITCH + c * 8);
+    }
+  }
+}
+
 // LDS of the stored-dS path: the dS image (64 keys x 256 rows, ds_off) and
 // K^T (tt_off) of a key step, three buffers (two steps in flight).
 constexpr int DQS_NBUF = 3;
@@ -99,6 +135,7 @@ struct DqStoredShared {
   uint16_t ds[DQS_NBUF][DS_IMAGE_ELEMS];
   uint16_t kt[DQS_NBUF][TILE_ELEMS];
 };
+static_assert(ROW_TILE * (HEAD_DIM + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ staging fits");
 
 // dQ of row tile `tile` from the dS images the dK/dV kernel stored:
 // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row], nothing recomputed.  Both
@@ -175,19 +212,9 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
     }
   }
 
-  const int row = tile * ROW_TILE + wave * 32 + tt_key_pos(l32);
-  if (row >= rows) return;
-  const int ti_ = fast_div(row, a.hq_mul, a.hq_shift);
-  const int hh = row - ti_ * a.hq;
-  const float scale = CAP ? 4.0f * a.lc.sigma : a.lc.sigma;
-  uint16_t* dqr = a.dq + (int64_t)(q0 + ti_) * a.dq_ts + (int64_t)hh * a.dq_hs + g * 4;
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq)
-      *reinterpret_cast<u32x2*>(dqr + db * 32 + rq * 8) =
-          u32x2{pack2<T>(scale * dQ[db][rq * 4 + 0], scale * dQ[db][rq * 4 + 1]),
-                pack2<T>(scale * dQ[db][rq * 4 + 2], scale * dQ[db][rq * 4 + 3])};
+  // lane l32 holds row 32 w + tt_key_pos(l32) of the tile
+  store_dq_tile<T>(a, sm.ds[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma,
+                   wave * 32 + tt_key_pos(l32), tile, q0, rows, wave, lane);
 }
 
 }  // namespace
@@ -344,16 +371,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
   }
 
-  if (!row_ok) return;
-  const float scale = CAP ? 4.0f * a.lc.sigma : a.lc.sigma;
-  uint16_t* dqr = a.dq + (int64_t)(q0 + ti) * a.dq_ts + (int64_t)hh * a.dq_hs + g * 4;
-#pragma unroll
-  for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-    for (int rq = 0; rq < 4; ++rq)
-      *reinterpret_cast<u32x2*>(dqr + db * 32 + rq * 8) =
-          u32x2{pack2<T>(scale * dQ[db][rq * 4 + 0], scale * dQ[db][rq * 4 + 1]),
-                pack2<T>(scale * dQ[db][rq * 4 + 2], scale * dQ[db][rq * 4 + 3])};
+  store_dq_tile<T>(a, sm.r.k[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma, wave * 32 + l32,
+                   tile, q0, rows, wave, lane);
 }
 
 template <class T>

@@ -291,6 +291,27 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   // accumulator layout a lane holds 8-byte pieces of one row, which would
   // touch a new row every lane.  Delta = dO . O uses the rounded O, as the
   // standalone backward does from the stored output.
+  // lanes 4q .. 4q + 3 of wave w later take row 32 w + 16 h + q (h = 0, 1),
+  // chunks (lane % 4) + 4 i; their dO pieces are requested first
+  int erow[2];
+  bool eok[2];
+  uint16_t* eout[2];
+  u32x4 dpre[2][CHUNKS / 4];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rg = tile * ROW_TILE + wave * 32 + 16 * h + (lane >> 2);
+    erow[h] = rg;
+    eok[h] = rg < rows;
+    const int rc = eok[h] ? rg : rows - 1;
+    const int tk = fast_div(rc, a.hq_mul, a.hq_shift);
+    const int hd = rc - tk * a.hq;
+    eout[h] = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
+    if (DELTA) {
+      const uint16_t* drow = a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs;
+#pragma unroll
+      for (int i = 0; i < CHUNKS / 4; ++i) dpre[h][i] = load16(drow + ((lane & 3) + 4 * i) * 8);
+    }
+  }
   lsum += swap_half(lsum);
   lsum_r += swap_half(lsum_r);
   const float inv = lsum_r > 0.0f ? 1.0f / lsum_r : 0.0f;
@@ -312,26 +333,19 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       a.lse[(int64_t)(q0 + ti) * a.hq + hh] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
   }
   __syncthreads();
-  // lanes 4q .. 4q + 3 take row 32 w + 16 h + q, chunks (lane % 4) + 4 i
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = wave * 32 + 16 * h + (lane >> 2);
-    const int rg = tile * ROW_TILE + r;
-    const bool ok = rg < rows;
-    const int rc = ok ? rg : rows - 1;
-    const int tk = fast_div(rc, a.hq_mul, a.hq_shift);
-    const int hd = rc - tk * a.hq;
-    uint16_t* orow = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
-    const uint16_t* drow = DELTA ? a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs
-                                 : nullptr;
+    const int rg = erow[h];
+    const bool ok = eok[h];
     float dpart = 0.0f;
 #pragma unroll
     for (int i = 0; i < CHUNKS / 4; ++i) {
       const int c = (lane & 3) + 4 * i;
       const u32x4 o = load16(obuf + r * O_PITCH + c * 8);
-      if (ok) *reinterpret_cast<u32x4*>(orow + c * 8) = o;
-      if (DELTA && ok) {
-        const u32x4 d = load16(drow + c * 8);
+      if (ok) *reinterpret_cast<u32x4*>(eout[h] + c * 8) = o;
+      if (DELTA) {
+        const u32x4 d = dpre[h][i];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           dpart += lo_f<T>(o[e]) * lo_f<T>(d[e]) + hi_f<T>(o[e]) * hi_f<T>(d[e]);
