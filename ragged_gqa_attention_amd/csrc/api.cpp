@@ -156,14 +156,6 @@ attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens,
   return ATTN_OK;
 }
 
-// Multiplier and shift for n / d with 0 <= n < 2^31 (see fast_div).
-void fast_div_consts(uint32_t d, uint32_t* mul, uint32_t* shift) {
-  uint32_t sh = 0;
-  while ((1ull << sh) < d) ++sh;
-  *shift = sh;
-  *mul = (uint32_t)((((1ull << sh) - d) << 32) / d + 1);
-}
-
 LogitConsts logit_consts(const attn_problem* p) {
   LogitConsts lc;
   const double sigma = (double)p->scale_multiplier / std::sqrt((double)HEAD_DIM);
@@ -239,7 +231,6 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.slopes = p->alibi_slopes;
   a.slopes_stride = p->slopes_stride;
   a.hq = p->hq;
-  fast_div_consts((uint32_t)p->hq, &a.hq_mul, &a.hq_shift);
   a.batch = p->batch;
   a.total_q = p->total_q;
   a.total_k = p->total_k;

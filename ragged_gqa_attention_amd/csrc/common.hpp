@@ -127,6 +127,8 @@ enum SeqField {
   SQ_TTOFF,   // first 64-key transposed tile of the sequence (prefix of ceil(Lk / 64))
   SQ_DSOFF,   // first stored dS image of the sequence, -1 when its dS is not stored
   SQ_KTOFF,   // first 128-key tile of the sequence in batch order (prefix of SQ_KTILES)
+  SQ_LQMUL,   // fast_div constants of Lq (folded rows are head-major, see unfold_row)
+  SQ_LQSHIFT,
   SEQ_FIELDS
 };
 
@@ -149,6 +151,14 @@ struct Plan {
 // multiplication", 1994): shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1.
 __device__ __forceinline__ int fast_div(int n, uint32_t mul, uint32_t shift) {
   return (int)((__umulhi((uint32_t)n, mul) + (uint32_t)n) >> shift);
+}
+
+// Folded row R of a sequence -> (token i, head h).  The Lq x Hq rows are
+// folded head-major, R = h * Lq + i: the rows of a tile share few heads, hence
+// similar ALiBi slopes.  sq: the sequence's planner record.
+__device__ __forceinline__ void unfold_row(int R, const int* sq, int& i, int& h) {
+  h = fast_div(R, (uint32_t)sq[SQ_LQMUL], (uint32_t)sq[SQ_LQSHIFT]);
+  i = R - h * sq[SQ_LQ];
 }
 
 // Largest rank r with off[r] <= idx, or -1 when idx is past the last item.

@@ -1,7 +1,7 @@
 // dK / dV kernel: recompute P from the stored row record, then
 //   dP = dO V^T,  dS = P * (dP - Delta) * (1 - tanh^2(s / c)),
 //   dV = sum_rows P^T dO,  dK = sigma sum_rows dS^T Q,
-// summed over every folded (token, head) row of the sequence, i.e. over all
+// summed over every folded (head, token) row of the sequence, i.e. over all
 // query heads that share the K/V head.
 //
 // Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "Hard
@@ -55,6 +55,7 @@ struct KvShared {
 // What a workgroup works on: rows [row_begin, row_end) of sequence b against
 // keys [key0, key0 + PAIR_KEYS) of the wave's pair.
 struct KvUnit {
+  const int* sq;   // the sequence's planner record
   int q0, k0, Lk, row_begin, row_end, key0, nchunk;
   int ds;    // first dS image of the sequence, -1 when dS is not stored
   int nks;   // 64-key steps of the sequence (images per row tile)
@@ -103,8 +104,9 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
     const int R = r0 + lrow;
     const int Rc = min(R, u.row_end - 1);
-    const uint32_t tok = (uint32_t)fast_div(Rc, a.hq_mul, a.hq_shift);
-    const uint32_t h = (uint32_t)Rc - tok * (uint32_t)hq;
+    int tok_, h_;
+    unfold_row(Rc, u.sq, tok_, h_);
+    const uint32_t tok = (uint32_t)tok_, h = (uint32_t)h_;
     const uint32_t t_abs = (uint32_t)u.q0 + tok;
     const bool ok = R < u.row_end;
     const uint16_t* base = ltensor ? a.dout : a.q;
@@ -348,6 +350,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   const int unit = a.plan.kv_map[2 * blockIdx.x + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   KvUnit u;
+  u.sq = sq;
   u.q0 = sq[SQ_Q0];
   u.k0 = sq[SQ_K0];
   u.Lk = sq[SQ_LK];

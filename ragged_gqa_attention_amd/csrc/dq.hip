@@ -100,7 +100,8 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
 template <class T>
 __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage,
                                               const f32x16 (&dQ)[DBLK], float scale, int lrow,
-                                              int tile, int q0, int rows, int wave, int lane) {
+                                              int tile, const int* sq, int wave, int lane) {
+  const int q0 = sq[SQ_Q0], rows = sq[SQ_ROWS];
   constexpr int PITCH = HEAD_DIM + 8;
   const int g = lane >> 5;
   __syncthreads();   // every wave is done with the tile buffers
@@ -117,8 +118,8 @@ __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage
     const int r = wave * 32 + 16 * h + (lane >> 2);
     const int rg = tile * ROW_TILE + r;
     if (rg >= rows) continue;
-    const int tk = fast_div(rg, a.hq_mul, a.hq_shift);
-    const int hd = rg - tk * a.hq;
+    int tk, hd;
+    unfold_row(rg, sq, tk, hd);
     uint16_t* drow = a.dq + (int64_t)(q0 + tk) * a.dq_ts + (int64_t)hd * a.dq_hs;
 #pragma unroll
     for (int i = 0; i < CHUNKS / 4; ++i) {
@@ -214,7 +215,7 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
 
   // lane l32 holds row 32 w + tt_key_pos(l32) of the tile
   store_dq_tile<T>(a, sm.ds[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma,
-                   wave * 32 + tt_key_pos(l32), tile, q0, rows, wave, lane);
+                   wave * 32 + tt_key_pos(l32), tile, sq, wave, lane);
 }
 
 }  // namespace
@@ -251,9 +252,9 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int row = tile * ROW_TILE + wave * 32 + l32;
   const bool row_ok = row < rows;
   const int rr = row_ok ? row : rows - 1;
-  const int ti = fast_div(rr, a.hq_mul, a.hq_shift);
-  const int hh = rr - ti * a.hq;
-  const int64_t ri = (int64_t)(q0 + ti) * a.hq + hh;
+  int ti, hh;
+  unfold_row(rr, sq, ti, hh);
+  const int64_t ri = (int64_t)q0 * a.hq + rr;   // folded row record
 
   const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
   const uint16_t* dorow = a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)hh * a.do_hs + g * 8;
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   }
 
   store_dq_tile<T>(a, sm.r.k[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma, wave * 32 + l32,
-                   tile, q0, rows, wave, lane);
+                   tile, sq, wave, lane);
 }
 
 template <class T>

@@ -1,4 +1,4 @@
-// Forward kernel: softmax attention over folded (token, head) rows.
+// Forward kernel: softmax attention over folded (head, token) rows.
 //
 // Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "What
 // You Have": logits are (scale_multiplier / sqrt(D)) q.k, soft-capped to
@@ -8,7 +8,7 @@
 // only O and L = m + log l.
 //
 // Every query head shares the one K/V head, so the Lq x Hq rows of a sequence
-// are folded into one M dimension (row = token * Hq + head): a workgroup's 256
+// are folded into one M dimension (row = head * Lq + token): a workgroup's 256
 // rows reuse each staged K/V tile 256 times.  Each wave owns 32 rows and forms
 // S^T = K Q^T (keys x rows, Q in registers), so an accumulator lane owns one row
 // and O^T = V^T P^T keeps the row scale per lane.  Key steps of 64 are copied
@@ -70,8 +70,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   const int row = tile * ROW_TILE + wave * 32 + l32;
   const bool row_ok = row < rows;
   const int rr = row_ok ? row : rows - 1;
-  const int ti = fast_div(rr, a.hq_mul, a.hq_shift);
-  const int hh = rr - ti * a.hq;
+  int ti, hh;
+  unfold_row(rr, sq, ti, hh);
 
   // Q row as B operand: k-step ks covers features 16ks + 8g .. +7
   const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
@@ -303,8 +303,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
     erow[h] = rg;
     eok[h] = rg < rows;
     const int rc = eok[h] ? rg : rows - 1;
-    const int tk = fast_div(rc, a.hq_mul, a.hq_shift);
-    const int hd = rc - tk * a.hq;
+    int tk, hd;
+    unfold_row(rc, sq, tk, hd);
     eout[h] = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
     if (DELTA) {
       const uint16_t* drow = a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs;

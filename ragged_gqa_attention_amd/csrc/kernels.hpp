@@ -38,7 +38,8 @@ struct AttnArgs {
   uint16_t* dk;         int64_t dk_ts;
   uint16_t* dv;         int64_t dv_ts;
   float* lse;           // [total_q * hq], natural log
-  // [total_q * hq] records of 4 floats per folded row, read by the backward:
+  // [total_q * hq] records of 4 floats, one per folded row (sequence b's rows
+  // at q0(b) * hq + R, R = h * Lq + i), read by the backward:
   //   slope * log2(e), clamped ALiBi centre max(i + Lk - Lq, 0),
   //   minus the base-2 log of the row's softmax sum relative to the row offset
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
@@ -56,7 +57,6 @@ struct AttnArgs {
   uint16_t* ds;
   const float* slopes;  int64_t slopes_stride;
   int hq;
-  uint32_t hq_mul, hq_shift;   // n / hq == (umulhi(n, hq_mul) + n) >> hq_shift for n < 2^31
   int batch;
   int64_t total_q;
   int64_t total_k;

@@ -109,6 +109,11 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
     int* s = seq + b * SEQ_FIELDS;
     s[SQ_Q0] = q0; s[SQ_LQ] = lq; s[SQ_K0] = k0; s[SQ_LK] = lk;
     s[SQ_ROWS] = rows; s[SQ_KTILES] = kt;
+    // n / Lq = (umulhi(n, mul) + n) >> shift (see fast_div)
+    uint32_t sh = 0;
+    while (lq > 0 && (1u << sh) < (uint32_t)lq) ++sh;
+    s[SQ_LQSHIFT] = (int)sh;
+    s[SQ_LQMUL] = lq > 0 ? (int)(uint32_t)((((1ull << sh) - (uint64_t)lq) << 32) / (uint64_t)lq + 1) : 0;
     cost += (long long)kt * rows;
   }
   const long long total_cost = block_sum(cost, red);
@@ -355,11 +360,12 @@ __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   const int* s = seq + lo * SEQ_FIELDS;
   const int i = (int)(t - s[SQ_Q0]);
   const int Lq = s[SQ_LQ], Lk = s[SQ_LK];
+  const int64_t fr = (int64_t)s[SQ_Q0] * a.hq + (int64_t)h * Lq + i;   // folded row record
   const float slope2 = a.slopes[(int64_t)lo * a.slopes_stride + h] * LOG2E;
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - i);
   const float L = a.lse[r];
   const float negres = Lk > 0 ? moff - L * LOG2E : 0.0f;
-  *reinterpret_cast<f32x4*>(a.rowinfo + r * 4) =
+  *reinterpret_cast<f32x4*>(a.rowinfo + fr * 4) =
       f32x4{slope2, (float)max(i + Lk - Lq, 0), negres, acc};
 }
 
