@@ -44,6 +44,15 @@
  * Determinism.  No atomics are used; every reduction runs in a fixed order, so
  * repeated calls with identical inputs give bitwise-identical outputs.
  *
+ * Far keys.  With softcap > 0 every capped logit lies in [-softcap, softcap],
+ * so a key whose ALiBi term slope * |i + Lk - Lq - j| exceeds the row's largest
+ * possible logit by enough (about 111 + 2 softcap in natural-log units) gets
+ * P == 0 exactly in FP32, in the forward and in the backward.  The kernels
+ * skip the 64-key steps in which every key is that far from every row of a
+ * 256-row tile; the results are bitwise those of evaluating them, provided the
+ * skipped q / k / v / dout values are finite (non-finite values there are not
+ * read, so they do not propagate).  ATTN_FLAG_ALL_KEYS turns this off.
+ *
  * Errors.  Functions return an attn_status; a failed host-side check launches
  * nothing.  attn_last_error() gives a human-readable detail for the calling
  * thread.  Inconsistent cu_q / cu_k contents (not monotone, cu[0] != 0,
@@ -72,6 +81,11 @@ typedef enum {
 } attn_status;
 
 typedef enum { ATTN_F16 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Bits of attn_problem.flags. */
+typedef enum {
+  ATTN_FLAG_ALL_KEYS = 1   /* evaluate every key, also where P is exactly 0 */
+} attn_flag;
 
 typedef enum {
   ATTN_ENTRY_FWD = 0,
@@ -106,6 +120,7 @@ typedef struct {
   int32_t window_right;        /* must be -1 */
   float softcap;               /* c > 0 caps logits at c*tanh(x/c); 0 = no cap */
   float scale_multiplier;      /* logit scale = scale_multiplier / sqrt(head_dim) */
+  int32_t flags;               /* attn_flag bits; 0 for the default behaviour */
 } attn_problem;
 
 /* Bytes of workspace that `entry` (attn_entry) needs for problem `p`.
@@ -184,6 +199,19 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p,
 /* Synchronises `stream` and reports the device-side cu_q / cu_k check of the
  * last call that used `workspace`: ATTN_OK or ATTN_BAD_SEQLENS. */
 attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream);
+
+/* Diagnostics: the key steps the last call of `entry` on `workspace` (same
+ * problem sizes) evaluated.  The folded rows of sequence b (row h * Lq + i for
+ * head h, token i) form ceil(Lq * hq / 256) tiles of 256; for each tile, in
+ * batch order, host_out receives two int32: the first and one past the last
+ * 64-key step of the sequence that the tile's rows visit (see "Far keys"
+ * above; 0 and ceil(Lk / 64) when nothing is skipped).  n_tiles is the number
+ * of such tiles (sum over b); host_out holds 2 * n_tiles values.  Synchronises
+ * `stream`.  Errors: ATTN_INVALID_ARG for a NULL pointer or n_tiles outside
+ * 0 .. the bound the workspace layout allows; ATTN_HIP_ERROR if the copy
+ * fails. */
+attn_status attn_varlen_key_steps(const attn_problem* p, int entry, const void* workspace,
+                                  int32_t* host_out, int64_t n_tiles, attn_stream_t stream);
 
 /* Static text for a status code. */
 const char* attn_status_string(int status);

@@ -22,6 +22,8 @@ ATTN_BAD_SEQLENS = -6
 ATTN_F16 = 0
 ATTN_BF16 = 1
 
+ATTN_FLAG_ALL_KEYS = 1   # evaluate every key, also where P is exactly 0
+
 ENTRY_FWD = 0
 ENTRY_BWD = 1
 ENTRY_FULL_VJP = 2
@@ -37,6 +39,7 @@ EXPORTED = (
     "attn_varlen_full_vjp",
     "attn_varlen_full_vjp_timed",
     "attn_varlen_check_plan",
+    "attn_varlen_key_steps",
     "attn_status_string",
     "attn_last_error",
 )
@@ -64,7 +67,8 @@ class AttnProblem(ctypes.Structure):
                 ("window_left", ctypes.c_int32),
                 ("window_right", ctypes.c_int32),
                 ("softcap", ctypes.c_float),
-                ("scale_multiplier", ctypes.c_float)]
+                ("scale_multiplier", ctypes.c_float),
+                ("flags", ctypes.c_int32)]
 
 
 class AttnError(RuntimeError):
@@ -107,6 +111,8 @@ def load() -> ctypes.CDLL:
         lib.attn_varlen_full_vjp_timed.argtypes = lib.attn_varlen_full_vjp.argtypes + [
             P(ctypes.c_void_p)]
         lib.attn_varlen_check_plan.argtypes = [vp, vp]
+        lib.attn_varlen_key_steps.argtypes = [P(AttnProblem), ctypes.c_int, vp, i32p,
+                                              ctypes.c_int64, vp]
         lib.attn_status_string.argtypes = [ctypes.c_int]
         lib.attn_status_string.restype = ctypes.c_char_p
         lib.attn_last_error.argtypes = []
@@ -114,7 +120,7 @@ def load() -> ctypes.CDLL:
         for name in ("attn_varlen_workspace_size", "attn_varlen_workspace_size_ds",
                      "attn_varlen_fwd", "attn_varlen_bwd",
                      "attn_varlen_full_vjp", "attn_varlen_full_vjp_timed",
-                     "attn_varlen_check_plan"):
+                     "attn_varlen_check_plan", "attn_varlen_key_steps"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
         return lib

@@ -36,7 +36,9 @@ def _view(t: torch.Tensor, name: str, dtype, heads=None) -> _lib.AttnTensor:
 
 
 def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                 softcap, scale_multiplier) -> _lib.AttnProblem:
+                 softcap, scale_multiplier, all_keys=False) -> _lib.AttnProblem:
+    """``all_keys``: evaluate every key, also the far ones whose P is exactly
+    zero (the library skips those by default; results are bitwise the same)."""
     if q.dtype not in _DTYPES:
         raise NotImplementedError(f"dtype {q.dtype} is not supported (FP16 / BF16 only)")
     for name, cu in (("cu_q", cu_q), ("cu_k", cu_k)):
@@ -60,7 +62,8 @@ def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_rig
         alibi_slopes=alibi_slopes.data_ptr(),
         slopes_stride=alibi_slopes.stride(0) if batch > 0 else hq,
         causal=int(bool(causal)), window_left=int(window_left), window_right=int(window_right),
-        softcap=float(softcap), scale_multiplier=float(scale_multiplier))
+        softcap=float(softcap), scale_multiplier=float(scale_multiplier),
+        flags=_lib.ATTN_FLAG_ALL_KEYS if all_keys else 0)
 
 
 def workspace_size(problem: _lib.AttnProblem, entry: int, cu_q=None, cu_k=None) -> int:
@@ -121,10 +124,10 @@ def _check_plan(ws, device):
 
 def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multiplier=0.75,
                     causal=False, window_left=-1, window_right=-1, *, out=None, lse=None,
-                    workspace=None, check=False):
+                    workspace=None, check=False, all_keys=False):
     """Forward only: returns (out [Tq,Hq,160] like q, lse float32 [Tq,Hq])."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                        softcap, scale_multiplier)
+                        softcap, scale_multiplier, all_keys)
     tq, tk = _view(q, "q", q.dtype), _view(k, "k", q.dtype)
     tv = _view(v, "v", q.dtype, heads=k.shape[1])
     if out is None:
@@ -147,11 +150,12 @@ def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multip
 
 def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3.0,
                     scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1, *,
-                    dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=True):
+                    dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=True,
+                    all_keys=False):
     """Backward from a saved forward: returns (dq, dk, dv).  ``store_ds``: see
     _bwd_workspace_size (ignored when ``workspace`` is given: its size decides)."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                        softcap, scale_multiplier)
+                        softcap, scale_multiplier, all_keys)
     dt = q.dtype
     tq, tk, tv = _view(q, "q", dt), _view(k, "k", dt), _view(v, "v", dt, heads=k.shape[1])
     to = _view(out, "out", dt, heads=q.shape[1])
@@ -190,9 +194,9 @@ class FullVJP:
 
     def __init__(self, q, k, v, cu_q, cu_k, alibi_slopes, dout, causal=False, window_left=-1,
                  window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False,
-                 store_ds=True):
+                 store_ds=True, all_keys=False):
         self.prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left,
-                                 window_right, softcap, scale_multiplier)
+                                 window_right, softcap, scale_multiplier, all_keys)
         dt, dev = q.dtype, q.device
         self.inputs = (q, k, v, dout, cu_q, cu_k, alibi_slopes)   # keep alive
         self.out = torch.empty(q.shape, dtype=dt, device=dev)
@@ -230,17 +234,38 @@ class FullVJP:
     def check_plan(self):
         _check_plan(self.ws, self.device)
 
+    def key_steps(self):
+        """Key-step ranges the last call visited (see key_steps)."""
+        return key_steps(self.prob, _lib.ENTRY_FULL_VJP, self.ws, self.inputs[4])
+
 
 def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
                          scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1,
-                         *, want_lse=False, check=False, store_ds=True):
+                         *, want_lse=False, check=False, store_ds=True, all_keys=False):
     """Forward + full VJP: returns (out, dq, dk, dv[, lse])."""
     call = FullVJP(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
-                   softcap, scale_multiplier, want_lse=want_lse, store_ds=store_ds)
+                   softcap, scale_multiplier, want_lse=want_lse, store_ds=store_ds,
+                   all_keys=all_keys)
     res = call()
     if check:
         call.check_plan()
     return res + ((call.lse,) if want_lse else ())
+
+
+def key_steps(problem: _lib.AttnProblem, entry: int, ws: torch.Tensor, cu_q) -> "np.ndarray":
+    """int32 [n_tiles, 2]: per 256-row tile of folded rows (row h * Lq + i of a
+    sequence, tiles in batch order) the first and one past the last 64-key step
+    the last call of ``entry`` on workspace ``ws`` visited.  Synchronises."""
+    import numpy as np
+    cq = cu_q.detach().to("cpu", torch.int64)
+    lq = (cq[1:] - cq[:-1]).numpy()
+    n = int(((lq * problem.hq + 255) // 256).sum()) if lq.size else 0
+    out = np.zeros((n, 2), dtype=np.int32)
+    st = _lib.load().attn_varlen_key_steps(
+        ctypes.byref(problem), entry, ctypes.c_void_p(ws.data_ptr()),
+        out.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), n, _stream(ws.device))
+    _lib.raise_for(st, "attn_varlen_key_steps")
+    return out
 
 
 def attention_varlen_feature_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal,

@@ -60,7 +60,7 @@ int device_cus() {
 }
 
 struct Layout {
-  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero, fwd_map, kv_map;
+  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero, fwd_map, kv_map, ksteps;
   size_t lse, rowinfo, part_dk, part_dv, kt, vt;
   size_t total;
   int64_t max_units;
@@ -93,6 +93,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_rank = take(sizeof(int) * B);
   L.fwd_map = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.kv_map = take(sizeof(int) * 2 * (size_t)L.max_units);
+  L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
   const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
   if (entry != ATTN_ENTRY_BWD) L.vt = take(tt_bytes);   // V^T for the forward
@@ -134,6 +135,8 @@ attn_status check_problem(const attn_problem* p) {
     return fail(ATTN_INVALID_ARG, "softcap must be finite and >= 0");
   if (!std::isfinite(p->scale_multiplier))
     return fail(ATTN_INVALID_ARG, "scale_multiplier must be finite");
+  if ((p->flags & ~ATTN_FLAG_ALL_KEYS) != 0)
+    return fail(ATTN_INVALID_ARG, "unknown flags 0x%x", (unsigned)p->flags);
   return ATTN_OK;
 }
 
@@ -235,8 +238,13 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.total_q = p->total_q;
   a.total_k = p->total_k;
   a.lc = logit_consts(p);
+  // far keys are skipped only under a cap (see row_key_steps)
+  a.skip_log2 = 0.0f;
+  if (p->softcap > 0.0f && (p->flags & ATTN_FLAG_ALL_KEYS) == 0)
+    a.skip_log2 = (float)(SKIP_UNDERFLOW + 2.0 * p->softcap * 1.4426950408889634);
   a.plan = plan_view(ws, L);
   char* base = static_cast<char*>(ws);
+  a.ksteps = reinterpret_cast<int*>(base + L.ksteps);
   a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
   if (L.kt) a.kt = reinterpret_cast<uint16_t*>(base + L.kt);
   if (L.vt) a.vt = reinterpret_cast<uint16_t*>(base + L.vt);
@@ -396,6 +404,7 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   RGA_TRY(launch_prep_phase(pa, a, L, s));
   if (p->batch == 0) return ATTN_OK;
   RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
+  RGA_TRY(hip_status(launch_ksteps(a, (int)L.row_tiles, s), "key-step launch"));
   return launch_backward(p, a, L, s);
 }
 
@@ -466,6 +475,27 @@ attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream) {
   RGA_TRY(hip_status(hipStreamSynchronize(s), "stream synchronise"));
   if (flag != 0) return fail(ATTN_BAD_SEQLENS, "cu_q / cu_k are not a valid packing");
   return ATTN_OK;
+}
+
+attn_status attn_varlen_key_steps(const attn_problem* p, int entry, const void* workspace,
+                                  int32_t* host_out, int64_t n_tiles, attn_stream_t stream) {
+  g_last_error.clear();
+  RGA_TRY(check_problem(p));
+  if (entry < ATTN_ENTRY_FWD || entry > ATTN_ENTRY_FULL_VJP)
+    return fail(ATTN_INVALID_ARG, "unknown entry %d", entry);
+  if (!workspace) return fail(ATTN_INVALID_ARG, "workspace is NULL");
+  const Layout L = make_layout(p, entry, device_cus());
+  if (n_tiles < 0 || n_tiles > L.row_tiles)
+    return fail(ATTN_INVALID_ARG, "n_tiles %lld outside 0..%lld", (long long)n_tiles,
+                (long long)L.row_tiles);
+  if (n_tiles == 0) return ATTN_OK;
+  if (!host_out) return fail(ATTN_INVALID_ARG, "host_out is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* src = static_cast<const char*>(workspace) + L.ksteps;
+  RGA_TRY(hip_status(hipMemcpyAsync(host_out, src, sizeof(int32_t) * 2 * (size_t)n_tiles,
+                                    hipMemcpyDeviceToHost, s),
+                     "reading the key steps"));
+  return hip_status(hipStreamSynchronize(s), "stream synchronise");
 }
 
 const char* attn_status_string(int status) {

@@ -129,6 +129,7 @@ enum SeqField {
   SQ_KTOFF,   // first 128-key tile of the sequence in batch order (prefix of SQ_KTILES)
   SQ_LQMUL,   // fast_div constants of Lq (folded rows are head-major, see unfold_row)
   SQ_LQSHIFT,
+  SQ_RTOFF,   // first 256-row tile of the sequence in batch order (prefix of row tiles)
   SEQ_FIELDS
 };
 

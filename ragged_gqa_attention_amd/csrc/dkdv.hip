@@ -31,6 +31,11 @@
 // Pipeline.  Q and dO tiles are copied global -> LDS with direct loads (no
 // staging registers) into blocked tiles, three buffers: step n is read by the
 // S/dP products, step n - 1 by the dV/dK products and step n + 1 is in flight.
+//
+// Far rows.  A 256-row tile whose recorded key steps (a.ksteps, see
+// row_key_steps) miss the workgroup's 128 keys has P == 0 exactly on all of
+// them, so its row steps are passed over; the steps a workgroup does visit
+// therefore cover every dS image the dQ kernel later reads.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -59,7 +64,39 @@ struct KvUnit {
   int q0, k0, Lk, row_begin, row_end, key0, nchunk;
   int ds;    // first dS image of the sequence, -1 when dS is not stored
   int nks;   // 64-key steps of the sequence (images per row tile)
+  const int* ksteps;   // key-step ranges of the sequence's row tiles
+  int step_lo;         // the workgroup's key steps [step_lo, step_lo + 2)
 };
+
+// Row tiles of rows [row_begin, row_end) that the workgroup visits, as a
+// 64-tile bit mask (kept in scalar registers, reloaded past its end).
+struct TileMask {
+  uint64_t bits;
+  int base;    // tile of bit 0
+  int last;    // last tile of the row range
+};
+
+__device__ __forceinline__ void tile_mask_load(TileMask& m, const KvUnit& u, int base, int lane) {
+  const int t = base + lane;
+  bool on = false;
+  if (t <= m.last) {
+    const int* r = u.ksteps + 2 * t;
+    on = r[0] < u.step_lo + 2 && r[1] > u.step_lo;
+  }
+  m.bits = __ballot(on);
+  m.base = base;
+}
+
+// First visited tile >= t, or a tile past m.last.
+__device__ __forceinline__ int tile_mask_next(TileMask& m, const KvUnit& u, int t, int lane) {
+  while (t <= m.last) {
+    if (t >= m.base + 64) tile_mask_load(m, u, t, lane);
+    const uint64_t rest = m.bits >> (t - m.base);
+    if (rest != 0) return t + (int)__builtin_ctzll(rest);
+    t = m.base + 64;
+  }
+  return t;
+}
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
 template <class T, bool CAP, int ROLE, bool LATE>
@@ -263,42 +300,64 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   };
 
-  const int nsteps = (u.row_end - u.row_begin + KV_ROW_STEP - 1) / KV_ROW_STEP;
-  issue_loads(u.row_begin, 0);
-  wait_vm();
-  __syncthreads();
-  if (nsteps > 1) issue_loads(u.row_begin + KV_ROW_STEP, 1);
-  f32x16 S[KB], dP[KB];
-  scores(0, S, dP);
-  pointwise_publish(0, 0, u.row_begin, S, dP, mine);
-  wait_vm();
-  __syncthreads();
-  int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
-  for (int n = 1; n < nsteps; ++n) {
-    if (n + 1 < nsteps) issue_loads(u.row_begin + (n + 1) * KV_ROW_STEP, next);
-    scores(cur, S, dP);
-    // products of the previous step (its partner half arrived before the
-    // barrier) and the pointwise work of this one are independent; the two
-    // waves sharing a SIMD take them in opposite orders, so one runs VALU
-    // while the other keeps the matrix core busy
-    if (LATE) {
-      accumulate(prev, (n - 1) & 1);
-      pointwise_publish(cur, n & 1, u.row_begin + n * KV_ROW_STEP, S, dP, mine);
-    } else {
-      u32x4 own[KB][2];
-      pointwise_publish(cur, n & 1, u.row_begin + n * KV_ROW_STEP, S, dP, own);
-      accumulate(prev, (n - 1) & 1);
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) { mine[kb][0] = own[kb][0]; mine[kb][1] = own[kb][1]; }
-    }
+  // visited row steps: every step of a visited tile inside [row_begin, row_end)
+  TileMask tm;
+  tm.last = (u.row_end - 1) / ROW_TILE;
+  tile_mask_load(tm, u, u.row_begin / ROW_TILE, lane);
+  // first step of a visited tile at or after tile t (row_end when none)
+  auto tile_start = [&](int t) {
+    t = tile_mask_next(tm, u, t, lane);
+    return t > tm.last ? u.row_end : max(u.row_begin, t * ROW_TILE);
+  };
+  // the visited step after the one at r0
+  auto next_step = [&](int r0) {
+    const int r = r0 + KV_ROW_STEP;
+    if (r >= u.row_end) return u.row_end;
+    return (r & (ROW_TILE - 1)) != 0 ? r : tile_start(r / ROW_TILE);
+  };
+  int rn = tile_start(u.row_begin / ROW_TILE);   // rows of the step after the current one
+  if (rn < u.row_end) {
+    const int r0 = rn;
+    rn = next_step(r0);
+    issue_loads(r0, 0);
     wait_vm();
     __syncthreads();
-    const int t = prev;
-    prev = cur;
-    cur = next;
-    next = t;
+    if (rn < u.row_end) issue_loads(rn, 1);
+    f32x16 S[KB], dP[KB];
+    scores(0, S, dP);
+    pointwise_publish(0, 0, r0, S, dP, mine);
+    wait_vm();
+    __syncthreads();
+    int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
+    int n = 1;
+    for (; rn < u.row_end; ++n) {
+      const int rc = rn;
+      rn = next_step(rc);
+      if (rn < u.row_end) issue_loads(rn, next);
+      scores(cur, S, dP);
+      // products of the previous step (its partner half arrived before the
+      // barrier) and the pointwise work of this one are independent; the two
+      // waves sharing a SIMD take them in opposite orders, so one runs VALU
+      // while the other keeps the matrix core busy
+      if (LATE) {
+        accumulate(prev, (n - 1) & 1);
+        pointwise_publish(cur, n & 1, rc, S, dP, mine);
+      } else {
+        u32x4 own[KB][2];
+        pointwise_publish(cur, n & 1, rc, S, dP, own);
+        accumulate(prev, (n - 1) & 1);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) { mine[kb][0] = own[kb][0]; mine[kb][1] = own[kb][1]; }
+      }
+      wait_vm();
+      __syncthreads();
+      const int t = prev;
+      prev = cur;
+      cur = next;
+      next = t;
+    }
+    accumulate(prev, (n - 1) & 1);
   }
-  accumulate(prev, (nsteps - 1) & 1);
 
   // lane owns key key0 + 32 kb + l32, features 32 db + 8 (r/4) + 4 g + r%4
   const float scale = ROLE ? (CAP ? 4.0f * a.lc.sigma : a.lc.sigma) : 1.0f;
@@ -357,6 +416,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   u.nchunk = sq[SQ_NCHUNK];
   u.ds = a.ds ? sq[SQ_DSOFF] : -1;
   u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
+  u.ksteps = a.ksteps + 2 * sq[SQ_RTOFF];
   const int rows = sq[SQ_ROWS], chunk = sq[SQ_CHUNK];
   const int ktile = unit / u.nchunk;
   const int ci = unit - ktile * u.nchunk;
@@ -365,6 +425,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   u.key0 = ktile * KEY_TILE + (wave >> 1) * PAIR_KEYS;
+  u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
   // every unit has at least one row (the planner never emits empty chunks)
   // waves w and w + 4 share a SIMD
   if (wave < 4) {

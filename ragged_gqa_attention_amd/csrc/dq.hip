@@ -18,7 +18,9 @@
 // A workgroup owns 256 folded rows (like the forward) and walks the keys in
 // steps of 64, copied to LDS with direct loads (double-buffered): K and V as
 // row tiles and K^T as its pre-transposed key tile, so every product reads
-// its LDS operand with one 16-byte read per MFMA.
+// its LDS operand with one 16-byte read per MFMA.  It visits only the key
+// steps the forward recorded for the tile (a.ksteps): outside them every P,
+// and so every dS, is exactly zero.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -147,7 +149,7 @@ static_assert(ROW_TILE * (HEAD_DIM + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ stagin
 // the dK / dV partial sums, so they land while it runs.
 template <class T, bool CAP>
 __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm, const int* sq,
-                                          int tile) {
+                                          int tile, int klo, int khi) {
   const int q0 = sq[SQ_Q0], Lk = sq[SQ_LK], rows = sq[SQ_ROWS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -186,20 +188,20 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   f32x16 dQ[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
-  if (nks > 0) issue(0, 0);
-  if (nks > 1) issue(1, 1);
-  for (int kt = 0; kt < nks; ++kt) {
+  if (klo < khi) issue(klo, klo % DQS_NBUF);
+  if (klo + 1 < khi) issue(klo + 1, (klo + 1) % DQS_NBUF);
+  for (int kt = klo; kt < khi; ++kt) {
     const int buf = kt % DQS_NBUF;
     // step kt has landed (step kt + 1 may still be in flight) for every wave,
     // and every wave is done with step kt - 1, whose buffer step kt + 2 takes
-    if (kt + 1 < nks) {
+    if (kt + 1 < khi) {
       if (wave < 4) wait_vm_le<7>();
       else wait_vm_le<6>();
     } else {
       wait_vm();
     }
     __syncthreads();
-    if (kt + 2 < nks) issue(kt + 2, (kt + 2) % DQS_NBUF);
+    if (kt + 2 < khi) issue(kt + 2, (kt + 2) % DQS_NBUF);
     const uint16_t* D = sm.ds[buf];
     const uint16_t* KT = sm.kt[buf];
 #pragma unroll
@@ -239,8 +241,10 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   }
   const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
+  const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
+  const int klo = ks[0], khi = ks[1];
   if (a.ds && sq[SQ_DSOFF] >= 0) {
-    dq_stored<T, CAP>(a, sm.d, sq, tile);
+    dq_stored<T, CAP>(a, sm.d, sq, tile, klo, khi);
     return;
   }
   const int q0 = sq[SQ_Q0], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
@@ -357,17 +361,17 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   auto advance = [&](int kt) {
     wait_vm();
     __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) & 1);
+    if (kt + 1 < khi) issue(kt + 1, (kt + 1) & 1);
   };
   // the key mask costs a compare and a select per logit, so only a partial
   // last key step runs the masked instance (after the loop)
   const int nfull = Lk / TILE_ROWS;
-  if (ntiles > 0) issue(0, 0);
-  for (int kt = 0; kt < nfull; ++kt) {
+  if (klo < khi) issue(klo, klo & 1);
+  for (int kt = klo; kt < min(khi, nfull); ++kt) {
     advance(kt);
     step(kt & 1, kt * TILE_ROWS, Flag<false>{});
   }
-  if (nfull < ntiles) {
+  if (nfull < ntiles && khi == ntiles) {
     advance(nfull);
     step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
   }

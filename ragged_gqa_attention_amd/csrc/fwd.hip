@@ -30,6 +30,11 @@
 // log2 l relative to m_i, so the backward never subtracts two large numbers.
 // The backward's per-row record (slope, centre, residual, Delta) is written
 // here in the full-VJP call, Delta = rowsum(dO * O) taken from the FP32 O.
+//
+// Far keys.  With a cap, a key farther from a row's centre than the skip
+// bound allows has P == 0 exactly (see row_key_steps), so a workgroup visits
+// only the key steps [lo, hi) that hold a key some row of its tile keeps, and
+// records that range for the backward.
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -56,6 +61,7 @@ static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared),
 template <class T, bool CAP, bool DELTA>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) FwdShared sm;
+  __shared__ int span[2][ROW_WAVES];
 
   const int b = a.plan.fwd_map[2 * blockIdx.x];
   if (b < 0) return;
@@ -93,6 +99,31 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   for (int db = 0; db < DBLK; ++db) O[db] = f32x16{};
 
   const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  // key steps [klo, khi) some row of the tile keeps (min / max over the rows)
+  int klo, khi;
+  row_key_steps(row_ok, slope2, max(ti + Lk - Lq, 0), Lk, CAP ? a.skip_log2 : 0.0f, klo, khi);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    klo = min(klo, __shfl_xor(klo, o, 64));
+    khi = max(khi, __shfl_xor(khi, o, 64));
+  }
+  if (lane == 0) {
+    span[0][wave] = klo;
+    span[1][wave] = khi;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < ROW_WAVES; ++w) {
+    klo = min(klo, span[0][w]);
+    khi = max(khi, span[1][w]);
+  }
+  klo = __builtin_amdgcn_readfirstlane(klo);
+  khi = __builtin_amdgcn_readfirstlane(khi);
+  if (tid == 0) {
+    int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
+    ks[0] = klo;
+    ks[1] = khi;
+  }
   const uint16_t* vt_seq = a.vt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
   // copies of key step kt: waves 0-3 the K rows (one 16-row group each),
   // waves 4-7 V^T (five 8-feature-row loads each)
@@ -189,15 +220,17 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   auto advance = [&](int kt) {
     wait_vm();
     __syncthreads();
-    if (kt + 1 < ntiles) issue(kt + 1, (kt + 1) % FWD_NBUF);
+    if (kt + 1 < khi) issue(kt + 1, (kt + 1) % FWD_NBUF);
   };
   // the key mask costs a compare and a select per logit, so only a partial
-  // last key step runs the masked instance (after the loop)
+  // last key step runs the masked instance (after the loop); steps
+  // [klo, kfull) are full ones
   const int nfull = Lk / TILE_ROWS;
-  const bool partial = nfull < ntiles;
+  const bool partial = nfull < ntiles && khi == ntiles;
+  const int kfull = min(khi, nfull);
   constexpr Flag<false> unmasked{};
   constexpr Flag<true> masked{};
-  if (ntiles > 0) issue(0, 0);
+  if (klo < khi) issue(klo, klo % FWD_NBUF);
 
   if (CAP) {
     // The offset is fixed, so the two 32-key blocks of a step are independent.
@@ -212,7 +245,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       constexpr bool LAG = decltype(lag)::value;
       auto step = [&](int kt, auto mk) {
         const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
-        if (LAG && kt > 0) {   // the previous step is a full one
+        if (LAG && kt > klo) {   // the previous step is a full one
           logits(1, kbase - TILE_ROWS, unmasked);
           probs(1);
           pv(1, sm.vt[(kt - 1) % FWD_NBUF]);
@@ -228,7 +261,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
           pv(1, sm.vt[buf]);
         }
       };
-      for (int kt = 0; kt < nfull; ++kt) {
+      for (int kt = klo; kt < kfull; ++kt) {
         advance(kt);
         step(kt, unmasked);
       }
@@ -236,8 +269,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
         advance(nfull);
         step(nfull, masked);
       }
-      if (LAG && ntiles > 0) {   // block 1 of the last step
-        const int kt = ntiles - 1;
+      if (LAG && klo < khi) {   // block 1 of the last step
+        const int kt = khi - 1;
         if (partial) logits(1, kt * TILE_ROWS, masked);
         else logits(1, kt * TILE_ROWS, unmasked);
         probs(1);
@@ -276,7 +309,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
       pv(0, sm.vt[buf]);
       pv(1, sm.vt[buf]);
     };
-    for (int kt = 0; kt < nfull; ++kt) {
+    for (int kt = klo; kt < kfull; ++kt) {
       advance(kt);
       step(kt, unmasked);
     }

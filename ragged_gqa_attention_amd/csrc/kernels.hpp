@@ -55,6 +55,15 @@ struct AttnArgs {
   // gave a slot (SQ_DSOFF >= 0); sequence images are row-tile major:
   // image SQ_DSOFF + row_tile * ceil(Lk / 64) + key_step.
   uint16_t* ds;
+  // Key steps [lo, hi) (64 keys each) of every 256-row tile, batch order
+  // (tile SQ_RTOFF + t of sequence b): the steps that hold a key whose P can
+  // be nonzero for some row of the tile (see row_key_steps).  Written by the
+  // forward, or by ksteps_kernel in the standalone backward, and read by the
+  // dK/dV and dQ kernels.
+  int* ksteps;
+  // Skip bound in log2 units (0 turns skipping off): the forward drops keys
+  // whose ALiBi term slope * log2(e) * |c_i - j| exceeds skip_log2.
+  float skip_log2;
   const float* slopes;  int64_t slopes_stride;
   int hq;
   int batch;
@@ -83,12 +92,52 @@ struct PlanArgs {
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
+// Exact skipping of far keys (capped logits only).  With a cap c every scaled,
+// capped logit of row i lies in [-c, c], so relative to the row offset the
+// forward uses (the largest value any logit of the row can take, see fwd.hip)
+// a key's exponent in log2 units is at most -slope2 |c_i - j| (slope2 =
+// slope * log2 e, c_i the clamped ALiBi centre).  The backward adds the
+// row's residual -log2 l, and l >= P of the centre key >= 2^(-2 c log2 e).
+// Once the exponent is below -SKIP_UNDERFLOW, exp2 returns exactly 0 (FP32's
+// smallest subnormal is 2^-149), so such a key adds exactly nothing to O, l,
+// dQ, dK or dV: a key whose slope2 |c_i - j| exceeds
+//   forward:  SKIP_UNDERFLOW + 2 c log2 e,
+//   backward: SKIP_UNDERFLOW + max(0, residual of the row)
+// is never evaluated, and the results are bitwise those of evaluating it.
+constexpr float SKIP_UNDERFLOW = 160.0f;
+
+// Key steps [lo, hi) (64 keys) holding every key of one row that the bound
+// `thr` (log2 units, 0 = none) keeps: the keys j with |c - j| <= floor(thr /
+// slope2).  A row that does not exist gives the empty range (INT_MAX, 0), the
+// neutral element of the min / max over a tile; rows whose slope is not a
+// positive finite number, or whose kept span reaches the sequence's ends,
+// keep every step.
+__device__ __forceinline__ void row_key_steps(bool exists, float slope2, int centre, int Lk,
+                                              float thr, int& lo, int& hi) {
+  lo = 0x7fffffff;
+  hi = 0;
+  if (!exists) return;
+  lo = 0;
+  hi = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  if (thr > 0.0f && slope2 > 0.0f) {   // false for NaN
+    const float span = thr / slope2;   // +inf for a tiny slope
+    if (span < (float)Lk) {
+      // a key outside [centre - ds, centre + ds] has |c - j| >= ds + 1 > span
+      const int ds = (int)span;
+      lo = max(0, centre - ds) / TILE_ROWS;
+      hi = min(Lk - 1, centre + ds) / TILE_ROWS + 1;
+    }
+  }
+}
+
 // Planner (one workgroup) and, alongside it, the transposed key tiles a.kt and /
 // or a.vt (null pointers are skipped), up to key_tiles tiles each.
 hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s);
 hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
                       hipStream_t s);
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
+// Key-step ranges of the standalone backward, from the row records.
+hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 

@@ -188,6 +188,10 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   block_exclusive_scan(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
   }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
+  // 256-row tiles in batch order (their key-step ranges are kept in this order)
+  block_exclusive_scan(B, [&](int b) {
+    return (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
+  }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_RTOFF] = v; }, part);
   // 128-key tiles in batch order (the dK / dV partial sums walk them)
   block_exclusive_scan(B, [&](int b) { return seq[b * SEQ_FIELDS + SQ_KTILES]; },
                        [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_KTOFF] = v; }, part);
@@ -367,6 +371,62 @@ __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   const float negres = Lk > 0 ? moff - L * LOG2E : 0.0f;
   *reinterpret_cast<f32x4*>(a.rowinfo + fr * 4) =
       f32x4{slope2, (float)max(i + Lk - Lq, 0), negres, acc};
+}
+
+// Key-step ranges of the standalone backward (the full-VJP call takes the
+// forward's): one workgroup per 256-row tile, a thread per row, from the row
+// records.  The row's bound is SKIP_UNDERFLOW plus its own residual (the
+// residual comes from the caller's L, so it is not bounded by the cap); a
+// row whose residual is not finite keeps every key.
+__global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
+  static_assert(WG_THREADS == ROW_TILE, "a thread per row of the tile");
+  __shared__ int span[2][WG_THREADS / 64];
+  const int b = a.plan.fwd_map[2 * blockIdx.x];
+  if (b < 0) return;
+  const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
+  const int* sq = a.plan.seq + b * SEQ_FIELDS;
+  const int R = tile * ROW_TILE + (int)threadIdx.x;
+  const bool ok = R < sq[SQ_ROWS];
+  const int Lk = sq[SQ_LK];
+  float slope2 = 0.0f, thr = 0.0f;
+  int centre = 0;
+  if (ok && Lk > 0) {
+    const f32x4 info =
+        *reinterpret_cast<const f32x4*>(a.rowinfo + ((int64_t)sq[SQ_Q0] * a.hq + R) * 4);
+    slope2 = info[0];
+    centre = (int)info[1];
+    const float radd = info[2];   // added to every exponent of the row
+    if (a.skip_log2 > 0.0f && __builtin_isfinite(radd))
+      thr = SKIP_UNDERFLOW + __builtin_fmaxf(radd, 0.0f);
+  }
+  int lo, hi;
+  row_key_steps(ok, slope2, centre, Lk, thr, lo, hi);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  if (lane == 0) {
+    span[0][wave] = lo;
+    span[1][wave] = hi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 0; w < WG_THREADS / 64; ++w) {
+      lo = min(lo, span[0][w]);
+      hi = max(hi, span[1][w]);
+    }
+    int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
+    ks[0] = lo;
+    ks[1] = hi;
+  }
+}
+
+hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s) {
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ksteps_kernel, grid, WG_THREADS, 0, s, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s) {
