@@ -49,7 +49,9 @@
  * possible logit by enough (about 111 + 2 softcap in natural-log units) gets
  * P == 0 exactly in FP32, in the forward and in the backward.  The kernels
  * skip the 64-key steps in which every key is that far from every row of a
- * 256-row tile; the results are bitwise those of evaluating them, provided the
+ * 256-row tile.  out, lse and dq are bitwise those of evaluating them, and dk
+ * and dv agree to within rounding of the FP32 partial sums (the split of a key
+ * tile's rows over workgroups follows the rows that visit it), provided the
  * skipped q / k / v / dout values are finite (non-finite values there are not
  * read, so they do not propagate).  ATTN_FLAG_ALL_KEYS turns this off.
  *

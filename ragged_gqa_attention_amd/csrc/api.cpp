@@ -33,11 +33,6 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 }
 
 constexpr size_t ALIGN = 256;
-constexpr int MIN_CHUNK_ROWS = 512;     // below this a row chunk is not worth its partials
-// dK/dV work units aimed at per compute unit, as a fraction: the dK/dV workgroup fills a
-// compute unit, so units run in about 1.5 rounds; more rounds balance better but write
-// more FP32 partials (modelled on the benchmark workloads, 1.5 was best).
-constexpr int UNITS_PER_CU_NUM = 3, UNITS_PER_CU_DEN = 2;
 constexpr int MAX_DEVICES = 64;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
@@ -60,11 +55,12 @@ int device_cus() {
 }
 
 struct Layout {
-  size_t seq, fwd_seq, fwd_off, kv_seq, kv_off, kv_rank, flag, zero, fwd_map, kv_map, ksteps;
+  size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps;
   size_t lse, rowinfo, part_dk, part_dv, kt, vt;
   size_t total;
-  int64_t max_units;
+  int64_t kv_wgs;       // dK/dV workgroups (one per compute unit)
   int64_t row_tiles;
+  int64_t kv_tiles;     // upper bound of the 128-key tiles
   int64_t key_tiles;    // upper bound of the transposed 64-key tiles
 };
 
@@ -75,7 +71,8 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   const int64_t B = p->batch;
   const int64_t rows = p->total_q * p->hq;
   L.row_tiles = ceil_div(rows, ROW_TILE) + B;
-  L.max_units = (int64_t)cus * UNITS_PER_CU_NUM / UNITS_PER_CU_DEN + ceil_div(p->total_k, KEY_TILE) + B;
+  L.kv_tiles = ceil_div(p->total_k, KEY_TILE) + B;
+  L.kv_wgs = cus;
   L.key_tiles = ceil_div(p->total_k, TILE_ROWS) + B;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -86,13 +83,10 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.flag = take(sizeof(int) * 4);   // first, so attn_varlen_check_plan can find it
   L.zero = take(512);
   L.seq = take(sizeof(int) * B * SEQ_FIELDS);
-  L.fwd_seq = take(sizeof(int) * B);
-  L.fwd_off = take(sizeof(int) * (B + 1));
-  L.kv_seq = take(sizeof(int) * B);
-  L.kv_off = take(sizeof(int) * (B + 1));
-  L.kv_rank = take(sizeof(int) * B);
   L.fwd_map = take(sizeof(int) * 2 * (size_t)L.row_tiles);
-  L.kv_map = take(sizeof(int) * 2 * (size_t)L.max_units);
+  L.ktab = take(sizeof(int) * KV_FIELDS * (size_t)L.kv_tiles);
+  L.wg_first = take(sizeof(int) * (size_t)L.kv_wgs);
+  L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
   const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
@@ -101,7 +95,8 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
     L.rowinfo = take(sizeof(float) * 4 * rows);
-    const size_t part = sizeof(float) * (size_t)L.max_units * KEY_TILE * HEAD_DIM;
+    // FP32 partial dK / dV: two key tiles per workgroup (its first and last)
+    const size_t part = sizeof(float) * 2 * (size_t)L.kv_wgs * KEY_TILE * HEAD_DIM;
     L.part_dk = take(part);
     L.part_dv = take(part);
   }
@@ -180,14 +175,11 @@ Plan plan_view(void* ws, const Layout& L) {
   char* base = static_cast<char*>(ws);
   Plan pl;
   pl.seq = reinterpret_cast<int*>(base + L.seq);
-  pl.fwd_seq = reinterpret_cast<int*>(base + L.fwd_seq);
-  pl.fwd_off = reinterpret_cast<int*>(base + L.fwd_off);
-  pl.kv_seq = reinterpret_cast<int*>(base + L.kv_seq);
-  pl.kv_off = reinterpret_cast<int*>(base + L.kv_off);
-  pl.kv_rank = reinterpret_cast<int*>(base + L.kv_rank);
+  pl.ktab = reinterpret_cast<int*>(base + L.ktab);
+  pl.wg_first = reinterpret_cast<int*>(base + L.wg_first);
+  pl.kv_head = reinterpret_cast<int*>(base + L.kv_head);
   pl.flag = reinterpret_cast<int*>(base + L.flag);
   pl.fwd_map = reinterpret_cast<int*>(base + L.fwd_map);
-  pl.kv_map = reinterpret_cast<int*>(base + L.kv_map);
   return pl;
 }
 
@@ -255,15 +247,18 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   }
   pa.cu_q = p->cu_q;
   pa.cu_k = p->cu_k;
+  pa.slopes = p->alibi_slopes;
+  pa.slopes_stride = p->slopes_stride;
+  pa.skip_log2 = a.skip_log2;
+  pa.ksteps = a.ksteps;
   pa.batch = p->batch;
   pa.hq = p->hq;
   pa.total_q = p->total_q;
   pa.total_k = p->total_k;
-  pa.target_units = cus * UNITS_PER_CU_NUM / UNITS_PER_CU_DEN;
-  pa.min_chunk = MIN_CHUNK_ROWS;
   pa.fwd_slots = (int)L.row_tiles;
   a.fwd_slots = (int)L.row_tiles;
-  pa.kv_slots = (int)L.max_units;
+  pa.kv_wgs = (int)L.kv_wgs;
+  a.kv_wgs = (int)L.kv_wgs;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;
   // workspace past the fixed layout holds stored dS images (backward entries)
@@ -298,7 +293,7 @@ attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layo
   const bool cap = p->softcap > 0.0f;
   if (p->batch > 0) {
     RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
-    RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.max_units, s), "dK/dV launch"));
+    RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.kv_wgs, s), "dK/dV launch"));
     RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
     // row tiles, then one partial-sum workgroup per compute unit
     RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles + device_cus(), s),
@@ -367,7 +362,7 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   a.lse = lse;
   RGA_TRY(launch_prep_phase(pa, a, L, s));
   if (p->batch == 0) return ATTN_OK;
-  return hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, false, (int)L.row_tiles, s),
+  return hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, false, false, s),
                     "forward launch");
 }
 
@@ -405,6 +400,7 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   if (p->batch == 0) return ATTN_OK;
   RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
   RGA_TRY(hip_status(launch_ksteps(a, (int)L.row_tiles, s), "key-step launch"));
+  RGA_TRY(hip_status(launch_units(pa, s), "unit-plan launch"));
   return launch_backward(p, a, L, s);
 }
 
@@ -445,7 +441,7 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
   RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
   if (p->batch > 0)
-    RGA_TRY(hip_status(launch_fwd(a, p->dtype, p->softcap > 0.0f, true, (int)L.row_tiles, s),
+    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, true, s),
                        "forward launch"));
   RGA_TRY(launch_backward(p, a, L, s, ev));
   if (p->batch == 0) {

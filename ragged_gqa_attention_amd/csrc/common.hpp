@@ -123,7 +123,8 @@ struct LogitConsts {
 
 // Per-sequence facts written by the planner (int32 each, SEQ_FIELDS per sequence).
 enum SeqField {
-  SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS, SQ_NCHUNK, SQ_CHUNK, SQ_KTILES,
+  SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS,
+  SQ_KTILES,  // 128-key tiles of the sequence (dK/dV)
   SQ_TTOFF,   // first 64-key transposed tile of the sequence (prefix of ceil(Lk / 64))
   SQ_DSOFF,   // first stored dS image of the sequence, -1 when its dS is not stored
   SQ_KTOFF,   // first 128-key tile of the sequence in batch order (prefix of SQ_KTILES)
@@ -133,18 +134,33 @@ enum SeqField {
   SEQ_FIELDS
 };
 
+// Fields of a 128-key tile's record for the dK/dV work split (int32 each,
+// KV_FIELDS per key tile, batch order): the key tile, its share of the
+// flattened visit list, and copies of its sequence's record so a workgroup
+// reads everything with one load.
+enum KvField {
+  KV_B = 0,    // sequence
+  KV_KTILE,    // 128-key tile of the sequence
+  KV_V,        // row tiles that visit the key tile
+  KV_S,        // first of its items in the visit list (prefix of KV_V)
+  KV_Q0, KV_K0, KV_LK, KV_ROWS, KV_RTOFF, KV_DSOFF, KV_LQ, KV_LQMUL, KV_LQSHIFT,
+  KV_PAD0, KV_PAD1, KV_PAD2,
+  KV_FIELDS
+};
+
 // Work lists built on the device; all arrays live in the caller's workspace.
 struct Plan {
   int* seq;        // [B * SEQ_FIELDS]
-  int* fwd_seq;    // [B]    rank -> sequence, row-tile kernels (cost ~ Lk)
-  int* fwd_off;    // [B+1]  exclusive prefix of row tiles over ranks
-  int* kv_seq;     // [B]    rank -> sequence, key-tile kernel (cost ~ rows per chunk)
-  int* kv_off;     // [B+1]  exclusive prefix of (key tile, row chunk) units over ranks
-  int* kv_rank;    // [B]    sequence -> rank in kv order
   int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation
-  // Workgroup -> work item, so a workgroup finds its item with one load:
-  int* fwd_map;    // [fwd_slots * 2]  row tile i: (sequence, tile in sequence), (-1, 0) past the end
-  int* kv_map;     // [kv_slots * 2]   dK/dV unit i: (sequence, unit in sequence), (-1, 0) past the end
+  // Row-tile workgroup i -> (sequence, tile in sequence), longest tiles first,
+  // (-1, 0) past the last tile; a workgroup finds its tile with one load.
+  int* fwd_map;    // [fwd_slots * 2]
+  // dK/dV work split (see plan_units): a record per 128-key tile (KvField),
+  // each workgroup's first key tile (-1: empty share); kv_head holds W, the
+  // number of key tiles and the number of row tiles.
+  int* ktab;       // [key tiles * KV_FIELDS]
+  int* wg_first;   // [kv_wgs]
+  int* kv_head;    // [4]
 };
 
 // n / d for 0 <= n < 2^31 with a host-computed multiplier (round-up method of
@@ -157,20 +173,13 @@ __device__ __forceinline__ int fast_div(int n, uint32_t mul, uint32_t shift) {
 // Folded row R of a sequence -> (token i, head h).  The Lq x Hq rows are
 // folded head-major, R = h * Lq + i: the rows of a tile share few heads, hence
 // similar ALiBi slopes.  sq: the sequence's planner record.
-__device__ __forceinline__ void unfold_row(int R, const int* sq, int& i, int& h) {
-  h = fast_div(R, (uint32_t)sq[SQ_LQMUL], (uint32_t)sq[SQ_LQSHIFT]);
-  i = R - h * sq[SQ_LQ];
+__device__ __forceinline__ void unfold_row(int R, int lq, uint32_t mul, uint32_t shift, int& i,
+                                           int& h) {
+  h = fast_div(R, mul, shift);
+  i = R - h * lq;
 }
-
-// Largest rank r with off[r] <= idx, or -1 when idx is past the last item.
-__device__ __forceinline__ int find_rank(const int* off, int nranks, int idx) {
-  if (nranks <= 0 || idx >= off[nranks]) return -1;
-  int lo = 0, hi = nranks - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (off[mid] <= idx) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+__device__ __forceinline__ void unfold_row(int R, const int* sq, int& i, int& h) {
+  unfold_row(R, sq[SQ_LQ], (uint32_t)sq[SQ_LQMUL], (uint32_t)sq[SQ_LQSHIFT], i, h);
 }
 
 }  // namespace rga

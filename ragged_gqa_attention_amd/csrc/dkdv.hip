@@ -14,8 +14,11 @@
 // With r = 1 / (1 + e^{2s/c}), 1 - tanh^2(s/c) = 4 r (1 - r); the kernel forms
 // r - r^2 and folds the factor 4 into the final sigma scale of dK.
 //
-// Work split.  A workgroup owns 128 keys of one sequence and a chunk of its
-// folded rows.  Its eight waves form four pairs; a pair owns 32 keys and keeps
+// Work split.  Every (128-key tile, visiting row tile) pair of the batch is
+// one item of a list the planner builds (see plan_units); each of the kv_wgs
+// workgroups takes an equal share of consecutive items and walks them key tile
+// by key tile: a segment is 128 keys of one sequence against a run of the row
+// tiles that visit them.  Its eight waves form four pairs; a pair owns 32 keys and keeps
 // their K and V rows in registers (MFMA operands, lane = key).  Rows are
 // streamed 64 at a time through LDS.  In each step the two waves of a pair
 // each form S, dP, P and dS for one half of the rows (32 rows x 32 keys), then
@@ -24,9 +27,9 @@
 // stays within 256 registers, so two waves share each SIMD; they take the
 // independent products and pointwise work of a step in opposite orders, so
 // one wave's VALU work overlaps the other's MFMAs.  The sum over rows happens
-// in registers in a fixed order; sequences split into several row chunks
-// write FP32 partials that a separate pass adds in chunk order.  No atomics
-// anywhere.
+// in registers in a fixed order; a key tile whose items fall to several
+// workgroups is written as FP32 partials (a workgroup's first and last key
+// tile) that a separate pass adds in workgroup order.  No atomics anywhere.
 //
 // Pipeline.  Q and dO tiles are copied global -> LDS with direct loads (no
 // staging registers) into blocked tiles, three buffers: step n is read by the
@@ -57,19 +60,22 @@ struct KvShared {
   u32x4 xch[2][KV_WAVES][KB * 2][64];     // [slot][writer wave][kb * 2 + s][lane]
 };
 
-// What a workgroup works on: rows [row_begin, row_end) of sequence b against
-// keys [key0, key0 + PAIR_KEYS) of the wave's pair.
+// What a segment works on: visiting row tiles number first .. last - 1 (in
+// tile order) of the 128-key tile, against keys [key0, key0 + PAIR_KEYS) of
+// the wave's pair.
 struct KvUnit {
-  const int* sq;   // the sequence's planner record
-  int q0, k0, Lk, row_begin, row_end, key0, nchunk;
+  int q0, k0, Lk, rows, key0;
+  int lq, lqmul, lqshift;   // unfold_row constants of the sequence
+  int first, last;
+  int part;  // FP32 partial slot of the segment, -1 when it stores dK / dV directly
   int ds;    // first dS image of the sequence, -1 when dS is not stored
   int nks;   // 64-key steps of the sequence (images per row tile)
   const int* ksteps;   // key-step ranges of the sequence's row tiles
   int step_lo;         // the workgroup's key steps [step_lo, step_lo + 2)
 };
 
-// Row tiles of rows [row_begin, row_end) that the workgroup visits, as a
-// 64-tile bit mask (kept in scalar registers, reloaded past its end).
+// Row tiles the workgroup visits, as a 64-tile bit mask (kept in scalar
+// registers, reloaded past its end).
 struct TileMask {
   uint64_t bits;
   int base;    // tile of bit 0
@@ -105,6 +111,16 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   const int l32 = lane & 31, g = lane >> 5;
   const int hq = a.hq;
 
+  // whether row tile t visits the key tile (its key-step range meets the
+  // key tile's two steps); the first 64 are requested before the K / V rows
+  const int ntile = (u.rows + ROW_TILE - 1) / ROW_TILE;
+  auto visits = [&](int t) {
+    if (t >= ntile) return false;
+    const int* r = u.ksteps + 2 * t;
+    return r[0] < u.step_lo + 2 && r[1] > u.step_lo;
+  };
+  const bool on0 = visits(lane);
+
   // K and V rows of the pair's keys as B operands (lane = key); keys past
   // the sequence end are zero and their results are never stored.
   u32x4 kf[KB][KSTEPS], vf[KB][KSTEPS];
@@ -124,6 +140,40 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   }
 
+  // The segment's run of visiting tiles, found in one pass over the row
+  // tiles, 64 per ballot (lane l examines tile base + l), while the K / V
+  // loads are in flight; the window holding the first tile seeds the tile
+  // mask.  rb, re: rows [rb, re) from the first to the end of the last tile
+  // of the run.  The first step's copies are requested as soon as rb is known.
+  int rb = 0, re = 0;
+  TileMask tm;
+  tm.bits = 0;
+  tm.base = 0;
+  tm.last = -1;
+  {
+    const int first = u.first, last = u.last;
+    const uint64_t below = (1ull << lane) - 1;   // lanes under this one
+    int seen = 0, t_first = -1, t_last = -1;
+    for (int base = 0; first < last && base < ntile && t_last < 0; base += 64) {
+      const bool on = base == 0 ? on0 : visits(base + lane);
+      const uint64_t m = __ballot(on);
+      const int rank = seen + __popcll(m & below);   // visited tiles before this lane's
+      const int c = __popcll(m);
+      if (t_first < 0 && seen + c > first) {
+        t_first = base + __builtin_ctzll(__ballot(on && rank == first));
+        tm.bits = m;
+        tm.base = base;
+      }
+      if (seen + c >= last) t_last = base + __builtin_ctzll(__ballot(on && rank == last - 1));
+      seen += c;
+    }
+    if (t_first >= 0 && t_last >= t_first) {
+      rb = t_first * ROW_TILE;
+      re = min(u.rows, (t_last + 1) * ROW_TILE);
+      tm.last = t_last;
+    }
+  }
+
   // Direct loads of step rows [r0, r0 + 64) into blocked tiles (see blk_off):
   // wave w copies rows 16 (w%4) .. +15 of Q (w < 4) or dO, one 4-chunk block
   // per load, lane l holding row 16 (w%4) + l / 4 for all five loads, so one
@@ -136,16 +186,16 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   auto issue_loads = [&](int r0, int buf) {
     if (wave == 0) {
       const int R = r0 + lane;
-      const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, u.row_end - 1)) * 4;
-      load_lds16(R < u.row_end ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
+      const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, re - 1)) * 4;
+      load_lds16(R < re ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
     }
     const int R = r0 + lrow;
-    const int Rc = min(R, u.row_end - 1);
+    const int Rc = min(R, re - 1);
     int tok_, h_;
-    unfold_row(Rc, u.sq, tok_, h_);
+    unfold_row(Rc, u.lq, (uint32_t)u.lqmul, (uint32_t)u.lqshift, tok_, h_);
     const uint32_t tok = (uint32_t)tok_, h = (uint32_t)h_;
     const uint32_t t_abs = (uint32_t)u.q0 + tok;
-    const bool ok = R < u.row_end;
+    const bool ok = R < re;
     const uint16_t* base = ltensor ? a.dout : a.q;
     const uint32_t ts = (uint32_t)(ltensor ? a.do_ts : a.q_ts);
     const uint32_t hs = (uint32_t)(ltensor ? a.do_hs : a.q_hs);
@@ -300,29 +350,27 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   };
 
-  // visited row steps: every step of a visited tile inside [row_begin, row_end)
-  TileMask tm;
-  tm.last = (u.row_end - 1) / ROW_TILE;
-  tile_mask_load(tm, u, u.row_begin / ROW_TILE, lane);
-  // first step of a visited tile at or after tile t (row_end when none)
+  // visited row steps: every step of a visited tile inside [rb, re) (an
+  // empty run leaves the accumulators zero)
+  // first step of a visited tile at or after tile t (re when none)
   auto tile_start = [&](int t) {
     t = tile_mask_next(tm, u, t, lane);
-    return t > tm.last ? u.row_end : max(u.row_begin, t * ROW_TILE);
+    return t > tm.last ? re : max(rb, t * ROW_TILE);
   };
   // the visited step after the one at r0
   auto next_step = [&](int r0) {
     const int r = r0 + KV_ROW_STEP;
-    if (r >= u.row_end) return u.row_end;
+    if (r >= re) return re;
     return (r & (ROW_TILE - 1)) != 0 ? r : tile_start(r / ROW_TILE);
   };
-  int rn = tile_start(u.row_begin / ROW_TILE);   // rows of the step after the current one
-  if (rn < u.row_end) {
+  int rn = rb;   // rows of the step after the current one (the first tile is visited)
+  if (rn < re) {
     const int r0 = rn;
-    rn = next_step(r0);
     issue_loads(r0, 0);
+    rn = next_step(r0);
     wait_vm();
     __syncthreads();
-    if (rn < u.row_end) issue_loads(rn, 1);
+    if (rn < re) issue_loads(rn, 1);
     f32x16 S[KB], dP[KB];
     scores(0, S, dP);
     pointwise_publish(0, 0, r0, S, dP, mine);
@@ -330,10 +378,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     __syncthreads();
     int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
     int n = 1;
-    for (; rn < u.row_end; ++n) {
+    for (; rn < re; ++n) {
       const int rc = rn;
       rn = next_step(rc);
-      if (rn < u.row_end) issue_loads(rn, next);
+      if (rn < re) issue_loads(rn, next);
       scores(cur, S, dP);
       // products of the previous step (its partner half arrived before the
       // barrier) and the pointwise work of this one are independent; the two
@@ -361,7 +409,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 
   // lane owns key key0 + 32 kb + l32, features 32 db + 8 (r/4) + 4 g + r%4
   const float scale = ROLE ? (CAP ? 4.0f * a.lc.sigma : a.lc.sigma) : 1.0f;
-  if (u.nchunk == 1) {
+  if (u.part < 0) {
     uint16_t* base = ROLE ? a.dk : a.dv;
     const int64_t ts = ROLE ? a.dk_ts : a.dv_ts;
 #pragma unroll
@@ -383,7 +431,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     float* base = ROLE ? a.part_dk : a.part_dv;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const int64_t slot = (int64_t)blockIdx.x * KEY_TILE + (u.key0 % KEY_TILE) + kb * 32 + l32;
+      const int64_t slot = (int64_t)u.part * KEY_TILE + (u.key0 % KEY_TILE) + kb * 32 + l32;
       float* dst = base + slot * HEAD_DIM + g * 4;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
@@ -404,36 +452,52 @@ template <class T, bool CAP>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) KvShared sm;
 
-  const int b = a.plan.kv_map[2 * blockIdx.x];
-  if (b < 0) return;
-  const int unit = a.plan.kv_map[2 * blockIdx.x + 1];
-  const int* sq = a.plan.seq + b * SEQ_FIELDS;
-  KvUnit u;
-  u.sq = sq;
-  u.q0 = sq[SQ_Q0];
-  u.k0 = sq[SQ_K0];
-  u.Lk = sq[SQ_LK];
-  u.nchunk = sq[SQ_NCHUNK];
-  u.ds = a.ds ? sq[SQ_DSOFF] : -1;
-  u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
-  u.ksteps = a.ksteps + 2 * sq[SQ_RTOFF];
-  const int rows = sq[SQ_ROWS], chunk = sq[SQ_CHUNK];
-  const int ktile = unit / u.nchunk;
-  const int ci = unit - ktile * u.nchunk;
-  u.row_begin = ci * chunk;
-  u.row_end = min(rows, u.row_begin + chunk);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  u.key0 = ktile * KEY_TILE + (wave >> 1) * PAIR_KEYS;
-  u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
-  // every unit has at least one row (the planner never emits empty chunks)
-  // waves w and w + 4 share a SIMD
-  if (wave < 4) {
-    if (wave & 1) dkdv_wave<T, CAP, 1, false>(a, sm, u, wave, lane);
-    else dkdv_wave<T, CAP, 0, false>(a, sm, u, wave, lane);
-  } else {
-    if (wave & 1) dkdv_wave<T, CAP, 1, true>(a, sm, u, wave, lane);
-    else dkdv_wave<T, CAP, 0, true>(a, sm, u, wave, lane);
+  // items [w0, w1) of the visit list
+  const long long W = a.plan.kv_head[0];
+  const int nkt = a.plan.kv_head[1];
+  const long long w0 = (long long)blockIdx.x * W / gridDim.x;
+  const long long w1 = (long long)(blockIdx.x + 1) * W / gridDim.x;
+  int gt = a.plan.wg_first[blockIdx.x];
+  if (w0 >= w1 || gt < 0) return;
+  for (long long w = w0; w < w1 && gt < nkt; ++gt) {
+    // lane and wave are re-derived per segment behind an empty asm, so the
+    // compiler cannot keep the segment's lane-constant offsets live across
+    // segments (that pushes the pipeline into scratch)
+    int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    asm volatile("" : "+v"(lane), "+v"(wv));
+    const int wave = __builtin_amdgcn_readfirstlane(wv);
+    const int* e = a.plan.ktab + (int64_t)KV_FIELDS * gt;
+    const int V = e[KV_V], S = e[KV_S];
+    if (S + V <= w) continue;   // a key tile no row tile visits
+    const int ktile = e[KV_KTILE];
+    KvUnit u;
+    u.q0 = e[KV_Q0];
+    u.k0 = e[KV_K0];
+    u.Lk = e[KV_LK];
+    u.rows = e[KV_ROWS];
+    u.lq = e[KV_LQ];
+    u.lqmul = e[KV_LQMUL];
+    u.lqshift = e[KV_LQSHIFT];
+    u.first = (int)(w - S);
+    u.last = (int)min((long long)V, w1 - S);
+    // a key tile split over workgroups: partial slot 2 p for the workgroup's
+    // first key tile, 2 p + 1 for its last
+    u.part = (u.first == 0 && u.last == V) ? -1 : 2 * (int)blockIdx.x + (w == w0 ? 0 : 1);
+    u.ds = a.ds ? e[KV_DSOFF] : -1;
+    u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
+    u.ksteps = a.ksteps + 2 * e[KV_RTOFF];
+    u.key0 = ktile * KEY_TILE + (wave >> 1) * PAIR_KEYS;
+    u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
+    // waves w and w + 4 share a SIMD
+    if (wave < 4) {
+      if (wave & 1) dkdv_wave<T, CAP, 1, false>(a, sm, u, wave, lane);
+      else dkdv_wave<T, CAP, 0, false>(a, sm, u, wave, lane);
+    } else {
+      if (wave & 1) dkdv_wave<T, CAP, 1, true>(a, sm, u, wave, lane);
+      else dkdv_wave<T, CAP, 0, true>(a, sm, u, wave, lane);
+    }
+    w = S + u.last;
+    __syncthreads();   // the next segment reuses the LDS buffers
   }
 }
 

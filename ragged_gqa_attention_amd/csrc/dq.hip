@@ -36,48 +36,53 @@ struct DqShared {
   uint16_t kt[2][TILE_ELEMS];
 };
 
-// dK / dV of the 128-key tiles part, part + parts, ... (batch order):
-// sequences whose rows were split over several dK/dV workgroups sum their FP32
-// partials in chunk order and round once; keys of sequences without query
-// rows get exact zeros; tiles of unsplit sequences were stored by the dK/dV
-// kernel.  The dK/dV kernel has finished (same stream), so its partials are
-// complete.  A tile is 128 x 40 groups of 4 features, ten per thread, whose
-// chunk sums are formed side by side (ten loads per tensor in flight).
+// dK / dV of the 128-key tiles part, part + parts, ... (batch order): key
+// tiles whose visits fell to several dK/dV workgroups (see plan_units) sum
+// the FP32 partials of those workgroups in workgroup order and round once;
+// key tiles no row tile visits (e.g. every key of a sequence without query
+// rows) get exact zeros; the others were stored by their one workgroup.  The
+// dK/dV kernel has finished (same stream), so its partials are complete.  A
+// tile is 128 x 40 groups of 4 features, ten per thread, whose sums are
+// formed side by side (ten loads per tensor in flight).
 template <class T>
 __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int parts) {
   constexpr int QUADS = HEAD_DIM / 4;
   constexpr int PER_THREAD = KEY_TILE * QUADS / ROW_THREADS;
   static_assert(PER_THREAD * ROW_THREADS == KEY_TILE * QUADS, "whole tiles per pass");
-  const int* seq = a.plan.seq;
-  const int B = a.batch;
-  if (B <= 0) return;
-  const int ntiles = seq[(B - 1) * SEQ_FIELDS + SQ_KTOFF] + seq[(B - 1) * SEQ_FIELDS + SQ_KTILES];
-  int b = 0;
-  for (int gt = part; gt < ntiles; gt += parts) {
-    while (b + 1 < B && seq[(b + 1) * SEQ_FIELDS + SQ_KTOFF] <= gt) ++b;   // gt only grows
-    const int* sb = seq + b * SEQ_FIELDS;
-    const int nchunk = sb[SQ_NCHUNK];
-    if (nchunk == 1) continue;
-    const int kt = gt - sb[SQ_KTOFF];
-    const int k0 = sb[SQ_K0] + kt * KEY_TILE;
-    const int nkeys = min(KEY_TILE, sb[SQ_LK] - kt * KEY_TILE);
+  const long long W = a.plan.kv_head[0];
+  const int nkt = a.plan.kv_head[1];
+  const long long G = a.kv_wgs;
+  for (int gt = part; gt < nkt; gt += parts) {
+    const int* e = a.plan.ktab + (int64_t)KV_FIELDS * gt;
+    const int V = e[KV_V];
+    const long long S = e[KV_S];
+    // workgroups holding items S and S + V - 1: the one whose share [p W / G,
+    // (p + 1) W / G) contains item x is p = ((x + 1) G - 1) / W
+    int pa = 0, pb = -1;
+    if (V > 0) {
+      pa = (int)(((S + 1) * G - 1) / W);
+      pb = (int)(((S + V) * G - 1) / W);
+      if (pa == pb) continue;   // stored by its one workgroup
+    }
+    const int k0 = e[KV_K0] + e[KV_KTILE] * KEY_TILE;
+    const int nkeys = min(KEY_TILE, e[KV_LK] - e[KV_KTILE] * KEY_TILE);
     f32x4 sk[PER_THREAD], sv[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
       sk[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
       sv[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
-    if (nchunk > 1) {
-      const int64_t base = (int64_t)a.plan.kv_off[a.plan.kv_rank[b]] + (int64_t)kt * nchunk;
-      for (int c = 0; c < nchunk; ++c) {
-        const float* pk = a.part_dk + (base + c) * KEY_TILE * HEAD_DIM;
-        const float* pv = a.part_dv + (base + c) * KEY_TILE * HEAD_DIM;
+    for (int p = pa; p <= pb; ++p) {
+      const long long p0 = (long long)p * W / G, p1 = (long long)(p + 1) * W / G;
+      if (p0 >= p1) continue;   // an empty share wrote nothing
+      const int64_t slot = 2 * (int64_t)p + (S <= p0 ? 0 : 1);
+      const float* pk = a.part_dk + slot * KEY_TILE * HEAD_DIM;
+      const float* pv = a.part_dv + slot * KEY_TILE * HEAD_DIM;
 #pragma unroll
-        for (int j = 0; j < PER_THREAD; ++j) {
-          const int i = threadIdx.x + j * ROW_THREADS;   // key i / 40, features 4 (i % 40)
-          sk[j] += *reinterpret_cast<const f32x4*>(pk + 4 * i);
-          sv[j] += *reinterpret_cast<const f32x4*>(pv + 4 * i);
-        }
+      for (int j = 0; j < PER_THREAD; ++j) {
+        const int i = threadIdx.x + j * ROW_THREADS;   // key i / 40, features 4 (i % 40)
+        sk[j] += *reinterpret_cast<const f32x4*>(pk + 4 * i);
+        sv[j] += *reinterpret_cast<const f32x4*>(pv + 4 * i);
       }
     }
 #pragma unroll
@@ -234,7 +239,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   // compute units the last row tiles leave idle.
   const int b = (int)blockIdx.x < a.fwd_slots ? a.plan.fwd_map[2 * blockIdx.x] : -1;
   if (b < 0) {
-    const int first = a.batch > 0 ? a.plan.fwd_off[a.batch] : 0;
+    const int first = a.batch > 0 ? a.plan.kv_head[2] : 0;   // row tiles
     if (a.total_k > 0 && (int)blockIdx.x >= first)
       reduce_kv_tiles<T>(a, blockIdx.x - first, gridDim.x - first);
     return;

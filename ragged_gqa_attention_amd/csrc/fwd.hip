@@ -33,9 +33,11 @@
 //
 // Far keys.  With a cap, a key farther from a row's centre than the skip
 // bound allows has P == 0 exactly (see row_key_steps), so a workgroup visits
-// only the key steps [lo, hi) that hold a key some row of its tile keeps, and
-// records that range for the backward.
+// only the key steps [lo, hi) that hold a key some row of its tile keeps (the
+// planner records that range per tile).  In the full-VJP call one more
+// workgroup plans the dK/dV units meanwhile.
 #include "kernels.hpp"
+#include "planner.hpp"
 #include "tiles.hpp"
 
 namespace rga {
@@ -58,14 +60,23 @@ static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared),
 
 }  // namespace
 
-template <class T, bool CAP, bool DELTA>
-__global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) FwdShared sm;
-  __shared__ int span[2][ROW_WAVES];
+static_assert(sizeof(UnitsShared) <= sizeof(FwdShared), "the unit planner fits the tile buffers");
 
-  const int b = a.plan.fwd_map[2 * blockIdx.x];
+template <class T, bool CAP, bool DELTA>
+__global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
+  __shared__ __attribute__((aligned(16))) FwdShared sm;
+
+  // With the unit planner (full-VJP call) workgroup 0 plans and row tile
+  // slot i runs in workgroup i + 1: the planner starts at once and is done
+  // long before the row tiles.
+  const int slot = (int)blockIdx.x - (int)(gridDim.x - a.fwd_slots);
+  if (slot < 0) {
+    plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
+    return;
+  }
+  const int b = a.plan.fwd_map[2 * slot];
   if (b < 0) return;
-  const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
+  const int tile = a.plan.fwd_map[2 * slot + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   const int q0 = sq[SQ_Q0], Lq = sq[SQ_LQ], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
   const int rows = sq[SQ_ROWS];
@@ -99,31 +110,9 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
   for (int db = 0; db < DBLK; ++db) O[db] = f32x16{};
 
   const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
-  // key steps [klo, khi) some row of the tile keeps (min / max over the rows)
-  int klo, khi;
-  row_key_steps(row_ok, slope2, max(ti + Lk - Lq, 0), Lk, CAP ? a.skip_log2 : 0.0f, klo, khi);
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    klo = min(klo, __shfl_xor(klo, o, 64));
-    khi = max(khi, __shfl_xor(khi, o, 64));
-  }
-  if (lane == 0) {
-    span[0][wave] = klo;
-    span[1][wave] = khi;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int w = 0; w < ROW_WAVES; ++w) {
-    klo = min(klo, span[0][w]);
-    khi = max(khi, span[1][w]);
-  }
-  klo = __builtin_amdgcn_readfirstlane(klo);
-  khi = __builtin_amdgcn_readfirstlane(khi);
-  if (tid == 0) {
-    int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
-    ks[0] = klo;
-    ks[1] = khi;
-  }
+  // key steps [klo, khi) some row of the tile keeps (the planner's range)
+  const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
+  const int klo = ks[0], khi = ks[1];
   const uint16_t* vt_seq = a.vt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
   // copies of key step kt: waves 0-3 the K rows (one 16-row group each),
   // waves 4-7 V^T (five 8-feature-row loads each)
@@ -397,23 +386,28 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a) {
 }
 
 template <class T>
-static hipError_t launch_fwd_t(const AttnArgs& a, bool cap, bool with_delta, int grid,
-                               hipStream_t s) {
+static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
+                               int grid, hipStream_t s) {
   if (cap) {
-    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a);
+    if (with_delta)
+      hipLaunchKernelGGL((fwd_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a, pa);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a, pa);
   } else {
-    if (with_delta) hipLaunchKernelGGL((fwd_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((fwd_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a);
+    if (with_delta)
+      hipLaunchKernelGGL((fwd_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a, pa);
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a, pa);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
-                      hipStream_t s) {
-  if (grid <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_fwd_t<BF16>(a, cap, with_delta, grid, s)
-                          : launch_fwd_t<F16>(a, cap, with_delta, grid, s);
+hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
+                      bool with_delta, bool plan_units, hipStream_t s) {
+  const int grid = a.fwd_slots + (plan_units ? 1 : 0);
+  if (a.batch <= 0) return hipSuccess;
+  return dtype == DT_BF16 ? launch_fwd_t<BF16>(a, pa, cap, with_delta, grid, s)
+                          : launch_fwd_t<F16>(a, pa, cap, with_delta, grid, s);
 }
 
 }  // namespace rga

@@ -58,11 +58,11 @@ struct AttnArgs {
   // Key steps [lo, hi) (64 keys each) of every 256-row tile, batch order
   // (tile SQ_RTOFF + t of sequence b): the steps that hold a key whose P can
   // be nonzero for some row of the tile (see row_key_steps).  Written by the
-  // forward, or by ksteps_kernel in the standalone backward, and read by the
-  // dK/dV and dQ kernels.
+  // planner (rewritten by ksteps_kernel in the standalone backward) and read
+  // by the forward, dK/dV and dQ kernels.
   int* ksteps;
-  // Skip bound in log2 units (0 turns skipping off): the forward drops keys
-  // whose ALiBi term slope * log2(e) * |c_i - j| exceeds skip_log2.
+  // Skip bound in log2 units (0 turns skipping off): keys whose ALiBi term
+  // slope * log2(e) * |c_i - j| exceeds it are dropped (the planner's ranges).
   float skip_log2;
   const float* slopes;  int64_t slopes_stride;
   int hq;
@@ -70,6 +70,7 @@ struct AttnArgs {
   int64_t total_q;
   int64_t total_k;
   int fwd_slots;        // entries of plan.fwd_map; the dQ grid has more (partial sums)
+  int kv_wgs;           // dK/dV workgroups (each takes an equal share of the visits)
   LogitConsts lc;
   Plan plan;
 };
@@ -77,18 +78,22 @@ struct AttnArgs {
 struct PlanArgs {
   const int* cu_q;
   const int* cu_k;
+  const float* slopes;  int64_t slopes_stride;
   int batch;
   int hq;
   int64_t total_q;
   int64_t total_k;
-  int target_units;     // desired number of dK/dV work units
-  int min_chunk;        // smallest row chunk worth splitting off (multiple of KV_ROW_STEP)
+  // Skip bound of the key-step ranges the planner records (log2 units, 0 =
+  // every key; see row_key_steps).
+  float skip_log2;
+  int* ksteps;          // [row tiles * 2] ranges the planner writes (AttnArgs::ksteps)
   long long ds_images;  // dS images that fit the workspace (0: no stored dS)
   int fwd_slots;        // entries of plan.fwd_map (the row-tile launches' grid)
-  int kv_slots;         // entries of plan.kv_map (the dK/dV launch's grid)
+  int kv_wgs;           // dK/dV workgroups (the dK/dV launch's grid)
   uint16_t* zero;       // 512 bytes the planner clears
   Plan plan;
 };
+
 
 enum { DT_F16 = 0, DT_BF16 = 1 };
 
@@ -103,7 +108,7 @@ enum { DT_F16 = 0, DT_BF16 = 1 };
 // dQ, dK or dV: a key whose slope2 |c_i - j| exceeds
 //   forward:  SKIP_UNDERFLOW + 2 c log2 e,
 //   backward: SKIP_UNDERFLOW + max(0, residual of the row)
-// is never evaluated, and the results are bitwise those of evaluating it.
+// is never evaluated: it would contribute exact zeros.
 constexpr float SKIP_UNDERFLOW = 160.0f;
 
 // Key steps [lo, hi) (64 keys) holding every key of one row that the bound
@@ -133,11 +138,15 @@ __device__ __forceinline__ void row_key_steps(bool exists, float slope2, int cen
 // Planner (one workgroup) and, alongside it, the transposed key tiles a.kt and /
 // or a.vt (null pointers are skipped), up to key_tiles tiles each.
 hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s);
-hipError_t launch_fwd(const AttnArgs& a, int dtype, bool cap, bool with_delta, int grid,
-                      hipStream_t s);
+// Forward over the a.fwd_slots row-tile slots; plan_units adds the workgroup
+// that plans the dK/dV units (from pa) alongside.
+hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
+                      bool with_delta, bool plan_units, hipStream_t s);
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
-// Key-step ranges of the standalone backward, from the row records.
+// Key-step ranges of the standalone backward, from the row records, and its
+// dK/dV units planned from them.
 hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s);
+hipError_t launch_units(const PlanArgs& pa, hipStream_t s);
 hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 

@@ -5,84 +5,45 @@
 // builds two work lists for the packed ragged batch (page "Noncausal Global
 // Extreme-GQA Ragged Attention Full VJP", section "What You Have": 18-52
 // sequences whose Q/K length ratio runs both ways):
-//   * row tiles (forward, dQ): ceil(Lq * Hq / 128) per sequence, cost ~ Lk;
-//   * key units (dK/dV): ceil(Lk / 128) key tiles per sequence, each split into
-//     row chunks so that the whole batch yields about `target_units` units.
-// Sequences are ranked by cost, largest first, so the longest work starts
-// first.  A workgroup finds its item by binary search over the rank prefix.
+//   * row tiles (forward, dQ): ceil(Lq * Hq / 256) per sequence, sequences
+//     ranked by Lk, largest first, so the longest work starts first;
+//   * dK/dV units: each 128-key tile of a sequence splits the row tiles that
+//     visit it (whose key-step range meets it, see row_key_steps) into runs of
+//     near-equal length, sized so that the units fill whole rounds of the
+//     compute units.
+// Each workgroup finds its item in a map with one load.
 #include "kernels.hpp"
+#include "planner.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
 constexpr int PLAN_THREADS = 256;
 constexpr int WG_THREADS = 256;          // row-record kernel
-constexpr int PLAN_SORT_LIMIT = 8192;   // larger batches keep their natural order
 
 constexpr int PLAN_WAVES = PLAN_THREADS / 64;
-
-// Sum over the block (wave shuffles, then the four wave totals).
-__device__ __forceinline__ long long block_sum(long long v, long long* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  long long r = 0;
-#pragma unroll
-  for (int w = 0; w < PLAN_WAVES; ++w) r += red[w];
-  __syncthreads();
-  return r;
-}
-
-// put(r, sum_{r' < r} count(r')) for r = 0..B.  Thread t owns a contiguous
-// segment of r; segment totals are scanned with wave shuffles.
-template <class V, class F, class G>
-__device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, V* part) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int seg = (B + PLAN_THREADS - 1) / PLAN_THREADS;
-  const int lo = min(B, tid * seg), hi = min(B, lo + seg);
-  V local = 0;
-  for (int r = lo; r < hi; ++r) local += count(r);
-  V x = local;   // inclusive scan inside the wave
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const V y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
-  if (lane == 63) part[wave] = x;
-  __syncthreads();
-  V base = 0;
-  for (int w = 0; w < wave; ++w) base += part[w];
-  if (tid == PLAN_THREADS - 1) put(B, base + x);
-  V run = base + x - local;
-  for (int r = lo; r < hi; ++r) {
-    put(r, run);
-    run += count(r);
-  }
-  __syncthreads();
-}
 
 // Batches up to this size are planned in LDS and copied out at the end (each
 // planning step re-reads what the previous one wrote; LDS keeps those round
 // trips short); larger ones are planned in place in global memory.
 constexpr int PLAN_LDS_B = 256;
+// Row tiles are dispatched longest first (by their key steps, counting-sorted
+// into this many classes; longer ones share the last class).  Tiles of equal
+// length go in the order the LDS atomics hand out, which only affects timing:
+// a tile's results do not depend on the workgroup that computes it.
+constexpr int PLAN_COST_CLASSES = 1024;
 
 __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   __shared__ int bad;
   __shared__ long long red[PLAN_WAVES];
   __shared__ int part[PLAN_WAVES];
   __shared__ int l_seq[PLAN_LDS_B * SEQ_FIELDS];
-  __shared__ int l_fseq[PLAN_LDS_B], l_kseq[PLAN_LDS_B];
-  __shared__ int l_foff[PLAN_LDS_B + 1], l_koff[PLAN_LDS_B + 1];
+  __shared__ float l_slopes[PLAN_LDS_SLOPES];
+  __shared__ int l_class[PLAN_COST_CLASSES + 1], l_foff_c[PLAN_COST_CLASSES];
   const int tid = threadIdx.x;
   const int B = a.batch;
   const bool in_lds = B <= PLAN_LDS_B;
   int* seq = in_lds ? l_seq : a.plan.seq;
-  int* fwd_seq = in_lds ? l_fseq : a.plan.fwd_seq;
-  int* kv_seq = in_lds ? l_kseq : a.plan.kv_seq;
-  int* fwd_off = in_lds ? l_foff : a.plan.fwd_off;
-  int* kv_off = in_lds ? l_koff : a.plan.kv_off;
 
   if (tid == 0) bad = 0;
   if (tid < 32) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
@@ -100,100 +61,90 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   if (tid == 0) a.plan.flag[0] = ok ? 0 : 1;
 
   // Per-sequence extents; an invalid batch plans every sequence as empty.
-  long long cost = 0;
   for (int b = tid; b < B; b += PLAN_THREADS) {
     const int q0 = ok ? a.cu_q[b] : 0, lq = ok ? a.cu_q[b + 1] - q0 : 0;
     const int k0 = ok ? a.cu_k[b] : 0, lk = ok ? a.cu_k[b + 1] - k0 : 0;
-    const int rows = lq * a.hq;
-    const int kt = (lk + KEY_TILE - 1) / KEY_TILE;
     int* s = seq + b * SEQ_FIELDS;
     s[SQ_Q0] = q0; s[SQ_LQ] = lq; s[SQ_K0] = k0; s[SQ_LK] = lk;
-    s[SQ_ROWS] = rows; s[SQ_KTILES] = kt;
+    s[SQ_ROWS] = lq * a.hq;
+    s[SQ_KTILES] = (lk + KEY_TILE - 1) / KEY_TILE;
     // n / Lq = (umulhi(n, mul) + n) >> shift (see fast_div)
     uint32_t sh = 0;
     while (lq > 0 && (1u << sh) < (uint32_t)lq) ++sh;
     s[SQ_LQSHIFT] = (int)sh;
     s[SQ_LQMUL] = lq > 0 ? (int)(uint32_t)((((1ull << sh) - (uint64_t)lq) << 32) / (uint64_t)lq + 1) : 0;
-    cost += (long long)kt * rows;
-  }
-  const long long total_cost = block_sum(cost, red);
-  long long target = (total_cost + a.target_units - 1) / a.target_units;
-  if (target < a.min_chunk) target = a.min_chunk;
-  target = (target + KV_ROW_STEP - 1) / KV_ROW_STEP * KV_ROW_STEP;
-  for (int b = tid; b < B; b += PLAN_THREADS) {
-    int* s = seq + b * SEQ_FIELDS;
-    const long long rows = s[SQ_ROWS];
-    int nchunk = 0, chunk = 0;
-    if (rows > 0 && s[SQ_KTILES] > 0) {
-      const long long n0 = (rows + target - 1) / target;
-      long long len = (rows + n0 - 1) / n0;
-      len = (len + KV_ROW_STEP - 1) / KV_ROW_STEP * KV_ROW_STEP;
-      chunk = (int)len;
-      nchunk = (int)((rows + len - 1) / len);
-    }
-    s[SQ_NCHUNK] = nchunk;
-    s[SQ_CHUNK] = chunk;
-  }
-  __syncthreads();
-
-  // Ranks: row tiles by Lk descending, key units by chunk length descending.
-  for (int b = tid; b < B; b += PLAN_THREADS) {
-    int rf = b, rk = b;
-    if (B <= PLAN_SORT_LIMIT) {
-      const int fb = seq[b * SEQ_FIELDS + SQ_LK], kb = seq[b * SEQ_FIELDS + SQ_CHUNK];
-      rf = 0;
-      rk = 0;
-      for (int o = 0; o < B; ++o) {
-        const int fo = seq[o * SEQ_FIELDS + SQ_LK], ko = seq[o * SEQ_FIELDS + SQ_CHUNK];
-        rf += (fo > fb) || (fo == fb && o < b);
-        rk += (ko > kb) || (ko == kb && o < b);
-      }
-    }
-    fwd_seq[rf] = b;
-    kv_seq[rk] = b;
-    a.plan.kv_rank[b] = rk;
   }
   __syncthreads();
 
   const int hq = a.hq;
-  block_exclusive_scan(B, [&](int r) {
-    const int b = fwd_seq[r];
-    return (seq[b * SEQ_FIELDS + SQ_LQ] * hq + ROW_TILE - 1) / ROW_TILE;
-  }, [&](int r, int v) { fwd_off[r] = v; }, part);
-  block_exclusive_scan(B, [&](int r) {
-    const int b = kv_seq[r];
-    return seq[b * SEQ_FIELDS + SQ_KTILES] * seq[b * SEQ_FIELDS + SQ_NCHUNK];
-  }, [&](int r, int v) { kv_off[r] = v; }, part);
-  // workgroup -> item maps (entries past the last item get sequence -1)
-  __threadfence_block();
-  __syncthreads();
-  auto fill_map = [&](int* map, int slots, const int* off, const int* order) {
-    for (int i = tid; i < slots; i += PLAN_THREADS) {
-      int r = -1;
-      if (B > 0 && i < off[B]) {
-        int lo = 0, hi = B - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (off[mid] <= i) lo = mid; else hi = mid - 1;
-        }
-        r = lo;
-      }
-      map[2 * i] = r >= 0 ? order[r] : -1;
-      map[2 * i + 1] = r >= 0 ? i - off[r] : 0;
-    }
-  };
-  fill_map(a.plan.fwd_map, a.fwd_slots, fwd_off, fwd_seq);
-  fill_map(a.plan.kv_map, a.kv_slots, kv_off, kv_seq);
-  // transposed 64-key tiles, in sequence order
-  block_exclusive_scan(B, [&](int b) {
-    return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
-  }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
   // 256-row tiles in batch order (their key-step ranges are kept in this order)
-  block_exclusive_scan(B, [&](int b) {
+  block_exclusive_scan<PLAN_THREADS>(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
   }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_RTOFF] = v; }, part);
-  // 128-key tiles in batch order (the dK / dV partial sums walk them)
-  block_exclusive_scan(B, [&](int b) { return seq[b * SEQ_FIELDS + SQ_KTILES]; },
+  const int nrt = B > 0 ? seq[(B - 1) * SEQ_FIELDS + SQ_RTOFF] +
+                              (seq[(B - 1) * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE
+                        : 0;
+
+  // Key-step range of every row tile (see tile_key_steps), from the slopes
+  // (staged in LDS, all loads in flight at once, when they fit).
+  const bool cached = (long long)B * hq <= PLAN_LDS_SLOPES;
+  if (cached) {
+    constexpr int PER = 8;
+    for (int i0 = 0; i0 < B * hq; i0 += PLAN_THREADS * PER) {
+      float v[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = i0 + k * PLAN_THREADS + tid;
+        const int b = i / hq;
+        v[k] = i < B * hq ? a.slopes[(int64_t)b * a.slopes_stride + (i - b * hq)] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = i0 + k * PLAN_THREADS + tid;
+        if (i < B * hq) l_slopes[i] = v[k];
+      }
+    }
+  }
+  for (int i = tid; i <= PLAN_COST_CLASSES; i += PLAN_THREADS) l_class[i] = 0;
+  __syncthreads();
+  auto seq_of_tile = [&](int g) {
+    return last_at_most(B, g, [&](int x) { return seq[x * SEQ_FIELDS + SQ_RTOFF]; });
+  };
+  for (int g = tid; g < nrt; g += PLAN_THREADS) {
+    const int b = seq_of_tile(g);
+    const int* s = seq + b * SEQ_FIELDS;
+    int lo, hi;
+    if (cached) tile_key_steps(a, s, g - s[SQ_RTOFF], l_slopes + b * hq, 1, lo, hi);
+    else tile_key_steps(a, s, g - s[SQ_RTOFF], a.slopes + (int64_t)b * a.slopes_stride, 1, lo, hi);
+    a.ksteps[2 * g] = lo;
+    a.ksteps[2 * g + 1] = hi;
+    // class 0 holds the longest tiles
+    atomicAdd(&l_class[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+  }
+  __syncthreads();
+  // workgroup -> row tile, longest first; entries past the last tile get
+  // sequence -1
+  block_exclusive_scan<PLAN_THREADS>(PLAN_COST_CLASSES, [&](int c) { return l_class[c]; },
+                                     [&](int c, int v) { if (c < PLAN_COST_CLASSES) l_foff_c[c] = v; },
+                                     part);
+  for (int g = tid; g < nrt; g += PLAN_THREADS) {
+    const int lo = a.ksteps[2 * g], hi = a.ksteps[2 * g + 1];
+    const int pos = atomicAdd(&l_foff_c[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+    const int b = seq_of_tile(g);
+    a.plan.fwd_map[2 * pos] = b;
+    a.plan.fwd_map[2 * pos + 1] = g - seq[b * SEQ_FIELDS + SQ_RTOFF];
+  }
+  for (int i = nrt + tid; i < a.fwd_slots; i += PLAN_THREADS) {
+    a.plan.fwd_map[2 * i] = -1;
+    a.plan.fwd_map[2 * i + 1] = 0;
+  }
+  if (tid == 0) a.plan.kv_head[2] = nrt;
+  // transposed 64-key tiles, in sequence order
+  block_exclusive_scan<PLAN_THREADS>(B, [&](int b) {
+    return (seq[b * SEQ_FIELDS + SQ_LK] + TILE_ROWS - 1) / TILE_ROWS;
+  }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_TTOFF] = v; }, part);
+  // 128-key tiles in batch order (dK / dV units and partial sums walk them)
+  block_exclusive_scan<PLAN_THREADS>(B, [&](int b) { return seq[b * SEQ_FIELDS + SQ_KTILES]; },
                        [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_KTOFF] = v; }, part);
   // stored dS images, in sequence order, while they fit the workspace (a
   // sequence that does not fit recomputes dS in the dQ kernel)
@@ -203,22 +154,15 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
     return (long long)((sb[SQ_ROWS] + ROW_TILE - 1) / ROW_TILE) *
            ((sb[SQ_LK] + TILE_ROWS - 1) / TILE_ROWS);
   };
-  block_exclusive_scan(B, images, [&](int b, long long off) {
+  block_exclusive_scan<PLAN_THREADS>(B, images, [&](int b, long long off) {
     if (b < B) {
       const long long n = images(b);
       seq[b * SEQ_FIELDS + SQ_DSOFF] = (n > 0 && off + n <= a.ds_images) ? (int)off : -1;
     }
   }, red);
+
   if (in_lds) {   // the kernels read the plan from global memory
     for (int i = tid; i < B * SEQ_FIELDS; i += PLAN_THREADS) a.plan.seq[i] = l_seq[i];
-    for (int i = tid; i < B; i += PLAN_THREADS) {
-      a.plan.fwd_seq[i] = l_fseq[i];
-      a.plan.kv_seq[i] = l_kseq[i];
-    }
-    for (int i = tid; i <= B; i += PLAN_THREADS) {
-      a.plan.fwd_off[i] = l_foff[i];
-      a.plan.kv_off[i] = l_koff[i];
-    }
   }
 }
 
@@ -421,6 +365,18 @@ __global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
     ks[0] = lo;
     ks[1] = hi;
   }
+}
+
+// dK/dV units of the standalone backward, planned after ksteps_kernel has
+// written the ranges (one workgroup; the sequence records are in global memory).
+__global__ __launch_bounds__(PLAN_THREADS) void units_kernel(const PlanArgs pa) {
+  __shared__ UnitsShared sh;
+  plan_units<PLAN_THREADS>(pa, pa.plan.seq, sh);
+}
+
+hipError_t launch_units(const PlanArgs& pa, hipStream_t s) {
+  hipLaunchKernelGGL(units_kernel, 1, PLAN_THREADS, 0, s, pa);
+  return hipGetLastError();
 }
 
 hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s) {
