@@ -34,6 +34,10 @@ attn_status fail(attn_status st, const char* fmt, ...) {
 
 constexpr size_t ALIGN = 256;
 constexpr int MAX_DEVICES = 64;
+// Fixed cost of a dK/dV segment (K / V loads, the pipeline's unoverlapped
+// first and last steps, the stores) in 64-row steps, for the work split; about
+// 12 us against about 3 us per step, measured on the Hq = 64 workload.
+constexpr int KV_SEGMENT_ITEMS = 4;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
@@ -55,7 +59,7 @@ int device_cus() {
 }
 
 struct Layout {
-  size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps;
+  size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps, head_hw;
   size_t lse, rowinfo, part_dk, part_dv, kt, vt;
   size_t total;
   int64_t kv_wgs;       // dK/dV workgroups (one per compute unit)
@@ -88,6 +92,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.wg_first = take(sizeof(int) * (size_t)L.kv_wgs);
   L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
+  L.head_hw = take(sizeof(int) * (size_t)B * p->hq);
   L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
   const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
   if (entry != ATTN_ENTRY_BWD) L.vt = take(tt_bytes);   // V^T for the forward
@@ -251,6 +256,7 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.slopes_stride = p->slopes_stride;
   pa.skip_log2 = a.skip_log2;
   pa.ksteps = a.ksteps;
+  pa.head_hw = reinterpret_cast<int*>(base + L.head_hw);
   pa.batch = p->batch;
   pa.hq = p->hq;
   pa.total_q = p->total_q;
@@ -258,6 +264,7 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.fwd_slots = (int)L.row_tiles;
   a.fwd_slots = (int)L.row_tiles;
   pa.kv_wgs = (int)L.kv_wgs;
+  pa.seg_items = KV_SEGMENT_ITEMS;
   a.kv_wgs = (int)L.kv_wgs;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;

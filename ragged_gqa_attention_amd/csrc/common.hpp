@@ -141,8 +141,8 @@ enum SeqField {
 enum KvField {
   KV_B = 0,    // sequence
   KV_KTILE,    // 128-key tile of the sequence
-  KV_V,        // row tiles that visit the key tile
-  KV_S,        // first of its items in the visit list (prefix of KV_V)
+  KV_V,        // 64-row steps of the row tiles that visit the key tile
+  KV_S,        // first of its items in the work list (see plan_units)
   KV_Q0, KV_K0, KV_LK, KV_ROWS, KV_RTOFF, KV_DSOFF, KV_LQ, KV_LQMUL, KV_LQSHIFT,
   KV_PAD0, KV_PAD1, KV_PAD2,
   KV_FIELDS
@@ -157,7 +157,7 @@ struct Plan {
   int* fwd_map;    // [fwd_slots * 2]
   // dK/dV work split (see plan_units): a record per 128-key tile (KvField),
   // each workgroup's first key tile (-1: empty share); kv_head holds W, the
-  // number of key tiles and the number of row tiles.
+  // number of key tiles, the number of row tiles and the segment items.
   int* ktab;       // [key tiles * KV_FIELDS]
   int* wg_first;   // [kv_wgs]
   int* kv_head;    // [4]

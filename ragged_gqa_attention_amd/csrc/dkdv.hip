@@ -14,11 +14,11 @@
 // With r = 1 / (1 + e^{2s/c}), 1 - tanh^2(s/c) = 4 r (1 - r); the kernel forms
 // r - r^2 and folds the factor 4 into the final sigma scale of dK.
 //
-// Work split.  Every (128-key tile, visiting row tile) pair of the batch is
-// one item of a list the planner builds (see plan_units); each of the kv_wgs
-// workgroups takes an equal share of consecutive items and walks them key tile
-// by key tile: a segment is 128 keys of one sequence against a run of the row
-// tiles that visit them.  Its eight waves form four pairs; a pair owns 32 keys and keeps
+// Work split.  Every (128-key tile, 64-row step of a visiting row tile) pair
+// of the batch is an item of a list the planner builds (see plan_units); each
+// of the kv_wgs workgroups takes an equal share of consecutive items and walks
+// them key tile by key tile: a segment is 128 keys of one sequence against a
+// run of the row steps that visit them.  Its eight waves form four pairs; a pair owns 32 keys and keeps
 // their K and V rows in registers (MFMA operands, lane = key).  Rows are
 // streamed 64 at a time through LDS.  In each step the two waves of a pair
 // each form S, dP, P and dS for one half of the rows (32 rows x 32 keys), then
@@ -60,9 +60,10 @@ struct KvShared {
   u32x4 xch[2][KV_WAVES][KB * 2][64];     // [slot][writer wave][kb * 2 + s][lane]
 };
 
-// What a segment works on: visiting row tiles number first .. last - 1 (in
-// tile order) of the 128-key tile, against keys [key0, key0 + PAIR_KEYS) of
-// the wave's pair.
+// What a segment works on: visiting 64-row steps number first .. last - 1 (in
+// row order) of the 128-key tile, against keys [key0, key0 + PAIR_KEYS) of the
+// wave's pair.  Every visiting row tile has four steps except a sequence's
+// last, which comes last.
 struct KvUnit {
   int q0, k0, Lk, rows, key0;
   int lq, lqmul, lqshift;   // unfold_row constants of the sequence
@@ -140,18 +141,20 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     }
   }
 
-  // The segment's run of visiting tiles, found in one pass over the row
+  // The segment's run: its first and last steps lie in the visiting tiles of
+  // ranks first / 4 and (last - 1) / 4, found in one pass over the row
   // tiles, 64 per ballot (lane l examines tile base + l), while the K / V
   // loads are in flight; the window holding the first tile seeds the tile
-  // mask.  rb, re: rows [rb, re) from the first to the end of the last tile
-  // of the run.  The first step's copies are requested as soon as rb is known.
+  // mask.  rb, re: rows [rb, re) from the first to the end of the last step.
+  // The first step's copies are requested as soon as rb is known.
   int rb = 0, re = 0;
   TileMask tm;
   tm.bits = 0;
   tm.base = 0;
   tm.last = -1;
   {
-    const int first = u.first, last = u.last;
+    constexpr int TS = ROW_TILE / KV_ROW_STEP;   // steps per row tile
+    const int first = u.first / TS, last = (u.last - 1) / TS + 1;   // tile ranks
     const uint64_t below = (1ull << lane) - 1;   // lanes under this one
     int seen = 0, t_first = -1, t_last = -1;
     for (int base = 0; first < last && base < ntile && t_last < 0; base += 64) {
@@ -168,8 +171,8 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
       seen += c;
     }
     if (t_first >= 0 && t_last >= t_first) {
-      rb = t_first * ROW_TILE;
-      re = min(u.rows, (t_last + 1) * ROW_TILE);
+      rb = t_first * ROW_TILE + (u.first % TS) * KV_ROW_STEP;
+      re = min(u.rows, t_last * ROW_TILE + ((u.last - 1) % TS + 1) * KV_ROW_STEP);
       tm.last = t_last;
     }
   }
@@ -452,9 +455,10 @@ template <class T, bool CAP>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) KvShared sm;
 
-  // items [w0, w1) of the visit list
+  // items [w0, w1) of the work list
   const long long W = a.plan.kv_head[0];
   const int nkt = a.plan.kv_head[1];
+  const int seg = a.plan.kv_head[3];
   const long long w0 = (long long)blockIdx.x * W / gridDim.x;
   const long long w1 = (long long)(blockIdx.x + 1) * W / gridDim.x;
   int gt = a.plan.wg_first[blockIdx.x];
@@ -468,7 +472,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(wv);
     const int* e = a.plan.ktab + (int64_t)KV_FIELDS * gt;
     const int V = e[KV_V], S = e[KV_S];
-    if (S + V <= w) continue;   // a key tile no row tile visits
+    const long long vs = (long long)S + seg;   // first visit item of the key tile
+    if (V == 0 || vs + V <= w) continue;       // nothing of this key tile left
+    const long long f = max(w, vs) - vs, l = min(w1, vs + V) - vs;
+    if (f >= l) break;   // the share ends among the key tile's segment items
     const int ktile = e[KV_KTILE];
     KvUnit u;
     u.q0 = e[KV_Q0];
@@ -478,11 +485,12 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.lq = e[KV_LQ];
     u.lqmul = e[KV_LQMUL];
     u.lqshift = e[KV_LQSHIFT];
-    u.first = (int)(w - S);
-    u.last = (int)min((long long)V, w1 - S);
+    u.first = (int)f;
+    u.last = (int)l;
     // a key tile split over workgroups: partial slot 2 p for the workgroup's
-    // first key tile, 2 p + 1 for its last
-    u.part = (u.first == 0 && u.last == V) ? -1 : 2 * (int)blockIdx.x + (w == w0 ? 0 : 1);
+    // first key tile (its share starts at or after the key tile's items),
+    // 2 p + 1 for its last
+    u.part = (f == 0 && l == V) ? -1 : 2 * (int)blockIdx.x + (S <= w0 ? 0 : 1);
     u.ds = a.ds ? e[KV_DSOFF] : -1;
     u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
     u.ksteps = a.ksteps + 2 * e[KV_RTOFF];
@@ -496,7 +504,7 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
       if (wave & 1) dkdv_wave<T, CAP, 1, true>(a, sm, u, wave, lane);
       else dkdv_wave<T, CAP, 0, true>(a, sm, u, wave, lane);
     }
-    w = S + u.last;
+    w = vs + l;
     __syncthreads();   // the next segment reuses the LDS buffers
   }
 }

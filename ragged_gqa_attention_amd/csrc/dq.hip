@@ -51,17 +51,20 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
   static_assert(PER_THREAD * ROW_THREADS == KEY_TILE * QUADS, "whole tiles per pass");
   const long long W = a.plan.kv_head[0];
   const int nkt = a.plan.kv_head[1];
+  const int seg = a.plan.kv_head[3];
   const long long G = a.kv_wgs;
   for (int gt = part; gt < nkt; gt += parts) {
     const int* e = a.plan.ktab + (int64_t)KV_FIELDS * gt;
     const int V = e[KV_V];
     const long long S = e[KV_S];
-    // workgroups holding items S and S + V - 1: the one whose share [p W / G,
-    // (p + 1) W / G) contains item x is p = ((x + 1) G - 1) / W
+    // workgroups holding its first and last visit items, S + seg and
+    // S + seg + V - 1: the one whose share [p W / G, (p + 1) W / G) contains
+    // item x is p = ((x + 1) G - 1) / W
     int pa = 0, pb = -1;
     if (V > 0) {
-      pa = (int)(((S + 1) * G - 1) / W);
-      pb = (int)(((S + V) * G - 1) / W);
+      const long long vs = S + seg;
+      pa = (int)(((vs + 1) * G - 1) / W);
+      pb = (int)(((vs + V) * G - 1) / W);
       if (pa == pb) continue;   // stored by its one workgroup
     }
     const int k0 = e[KV_K0] + e[KV_KTILE] * KEY_TILE;

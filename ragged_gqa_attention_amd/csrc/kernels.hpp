@@ -87,9 +87,11 @@ struct PlanArgs {
   // every key; see row_key_steps).
   float skip_log2;
   int* ksteps;          // [row tiles * 2] ranges the planner writes (AttnArgs::ksteps)
+  int* head_hw;         // [B * hq] key half-widths, when they do not fit the planner's LDS
   long long ds_images;  // dS images that fit the workspace (0: no stored dS)
   int fwd_slots;        // entries of plan.fwd_map (the row-tile launches' grid)
   int kv_wgs;           // dK/dV workgroups (the dK/dV launch's grid)
+  int seg_items;        // modelled fixed cost of a dK/dV segment, in 64-row steps
   uint16_t* zero;       // 512 bytes the planner clears
   Plan plan;
 };
@@ -117,22 +119,35 @@ constexpr float SKIP_UNDERFLOW = 160.0f;
 // neutral element of the min / max over a tile; rows whose slope is not a
 // positive finite number, or whose kept span reaches the sequence's ends,
 // keep every step.
+// Half-width ds = floor(thr / slope2) of the keys a row keeps, or -1 when it
+// keeps every key (no bound, a slope that is not a positive finite number, or
+// a span that reaches past Lk).  A key outside [centre - ds, centre + ds] has
+// |c - j| >= ds + 1 > thr / slope2.
+__device__ __forceinline__ int key_half_width(float slope2, int Lk, float thr) {
+  if (thr > 0.0f && slope2 > 0.0f) {   // false for NaN
+    const float span = thr / slope2;   // +inf for a tiny slope
+    if (span < (float)Lk) return (int)span;
+  }
+  return -1;
+}
+
+// Key steps of a row with the given centre and half-width (key_half_width).
+__device__ __forceinline__ void key_steps_of(int centre, int ds, int Lk, int& lo, int& hi) {
+  if (ds < 0) {
+    lo = 0;
+    hi = (Lk + TILE_ROWS - 1) / TILE_ROWS;
+  } else {
+    lo = max(0, centre - ds) / TILE_ROWS;
+    hi = min(Lk - 1, centre + ds) / TILE_ROWS + 1;
+  }
+}
+
 __device__ __forceinline__ void row_key_steps(bool exists, float slope2, int centre, int Lk,
                                               float thr, int& lo, int& hi) {
   lo = 0x7fffffff;
   hi = 0;
   if (!exists) return;
-  lo = 0;
-  hi = (Lk + TILE_ROWS - 1) / TILE_ROWS;
-  if (thr > 0.0f && slope2 > 0.0f) {   // false for NaN
-    const float span = thr / slope2;   // +inf for a tiny slope
-    if (span < (float)Lk) {
-      // a key outside [centre - ds, centre + ds] has |c - j| >= ds + 1 > span
-      const int ds = (int)span;
-      lo = max(0, centre - ds) / TILE_ROWS;
-      hi = min(Lk - 1, centre + ds) / TILE_ROWS + 1;
-    }
-  }
+  key_steps_of(centre, key_half_width(slope2, Lk, thr), Lk, lo, hi);
 }
 
 // Planner (one workgroup) and, alongside it, the transposed key tiles a.kt and /

@@ -38,7 +38,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   __shared__ long long red[PLAN_WAVES];
   __shared__ int part[PLAN_WAVES];
   __shared__ int l_seq[PLAN_LDS_B * SEQ_FIELDS];
-  __shared__ float l_slopes[PLAN_LDS_SLOPES];
+  __shared__ int l_hw[PLAN_LDS_HEADS];
   __shared__ int l_class[PLAN_COST_CLASSES + 1], l_foff_c[PLAN_COST_CLASSES];
   const int tid = threadIdx.x;
   const int B = a.batch;
@@ -85,10 +85,11 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
                               (seq[(B - 1) * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE
                         : 0;
 
-  // Key-step range of every row tile (see tile_key_steps), from the slopes
-  // (staged in LDS, all loads in flight at once, when they fit).
-  const bool cached = (long long)B * hq <= PLAN_LDS_SLOPES;
-  if (cached) {
+  // Key-step range of every row tile (see tile_key_steps), from each head's
+  // key half-width (LDS when they fit, else the workspace; the slopes are
+  // read with eight loads in flight per thread).
+  int* hw = (long long)B * hq <= PLAN_LDS_HEADS ? l_hw : a.head_hw;
+  {
     constexpr int PER = 8;
     for (int i0 = 0; i0 < B * hq; i0 += PLAN_THREADS * PER) {
       float v[PER];
@@ -101,11 +102,13 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
         const int i = i0 + k * PLAN_THREADS + tid;
-        if (i < B * hq) l_slopes[i] = v[k];
+        if (i < B * hq)
+          hw[i] = key_half_width(v[k] * LOG2E, seq[(i / hq) * SEQ_FIELDS + SQ_LK], a.skip_log2);
       }
     }
   }
   for (int i = tid; i <= PLAN_COST_CLASSES; i += PLAN_THREADS) l_class[i] = 0;
+  __threadfence_block();
   __syncthreads();
   auto seq_of_tile = [&](int g) {
     return last_at_most(B, g, [&](int x) { return seq[x * SEQ_FIELDS + SQ_RTOFF]; });
@@ -114,8 +117,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
     const int b = seq_of_tile(g);
     const int* s = seq + b * SEQ_FIELDS;
     int lo, hi;
-    if (cached) tile_key_steps(a, s, g - s[SQ_RTOFF], l_slopes + b * hq, 1, lo, hi);
-    else tile_key_steps(a, s, g - s[SQ_RTOFF], a.slopes + (int64_t)b * a.slopes_stride, 1, lo, hi);
+    tile_key_steps(s, g - s[SQ_RTOFF], hw + b * hq, lo, hi);
     a.ksteps[2 * g] = lo;
     a.ksteps[2 * g + 1] = hi;
     // class 0 holds the longest tiles

@@ -57,13 +57,12 @@ __device__ __forceinline__ void block_exclusive_scan(int B, F count, G put, V* p
 // every key tile (the dK/dV kernel still skips, units just come out uneven).
 constexpr int PLAN_LDS_KT = 2048;
 
-// Key-step range [lo, hi) of row tile t of a sequence (record s, the slopes of
-// its heads at slopes[h * hstride]): min / max of
+// Key-step range [lo, hi) of row tile t of a sequence (record s; the
+// half-widths key_half_width of its heads at hw[h]): min / max of
 // row_key_steps over its rows.  For one head both bounds grow with the token
 // (the centre does), so each head the tile spans contributes its first and
 // its last row.
-__device__ __forceinline__ void tile_key_steps(const PlanArgs& a, const int* s, int t,
-                                               const float* slopes, int64_t hstride, int& lo,
+__device__ __forceinline__ void tile_key_steps(const int* s, int t, const int* hw, int& lo,
                                                int& hi) {
   const int Lq = s[SQ_LQ], Lk = s[SQ_LK], rows = s[SQ_ROWS];
   const int R0 = t * ROW_TILE, R1 = min(rows, R0 + ROW_TILE);
@@ -73,10 +72,9 @@ __device__ __forceinline__ void tile_key_steps(const PlanArgs& a, const int* s, 
   for (int h = hfirst; h <= hlast; ++h) {
     const int ia = h == hfirst ? R0 - h * Lq : 0;
     const int ib = h == hlast ? R1 - 1 - h * Lq : Lq - 1;
-    const float slope2 = slopes[h * hstride] * LOG2E;
     int l0, u0, l1, u1;
-    row_key_steps(true, slope2, max(ia + Lk - Lq, 0), Lk, a.skip_log2, l0, u0);
-    row_key_steps(true, slope2, max(ib + Lk - Lq, 0), Lk, a.skip_log2, l1, u1);
+    key_steps_of(max(ia + Lk - Lq, 0), hw[h], Lk, l0, u0);
+    key_steps_of(max(ib + Lk - Lq, 0), hw[h], Lk, l1, u1);
     lo = min(lo, l0);
     hi = max(hi, u1);
   }
@@ -93,22 +91,26 @@ __device__ __forceinline__ int last_at_most(int n, int x, F key) {
   return lo;
 }
 
-// Slopes the prep planner stages in LDS while it evaluates tile ranges
-// (batches with more (sequence, head) pairs read them from global memory).
-constexpr int PLAN_LDS_SLOPES = 4096;
+// Per-head key half-widths the prep planner keeps in LDS while it evaluates
+// tile ranges (batches with more (sequence, head) pairs keep them in the
+// workspace).
+constexpr int PLAN_LDS_HEADS = 4096;
 
 // dK/dV work split, planned by one workgroup of NT threads from the row
 // tiles' key-step ranges in a.ksteps (seq: the sequence records).
 //
-// A 128-key tile is visited by the V row tiles whose range meets its two key
-// steps (counted with a difference array over the sequence's key tiles and a
-// prefix sum).  The visits of all key tiles, in batch order, form one list of
-// W items (key tile g holds items [S_g, S_g + V_g)); dK/dV workgroup p of
-// kv_wgs takes items [p W / kv_wgs, (p + 1) W / kv_wgs), so every workgroup
-// gets the same number of row tiles up to one.  Key tiles whose items fall to
-// several workgroups are summed from FP32 partials afterwards.  The planner
-// writes one record per key tile (KvField; a workgroup reads a record with
-// one load), the first key tile of every workgroup and W.
+// A 128-key tile is visited by the row tiles whose range meets its two key
+// steps; V counts their 64-row steps (a difference array over the sequence's
+// key tiles and a prefix sum).  The key tiles, in batch order, form one list
+// of W items: key tile g holds a_seg leading items that stand for the fixed
+// cost of starting a segment (loading K / V, the pipeline's first and last
+// steps), then its V visit steps, items [S_g, S_g + a_seg + V_g) (nothing when
+// V_g = 0).  dK/dV workgroup p of kv_wgs takes items [p W / kv_wgs,
+// (p + 1) W / kv_wgs), so the workgroups get near-equal modelled work.  Key
+// tiles whose visit steps fall to several workgroups are summed from FP32
+// partials afterwards.  The planner writes one record per key tile (KvField;
+// a workgroup reads a record with one load), the first key tile of every
+// workgroup, and W, the key tile count and a_seg in kv_head.
 struct UnitsShared {
   long long red[16];   // one slot per wave
   int part[16];
@@ -145,8 +147,11 @@ __device__ __forceinline__ void plan_units(const PlanArgs& a, const int* seq, Un
     const int lo = a.ksteps[2 * g], hi = a.ksteps[2 * g + 1];
     if (exact && hi > lo) {
       const int kt_lo = lo / 2, kt_hi = (hi - 1) / 2;   // key tiles of 2 key steps
-      atomicAdd(&l_kvis[s[SQ_KTOFF] + kt_lo], 1);
-      if (kt_hi + 1 < s[SQ_KTILES]) atomicAdd(&l_kvis[s[SQ_KTOFF] + kt_hi + 1], -1);
+      // 64-row steps of the tile (only a sequence's last tile has fewer than 4)
+      const int rest = s[SQ_ROWS] - (g - s[SQ_RTOFF]) * ROW_TILE;
+      const int steps = min(ROW_TILE / KV_ROW_STEP, (rest + KV_ROW_STEP - 1) / KV_ROW_STEP);
+      atomicAdd(&l_kvis[s[SQ_KTOFF] + kt_lo], steps);
+      if (kt_hi + 1 < s[SQ_KTILES]) atomicAdd(&l_kvis[s[SQ_KTOFF] + kt_hi + 1], -steps);
     }
   }
   __syncthreads();
@@ -162,10 +167,11 @@ __device__ __forceinline__ void plan_units(const PlanArgs& a, const int* seq, Un
   auto visits = [&](int g) {
     if (exact) return l_kvis[g];
     const int* s = seq + seq_of_ktile(g) * SEQ_FIELDS;
-    return (s[SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
+    return (s[SQ_ROWS] + KV_ROW_STEP - 1) / KV_ROW_STEP;
   };
+  auto items = [&](int g) { const int v = visits(g); return v > 0 ? v + a.seg_items : 0; };
   // key tile records; item starts S_g (kept in LDS when they fit)
-  block_exclusive_scan<NT>(nkt, visits, [&](int g, int s0) {
+  block_exclusive_scan<NT>(nkt, items, [&](int g, int s0) {
     if (g == nkt) {
       sh.total = s0;
       return;
@@ -186,6 +192,7 @@ __device__ __forceinline__ void plan_units(const PlanArgs& a, const int* seq, Un
   if (tid == 0) {
     a.plan.kv_head[0] = (int)W;
     a.plan.kv_head[1] = nkt;
+    a.plan.kv_head[3] = a.seg_items;
   }
   // first key tile of every workgroup's share (-1 for an empty share)
   for (int p = tid; p < a.kv_wgs; p += NT) {

@@ -94,6 +94,26 @@ def test_special_sequences():
     assert_lse(lse, ref["lse"], "special")
 
 
+def test_large_batch_planner_paths():
+    """300 sequences: the planner keeps its records in global memory (more
+    than 256 sequences), the per-head key half-widths in the workspace (more
+    than 4096 sequence-head pairs) and counts key-tile visits conservatively
+    (more than 2048 key tiles)."""
+    need_gpu()
+    rng = np.random.default_rng(17)
+    lq = rng.integers(0, 4, size=300)
+    lk = rng.integers(850, 1000, size=300)
+    wl = W.custom_workload(lq=lq.tolist(), lk=lk.tolist(), hq=64, dtype="bf16", width=160, step=1,
+                           seed=8)
+    assert sum((int(k) + 127) // 128 for k in lk) > 2048
+    g = wl.to("cuda")
+    got = gpu_full(g)
+    ref = oracle_full(wl)
+    for name in ("out", "dq", "dk", "dv"):
+        assert_close(name, to_np(got[name]), ref[name], TOL[wl.dtype], "large batch")
+    assert_lse(to_np(got["lse"]), ref["lse"], "large batch")
+
+
 def test_empty_batch():
     need_gpu()
     wl = W.custom_workload(lq=[0, 0], lk=[0, 0], hq=48)
