@@ -32,38 +32,44 @@ constexpr int PLAN_LDS_B = 256;
 // length go in the order the LDS atomics hand out, which only affects timing:
 // a tile's results do not depend on the workgroup that computes it.
 constexpr int PLAN_COST_CLASSES = 1024;
+// Row tiles whose sequence the planner looks up in an LDS table (the rest by
+// binary search).
+constexpr int PLAN_LDS_TILES = 4096;
 
 __device__ __forceinline__ void plan_block(const PlanArgs& a) {
-  __shared__ int bad;
   __shared__ long long red[PLAN_WAVES];
   __shared__ int part[PLAN_WAVES];
   __shared__ int l_seq[PLAN_LDS_B * SEQ_FIELDS];
   __shared__ int l_hw[PLAN_LDS_HEADS];
   __shared__ int l_class[PLAN_COST_CLASSES + 1], l_foff_c[PLAN_COST_CLASSES];
+  __shared__ int l_tseq[PLAN_LDS_TILES];
   const int tid = threadIdx.x;
   const int B = a.batch;
+  const int hq = a.hq;
   const bool in_lds = B <= PLAN_LDS_B;
   int* seq = in_lds ? l_seq : a.plan.seq;
 
-  if (tid == 0) bad = 0;
   if (tid < 32) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
-  __syncthreads();
-  for (int b = tid; b <= B; b += PLAN_THREADS) {
-    const int cq = a.cu_q[b], ck = a.cu_k[b];
-    bool fail = cq < 0 || (int64_t)cq > a.total_q || ck < 0 || (int64_t)ck > a.total_k;
-    if (b == 0) fail |= (cq != 0) || (ck != 0);
-    if (b == B) fail |= ((int64_t)cq != a.total_q) || ((int64_t)ck != a.total_k);
-    if (b < B) fail |= (a.cu_q[b + 1] < cq) || (a.cu_k[b + 1] < ck);
-    if (fail) bad = 1;   // benign race: every writer stores 1
+  // the slopes, requested first (their loads overlap those of the checks
+  // below); thread tid takes (sequence, head) pairs tid + 256 k
+  constexpr int SPER = PLAN_LDS_HEADS / PLAN_THREADS;
+  const bool hw_lds = (long long)B * hq <= PLAN_LDS_HEADS;
+  const int sb0 = tid / hq, sh0 = tid - sb0 * hq;   // pair tid
+  const int sdb = PLAN_THREADS / hq, sdh = PLAN_THREADS - sdb * hq;
+  float sv[SPER];
+  {
+    int b = sb0, h = sh0;
+#pragma unroll
+    for (int k = 0; k < SPER; ++k) {
+      sv[k] = hw_lds && b < B ? a.slopes[(int64_t)b * a.slopes_stride + h] : 0.0f;
+      b += sdb;
+      h += sdh;
+      if (h >= hq) { h -= hq; ++b; }
+    }
   }
-  __syncthreads();
-  const bool ok = bad == 0;
-  if (tid == 0) a.plan.flag[0] = ok ? 0 : 1;
-
-  // Per-sequence extents; an invalid batch plans every sequence as empty.
-  for (int b = tid; b < B; b += PLAN_THREADS) {
-    const int q0 = ok ? a.cu_q[b] : 0, lq = ok ? a.cu_q[b + 1] - q0 : 0;
-    const int k0 = ok ? a.cu_k[b] : 0, lk = ok ? a.cu_k[b + 1] - k0 : 0;
+  // checks of cu_q / cu_k and the per-sequence extents in one pass; an
+  // invalid batch is then planned with every sequence empty
+  auto extents = [&](int b, int q0, int lq, int k0, int lk) {
     int* s = seq + b * SEQ_FIELDS;
     s[SQ_Q0] = q0; s[SQ_LQ] = lq; s[SQ_K0] = k0; s[SQ_LK] = lk;
     s[SQ_ROWS] = lq * a.hq;
@@ -73,23 +79,58 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
     while (lq > 0 && (1u << sh) < (uint32_t)lq) ++sh;
     s[SQ_LQSHIFT] = (int)sh;
     s[SQ_LQMUL] = lq > 0 ? (int)(uint32_t)((((1ull << sh) - (uint64_t)lq) << 32) / (uint64_t)lq + 1) : 0;
+  };
+  bool bad = false;
+  for (int b = tid; b <= B; b += PLAN_THREADS) {
+    const int cq = a.cu_q[b], ck = a.cu_k[b];
+    const int nq = b < B ? a.cu_q[b + 1] : cq, nk = b < B ? a.cu_k[b + 1] : ck;
+    bool fail = cq < 0 || (int64_t)cq > a.total_q || ck < 0 || (int64_t)ck > a.total_k;
+    if (b == 0) fail |= (cq != 0) || (ck != 0);
+    if (b == B) fail |= ((int64_t)cq != a.total_q) || ((int64_t)ck != a.total_k);
+    if (b < B) fail |= (nq < cq) || (nk < ck);
+    bad |= fail;
+    // (a failed check leaves this sequence empty, so no length is negative)
+    if (b < B) {
+      if (fail) extents(b, 0, 0, 0, 0);
+      else extents(b, cq, nq - cq, ck, nk - ck);
+    }
   }
-  __syncthreads();
+  const bool ok = __syncthreads_or(bad) == 0;
+  if (tid == 0) a.plan.flag[0] = ok ? 0 : 1;
+  if (!ok) {
+    for (int b = tid; b < B; b += PLAN_THREADS) extents(b, 0, 0, 0, 0);
+    __syncthreads();
+  }
 
-  const int hq = a.hq;
-  // 256-row tiles in batch order (their key-step ranges are kept in this order)
+  // 256-row tiles in batch order (their key-step ranges are kept in this
+  // order); tile -> sequence in LDS when the tiles fit
   block_exclusive_scan<PLAN_THREADS>(B, [&](int b) {
     return (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
-  }, [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_RTOFF] = v; }, part);
+  }, [&](int b, int v) {
+    if (b >= B) return;
+    seq[b * SEQ_FIELDS + SQ_RTOFF] = v;
+    const int n = (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
+    for (int t = v; t < min(v + n, PLAN_LDS_TILES); ++t) l_tseq[t] = b;
+  }, part);
   const int nrt = B > 0 ? seq[(B - 1) * SEQ_FIELDS + SQ_RTOFF] +
                               (seq[(B - 1) * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE
                         : 0;
 
   // Key-step range of every row tile (see tile_key_steps), from each head's
-  // key half-width (LDS when they fit, else the workspace; the slopes are
-  // read with eight loads in flight per thread).
-  int* hw = (long long)B * hq <= PLAN_LDS_HEADS ? l_hw : a.head_hw;
-  {
+  // key half-width (LDS, from the slopes requested at the start, when they
+  // fit; else the workspace, eight slope loads in flight per thread).
+  int* hw = hw_lds ? l_hw : a.head_hw;
+  if (hw_lds) {
+    int b = sb0, h = sh0;
+#pragma unroll
+    for (int k = 0; k < SPER; ++k) {
+      if (b < B)
+        hw[b * hq + h] = key_half_width(sv[k] * LOG2E, seq[b * SEQ_FIELDS + SQ_LK], a.skip_log2);
+      b += sdb;
+      h += sdh;
+      if (h >= hq) { h -= hq; ++b; }
+    }
+  } else {
     constexpr int PER = 8;
     for (int i0 = 0; i0 < B * hq; i0 += PLAN_THREADS * PER) {
       float v[PER];
@@ -111,6 +152,7 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   __threadfence_block();
   __syncthreads();
   auto seq_of_tile = [&](int g) {
+    if (g < PLAN_LDS_TILES) return l_tseq[g];
     return last_at_most(B, g, [&](int x) { return seq[x * SEQ_FIELDS + SQ_RTOFF]; });
   };
   for (int g = tid; g < nrt; g += PLAN_THREADS) {
