@@ -459,9 +459,15 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   const long long W = a.plan.kv_head[0];
   const int nkt = a.plan.kv_head[1];
   const int seg = a.plan.kv_head[3];
-  const long long w0 = (long long)blockIdx.x * W / gridDim.x;
-  const long long w1 = (long long)(blockIdx.x + 1) * W / gridDim.x;
-  int gt = a.plan.wg_first[blockIdx.x];
+  // Workgroup i runs on XCD i % 8 (round-robin dispatch): it takes share
+  // (i % 8) * G / 8 + i / 8, so the shares of one XCD are consecutive and
+  // its workgroups walk neighbouring key tiles of the same sequences, whose
+  // Q / dO rows then come from that XCD's L2.
+  const int G = gridDim.x;
+  const int sh = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
+  const long long w0 = (long long)sh * W / G;
+  const long long w1 = (long long)(sh + 1) * W / G;
+  int gt = a.plan.wg_first[sh];
   if (w0 >= w1 || gt < 0) return;
   for (long long w = w0; w < w1 && gt < nkt; ++gt) {
     // lane and wave are re-derived per segment behind an empty asm, so the
@@ -487,10 +493,10 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.lqshift = e[KV_LQSHIFT];
     u.first = (int)f;
     u.last = (int)l;
-    // a key tile split over workgroups: partial slot 2 p for the workgroup's
-    // first key tile (its share starts at or after the key tile's items),
-    // 2 p + 1 for its last
-    u.part = (f == 0 && l == V) ? -1 : 2 * (int)blockIdx.x + (S <= w0 ? 0 : 1);
+    // a key tile split over shares: partial slot 2 sh for the share's first
+    // key tile (the share starts at or after the key tile's items), 2 sh + 1
+    // for its last
+    u.part = (f == 0 && l == V) ? -1 : 2 * sh + (S <= w0 ? 0 : 1);
     u.ds = a.ds ? e[KV_DSOFF] : -1;
     u.nks = (u.Lk + TILE_ROWS - 1) / TILE_ROWS;
     u.ksteps = a.ksteps + 2 * e[KV_RTOFF];
