@@ -237,17 +237,21 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     DqStoredShared d;
   } sm;
 
-  // Workgroups past the row tiles (the grid's tail) sum the split dK / dV
-  // partials, a slice each: they start as the row tiles drain and fill the
-  // compute units the last row tiles leave idle.
-  const int b = (int)blockIdx.x < a.fwd_slots ? a.plan.fwd_map[2 * blockIdx.x] : -1;
-  if (b < 0) {
-    const int first = a.batch > 0 ? a.plan.kv_head[2] : 0;   // row tiles
-    if (a.total_k > 0 && (int)blockIdx.x >= first)
-      reduce_kv_tiles<T>(a, blockIdx.x - first, gridDim.x - first);
+  // The grid holds the row-tile slots plus R workgroups that sum the split
+  // dK / dV partials, a slice each; those come right after the first round
+  // of row tiles (one per compute unit), so they run while the longest tiles
+  // do instead of lengthening the tail.
+  const int R = (int)gridDim.x - a.fwd_slots;
+  const int nrt = a.batch > 0 ? a.plan.kv_head[2] : 0;   // row tiles
+  const int at = min(nrt, a.kv_wgs);
+  if ((int)blockIdx.x >= at && (int)blockIdx.x < at + R) {
+    if (a.total_k > 0) reduce_kv_tiles<T>(a, blockIdx.x - at, R);
     return;
   }
-  const int tile = a.plan.fwd_map[2 * blockIdx.x + 1];
+  const int slot = (int)blockIdx.x < at ? (int)blockIdx.x : (int)blockIdx.x - R;
+  const int b = a.plan.fwd_map[2 * slot];
+  if (b < 0) return;
+  const int tile = a.plan.fwd_map[2 * slot + 1];
   const int* sq = a.plan.seq + b * SEQ_FIELDS;
   const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
   const int klo = ks[0], khi = ks[1];
