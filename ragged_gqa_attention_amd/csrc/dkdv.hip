@@ -84,6 +84,7 @@ struct TileMask {
 };
 
 __device__ __forceinline__ void tile_mask_load(TileMask& m, const KvUnit& u, int base, int lane) {
+  asm volatile("" : "+v"(lane));   // (per call: no hoisted per-lane addresses)
   const int t = base + lane;
   bool on = false;
   if (t <= m.last) {
@@ -184,18 +185,25 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // also copies the 64 row records.
   const int lgroup = wave & 3;            // 16-row group this wave copies
   const int ltensor = wave >> 2;          // 0: Q, 1: dO
-  const int lrow = 16 * lgroup + (lane >> 2);
-  const int lchunk = (lane & 3) ^ ((lane >> 4) & 3);
   auto issue_loads = [&](int r0, int buf) {
+    // the lane's row and chunk are recomputed per step (an empty asm keeps
+    // the compiler from hoisting them into registers it would then spill)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lrow = 16 * lgroup + (ln >> 2);
+    const int lchunk = (ln & 3) ^ ((ln >> 4) & 3);
     if (wave == 0) {
       const int R = r0 + lane;
       const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, re - 1)) * 4;
-      load_lds16(R < re ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
+      load_lds16_unseen(R < re ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
     }
     const int R = r0 + lrow;
     const int Rc = min(R, re - 1);
     int tok_, h_;
-    unfold_row(Rc, u.lq, (uint32_t)u.lqmul, (uint32_t)u.lqshift, tok_, h_);
+    // (uniform: kept in scalar registers rather than spilled vector ones)
+    unfold_row(Rc, __builtin_amdgcn_readfirstlane(u.lq),
+               (uint32_t)__builtin_amdgcn_readfirstlane(u.lqmul),
+               (uint32_t)__builtin_amdgcn_readfirstlane(u.lqshift), tok_, h_);
     const uint32_t tok = (uint32_t)tok_, h = (uint32_t)h_;
     const uint32_t t_abs = (uint32_t)u.q0 + tok;
     const bool ok = R < re;
@@ -205,7 +213,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     const uint16_t* src = (ok ? base + ((uint64_t)t_abs * ts + (uint64_t)h * hs) : a.zero) + lchunk * 8;
 #pragma unroll
     for (int p = 0; p < LOADS_PER_WAVE; ++p)
-      load_lds16(src + p * 32, &sm.qd[buf][ltensor][(lgroup * LOADS_PER_WAVE + p) * BLK_ELEMS]);
+      load_lds16_unseen(src + p * 32, &sm.qd[buf][ltensor][(lgroup * LOADS_PER_WAVE + p) * BLK_ELEMS]);
   };
 
   // Lane-constant LDS offsets (elements).  Row reads of the S / dP A operand:
@@ -366,6 +374,13 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     if (r >= re) return re;
     return (r & (ROW_TILE - 1)) != 0 ? r : tile_start(r / ROW_TILE);
   };
+  // End of a step: the next step's copies (requested before this step's
+  // dS stores, the wave's last 2 KB of vector memory operations) have landed.
+  // The stores need not have: nothing in the kernel reads the images.
+  auto wait_step_loads = [&]() {
+    if (ds_on) wait_vm_le<2 * KB>();
+    else wait_vm();
+  };
   int rn = rb;   // rows of the step after the current one (the first tile is visited)
   if (rn < re) {
     const int r0 = rn;
@@ -377,7 +392,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     f32x16 S[KB], dP[KB];
     scores(0, S, dP);
     pointwise_publish(0, 0, r0, S, dP, mine);
-    wait_vm();
+    wait_step_loads();
     __syncthreads();
     int prev = 0, cur = 1, next = 2;   // buffers of steps n - 1, n, n + 1
     int n = 1;
@@ -400,7 +415,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) { mine[kb][0] = own[kb][0]; mine[kb][1] = own[kb][1]; }
       }
-      wait_vm();
+      wait_step_loads();
       __syncthreads();
       const int t = prev;
       prev = cur;

@@ -97,6 +97,23 @@ __device__ __forceinline__ void load_lds16(const void* src, void* wave_dst) {
                                    16, 0, 0);
 }
 
+// The same copy, issued where the compiler does not see it.  The compiler
+// orders every LDS read it cannot tell apart from a pending direct load after
+// that load (and, as vector memory operations complete in issue order, after
+// everything issued before it), which defeats a prefetch into one buffer of a
+// ring while another is being read.  Callers of this form must themselves
+// wait (wait_vm / wait_vm_le, then a barrier) before any wave reads the bytes.
+__device__ __forceinline__ void load_lds16_unseen(const void* src, void* wave_dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(lds_void_t*)wave_dst);
+  // M0 holds the LDS base of the copy; one wait state between the M0 write
+  // and the copy that reads it
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "m0");
+}
+
 // Wait for this wave's outstanding global loads (direct LDS loads included).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // Wait until at most N of this wave's vector memory operations are
