@@ -169,16 +169,19 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   // three and waves 4-7 two of the 20 K^T loads (7 or 6 per wave)
   constexpr int IMG_LOADS = DS_IMAGE_ELEMS / BLK_ELEMS / ROW_WAVES;
   static_assert(IMG_LOADS == 4, "waits below count 4 + 3 or 4 + 2 loads per step");
+  // (issued unseen by the compiler, which would otherwise hold each step's
+  // transposing reads until the copies of the two steps ahead had landed;
+  // the waits below order the buffers)
   auto issue = [&](int kt, int buf) {
     const uint16_t* img = img0 + (int64_t)kt * DS_IMAGE_ELEMS;
 #pragma unroll
     for (int j = 0; j < IMG_LOADS; ++j) {
       const int blk = IMG_LOADS * wave + j;
-      load_lds16(img + blk * BLK_ELEMS + lane * 8, sm.ds[buf] + blk * BLK_ELEMS);
+      load_lds16_unseen(img + blk * BLK_ELEMS + lane * 8, sm.ds[buf] + blk * BLK_ELEMS);
     }
     const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
-    if (wave < 4) load_tt_tile<3>(sm.kt[buf], ktt, 3 * wave, lane);
-    else load_tt_tile<2>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
+    if (wave < 4) load_tt_tile<3, true>(sm.kt[buf], ktt, 3 * wave, lane);
+    else load_tt_tile<2, true>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
   };
 
   // transposing reads (see read_tr): lane (i, G) addresses key rows

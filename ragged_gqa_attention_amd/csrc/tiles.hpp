@@ -142,7 +142,8 @@ __device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* sr
 
 // Copies wave loads [i0, i0 + n) of a transposed key tile (20 loads of 8
 // feature rows each) from its global copy `src` (160 x 64 elements, unswizzled).
-template <int N>
+// UNSEEN: issue them as load_lds16_unseen.
+template <int N, bool UNSEEN = false>
 __device__ __forceinline__ void load_tt_tile(uint16_t* tile, const uint16_t* src, int i0, int lane) {
   const int dl = lane >> 3, pc = lane & 7;
 #pragma unroll
@@ -150,7 +151,8 @@ __device__ __forceinline__ void load_tt_tile(uint16_t* tile, const uint16_t* src
     const int i = i0 + n;
     const int d = 8 * i + dl;
     const int c = pc ^ ((d >> 1) & 7);
-    load_lds16(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
+    if (UNSEEN) load_lds16_unseen(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
+    else load_lds16(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
   }
 }
 
