@@ -36,8 +36,8 @@ constexpr size_t ALIGN = 256;
 constexpr int MAX_DEVICES = 64;
 // Fixed cost of a dK/dV segment (K / V loads, the pipeline's unoverlapped
 // first and last steps, the stores) in 64-row steps, for the work split; about
-// 12 us against about 3 us per step, measured on the Hq = 64 workload.
-constexpr int KV_SEGMENT_ITEMS = 4;
+// 15 us against about 2.9 us per step, measured on the Hq = 64 workload.
+constexpr int KV_SEGMENT_ITEMS = 5;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
