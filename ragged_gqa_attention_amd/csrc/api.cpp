@@ -60,7 +60,7 @@ int device_cus() {
 
 struct Layout {
   size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps, head_hw;
-  size_t lse, rowinfo, part_dk, part_dv, kt, vt;
+  size_t lse, rowinfo, part_dk, part_dv, kt;
   size_t total;
   int64_t kv_wgs;       // dK/dV workgroups (one per compute unit)
   int64_t row_tiles;
@@ -93,9 +93,8 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.head_hw = take(sizeof(int) * (size_t)B * p->hq);
-  L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = L.vt = 0;
+  L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = 0;
   const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
-  if (entry != ATTN_ENTRY_BWD) L.vt = take(tt_bytes);   // V^T for the forward
   if (entry != ATTN_ENTRY_FWD) L.kt = take(tt_bytes);   // K^T for dQ
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
@@ -244,7 +243,6 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.ksteps = reinterpret_cast<int*>(base + L.ksteps);
   a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
   if (L.kt) a.kt = reinterpret_cast<uint16_t*>(base + L.kt);
-  if (L.vt) a.vt = reinterpret_cast<uint16_t*>(base + L.vt);
   if (L.rowinfo) a.rowinfo = reinterpret_cast<float*>(base + L.rowinfo);
   if (L.part_dk) {
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);

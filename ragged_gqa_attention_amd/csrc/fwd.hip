@@ -12,9 +12,10 @@
 // rows reuse each staged K/V tile 256 times.  Each wave owns 32 rows and forms
 // S^T = K Q^T (keys x rows, Q in registers), so an accumulator lane owns one row
 // and O^T = V^T P^T keeps the row scale per lane.  Key steps of 64 are copied
-// to LDS with direct loads (double-buffered): K as a row tile, V as its
-// pre-transposed key tile, so both products read their LDS operand with one
-// 16-byte read per MFMA.
+// to LDS with direct loads (three buffers), K and V as row tiles: S^T reads
+// its K operand with one 16-byte read per MFMA, P V its V^T operand with two
+// transposing reads (ds_read_b64_tr_b16), so the forward needs no transposed
+// copy of V.
 //
 // Softmax offset.  Distances are measured from the clamped centre
 // c_i = max(i + Lk - Lq, 0): for a row with i + Lk - Lq < 0 every key lies to
@@ -44,13 +45,13 @@ namespace rga {
 
 namespace {
 
-// LDS of a key step: the K rows (row tile, blk_off) and V^T (transposed key
-// tile, tt_off), three buffers (one step in flight, one being read, and the
-// previous one still read by the deferred half of the lag waves).
+// LDS of a key step: the K and V rows (row tiles, blk_off), three buffers
+// (one step in flight, one being read, and the previous one still read by the
+// deferred half of the lag waves).
 constexpr int FWD_NBUF = 3;
 struct FwdShared {
   uint16_t k[FWD_NBUF][TILE_ELEMS];
-  uint16_t vt[FWD_NBUF][TILE_ELEMS];
+  uint16_t v[FWD_NBUF][TILE_ELEMS];
 };
 // After the key loop the same LDS holds the normalised O rows (pitch of 168
 // elements) and each row's record.
@@ -113,25 +114,29 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   // key steps [klo, khi) some row of the tile keeps (the planner's range)
   const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
   const int klo = ks[0], khi = ks[1];
-  const uint16_t* vt_seq = a.vt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
-  // copies of key step kt: waves 0-3 the K rows (one 16-row group each),
-  // waves 4-7 V^T (five 8-feature-row loads each)
+  // copies of key step kt: waves 0-3 the K rows, waves 4-7 the V rows (one
+  // 16-row group each); keys past Lk read zeros.  Issued unseen by the
+  // compiler (it would hold the step's transposing reads until the next
+  // step's copies had landed); advance() orders the buffers.
   auto issue = [&](int kt, int buf) {
     if (wave < 4)
-      load_row_tile(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
-                    wave, lane);
+      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
+                          a.zero, wave, lane);
     else
-      load_tt_tile<5>(sm.vt[buf], vt_seq + (int64_t)kt * TILE_ELEMS, 5 * (wave - 4), lane);
+      load_row_tile<true>(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
+                          a.zero, wave - 4, lane);
   };
 
   // lane-constant LDS offsets: K row reads (row kb * 32 + l32, chunk 2 ks + g)
-  // and V^T reads (feature row 32 db + l32, chunk 2 (2 kb + s) + g)
+  // and transposing V reads (see read_tr): lane (i, G) addresses key rows
+  // 4 (G/2) + i/4 and + 8 of a 16-key k-step, chunk 2 (G%2) + (i%4)/2 of a
+  // 32-feature block, the low or high half of its 16 bytes by i % 2
   const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
-  int voff[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) voff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
+  const int vi = lane & 15, vG = lane >> 4;
+  const int vrow = 4 * (vG >> 1) + (vi >> 2);
+  const int vcl = 2 * (vG & 1) + ((vi & 3) >> 1);
+  const int voff_lo = blk_off(vrow, vcl) + 4 * (vi & 1);
+  const int voff_hi = blk_off(vrow + 8, vcl) + 4 * (vi & 1);
 
   // S^T[key][row] = K Q^T (lane = row) for key block kb of the K tile Kb
   // (LDS operands are read two k-steps ahead of the MFMA that uses them)
@@ -190,10 +195,16 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
       for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
     }
   };
-  // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb of the V^T
-  // tile Vb; the V^T operand is one 16-byte read in the key order of pb
+  // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb of the V row
+  // tile Vb; product i = 2 db + s takes features 32 db .. + 31 and the
+  // 16-key k-step 2 kb + s, read transposed in the key order of pb
   auto pv = [&](int kb, const uint16_t* Vb) {
-    auto vop = [&](int i) { return load16(Vb + voff[kb][i & 1] + (i >> 1) * 32 * TILE_ROWS); };
+    auto vop = [&](int i) {
+      const int off = ((2 * kb + (i & 1)) * BLK_COLS + (i >> 1)) * BLK_ELEMS;
+      const u32x2 lo = read_tr(Vb + voff_lo + off);
+      const u32x2 hi = read_tr(Vb + voff_hi + off);
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
     u32x4 va[3];
     va[0] = vop(0);
     va[1] = vop(1);
@@ -229,7 +240,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     // (lag) defers block 1 of each step into the next one: (logits/P 1 | PV1
     // of the previous step) S0 S1 | logits/P 0 | PV0, so its VALU work falls on
     // the lead wave's products and the other way round.  A deferred block reads
-    // the previous step's V^T, hence three LDS buffers.
+    // the previous step's V tile, hence three LDS buffers.
     auto run = [&](auto lag) {
       constexpr bool LAG = decltype(lag)::value;
       auto step = [&](int kt, auto mk) {
@@ -237,17 +248,17 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
         if (LAG && kt > klo) {   // the previous step is a full one
           logits(1, kbase - TILE_ROWS, unmasked);
           probs(1);
-          pv(1, sm.vt[(kt - 1) % FWD_NBUF]);
+          pv(1, sm.v[(kt - 1) % FWD_NBUF]);
         }
         scores(0, sm.k[buf]);
         scores(1, sm.k[buf]);
         logits(0, kbase, mk);
         probs(0);
-        pv(0, sm.vt[buf]);
+        pv(0, sm.v[buf]);
         if (!LAG) {
           logits(1, kbase, mk);
           probs(1);
-          pv(1, sm.vt[buf]);
+          pv(1, sm.v[buf]);
         }
       };
       for (int kt = klo; kt < kfull; ++kt) {
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
         if (partial) logits(1, kt * TILE_ROWS, masked);
         else logits(1, kt * TILE_ROWS, unmasked);
         probs(1);
-        pv(1, sm.vt[kt % FWD_NBUF]);
+        pv(1, sm.v[kt % FWD_NBUF]);
       }
     };
     if (wave < 4) run(Flag<false>{});
@@ -295,8 +306,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
         for (int r = 0; r < 16; ++r) S[kb][r] -= mnew;
       probs(0);
       probs(1);
-      pv(0, sm.vt[buf]);
-      pv(1, sm.vt[buf]);
+      pv(0, sm.v[buf]);
+      pv(1, sm.v[buf]);
     };
     for (int kt = klo; kt < kfull; ++kt) {
       advance(kt);

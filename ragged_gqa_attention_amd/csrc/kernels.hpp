@@ -45,10 +45,9 @@ struct AttnArgs {
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;
   const uint16_t* zero; // 512 zero bytes: source of the loads of rows past a tile's end
-  // Transposed 64-key tiles of K and V (see tt_key_pos), tile i at i * 64 * 160:
-  // [feature][key], written by transpose_keys_kernel; keys past Lk are zero.
+  // Transposed 64-key tiles of K (see tt_key_pos), tile i at i * 64 * 160:
+  // [feature][key], written by the prep kernel for dQ; keys past Lk are zero.
   uint16_t* kt;
-  uint16_t* vt;
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
   // dS images written by dK/dV and read by dQ for the sequences the planner
@@ -150,8 +149,8 @@ __device__ __forceinline__ void row_key_steps(bool exists, float slope2, int cen
   key_steps_of(centre, key_half_width(slope2, Lk, thr), Lk, lo, hi);
 }
 
-// Planner (one workgroup) and, alongside it, the transposed key tiles a.kt and /
-// or a.vt (null pointers are skipped), up to key_tiles tiles each.
+// Planner (one workgroup) and, alongside it, the transposed key tiles a.kt (a
+// null pointer skips them), up to key_tiles tiles.
 hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s);
 // Forward over the a.fwd_slots row-tile slots; plan_units adds the workgroup
 // that plans the dK/dV units (from pa) alongside.

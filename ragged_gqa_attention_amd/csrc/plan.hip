@@ -210,8 +210,8 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a) {
   }
 }
 
-// Transposed key tile `tile` of K and of V (see tt_key_pos; null outputs are
-// skipped): keys [64 j, 64 j + 64) of the sequence whose tiles start at or
+// Transposed key tile `tile` of K (see tt_key_pos; read by the dQ kernel):
+// keys [64 j, 64 j + 64) of the sequence whose tiles start at or
 // before `tile` (j = tile - first tile, tiles counted as in the planner's
 // SQ_TTOFF); keys past Lk become zeros.  The sequence is found from cu_k
 // directly, so this runs alongside the planner: wave 0 checks cu_k and scans
@@ -222,7 +222,7 @@ __device__ __forceinline__ void transpose_tiles(const PlanArgs& pa, const AttnAr
   __shared__ __attribute__((aligned(16))) uint16_t rows[TILE_ROWS][HEAD_DIM + 8];
   __shared__ int s_b, s_j;
   const int B = pa.batch;
-  if ((!a.kt && !a.vt) || B <= 0) return;
+  if (!a.kt || B <= 0) return;
   const int tid = threadIdx.x;
   if (tid < 64) {
     const int lane = tid;
@@ -268,19 +268,15 @@ __device__ __forceinline__ void transpose_tiles(const PlanArgs& pa, const AttnAr
   const int Lk = pa.cu_k[b + 1] - k0;
   const int kbase = k0 + j * TILE_ROWS;
   const int nkeys = min(TILE_ROWS, Lk - j * TILE_ROWS);
-  for (int t = 0; t < 2; ++t) {
-    uint16_t* dst = t ? a.vt : a.kt;
-    if (!dst) continue;
-    const uint16_t* src = t ? a.v : a.k;
-    const int64_t ts = t ? a.v_ts : a.k_ts;
+  {
     for (int i = tid; i < TILE_ROWS * CHUNKS; i += PLAN_THREADS) {
       const int key = i / CHUNKS, c = i - key * CHUNKS;
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (key < nkeys) x = load16(src + (int64_t)(kbase + key) * ts + c * 8);
+      if (key < nkeys) x = load16(a.k + (int64_t)(kbase + key) * a.k_ts + c * 8);
       *reinterpret_cast<u32x4*>(&rows[key][c * 8]) = x;
     }
     __syncthreads();
-    dst += (int64_t)tile * TILE_ELEMS;
+    uint16_t* dst = a.kt + (int64_t)tile * TILE_ELEMS;
     // task: feature pair (2 dp, 2 dp + 1) x chunk c of 8 keys
     for (int o = tid; o < (HEAD_DIM / 2) * (TILE_ROWS / 8); o += PLAN_THREADS) {
       const int dp = o / (TILE_ROWS / 8), c = o - dp * (TILE_ROWS / 8);
@@ -308,7 +304,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void prep_kernel(const PlanArgs pa, c
 }
 
 hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s) {
-  const int transposers = (a.kt || a.vt) ? key_tiles : 0;
+  const int transposers = a.kt ? key_tiles : 0;
   hipLaunchKernelGGL(prep_kernel, 1 + transposers, PLAN_THREADS, 0, s, pa, a);
   return hipGetLastError();
 }

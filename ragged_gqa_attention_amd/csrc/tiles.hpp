@@ -14,10 +14,10 @@
 //    contracts over features) or with the transposing read (the operand of a
 //    product that contracts over rows).
 //  * Transposed key tile: 160 feature rows x 64 keys, written once per call
-//    into the workspace by transpose_keys_kernel with the keys of each
-//    16-key group permuted (tt_key_pos) so that one 16-byte read gives a lane
+//    into the workspace by the prep kernel with the keys of each 16-key
+//    group permuted (tt_key_pos) so that one 16-byte read gives a lane
 //    exactly the keys that the accumulator layout of P / dS assigns it.  It
-//    replaces the transposing read for K^T (dQ) and V^T (P V).
+//    replaces the transposing read for K^T in dQ.
 //
 // Rows at or past a sequence's end are loaded from a zero block: the padding
 // of the packed views is arbitrary (NaN in the tests) and 0 * NaN would poison
@@ -127,7 +127,9 @@ __device__ __forceinline__ void wait_vm_le() {
 // Copies the blocked row tile of rows [row0, row0 + 64) of a strided
 // [tokens, 160] view (rows past `nrows` read `zero`) with four waves: wave
 // group w (0..3) copies rows 16 w .. 16 w + 15, lane l holding row
-// 16 w + l / 4 for all five of its loads.
+// 16 w + l / 4 for all five of its loads.  UNSEEN: issue them as
+// load_lds16_unseen.
+template <bool UNSEEN = false>
 __device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* src, int64_t ts,
                                               int row0, int nrows, const uint16_t* zero,
                                               int w, int lane) {
@@ -136,8 +138,10 @@ __device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* sr
   const bool ok = row0 + r < nrows;
   const uint16_t* p = (ok ? src + (int64_t)(row0 + r) * ts : zero) + c * 8;
 #pragma unroll
-  for (int b = 0; b < BLK_COLS; ++b)
-    load_lds16(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
+  for (int b = 0; b < BLK_COLS; ++b) {
+    if (UNSEEN) load_lds16_unseen(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
+    else load_lds16(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
+  }
 }
 
 // Copies wave loads [i0, i0 + n) of a transposed key tile (20 loads of 8
