@@ -60,12 +60,11 @@ int device_cus() {
 
 struct Layout {
   size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps, head_hw;
-  size_t lse, rowinfo, part_dk, part_dv, kt;
+  size_t lse, rowinfo, part_dk, part_dv;
   size_t total;
   int64_t kv_wgs;       // dK/dV workgroups (one per compute unit)
   int64_t row_tiles;
   int64_t kv_tiles;     // upper bound of the 128-key tiles
-  int64_t key_tiles;    // upper bound of the transposed 64-key tiles
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -77,7 +76,6 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.row_tiles = ceil_div(rows, ROW_TILE) + B;
   L.kv_tiles = ceil_div(p->total_k, KEY_TILE) + B;
   L.kv_wgs = cus;
-  L.key_tiles = ceil_div(p->total_k, TILE_ROWS) + B;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -93,9 +91,7 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.head_hw = take(sizeof(int) * (size_t)B * p->hq);
-  L.lse = L.rowinfo = L.part_dk = L.part_dv = L.kt = 0;
-  const size_t tt_bytes = sizeof(uint16_t) * (size_t)L.key_tiles * TILE_ELEMS;
-  if (entry != ATTN_ENTRY_FWD) L.kt = take(tt_bytes);   // K^T for dQ
+  L.lse = L.rowinfo = L.part_dk = L.part_dv = 0;
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
     L.rowinfo = take(sizeof(float) * 4 * rows);
@@ -242,12 +238,12 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   char* base = static_cast<char*>(ws);
   a.ksteps = reinterpret_cast<int*>(base + L.ksteps);
   a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
-  if (L.kt) a.kt = reinterpret_cast<uint16_t*>(base + L.kt);
   if (L.rowinfo) a.rowinfo = reinterpret_cast<float*>(base + L.rowinfo);
   if (L.part_dk) {
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
     a.part_dv = reinterpret_cast<float*>(base + L.part_dv);
   }
+  std::memset(&pa, 0, sizeof(pa));
   pa.cu_q = p->cu_q;
   pa.cu_k = p->cu_k;
   pa.slopes = p->alibi_slopes;
@@ -276,11 +272,11 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   return ATTN_OK;
 }
 
-// Planner plus the transposed key tiles the entry needs (after the views are set).
+// The planner as a launch of its own (after the views are set).
 attn_status launch_prep_phase(const PlanArgs& pa, const AttnArgs& a, const Layout& L,
                               hipStream_t s, const hipEvent_t* ev = nullptr) {
   RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
-  return hip_status(launch_prep(pa, a, (int)L.key_tiles, s), "plan launch");
+  return hip_status(launch_prep(pa, s), "plan launch");
 }
 
 attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
@@ -365,9 +361,9 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   set_view(v, &a.v, &a.v_ts, nullptr);
   set_view(out, &a.out, &a.o_ts, &a.o_hs);
   a.lse = lse;
-  RGA_TRY(launch_prep_phase(pa, a, L, s));
-  if (p->batch == 0) return ATTN_OK;
-  return hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, false, false, s),
+  // an empty batch still runs the planner (it records the cu_q / cu_k check)
+  if (p->batch == 0) return launch_prep_phase(pa, a, L, s);
+  return hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, false, s),
                     "forward launch");
 }
 
@@ -443,11 +439,17 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
   set_view(dk, &a.dk, &a.dk_ts, nullptr);
   set_view(dv, &a.dv, &a.dv_ts, nullptr);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
-  RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
-  RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
-  if (p->batch > 0)
-    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, true, s),
+  // the planner runs inside the forward's grid (the plan phase is empty); an
+  // empty batch runs the planner alone
+  if (p->batch == 0) {
+    RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
+    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+  } else {
+    RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
+    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, s),
                        "forward launch"));
+  }
   RGA_TRY(launch_backward(p, a, L, s, ev));
   if (p->batch == 0) {
     RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));

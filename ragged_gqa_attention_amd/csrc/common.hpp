@@ -12,8 +12,8 @@
 // When a result tile D is reused as a B operand of the next product (P or dS
 // feeding PV / dQ / dK / dV), the sixteen k-values a lane owns are not the
 // canonical 8g..8g+7 but {16s + 4g + 0..3, 16s + 8 + 4g + 0..3} for k-step
-// s = 0, 1.  The matching A operand is read with the same permutation from a
-// transposed LDS tile, so the contraction is unchanged.
+// s = 0, 1.  The matching A operand is read in the same order with the
+// transposing LDS read (see read_tr), so the contraction is unchanged.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -125,7 +125,6 @@ struct LogitConsts {
 enum SeqField {
   SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS,
   SQ_KTILES,  // 128-key tiles of the sequence (dK/dV)
-  SQ_TTOFF,   // first 64-key transposed tile of the sequence (prefix of ceil(Lk / 64))
   SQ_DSOFF,   // first stored dS image of the sequence, -1 when its dS is not stored
   SQ_KTOFF,   // first 128-key tile of the sequence in batch order (prefix of SQ_KTILES)
   SQ_LQMUL,   // fast_div constants of Lq (folded rows are head-major, see unfold_row)
@@ -168,6 +167,15 @@ struct Plan {
 // multiplication", 1994): shift = ceil(log2 d), mul = floor(2^32 (2^shift - d) / d) + 1.
 __device__ __forceinline__ int fast_div(int n, uint32_t mul, uint32_t shift) {
   return (int)((__umulhi((uint32_t)n, mul) + (uint32_t)n) >> shift);
+}
+
+// fast_div constants of d >= 0 (d = 0 gives zeros; nothing divides by it):
+// n / d = (umulhi(n, mul) + n) >> shift.
+__device__ __forceinline__ void fast_div_consts(int d, uint32_t& mul, uint32_t& shift) {
+  uint32_t sh = 0;
+  while (d > 0 && (1u << sh) < (uint32_t)d) ++sh;
+  shift = sh;
+  mul = d > 0 ? (uint32_t)((((1ull << sh) - (uint64_t)d) << 32) / (uint64_t)d + 1) : 0u;
 }
 
 // Folded row R of a sequence -> (token i, head h).  The Lq x Hq rows are

@@ -17,8 +17,8 @@
 //
 // A workgroup owns 256 folded rows (like the forward) and walks the keys in
 // steps of 64, copied to LDS with direct loads (double-buffered): K and V as
-// row tiles and K^T as its pre-transposed key tile, so every product reads
-// its LDS operand with one 16-byte read per MFMA.  It visits only the key
+// row tiles; S^T and dP^T read their K / V operand with one 16-byte read per
+// MFMA, dQ^T its K^T operand with two transposing reads of the K rows.  It visits only the key
 // steps the forward recorded for the tile (a.ksteps): outside them every P,
 // and so every dS, is exactly zero.
 #include "kernels.hpp"
@@ -28,12 +28,10 @@ namespace rga {
 
 namespace {
 
-// LDS of one key step: K and V rows (row tiles, blk_off) and K^T (transposed
-// key tile, tt_off), double-buffered.
+// LDS of one key step: K and V rows (row tiles, blk_off), double-buffered.
 struct DqShared {
   uint16_t k[2][TILE_ELEMS];
   uint16_t v[2][TILE_ELEMS];
-  uint16_t kt[2][TILE_ELEMS];
 };
 
 // dK / dV of the 128-key tiles part, part + parts, ... (batch order): key
@@ -140,19 +138,19 @@ __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage
 }
 
 // LDS of the stored-dS path: the dS image (64 keys x 256 rows, ds_off) and
-// K^T (tt_off) of a key step, three buffers (two steps in flight).
+// the K rows (blk_off) of a key step, three buffers (two steps in flight).
 constexpr int DQS_NBUF = 3;
 struct DqStoredShared {
   uint16_t ds[DQS_NBUF][DS_IMAGE_ELEMS];
-  uint16_t kt[DQS_NBUF][TILE_ELEMS];
+  uint16_t k[DQS_NBUF][TILE_ELEMS];
 };
 static_assert(ROW_TILE * (HEAD_DIM + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ staging fits");
 
 // dQ of row tile `tile` from the dS images the dK/dV kernel stored:
 // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row], nothing recomputed.  Both
-// operands come from LDS: K^T with one 16-byte read, dS^T with two
-// transposing reads of the image (lane l32 gets row 32 w + tt_key_pos(l32),
-// keys in the order of the K^T read).  Limited by the HBM reads of the images.
+// operands come from LDS with two transposing reads each: K^T from the K rows,
+// dS^T from the image (lane l32 gets row 32 w + tt_key_pos(l32), keys in the
+// order of the K^T read).  Limited by the HBM reads of the images.
 // The first two steps' copies are issued before the workgroup's slice of
 // the dK / dV partial sums, so they land while it runs.
 template <class T, bool CAP>
@@ -164,11 +162,11 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int nks = (Lk + TILE_ROWS - 1) / TILE_ROWS;
   const uint16_t* img0 = a.ds + ((int64_t)sq[SQ_DSOFF] + (int64_t)tile * nks) * DS_IMAGE_ELEMS;
-  const uint16_t* kt_seq = a.kt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
+  const int k0 = sq[SQ_K0];
   // copies of key step kt: each wave four 1 KB blocks of the image, waves 0-3
-  // three and waves 4-7 two of the 20 K^T loads (7 or 6 per wave)
+  // also a 16-row group of the K rows (five loads: 9 or 4 per wave)
   constexpr int IMG_LOADS = DS_IMAGE_ELEMS / BLK_ELEMS / ROW_WAVES;
-  static_assert(IMG_LOADS == 4, "waits below count 4 + 3 or 4 + 2 loads per step");
+  static_assert(IMG_LOADS == 4 && BLK_COLS == 5, "waits below count 4 + 5 or 4 loads per step");
   // (issued unseen by the compiler, which would otherwise hold each step's
   // transposing reads until the copies of the two steps ahead had landed;
   // the waits below order the buffers)
@@ -179,9 +177,9 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
       const int blk = IMG_LOADS * wave + j;
       load_lds16_unseen(img + blk * BLK_ELEMS + lane * 8, sm.ds[buf] + blk * BLK_ELEMS);
     }
-    const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
-    if (wave < 4) load_tt_tile<3, true>(sm.kt[buf], ktt, 3 * wave, lane);
-    else load_tt_tile<2, true>(sm.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
+    if (wave < 4)
+      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
+                          a.zero, wave, lane);
   };
 
   // transposing reads (see read_tr): lane (i, G) addresses key rows
@@ -192,9 +190,12 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   const int dlo = ds_off(krow, chunk) + 4 * (ti & 1);
   const int dhi = ds_off(krow + 8, chunk) + 4 * (ti & 1);
   constexpr int KSTEP_ELEMS = (ROW_TILE / 32) * BLK_ELEMS;   // 16 keys of an image
-  int toff[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) toff[t] = tt_off(l32, 2 * t + g);
+  // K^T operand: transposing reads of the K row tile in the same key order
+  // (lane (i, G): key rows 4 (G/2) + i/4 and + 8 of the k-step, chunk
+  // 2 (G%2) + (i%4)/2 of the feature block, half i % 2)
+  const int kcl = 2 * (tG & 1) + ((ti & 3) >> 1);
+  const int koff_lo = blk_off(krow, kcl) + 4 * (ti & 1);
+  const int koff_hi = blk_off(krow + 8, kcl) + 4 * (ti & 1);
 
   f32x16 dQ[DBLK];
 #pragma unroll
@@ -206,23 +207,27 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
     // step kt has landed (step kt + 1 may still be in flight) for every wave,
     // and every wave is done with step kt - 1, whose buffer step kt + 2 takes
     if (kt + 1 < khi) {
-      if (wave < 4) wait_vm_le<7>();
-      else wait_vm_le<6>();
+      if (wave < 4) wait_vm_le<9>();
+      else wait_vm_le<4>();
     } else {
       wait_vm();
     }
     __syncthreads();
     if (kt + 2 < khi) issue(kt + 2, (kt + 2) % DQS_NBUF);
     const uint16_t* D = sm.ds[buf];
-    const uint16_t* KT = sm.kt[buf];
+    const uint16_t* Kb = sm.k[buf];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const u32x2 lo = read_tr(D + dlo + t * KSTEP_ELEMS);
       const u32x2 hi = read_tr(D + dhi + t * KSTEP_ELEMS);
       const u32x4 bt = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-        dQ[db] = mfma32<T>(load16(KT + toff[t] + db * 32 * TILE_ROWS), bt, dQ[db]);
+      for (int db = 0; db < DBLK; ++db) {
+        const int off = (t * BLK_COLS + db) * BLK_ELEMS;
+        const u32x2 klo2 = read_tr(Kb + koff_lo + off);
+        const u32x2 khi2 = read_tr(Kb + koff_hi + off);
+        dQ[db] = mfma32<T>(u32x4{klo2[0], klo2[1], khi2[0], khi2[1]}, bt, dQ[db]);
+      }
     }
   }
 
@@ -296,36 +301,31 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
 
   const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
-  const uint16_t* kt_seq = a.kt + (int64_t)sq[SQ_TTOFF] * TILE_ELEMS;
-  // copies of key step kt (60 wave loads): waves 0-3 copy a 16-row group of K
-  // and three K^T loads each, waves 4-7 a 16-row group of V and two K^T loads
+  // copies of key step kt (40 wave loads): waves 0-3 a 16-row group of K,
+  // waves 4-7 one of V; issued unseen by the compiler (advance() orders the
+  // buffers before the transposing reads of K)
   auto issue = [&](int kt, int buf) {
-    const uint16_t* ktt = kt_seq + (int64_t)kt * TILE_ELEMS;
-    if (wave < 4) {
-      load_row_tile(sm.r.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk, a.zero,
-                    wave, lane);
-      load_tt_tile<3>(sm.r.kt[buf], ktt, 3 * wave, lane);
-    } else {
-      load_row_tile(sm.r.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk, a.zero,
-                    wave - 4, lane);
-      load_tt_tile<2>(sm.r.kt[buf], ktt, 12 + 2 * (wave - 4), lane);
-    }
+    if (wave < 4)
+      load_row_tile<true>(sm.r.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
+                          a.zero, wave, lane);
+    else
+      load_row_tile<true>(sm.r.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
+                          a.zero, wave - 4, lane);
   };
 
   // lane-constant LDS offsets: K / V row reads (row kb * 32 + l32, chunk
-  // 2 ks + g) and K^T reads (feature row 32 db + l32, chunk 2 (2 kb + s) + g)
+  // 2 ks + g) and transposing K reads for the K^T operand (lane (i, G): key
+  // rows 4 (G/2) + i/4 and + 8 of a k-step, chunk 2 (G%2) + (i%4)/2, half i % 2)
   const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
-  int toff[2][2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) toff[kb][s] = tt_off(l32, 2 * (2 * kb + s) + g);
+  const int vi = lane & 15, vG = lane >> 4;
+  const int trow = 4 * (vG >> 1) + (vi >> 2), tcl = 2 * (vG & 1) + ((vi & 3) >> 1);
+  const int toff_lo = blk_off(trow, tcl) + 4 * (vi & 1);
+  const int toff_hi = blk_off(trow + 8, tcl) + 4 * (vi & 1);
 
   // one key step on the tiles in LDS buffer buf; masked: keys past Lk get P = 0
   auto step = [&](int buf, int kbase, auto masked) {
     const uint16_t* Kb = sm.r.k[buf];
     const uint16_t* Vb = sm.r.v[buf];
-    const uint16_t* KTb = sm.r.kt[buf];
     const float cb = cb0 - (float)kbase;
     const int kleft = Lk - kbase - 4 * g;
 
@@ -361,13 +361,17 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
       for (int s = 0; s < 2; ++s)
         sb[s] = u32x4{pack2<T>(S[8 * s + 0], S[8 * s + 1]), pack2<T>(S[8 * s + 2], S[8 * s + 3]),
                       pack2<T>(S[8 * s + 4], S[8 * s + 5]), pack2<T>(S[8 * s + 6], S[8 * s + 7])};
-      // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row]; the K^T operand is one
-      // 16-byte read in the key order of sb
+      // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row]; the K^T operand is two
+      // transposing reads of the K rows, in the key order of sb
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-          dQ[db] = mfma32<T>(load16(KTb + toff[kb][s] + db * 32 * TILE_ROWS), sb[s], dQ[db]);
+        for (int s = 0; s < 2; ++s) {
+          const int off = ((2 * kb + s) * BLK_COLS + db) * BLK_ELEMS;
+          const u32x2 lo = read_tr(Kb + toff_lo + off);
+          const u32x2 hi = read_tr(Kb + toff_hi + off);
+          dQ[db] = mfma32<T>(u32x4{lo[0], lo[1], hi[0], hi[1]}, sb[s], dQ[db]);
+        }
     }
   };
 

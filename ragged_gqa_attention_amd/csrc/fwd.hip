@@ -62,34 +62,82 @@ static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared),
 }  // namespace
 
 static_assert(sizeof(UnitsShared) <= sizeof(FwdShared), "the unit planner fits the tile buffers");
+static_assert(sizeof(PlanShared) <= sizeof(FwdShared), "the planner fits the tile buffers");
 
+// Grid: workgroup 0 runs the planner (then, in the full-VJP call, the dK/dV
+// unit plan), workgroups 1 .. a.fwd_slots the row tiles.  The row tiles do
+// not wait for the planner: each finds its tile and key-step range from
+// cu_q / cu_k itself (find_row_tile, tile_key_range), so the planner runs
+// beside them on one compute unit.
 template <class T, bool CAP, bool DELTA>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) FwdShared sm;
 
-  // With the unit planner (full-VJP call) workgroup 0 plans and row tile
-  // slot i runs in workgroup i + 1: the planner starts at once and is done
-  // long before the row tiles.
-  const int slot = (int)blockIdx.x - (int)(gridDim.x - a.fwd_slots);
-  if (slot < 0) {
-    plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
+  if (blockIdx.x == 0) {
+    plan_block<ROW_THREADS>(pa, *reinterpret_cast<PlanShared*>(&sm));
+    if (DELTA) {   // the full-VJP call: the dK/dV units, from the planner's ranges
+      __syncthreads();
+      plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
+    }
     return;
   }
-  const int b = a.plan.fwd_map[2 * slot];
-  if (b < 0) return;
-  const int tile = a.plan.fwd_map[2 * slot + 1];
-  const int* sq = a.plan.seq + b * SEQ_FIELDS;
-  const int q0 = sq[SQ_Q0], Lq = sq[SQ_LQ], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
-  const int rows = sq[SQ_ROWS];
-
+  const int slot = (int)blockIdx.x - 1;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+
+  // Wave 0 finds the slot's row tile and its key steps [klo, khi) (the
+  // planner's range; the other waves would only repeat its loads) and hands
+  // them over through LDS.
+  __shared__ int tinfo[8];
+  if (wave == 0) {
+    RowTile rt;
+    int lo = 0, hi = 0;
+    const bool ok = find_row_tile(pa, slot, rt);
+    if (ok) tile_key_range(pa, rt, lo, hi);
+    if (lane == 0) {
+      tinfo[0] = ok ? rt.b : -1;
+      tinfo[1] = rt.tile;
+      tinfo[2] = rt.q0;
+      tinfo[3] = rt.lq;
+      tinfo[4] = rt.k0;
+      tinfo[5] = rt.lk;
+      tinfo[6] = lo;
+      tinfo[7] = hi;
+    }
+  }
+  __syncthreads();
+  const int b = tinfo[0];
+  if (b < 0) return;
+  const int tile = tinfo[1];
+  const int q0 = tinfo[2], Lq = tinfo[3], k0 = tinfo[4], Lk = tinfo[5];
+  const int klo = tinfo[6], khi = tinfo[7];
+  const int rows = Lq * a.hq;
+
+  // copies of key step kt: waves 0-3 the K rows, waves 4-7 the V rows (one
+  // 16-row group each).  Rows past Lk repeat row Lk - 1 (the tile runs before
+  // the planner has cleared the zero block): only the last, masked step has
+  // them, where their logits are -inf, so they add 0 * (a finite V row).
+  // Issued unseen by the compiler (it would hold the step's transposing reads
+  // until the next step's copies had landed); advance() orders the buffers.
+  // The first step's copies go out before the Q rows are requested.
+  const uint16_t* klast = a.k + (int64_t)(k0 + max(Lk, 1) - 1) * a.k_ts;
+  const uint16_t* vlast = a.v + (int64_t)(k0 + max(Lk, 1) - 1) * a.v_ts;
+  auto issue = [&](int kt, int buf) {
+    if (wave < 4)
+      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
+                          klast, wave, lane);
+    else
+      load_row_tile<true>(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
+                          vlast, wave - 4, lane);
+  };
+  if (klo < khi) issue(klo, klo % FWD_NBUF);
+
   const int row = tile * ROW_TILE + wave * 32 + l32;
   const bool row_ok = row < rows;
   const int rr = row_ok ? row : rows - 1;
-  int ti, hh;
-  unfold_row(rr, sq, ti, hh);
+  // folded row -> (token, head): R = h * Lq + i (two divisions per workgroup)
+  const int hh = rr / Lq, ti = rr - hh * Lq;
 
   // Q row as B operand: k-step ks covers features 16ks + 8g .. +7
   const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
@@ -111,21 +159,6 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   for (int db = 0; db < DBLK; ++db) O[db] = f32x16{};
 
   const int ntiles = (Lk + TILE_ROWS - 1) / TILE_ROWS;
-  // key steps [klo, khi) some row of the tile keeps (the planner's range)
-  const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
-  const int klo = ks[0], khi = ks[1];
-  // copies of key step kt: waves 0-3 the K rows, waves 4-7 the V rows (one
-  // 16-row group each); keys past Lk read zeros.  Issued unseen by the
-  // compiler (it would hold the step's transposing reads until the next
-  // step's copies had landed); advance() orders the buffers.
-  auto issue = [&](int kt, int buf) {
-    if (wave < 4)
-      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
-                          a.zero, wave, lane);
-    else
-      load_row_tile<true>(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
-                          a.zero, wave - 4, lane);
-  };
 
   // lane-constant LDS offsets: K row reads (row kb * 32 + l32, chunk 2 ks + g)
   // and transposing V reads (see read_tr): lane (i, G) addresses key rows
@@ -230,7 +263,6 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   const int kfull = min(khi, nfull);
   constexpr Flag<false> unmasked{};
   constexpr Flag<true> masked{};
-  if (klo < khi) issue(klo, klo % FWD_NBUF);
 
   if (CAP) {
     // The offset is fixed, so the two 32-key blocks of a step are independent.
@@ -336,8 +368,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     erow[h] = rg;
     eok[h] = rg < rows;
     const int rc = eok[h] ? rg : rows - 1;
-    int tk, hd;
-    unfold_row(rc, sq, tk, hd);
+    const int hd = rc / Lq, tk = rc - hd * Lq;
     eout[h] = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
     if (DELTA) {
       const uint16_t* drow = a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs;
@@ -414,8 +445,8 @@ static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, 
 }
 
 hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
-                      bool with_delta, bool plan_units, hipStream_t s) {
-  const int grid = a.fwd_slots + (plan_units ? 1 : 0);
+                      bool with_delta, hipStream_t s) {
+  const int grid = 1 + a.fwd_slots;
   if (a.batch <= 0) return hipSuccess;
   return dtype == DT_BF16 ? launch_fwd_t<BF16>(a, pa, cap, with_delta, grid, s)
                           : launch_fwd_t<F16>(a, pa, cap, with_delta, grid, s);

@@ -16,8 +16,8 @@ constexpr int ROW_TILE = ROW_WAVES * 32;
 // Key-tile kernel (dK/dV): one workgroup = 8 waves = 4 wave pairs x 32 keys.
 constexpr int KV_THREADS = 512;
 constexpr int KEY_TILE = 128;
-// Rows or keys of one LDS tile (row tiles and transposed key tiles, see
-// tiles.hpp): the key step of the row-tile kernels and the row step of dK/dV.
+// Rows or keys of one LDS row tile (see tiles.hpp): the key step of the
+// row-tile kernels and the row step of dK/dV.
 constexpr int TILE_ROWS = 64;
 constexpr int TILE_ELEMS = TILE_ROWS * HEAD_DIM;
 // Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
@@ -45,9 +45,6 @@ struct AttnArgs {
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;
   const uint16_t* zero; // 512 zero bytes: source of the loads of rows past a tile's end
-  // Transposed 64-key tiles of K (see tt_key_pos), tile i at i * 64 * 160:
-  // [feature][key], written by the prep kernel for dQ; keys past Lk are zero.
-  uint16_t* kt;
   float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
   float* part_dv;
   // dS images written by dK/dV and read by dQ for the sequences the planner
@@ -149,13 +146,13 @@ __device__ __forceinline__ void row_key_steps(bool exists, float slope2, int cen
   key_steps_of(centre, key_half_width(slope2, Lk, thr), Lk, lo, hi);
 }
 
-// Planner (one workgroup) and, alongside it, the transposed key tiles a.kt (a
-// null pointer skips them), up to key_tiles tiles.
-hipError_t launch_prep(const PlanArgs& pa, const AttnArgs& a, int key_tiles, hipStream_t s);
-// Forward over the a.fwd_slots row-tile slots; plan_units adds the workgroup
-// that plans the dK/dV units (from pa) alongside.
+// Planner (one workgroup), for the calls whose forward grid does not hold it.
+hipError_t launch_prep(const PlanArgs& pa, hipStream_t s);
+// Forward over the a.fwd_slots row-tile slots, with the planner (pa) in an
+// extra workgroup beside them; with_delta (the full-VJP call) also plans the
+// dK/dV units there and writes the row records.
 hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
-                      bool with_delta, bool plan_units, hipStream_t s);
+                      bool with_delta, hipStream_t s);
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
 // Key-step ranges of the standalone backward, from the row records, and its
 // dK/dV units planned from them.

@@ -3,6 +3,7 @@
 #pragma once
 
 #include "kernels.hpp"
+#include "tiles.hpp"
 
 namespace rga {
 
@@ -95,6 +96,30 @@ __device__ __forceinline__ int last_at_most(int n, int x, F key) {
 // tile ranges (batches with more (sequence, head) pairs keep them in the
 // workspace).
 constexpr int PLAN_LDS_HEADS = 4096;
+
+// Batches up to this size are planned in LDS and copied out at the end (each
+// planning step re-reads what the previous one wrote; LDS keeps those round
+// trips short); larger ones are planned in place in global memory.
+constexpr int PLAN_LDS_B = 256;
+// Row tiles are dispatched longest first (by their key steps, counting-sorted
+// into this many classes; longer ones share the last class).  Tiles of equal
+// length go in the order the LDS atomics hand out, which only affects timing:
+// a tile's results do not depend on the workgroup that computes it.
+constexpr int PLAN_COST_CLASSES = 1024;
+// Row tiles whose sequence the planner looks up in an LDS table (the rest by
+// binary search).
+constexpr int PLAN_LDS_TILES = 4096;
+
+// LDS of plan_block (up to 16 waves).
+struct PlanShared {
+  long long red[16];
+  int part[16];
+  int seq[PLAN_LDS_B * SEQ_FIELDS];
+  int hw[PLAN_LDS_HEADS];
+  int cls[PLAN_COST_CLASSES + 1];
+  int foff[PLAN_COST_CLASSES];
+  int tseq[PLAN_LDS_TILES];
+};
 
 // dK/dV work split, planned by one workgroup of NT threads from the row
 // tiles' key-step ranges in a.ksteps (seq: the sequence records).
@@ -205,5 +230,316 @@ __device__ __forceinline__ void plan_units(const PlanArgs& a, const int* seq, Un
     a.plan.wg_first[p] = g;
   }
 }
+
+template <int NT>
+__device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
+  long long* red = sh.red;
+  int* part = sh.part;
+  int* l_seq = sh.seq;
+  int* l_hw = sh.hw;
+  int* l_class = sh.cls;
+  int* l_foff_c = sh.foff;
+  int* l_tseq = sh.tseq;
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  const int hq = a.hq;
+  const bool in_lds = B <= PLAN_LDS_B;
+  int* seq = in_lds ? l_seq : a.plan.seq;
+
+  if (tid < 32) reinterpret_cast<u32x4*>(a.zero)[tid] = u32x4{0u, 0u, 0u, 0u};
+  // the slopes, requested first (their loads overlap those of the checks
+  // below); thread tid takes (sequence, head) pairs tid + 256 k
+  constexpr int SPER = PLAN_LDS_HEADS / NT;
+  const bool hw_lds = (long long)B * hq <= PLAN_LDS_HEADS;
+  const int sb0 = tid / hq, sh0 = tid - sb0 * hq;   // pair tid
+  const int sdb = NT / hq, sdh = NT - sdb * hq;
+  float sv[SPER];
+  if (hw_lds && B > 0) {   // unconditional loads (pairs past the last read (B - 1, h)), all in flight at once
+    int b = sb0, h = sh0;
+#pragma unroll
+    for (int k = 0; k < SPER; ++k) {
+      sv[k] = a.slopes[(int64_t)min(b, B - 1) * a.slopes_stride + h];
+      b += sdb;
+      h += sdh;
+      if (h >= hq) { h -= hq; ++b; }
+    }
+  }
+  // checks of cu_q / cu_k and the per-sequence extents in one pass; an
+  // invalid batch is then planned with every sequence empty
+  auto extents = [&](int b, int q0, int lq, int k0, int lk) {
+    int* s = seq + b * SEQ_FIELDS;
+    s[SQ_Q0] = q0; s[SQ_LQ] = lq; s[SQ_K0] = k0; s[SQ_LK] = lk;
+    s[SQ_ROWS] = lq * a.hq;
+    s[SQ_KTILES] = (lk + KEY_TILE - 1) / KEY_TILE;
+    uint32_t mul, sh;
+    fast_div_consts(lq, mul, sh);
+    s[SQ_LQSHIFT] = (int)sh;
+    s[SQ_LQMUL] = (int)mul;
+  };
+  bool bad = false;
+  for (int b = tid; b <= B; b += NT) {
+    const int cq = a.cu_q[b], ck = a.cu_k[b];
+    const int nq = b < B ? a.cu_q[b + 1] : cq, nk = b < B ? a.cu_k[b + 1] : ck;
+    bool fail = cq < 0 || (int64_t)cq > a.total_q || ck < 0 || (int64_t)ck > a.total_k;
+    if (b == 0) fail |= (cq != 0) || (ck != 0);
+    if (b == B) fail |= ((int64_t)cq != a.total_q) || ((int64_t)ck != a.total_k);
+    if (b < B) fail |= (nq < cq) || (nk < ck);
+    bad |= fail;
+    // (a failed check leaves this sequence empty, so no length is negative)
+    if (b < B) {
+      if (fail) extents(b, 0, 0, 0, 0);
+      else extents(b, cq, nq - cq, ck, nk - ck);
+    }
+  }
+  const bool ok = __syncthreads_or(bad) == 0;
+  if (tid == 0) a.plan.flag[0] = ok ? 0 : 1;
+  if (!ok) {
+    for (int b = tid; b < B; b += NT) extents(b, 0, 0, 0, 0);
+    __syncthreads();
+  }
+
+  // 256-row tiles in batch order (their key-step ranges are kept in this
+  // order); tile -> sequence in LDS when the tiles fit
+  block_exclusive_scan<NT>(B, [&](int b) {
+    return (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
+  }, [&](int b, int v) {
+    if (b >= B) return;
+    seq[b * SEQ_FIELDS + SQ_RTOFF] = v;
+    const int n = (seq[b * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE;
+    for (int t = v; t < min(v + n, PLAN_LDS_TILES); ++t) l_tseq[t] = b;
+  }, part);
+  const int nrt = B > 0 ? seq[(B - 1) * SEQ_FIELDS + SQ_RTOFF] +
+                              (seq[(B - 1) * SEQ_FIELDS + SQ_ROWS] + ROW_TILE - 1) / ROW_TILE
+                        : 0;
+
+  // Key-step range of every row tile (see tile_key_steps), from each head's
+  // key half-width (LDS, from the slopes requested at the start, when they
+  // fit; else the workspace, eight slope loads in flight per thread).
+  int* hw = hw_lds ? l_hw : a.head_hw;
+  if (hw_lds) {
+    int b = sb0, h = sh0;
+#pragma unroll
+    for (int k = 0; k < SPER; ++k) {
+      if (b < B)
+        hw[b * hq + h] = key_half_width(sv[k] * LOG2E, seq[b * SEQ_FIELDS + SQ_LK], a.skip_log2);
+      b += sdb;
+      h += sdh;
+      if (h >= hq) { h -= hq; ++b; }
+    }
+  } else {
+    constexpr int PER = 8;
+    for (int i0 = 0; i0 < B * hq; i0 += NT * PER) {
+      float v[PER];
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = i0 + k * NT + tid;
+        const int b = i / hq;
+        v[k] = i < B * hq ? a.slopes[(int64_t)b * a.slopes_stride + (i - b * hq)] : 0.0f;
+      }
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const int i = i0 + k * NT + tid;
+        if (i < B * hq)
+          hw[i] = key_half_width(v[k] * LOG2E, seq[(i / hq) * SEQ_FIELDS + SQ_LK], a.skip_log2);
+      }
+    }
+  }
+  for (int i = tid; i <= PLAN_COST_CLASSES; i += NT) l_class[i] = 0;
+  __threadfence_block();
+  __syncthreads();
+  auto seq_of_tile = [&](int g) {
+    if (g < PLAN_LDS_TILES) return l_tseq[g];
+    return last_at_most(B, g, [&](int x) { return seq[x * SEQ_FIELDS + SQ_RTOFF]; });
+  };
+  for (int g = tid; g < nrt; g += NT) {
+    const int b = seq_of_tile(g);
+    const int* s = seq + b * SEQ_FIELDS;
+    int lo, hi;
+    tile_key_steps(s, g - s[SQ_RTOFF], hw + b * hq, lo, hi);
+    a.ksteps[2 * g] = lo;
+    a.ksteps[2 * g + 1] = hi;
+    // class 0 holds the longest tiles
+    atomicAdd(&l_class[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+  }
+  __syncthreads();
+  // workgroup -> row tile, longest first; entries past the last tile get
+  // sequence -1
+  block_exclusive_scan<NT>(PLAN_COST_CLASSES, [&](int c) { return l_class[c]; },
+                                     [&](int c, int v) { if (c < PLAN_COST_CLASSES) l_foff_c[c] = v; },
+                                     part);
+  for (int g = tid; g < nrt; g += NT) {
+    const int lo = a.ksteps[2 * g], hi = a.ksteps[2 * g + 1];
+    const int pos = atomicAdd(&l_foff_c[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+    const int b = seq_of_tile(g);
+    a.plan.fwd_map[2 * pos] = b;
+    a.plan.fwd_map[2 * pos + 1] = g - seq[b * SEQ_FIELDS + SQ_RTOFF];
+  }
+  for (int i = nrt + tid; i < a.fwd_slots; i += NT) {
+    a.plan.fwd_map[2 * i] = -1;
+    a.plan.fwd_map[2 * i + 1] = 0;
+  }
+  if (tid == 0) a.plan.kv_head[2] = nrt;
+  // 128-key tiles in batch order (dK / dV units and partial sums walk them)
+  block_exclusive_scan<NT>(B, [&](int b) { return seq[b * SEQ_FIELDS + SQ_KTILES]; },
+                       [&](int b, int v) { if (b < B) seq[b * SEQ_FIELDS + SQ_KTOFF] = v; }, part);
+  // stored dS images, in sequence order, while they fit the workspace (a
+  // sequence that does not fit recomputes dS in the dQ kernel)
+  auto images = [&](int b) -> long long {
+    const int* sb = seq + b * SEQ_FIELDS;
+    if (sb[SQ_ROWS] == 0 || sb[SQ_LK] == 0) return 0;
+    return (long long)((sb[SQ_ROWS] + ROW_TILE - 1) / ROW_TILE) *
+           ((sb[SQ_LK] + TILE_ROWS - 1) / TILE_ROWS);
+  };
+  block_exclusive_scan<NT>(B, images, [&](int b, long long off) {
+    if (b < B) {
+      const long long n = images(b);
+      seq[b * SEQ_FIELDS + SQ_DSOFF] = (n > 0 && off + n <= a.ds_images) ? (int)off : -1;
+    }
+  }, red);
+
+  if (in_lds) {   // the kernels read the plan from global memory
+    for (int i = tid; i < B * SEQ_FIELDS; i += NT) a.plan.seq[i] = l_seq[i];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// A forward workgroup's row tile, found without the planner so the forward
+// need not wait for it.  The 256-row tiles of the batch are taken in an order
+// computable from cu_q / cu_k alone: sequences by key length, longest first
+// (ties by index), when there are at most 64 of them, else in batch order;
+// slot i gets tile i of that order (long tiles start first, short ones fill
+// the tail).  Every wave computes the same answer from the same loads (no
+// LDS, no barrier).  cu_q / cu_k are checked as the planner checks them.
+struct RowTile {
+  int b, tile;          // sequence, 256-row tile of the sequence
+  int q0, lq, k0, lk;   // the sequence's extents
+};
+
+// false past the last tile, or when cu_q / cu_k are invalid (the planner
+// flags that case and plans nothing)
+__device__ __forceinline__ bool find_row_tile(const PlanArgs& pa, int slot, RowTile& t) {
+  const int lane = threadIdx.x & 63;
+  const int B = pa.batch, hq = pa.hq;
+  if (B <= 0) return false;
+  if (B <= 64) {
+    const int b = lane;
+    const bool live = b < B;
+    // unconditional loads (lanes past B - 1 repeat the last sequence), so
+    // the four requests are in flight together
+    const int bl = min(b, B - 1);
+    int cq = pa.cu_q[bl], nq = pa.cu_q[bl + 1];
+    int ck = pa.cu_k[bl], nk = pa.cu_k[bl + 1];
+    if (!live) cq = nq = ck = nk = 0;
+    bool bad = live && (cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
+                        (int64_t)nk > pa.total_k);
+    if (b == 0 && live) bad |= cq != 0 || ck != 0;
+    if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
+    if (__any(bad)) return false;
+    const int lq = nq - cq, lk = nk - ck;
+    const int n = live ? (lq * hq + ROW_TILE - 1) / ROW_TILE : 0;
+    // first tile of sequence b: the tiles of the sequences ranked before it
+    int start = 0;
+    for (int j = 0; j < B; ++j) {
+      const int lkj = __builtin_amdgcn_readlane(lk, j), nj = __builtin_amdgcn_readlane(n, j);
+      start += (lkj > lk || (lkj == lk && j < b)) ? nj : 0;
+    }
+    const uint64_t own = __ballot(live && start <= slot && slot < start + n);
+    if (own == 0) return false;
+    const int ob = __ffsll((long long)own) - 1;
+    t.b = ob;
+    t.tile = slot - __builtin_amdgcn_readlane(start, ob);
+    t.q0 = __builtin_amdgcn_readlane(cq, ob);
+    t.lq = __builtin_amdgcn_readlane(lq, ob);
+    t.k0 = __builtin_amdgcn_readlane(ck, ob);
+    t.lk = __builtin_amdgcn_readlane(lk, ob);
+    return true;
+  }
+  // batch order: lane l owns sequences [l seg, l seg + seg)
+  const int seg = (B + 63) / 64;
+  const int lo = min(B, lane * seg), hi = min(B, lo + seg);
+  bool bad = false;
+  int count = 0;
+  int pq = pa.cu_q[lo], pk = pa.cu_k[lo];
+  if (lo == 0) bad |= pq != 0 || pk != 0;
+  bad |= pq < 0 || pk < 0;
+  for (int b = lo; b < hi; ++b) {
+    const int nq = pa.cu_q[b + 1], nk = pa.cu_k[b + 1];
+    bad |= nq < pq || nk < pk || (int64_t)nq > pa.total_q || (int64_t)nk > pa.total_k;
+    count += ((nq - pq) * hq + ROW_TILE - 1) / ROW_TILE;
+    pq = nq;
+    pk = nk;
+  }
+  if (lo < hi && hi == B) bad |= (int64_t)pq != pa.total_q || (int64_t)pk != pa.total_k;
+  if (__any(bad)) return false;
+  int x = count;   // inclusive scan over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  const int run0 = x - count;
+  const uint64_t own = __ballot(run0 <= slot && slot < x);
+  if (own == 0) return false;
+  const int ol = __ffsll((long long)own) - 1;
+  if (lane == ol) {
+    int run = run0;
+    for (int b = lo; b < hi; ++b) {
+      const int q = pa.cu_q[b], nq = pa.cu_q[b + 1];
+      const int n = ((nq - q) * hq + ROW_TILE - 1) / ROW_TILE;
+      if (slot < run + n) {
+        t.b = b;
+        t.tile = slot - run;
+        t.q0 = q;
+        t.lq = nq - q;
+        t.k0 = pa.cu_k[b];
+        t.lk = pa.cu_k[b + 1] - t.k0;
+        break;
+      }
+      run += n;
+    }
+  }
+  t.b = __builtin_amdgcn_readlane(t.b, ol);
+  t.tile = __builtin_amdgcn_readlane(t.tile, ol);
+  t.q0 = __builtin_amdgcn_readlane(t.q0, ol);
+  t.lq = __builtin_amdgcn_readlane(t.lq, ol);
+  t.k0 = __builtin_amdgcn_readlane(t.k0, ol);
+  t.lk = __builtin_amdgcn_readlane(t.lk, ol);
+  return true;
+}
+
+// The tile's key-step range, equal to the planner's tile_key_steps: each head
+// the tile spans (one per lane, 64 at a time) contributes the ranges of its
+// first and its last row of the tile, from its half-width key_half_width.
+__device__ __forceinline__ void tile_key_range(const PlanArgs& pa, const RowTile& t, int& lo,
+                                               int& hi) {
+  const int lane = threadIdx.x & 63;
+  const int rows = t.lq * pa.hq;
+  const int R0 = t.tile * ROW_TILE, R1 = min(rows, R0 + ROW_TILE);
+  const int hfirst = R0 / t.lq, hlast = (R1 - 1) / t.lq;
+  lo = 0x7fffffff;
+  hi = 0;
+  for (int h0 = hfirst; h0 <= hlast; h0 += 64) {
+    const int h = h0 + lane;
+    if (h <= hlast) {
+      const float slope = pa.slopes[(int64_t)t.b * pa.slopes_stride + h];
+      const int hw = key_half_width(slope * LOG2E, t.lk, pa.skip_log2);
+      const int ia = h == hfirst ? R0 - h * t.lq : 0;
+      const int ib = h == hlast ? R1 - 1 - h * t.lq : t.lq - 1;
+      int l0, u0, l1, u1;
+      key_steps_of(max(ia + t.lk - t.lq, 0), hw, t.lk, l0, u0);
+      key_steps_of(max(ib + t.lk - t.lq, 0), hw, t.lk, l1, u1);
+      lo = min(lo, l0);
+      hi = max(hi, u1);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    lo = min(lo, __shfl_xor(lo, o, 64));
+    hi = max(hi, __shfl_xor(hi, o, 64));
+  }
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  hi = __builtin_amdgcn_readfirstlane(hi);
+}
+
 
 }  // namespace rga

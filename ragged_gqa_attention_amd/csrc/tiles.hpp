@@ -1,9 +1,9 @@
 // LDS tile layouts, direct global -> LDS copies, operand reads and the logit
 // pipeline shared by the gfx950 kernels.
 //
-// Two tile layouts, both filled by direct loads (global_load_lds_dwordx4: one
-// wave instruction copies 64 lanes x 16 bytes into 64 consecutive 16-byte LDS
-// slots, so no staging registers are needed) and both read without LDS bank
+// Tiles are filled by direct loads (global_load_lds_dwordx4: one wave
+// instruction copies 64 lanes x 16 bytes into 64 consecutive 16-byte LDS
+// slots, so no staging registers are needed) and read without LDS bank
 // conflicts.  LDS serves a 16-byte read 16 lanes at a time from 16 bank
 // slots of 16 bytes (measured on gfx950: odd row strides in 16-byte units are
 // conflict-free, a 320-byte stride is 4-way).
@@ -13,11 +13,9 @@
 //    Read one chunk per lane ("row read", the A/B operand of a product that
 //    contracts over features) or with the transposing read (the operand of a
 //    product that contracts over rows).
-//  * Transposed key tile: 160 feature rows x 64 keys, written once per call
-//    into the workspace by the prep kernel with the keys of each 16-key
-//    group permuted (tt_key_pos) so that one 16-byte read gives a lane
-//    exactly the keys that the accumulator layout of P / dS assigns it.  It
-//    replaces the transposing read for K^T in dQ.
+//  * dS image (ds_off): a row tile with 64 keys as its rows and the 256
+//    folded rows of a row tile as its columns, its key rows permuted inside
+//    every 16-key group (tt_key_pos) in the order of the accumulator layout.
 //
 // Rows at or past a sequence's end are loaded from a zero block: the padding
 // of the packed views is arbitrary (NaN in the tests) and 0 * NaN would poison
@@ -62,21 +60,13 @@ __device__ __forceinline__ int blk_off(int r, int c) {
   return (((r >> 4) * BLK_COLS + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
 }
 
-// Position of key k (0..63) inside a feature row of a transposed key tile:
-// the middle two quads of every 16-key group are swapped, so lane half g of a
-// 16-byte read at chunk 2 s + g gets keys 16 s + {4g .. 4g + 3, 8 + 4g .. 8 + 4g + 3}.
+// Key order of the accumulator layout reused as a B operand: the middle two
+// quads of every 16-key group are swapped, so that lane half g of k-step s
+// holds keys 16 s + {4g .. 4g + 3, 8 + 4g .. 8 + 4g + 3} (see common.hpp).
 __device__ __forceinline__ int tt_key_pos(int k) {
   const int j = k & 15;
   const int q = j >> 2;
   return (k & ~15) | ((q == 1 ? 2 : q == 2 ? 1 : q) << 2) | (j & 3);
-}
-
-// Element offset of 16-byte chunk c (keys 8c .. 8c + 7 in tt_key_pos order)
-// of feature row d in a transposed key tile in LDS: the chunk index is XOR-ed
-// with (d / 2) % 8, so 16 consecutive feature rows of one chunk hit 16
-// distinct bank slots.
-__device__ __forceinline__ int tt_off(int d, int c) {
-  return d * TILE_ROWS + ((c ^ ((d >> 1) & 7)) << 3);
 }
 
 // Element offset of 16-byte chunk c (c = 0..31) of key k (0..63) in a dS
@@ -141,22 +131,6 @@ __device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* sr
   for (int b = 0; b < BLK_COLS; ++b) {
     if (UNSEEN) load_lds16_unseen(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
     else load_lds16(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
-  }
-}
-
-// Copies wave loads [i0, i0 + n) of a transposed key tile (20 loads of 8
-// feature rows each) from its global copy `src` (160 x 64 elements, unswizzled).
-// UNSEEN: issue them as load_lds16_unseen.
-template <int N, bool UNSEEN = false>
-__device__ __forceinline__ void load_tt_tile(uint16_t* tile, const uint16_t* src, int i0, int lane) {
-  const int dl = lane >> 3, pc = lane & 7;
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const int i = i0 + n;
-    const int d = 8 * i + dl;
-    const int c = pc ^ ((d >> 1) & 7);
-    if (UNSEEN) load_lds16_unseen(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
-    else load_lds16(src + d * TILE_ROWS + c * 8, tile + i * BLK_ELEMS);
   }
 }
 
