@@ -69,49 +69,16 @@ static_assert(sizeof(PlanShared) <= sizeof(FwdShared), "the planner fits the til
 // not wait for the planner: each finds its tile and key-step range from
 // cu_q / cu_k itself (find_row_tile, tile_key_range), so the planner runs
 // beside them on one compute unit.
+// One 256-row tile of the forward: sequence b (extents q0, Lq, k0, Lk), tile
+// `tile` of its folded rows, key steps [klo, khi).
 template <class T, bool CAP, bool DELTA>
-__global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
-  __shared__ __attribute__((aligned(16))) FwdShared sm;
-
-  if (blockIdx.x == 0) {
-    plan_block<ROW_THREADS>(pa, *reinterpret_cast<PlanShared*>(&sm));
-    if (DELTA) {   // the full-VJP call: the dK/dV units, from the planner's ranges
-      __syncthreads();
-      plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
-    }
-    return;
-  }
-  const int slot = (int)blockIdx.x - 1;
+__device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const int b,
+                                         const int tile, const int q0, const int Lq,
+                                         const int k0, const int Lk, const int klo,
+                                         const int khi) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-
-  // Wave 0 finds the slot's row tile and its key steps [klo, khi) (the
-  // planner's range; the other waves would only repeat its loads) and hands
-  // them over through LDS.
-  __shared__ int tinfo[8];
-  if (wave == 0) {
-    RowTile rt;
-    int lo = 0, hi = 0;
-    const bool ok = find_row_tile(pa, slot, rt);
-    if (ok) tile_key_range(pa, rt, lo, hi);
-    if (lane == 0) {
-      tinfo[0] = ok ? rt.b : -1;
-      tinfo[1] = rt.tile;
-      tinfo[2] = rt.q0;
-      tinfo[3] = rt.lq;
-      tinfo[4] = rt.k0;
-      tinfo[5] = rt.lk;
-      tinfo[6] = lo;
-      tinfo[7] = hi;
-    }
-  }
-  __syncthreads();
-  const int b = tinfo[0];
-  if (b < 0) return;
-  const int tile = tinfo[1];
-  const int q0 = tinfo[2], Lq = tinfo[3], k0 = tinfo[4], Lk = tinfo[5];
-  const int klo = tinfo[6], khi = tinfo[7];
   const int rows = Lq * a.hq;
 
   // copies of key step kt: waves 0-3 the K rows, waves 4-7 the V rows (one
@@ -427,6 +394,330 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   }
 }
 
+// The forward's row tiles in a fixed order: sequences by key length, longest
+// first (ties by index), for up to 64 sequences, else batch order; each
+// workgroup builds the table of that order once (from cu_q / cu_k alone).
+constexpr int FWD_ORDER_MAX = 512;
+struct FwdOrder {
+  int status;   // 1: table, 2: too many sequences (find_row_tile per rank), 0: nothing
+  int n, nrt;
+  int start[FWD_ORDER_MAX + 1];   // first rank of entry k; start[n] = nrt
+  int seq[FWD_ORDER_MAX], q0[FWD_ORDER_MAX], lq[FWD_ORDER_MAX], k0[FWD_ORDER_MAX],
+      lk[FWD_ORDER_MAX];
+  int part[16];   // block scan partials
+};
+
+template <int NT>
+__device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& ord) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = pa.batch, hq = pa.hq;
+  if (B <= 64) {
+    if (wave == 0) {
+      const int b = lane;
+      const bool live = b < B;
+      const int bl = min(b, B - 1);   // B >= 1: the forward is not launched otherwise
+      int cq = pa.cu_q[bl], nq = pa.cu_q[bl + 1];
+      int ck = pa.cu_k[bl], nk = pa.cu_k[bl + 1];
+      bool bad = live && (cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
+                          (int64_t)nk > pa.total_k);
+      if (b == 0) bad |= cq != 0 || ck != 0;
+      if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
+      const bool any_bad = __any(bad);
+      const int lq = live ? nq - cq : 0, lk = live ? nk - ck : 0;
+      const int n = live ? (lq * hq + ROW_TILE - 1) / ROW_TILE : 0;
+      int start = 0, rank = 0;   // over the sequences ranked before b
+      for (int j = 0; j < B; ++j) {
+        const int lkj = __builtin_amdgcn_readlane(lk, j), nj = __builtin_amdgcn_readlane(n, j);
+        const bool before = lkj > lk || (lkj == lk && j < b);
+        start += before ? nj : 0;
+        rank += before ? 1 : 0;
+      }
+      int total = n;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) total += __shfl_xor(total, o, 64);
+      if (live) {
+        ord.start[rank] = start;
+        ord.seq[rank] = b;
+        ord.q0[rank] = cq;
+        ord.lq[rank] = lq;
+        ord.k0[rank] = ck;
+        ord.lk[rank] = lk;
+      }
+      if (lane == 0) {
+        ord.start[B] = total;
+        ord.n = B;
+        ord.nrt = total;
+        ord.status = any_bad ? 0 : 1;
+      }
+    }
+  } else if (B <= FWD_ORDER_MAX) {
+    bool bad = false;
+    for (int b = tid; b < B; b += NT) {
+      const int cq = pa.cu_q[b], nq = pa.cu_q[b + 1], ck = pa.cu_k[b], nk = pa.cu_k[b + 1];
+      bad |= cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
+             (int64_t)nk > pa.total_k;
+      if (b == 0) bad |= cq != 0 || ck != 0;
+      if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
+      ord.seq[b] = b;
+      ord.q0[b] = cq;
+      ord.lq[b] = max(nq - cq, 0);
+      ord.k0[b] = ck;
+      ord.lk[b] = max(nk - ck, 0);
+    }
+    const bool any_bad = __syncthreads_or(bad);
+    block_exclusive_scan<NT>(B, [&](int b) { return (ord.lq[b] * hq + ROW_TILE - 1) / ROW_TILE; },
+                             [&](int b, int v) { ord.start[b] = v; }, ord.part);
+    if (tid == 0) {
+      ord.n = B;
+      ord.nrt = ord.start[B];
+      ord.status = any_bad ? 0 : 1;
+    }
+  } else if (tid == 0) {
+    ord.status = 2;
+  }
+  __syncthreads();
+}
+
+// Longest-first ranks.  For batches of up to 64 sequences, 4096 (sequence,
+// head) pairs and 2048 row tiles, each persistent workgroup also ranks every
+// tile by its key steps (longest first, ties in table order: every workgroup
+// derives the same ranking) and resolves the ranks it deals itself before its
+// first tile; the snake then pairs long tiles with short ones.  The scratch
+// lives in the key-tile buffers, which no tile uses yet.
+constexpr int LPT_MAX_HEADS = 4096;
+constexpr int LPT_MAX_TILES = 2048;
+constexpr int LPT_CLASSES = 1024;   // key steps (longer tiles share class 0)
+constexpr int FWD_LIST_MAX = 16;    // tiles one workgroup resolves in advance
+struct LptScratch {
+  int hw[LPT_MAX_HEADS];          // key half-width of (table entry, head)
+  int cls[LPT_MAX_TILES];         // class of tile t (t: rank in table order)
+  int ks[LPT_MAX_TILES][2];       // key-step range of tile t
+  int hist[LPT_CLASSES];
+  int off[LPT_CLASSES + 1];       // first rank of each class
+};
+
+// Fills list[i] = {b, tile, q0, lq, k0, lk, klo, khi} for the workgroup's
+// ranks r < nrt (round i of the snake); returns their count, or -1 when the
+// batch does not qualify (the caller then finds each tile itself).
+template <int NT>
+__device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord, LptScratch& sc,
+                                        int (*list)[8], int w, int P) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = pa.batch, hq = pa.hq, nrt = ord.nrt;
+  if (B > 64 || B * hq > LPT_MAX_HEADS || nrt > LPT_MAX_TILES) return -1;
+  // rounds of the snake; a workgroup's ranks grow from round to round, so it
+  // stops at its first rank past the last tile
+  const int rounds = (nrt + P - 1) / P;
+  if (rounds > FWD_LIST_MAX) return -1;
+  // half-widths of every (table entry k, head h), all slope loads in flight
+  constexpr int SPER = LPT_MAX_HEADS / NT;
+  float sv[SPER];
+  {
+    int k = tid / hq, h = tid - (tid / hq) * hq;
+    const int dk = NT / hq, dh = NT - (NT / hq) * hq;
+#pragma unroll
+    for (int i = 0; i < SPER; ++i) {
+      if (i * NT < B * hq)   // uniform
+        sv[i] = pa.slopes[(int64_t)ord.seq[min(k, B - 1)] * pa.slopes_stride + h];
+      k += dk;
+      h += dh;
+      if (h >= hq) { h -= hq; ++k; }
+    }
+  }
+  for (int c = tid; c < LPT_CLASSES; c += NT) sc.hist[c] = 0;
+#pragma unroll
+  for (int i = 0; i < SPER; ++i) {
+    const int p = tid + i * NT;
+    if (i * NT < B * hq && p < B * hq)
+      sc.hw[p] = key_half_width(sv[i] * LOG2E, ord.lk[p / hq], pa.skip_log2);
+  }
+  __syncthreads();
+  auto entry_of = [&](int t) {   // last table entry whose first rank is <= t
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ord.start[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  };
+  for (int t = tid; t < nrt; t += NT) {   // tile_key_steps of every tile
+    const int k = entry_of(t);
+    const int lq = ord.lq[k], lk = ord.lk[k];
+    const int R0 = (t - ord.start[k]) * ROW_TILE, R1 = min(lq * hq, R0 + ROW_TILE);
+    const int hfirst = R0 / lq, hlast = (R1 - 1) / lq;
+    int lo = 0x7fffffff, hi = 0;
+    for (int h = hfirst; h <= hlast; ++h) {
+      const int ia = h == hfirst ? R0 - h * lq : 0;
+      const int ib = h == hlast ? R1 - 1 - h * lq : lq - 1;
+      const int hw = sc.hw[k * hq + h];
+      int l0, u0, l1, u1;
+      key_steps_of(max(ia + lk - lq, 0), hw, lk, l0, u0);
+      key_steps_of(max(ib + lk - lq, 0), hw, lk, l1, u1);
+      lo = min(lo, l0);
+      hi = max(hi, u1);
+    }
+    const int c = LPT_CLASSES - 1 - min(hi - lo, LPT_CLASSES - 1);
+    sc.cls[t] = c;
+    sc.ks[t][0] = lo;
+    sc.ks[t][1] = hi;
+    atomicAdd(&sc.hist[c], 1);
+  }
+  __syncthreads();
+  if (wave == 0) {   // class offsets: lane l scans classes 16 l .. 16 l + 15
+    constexpr int CPL = LPT_CLASSES / 64;
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) sum += sc.hist[lane * CPL + i];
+    int x = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    int run = x - sum;
+    for (int i = 0; i < CPL; ++i) {
+      sc.off[lane * CPL + i] = run;
+      run += sc.hist[lane * CPL + i];
+    }
+    if (lane == 63) sc.off[LPT_CLASSES] = run;
+  }
+  __syncthreads();
+  // wave 0 resolves the workgroup's ranks: class c of rank r (last class with
+  // off <= r), then the (r - off[c])-th tile of class c in table order
+  int n = 0;
+  if (wave == 0) {
+    for (int round = 0; round < rounds; ++round) {
+      const int r = round * P + ((round & 1) ? P - 1 - w : w);
+      if (r >= nrt) break;
+      int lo = 0, hi = LPT_CLASSES - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sc.off[mid] <= r) lo = mid; else hi = mid - 1;
+      }
+      const int c = lo;
+      int want = r - sc.off[c], t = -1;
+      for (int base = 0; base < nrt && t < 0; base += 64) {
+        const uint64_t m = __ballot(base + lane < nrt && sc.cls[base + lane] == c);
+        const int cnt = __popcll(m);
+        if (want < cnt) {
+          uint64_t mm = m;
+          for (int i = 0; i < want; ++i) mm &= mm - 1;   // drop the lowest want bits
+          t = base + __builtin_ctzll(mm);
+        } else {
+          want -= cnt;
+        }
+      }
+      const int k = entry_of(t);
+      if (lane == 0) {
+        list[n][0] = ord.seq[k];
+        list[n][1] = t - ord.start[k];
+        list[n][2] = ord.q0[k];
+        list[n][3] = ord.lq[k];
+        list[n][4] = ord.k0[k];
+        list[n][5] = ord.lk[k];
+        list[n][6] = sc.ks[t][0];
+        list[n][7] = sc.ks[t][1];
+      }
+      ++n;
+    }
+  }
+  return n;   // valid in wave 0; the caller broadcasts it
+}
+
+// Grid: workgroup 0 runs the planner (then, in the full-VJP call, the dK/dV
+// unit plan); workgroups 1 .. P (one per remaining compute unit) are
+// persistent and deal the row tiles among themselves like cards in a snake:
+// in round r workgroup w takes rank r P + w (r even) or r P + P - 1 - w (r
+// odd), so a workgroup whose first tile was among the longest takes one of
+// the shortest next.  The row tiles never wait for the planner: a workgroup
+// finds each tile and its key-step range from cu_q / cu_k itself (the order
+// table, tile_key_range), so the planner runs beside them.
+template <class T, bool CAP, bool DELTA>
+__global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
+  __shared__ __attribute__((aligned(16))) FwdShared sm;
+  __shared__ FwdOrder ord;
+  __shared__ int tinfo[8];
+  static_assert(sizeof(LptScratch) <= sizeof(FwdShared), "the ranking fits the tile buffers");
+
+  if (blockIdx.x == 0) {
+    plan_block<ROW_THREADS>(pa, *reinterpret_cast<PlanShared*>(&sm));
+    if (DELTA) {   // the full-VJP call: the dK/dV units, from the planner's ranges
+      __syncthreads();
+      plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
+    }
+    return;
+  }
+  const int w = (int)blockIdx.x - 1, P = (int)gridDim.x - 1;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  build_fwd_order<ROW_THREADS>(pa, ord);
+  const int status = ord.status;
+  if (status == 0) return;
+  // longest-first: the workgroup's tiles resolved in advance (nlist >= 0)
+  __shared__ int list[FWD_LIST_MAX][8];
+  __shared__ int nlist_s;
+  if (status == 1) {
+    const int n = lpt_list<ROW_THREADS>(pa, ord, *reinterpret_cast<LptScratch*>(&sm), list, w, P);
+    if (threadIdx.x == 0) nlist_s = n;
+  } else if (threadIdx.x == 0) {
+    nlist_s = -1;
+  }
+  __syncthreads();
+  const int nlist = nlist_s;
+  if (nlist >= 0) {
+    for (int i = 0; i < nlist; ++i) {
+      fwd_tile<T, CAP, DELTA>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3], list[i][4],
+                              list[i][5], list[i][6], list[i][7]);
+      __syncthreads();   // the next tile reuses the LDS buffers
+    }
+    return;
+  }
+  for (int round = 0;; ++round) {
+    const int r = round * P + ((round & 1) ? P - 1 - w : w);
+    if (status == 1 && r >= ord.nrt) break;
+    // wave 0 finds the tile of rank r and its key steps (the planner's
+    // range) and hands them over through LDS
+    if (wave == 0) {
+      RowTile rt;
+      bool ok = true;
+      if (status == 1) {   // last table entry whose first rank is <= r (a nonempty one)
+        int lo = 0, hi = ord.n - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (ord.start[mid] <= r) lo = mid; else hi = mid - 1;
+        }
+        rt.b = ord.seq[lo];
+        rt.tile = r - ord.start[lo];
+        rt.q0 = ord.q0[lo];
+        rt.lq = ord.lq[lo];
+        rt.k0 = ord.k0[lo];
+        rt.lk = ord.lk[lo];
+      } else {
+        ok = find_row_tile(pa, r, rt);
+      }
+      int klo = 0, khi = 0;
+      if (ok) tile_key_range(pa, rt, klo, khi);
+      if (lane == 0) {
+        tinfo[0] = ok ? rt.b : -1;
+        tinfo[1] = rt.tile;
+        tinfo[2] = rt.q0;
+        tinfo[3] = rt.lq;
+        tinfo[4] = rt.k0;
+        tinfo[5] = rt.lk;
+        tinfo[6] = klo;
+        tinfo[7] = khi;
+      }
+    }
+    __syncthreads();
+    const int b = tinfo[0];
+    if (b < 0) break;
+    fwd_tile<T, CAP, DELTA>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5], tinfo[6],
+                            tinfo[7]);
+    __syncthreads();   // the next tile reuses tinfo and the LDS buffers
+  }
+}
+
+
 template <class T>
 static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
                                int grid, hipStream_t s) {
@@ -446,7 +737,8 @@ static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, 
 
 hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
                       bool with_delta, hipStream_t s) {
-  const int grid = 1 + a.fwd_slots;
+  // the planner plus one persistent workgroup per remaining compute unit
+  const int grid = 1 + max(1, a.kv_wgs - 1);
   if (a.batch <= 0) return hipSuccess;
   return dtype == DT_BF16 ? launch_fwd_t<BF16>(a, pa, cap, with_delta, grid, s)
                           : launch_fwd_t<F16>(a, pa, cap, with_delta, grid, s);
