@@ -114,6 +114,24 @@ def test_large_batch_planner_paths():
     assert_lse(to_np(got["lse"]), ref["lse"], "large batch")
 
 
+def test_many_short_sequences():
+    """600 sequences: past the forward's 512-entry tile table, so each forward
+    workgroup finds its tiles with the batch-order search (find_row_tile); a
+    fifth of the sequences have no query rows."""
+    need_gpu()
+    rng = np.random.default_rng(23)
+    lq = rng.integers(0, 5, size=600)
+    lk = rng.integers(1, 90, size=600)
+    wl = W.custom_workload(lq=lq.tolist(), lk=lk.tolist(), hq=48, dtype="f16", width=160, step=1,
+                           seed=12)
+    g = wl.to("cuda")
+    got = gpu_full(g)
+    ref = oracle_full(wl)
+    for name in ("out", "dq", "dk", "dv"):
+        assert_close(name, to_np(got[name]), ref[name], TOL[wl.dtype], "many short")
+    assert_lse(to_np(got["lse"]), ref["lse"], "many short")
+
+
 def test_empty_batch():
     need_gpu()
     wl = W.custom_workload(lq=[0, 0], lk=[0, 0], hq=48)
