@@ -4,6 +4,6 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library.  It shares no code with
 the HIP path.
 """
-from .attention import forward, rows_vjp, sequence_vjp, vjp
+from .attention import forward, rows_vjp, sequence_vjp, vjp, window_bounds
 
 __all__ = ["forward", "vjp", "sequence_vjp", "rows_vjp"]

@@ -14,8 +14,9 @@ What is computed (sources are the pages' own words, restated):
   ``scale_multiplier / sqrt(head_dim)`` (0.75 on the page), passed through the
   soft cap ``c * tanh(x / c)`` (c = 3 on the page), then shifted by the ALiBi
   term ``-slope[b, h] * |i + Lk - Lq - j|`` with positions local to the
-  sequence, and normalised by a softmax over that sequence's keys.  Every case
-  is noncausal with no window.
+  sequence, and normalised by a softmax over that sequence's keys.  The page's
+  cases are all noncausal with no window; its signature still carries
+  ``causal``, ``window_left`` and ``window_right``.
 * Same page, section "Hard Constraints": the cap is applied to the scaled dot
   product before ALiBi and before any masking; the K/V gradients are summed
   over every query head that shares the K/V head; the function returns
@@ -34,6 +35,14 @@ Readings taken where the pages are silent (each is listed in the design doc):
         dS = dA * (1 - tanh^2(S / c)),  dQ = sigma dS K,
         dK = sigma sum_h dS^T Q,  dV = sum_h P^T dO.
 
+  - masks (the pages name the arguments but never define them): key j of
+    query row i is kept iff i + Lk - Lq - window_left <= j <= i + Lk - Lq +
+    window_right, a negative bound meaning no limit on that side; ``causal``
+    sets window_right = 0 (alignment at the bottom right, like the ALiBi
+    centre).  Masking drops keys from the softmax; the cap and ALiBi are
+    unchanged for the kept keys.  A row that keeps no key is a row with no
+    keys (L = -inf, output and gradients 0).
+
 Everything is dense per (sequence, head): no tiling, no online softmax, no
 fusion.  Rows may be processed in chunks to bound memory; each row's softmax
 still spans all of its sequence's keys, so the arithmetic is unchanged.
@@ -44,14 +53,21 @@ import math
 
 import numpy as np
 
-__all__ = ["sequence_vjp", "forward", "vjp", "rows_vjp"]
+__all__ = ["sequence_vjp", "forward", "vjp", "rows_vjp", "window_bounds"]
+
+
+def window_bounds(causal=False, window_left=-1, window_right=-1):
+    """(left, right) key bounds relative to a row's centre i + Lk - Lq; -1 = none."""
+    wl = int(window_left) if window_left is not None and window_left >= 0 else -1
+    wr = 0 if causal else (int(window_right) if window_right is not None and window_right >= 0 else -1)
+    return wl, wr
 
 
 def _as_f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv):
+def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv, window=(-1, -1)):
     """Forward and VJP for one head of one sequence, rows at query positions ``i_pos``.
 
     Qh [n, D], dOh [n, D] (or None), K/V [Lk, D]; ``i_pos`` are the local
@@ -84,13 +100,25 @@ def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv):
     # ALiBi: -slope * |q_position + key_length - query_length - k_position|
     dist = np.abs(i_pos[:, None] + (Lk - Lq) - np.arange(Lk)[None, :]).astype(np.float64)
     A = T - slope * dist
-    # softmax over the sequence's keys
-    m = A.max(axis=1, keepdims=True)
+    # mask: keys outside [centre - window_left, centre + window_right] leave
+    # the softmax (a negative bound is no bound)
+    wl, wr = window
+    centre = i_pos[:, None] + (Lk - Lq)
+    j = np.arange(Lk)[None, :]
+    keep = np.ones((n, Lk), dtype=bool)
+    if wl >= 0:
+        keep &= j >= centre - wl
+    if wr >= 0:
+        keep &= j <= centre + wr
+    A = np.where(keep, A, -np.inf)
+    has = keep.any(axis=1)
+    # softmax over the kept keys; a row that keeps none stays at zero
+    m = np.where(has, A.max(axis=1), 0.0)[:, None]
     E = np.exp(A - m)
     l = E.sum(axis=1, keepdims=True)
-    P = E / l
+    P = E / np.where(l > 0.0, l, 1.0)
     res["out"] = P @ V
-    res["lse"] = (m + np.log(l))[:, 0]
+    res["lse"] = np.where(has, (m + np.log(np.where(l > 0.0, l, 1.0)))[:, 0], -np.inf)
     if dOh is None:
         return res
 
@@ -106,7 +134,7 @@ def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv):
     return res
 
 
-def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096):
+def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096, window=(-1, -1)):
     """Forward and full VJP of one sequence.
 
     Q, dO: [Lq, Hq, D]; K, V: [Lk, Hkv, D]; slopes: [Hq].  ``dO`` may be None
@@ -135,7 +163,7 @@ def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096)
             part = _head_rows(Q[r0:r1, h], K[:, g], V[:, g],
                               None if dO is None else dO[r0:r1, h],
                               np.arange(r0, r1), Lq, Lk, float(slopes[h]),
-                              softcap, sigma, want_kv=True)
+                              softcap, sigma, want_kv=True, window=window)
             out[r0:r1, h] = part["out"]
             lse[r0:r1, h] = part["lse"]
             if dO is not None:
@@ -148,7 +176,7 @@ def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096)
     return res
 
 
-def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
+def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, window=(-1, -1)):
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
@@ -169,7 +197,7 @@ def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
         k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
         part = sequence_vjp(q[q0:q1], k[k0:k1], v[k0:k1],
                             None if dout is None else dout[q0:q1],
-                            slopes[b], softcap, scale_multiplier)
+                            slopes[b], softcap, scale_multiplier, window=window)
         res["out"][q0:q1] = part["out"]
         res["lse"][q0:q1] = part["lse"]
         if dout is not None:
@@ -180,18 +208,23 @@ def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
     return res
 
 
-def forward(q, k, v, cu_q, cu_k, alibi_slopes, softcap, scale_multiplier):
+def forward(q, k, v, cu_q, cu_k, alibi_slopes, softcap, scale_multiplier, causal=False,
+            window_left=-1, window_right=-1):
     """out [Tq,Hq,D] and lse [Tq,Hq] (natural log) for a packed ragged batch."""
-    res = _run(q, k, v, cu_q, cu_k, alibi_slopes, None, softcap, scale_multiplier)
+    res = _run(q, k, v, cu_q, cu_k, alibi_slopes, None, softcap, scale_multiplier,
+               window_bounds(causal, window_left, window_right))
     return res["out"], res["lse"]
 
 
-def vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier):
+def vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, causal=False,
+        window_left=-1, window_right=-1):
     """Forward plus full VJP; dict with out, dq, dk, dv, lse, delta (float64)."""
-    return _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier)
+    return _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier,
+                window_bounds(causal, window_left, window_right))
 
 
-def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads):
+def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads, causal=False,
+             window_left=-1, window_right=-1):
     """out, lse, dq, delta for selected rows of one sequence.
 
     Each row's result depends only on its own q/dout row and the sequence's
@@ -217,7 +250,8 @@ def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads):
         g = int(h) // group
         part = _head_rows(Q[tokens[sel], h], K[:, g], V[:, g], dO[tokens[sel], h],
                           tokens[sel], Lq, Lk, float(slopes[h]), softcap, sigma,
-                          want_kv=False)
+                          want_kv=False,
+                          window=window_bounds(causal, window_left, window_right))
         for key in res:
             res[key][sel] = part[key]
     return res

@@ -386,3 +386,119 @@ def test_rows_vjp_matches_sequence():
                            case["alibi_slopes"][0], 3.0, 0.75, toks, heads)
     for name in ("out", "dq", "lse", "delta"):
         np.testing.assert_allclose(part[name], full[name][toks, heads], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- causal / window masks
+# The pages name causal, window_left and window_right without defining them;
+# the reading pinned here keeps key j of row i iff
+# i + Lk - Lq - window_left <= j <= i + Lk - Lq + window_right (negative = no
+# bound, causal = right bound 0).
+
+def _vjp_w(case, causal=False, wl=-1, wr=-1):
+    return oracle.vjp(case["q"], case["k"], case["v"], case["cu_q"], case["cu_k"],
+                      case["alibi_slopes"], case["dout"], case["softcap"],
+                      case["scale_multiplier"], causal=causal, window_left=wl, window_right=wr)
+
+
+def test_window_bounds_reading():
+    assert oracle.window_bounds(False, -1, -1) == (-1, -1)
+    assert oracle.window_bounds(True, -1, -1) == (-1, 0)
+    assert oracle.window_bounds(True, 5, 7) == (5, 0)
+    assert oracle.window_bounds(False, 3, 0) == (3, 0)
+
+
+def test_window_zero_width_is_one_key():
+    """window (0, 0): each row keeps only the key at its centre i + Lk - Lq, so
+    out = v_centre, L = its logit, dq = dk = 0 and dv_c = sum of dout over the
+    rows centred on c; rows whose centre lies before key 0 keep nothing."""
+    rng = np.random.default_rng(31)
+    case = _rand_case(rng, [6, 3], [4, 9], hq=3, D=5, scale=1.5)
+    res = _vjp_w(case, wl=0, wr=0)
+    sigma = case["scale_multiplier"] / math.sqrt(5)
+    dv = np.zeros_like(case["v"])
+    for b in range(2):
+        q0, q1 = case["cu_q"][b], case["cu_q"][b + 1]
+        k0, k1 = case["cu_k"][b], case["cu_k"][b + 1]
+        Lq, Lk = q1 - q0, k1 - k0
+        for i in range(Lq):
+            c = i + Lk - Lq
+            for h in range(3):
+                if c < 0:
+                    assert res["lse"][q0 + i, h] == -np.inf
+                    assert np.all(res["out"][q0 + i, h] == 0)
+                    continue
+                np.testing.assert_allclose(res["out"][q0 + i, h], case["v"][k0 + c, 0], atol=1e-15)
+                s = sigma * case["q"][q0 + i, h] @ case["k"][k0 + c, 0]
+                assert abs(res["lse"][q0 + i, h] - 3.0 * math.tanh(s / 3.0)) < 1e-14
+                dv[k0 + c, 0] += case["dout"][q0 + i, h]
+    assert np.abs(res["dq"]).max() <= 1e-14 and np.abs(res["dk"]).max() <= 1e-14
+    np.testing.assert_allclose(res["dv"], dv, atol=1e-14)
+
+
+def test_no_bounds_is_noncausal():
+    rng = np.random.default_rng(32)
+    case = _rand_case(rng, [4, 7], [9, 3], hq=2)
+    a, b = _vjp(case), _vjp_w(case, False, -1, -1)
+    for key in ("out", "lse", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("lq,lk", [(5, 11), (9, 4), (7, 7)])
+@pytest.mark.parametrize("causal,wl,wr", [(True, -1, -1), (True, 2, -1), (False, 3, 0),
+                                          (False, 0, 2), (False, 2, 5), (False, -1, 3),
+                                          (False, 4, -1)])
+def test_window_row_equals_unmasked_slice(lq, lk, causal, wl, wr):
+    """Each masked row equals the unmasked oracle on the keys it keeps: row i
+    of the masked problem is placed at position i' = c - lo of a square
+    problem over keys lo..hi (c = i + Lk - Lq), whose centre i' + 0 sits at
+    the same distance from every key; other rows of the square problem are
+    zero (zero q and dout rows add nothing to dK / dV).  dK / dV of the masked
+    problem are the sums of the slices' dK / dV over rows and heads."""
+    rng = np.random.default_rng(100 + lq * 13 + lk)
+    hq, D = 2, 4
+    case = _rand_case(rng, [lq], [lk], hq=hq, D=D, scale=1.3)
+    res = _vjp_w(case, causal, wl, wr)
+    ewl, ewr = oracle.window_bounds(causal, wl, wr)
+    dk = np.zeros_like(case["k"])
+    dv = np.zeros_like(case["v"])
+    for i in range(lq):
+        c = i + lk - lq
+        lo = max(0, c - ewl) if ewl >= 0 else 0
+        hi = min(lk - 1, c + ewr) if ewr >= 0 else lk - 1
+        for h in range(hq):
+            if lo > hi:
+                assert res["lse"][i, h] == -np.inf and np.all(res["out"][i, h] == 0)
+                assert np.all(res["dq"][i, h] == 0)
+                continue
+            n = hi - lo + 1
+            # a problem over keys lo..hi whose row i' has centre i' + n - Lq' =
+            # c - lo (before key 0 when the row's centre is clamped)
+            ip = c - lo
+            Lqs, ir = n - min(ip, 0), max(ip, 0)
+            sq = np.zeros((Lqs, 1, D))
+            sd = np.zeros((Lqs, 1, D))
+            sq[ir, 0] = case["q"][i, h]
+            sd[ir, 0] = case["dout"][i, h]
+            part = oracle.sequence_vjp(sq, case["k"][lo:hi + 1], case["v"][lo:hi + 1], sd,
+                                       case["alibi_slopes"][0][h:h + 1], case["softcap"],
+                                       case["scale_multiplier"])
+            np.testing.assert_allclose(res["out"][i, h], part["out"][ir, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(res["lse"][i, h], part["lse"][ir, 0], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(res["dq"][i, h], part["dq"][ir, 0], rtol=0, atol=1e-13)
+            dk[lo:hi + 1] += part["dk"]
+            dv[lo:hi + 1] += part["dv"]
+    np.testing.assert_allclose(res["dk"], dk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(res["dv"], dv, rtol=0, atol=1e-12)
+
+
+def test_window_mirror_symmetry():
+    """With Lq = Lk, reversing the order of queries and keys maps centre i to
+    centre Lq - 1 - i and swaps the two window bounds."""
+    rng = np.random.default_rng(33)
+    case = _rand_case(rng, [9], [9], hq=2, D=4)
+    a = _vjp_w(case, False, 1, 4)
+    rev = dict(case, q=case["q"][::-1].copy(), k=case["k"][::-1].copy(), v=case["v"][::-1].copy(),
+               dout=case["dout"][::-1].copy())
+    b = _vjp_w(rev, False, 4, 1)
+    for key in ("out", "lse", "dq", "dk", "dv"):
+        np.testing.assert_allclose(a[key], b[key][::-1], rtol=0, atol=1e-13, err_msg=key)
