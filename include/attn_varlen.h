@@ -23,9 +23,18 @@
  *   flash-attention-gradient-recompute", section "Root causes addressed");
  *   keys of a sequence with Lq == 0 get dk = dv = 0.
  *
+ * Masks.  The page's signature carries causal, window_left and window_right
+ * but every case it defines is noncausal with no window (-1, -1).  Reading
+ * taken for the other values: key j of local query row i is kept iff
+ *   i + Lk - Lq - window_left <= j <= i + Lk - Lq + window_right,
+ * a bound of -1 meaning no bound on that side and causal = 1 setting
+ * window_right = 0 (aligned at the bottom right, like the ALiBi centre).  The
+ * cap and ALiBi of kept keys are unchanged; a row that keeps no key is a row
+ * with no keys (out = 0, dq = 0, lse = -inf).
+ *
  * Supported: dtype F16 or BF16 (one dtype for every 16-bit tensor), hkv == 1,
- * head_dim == 160, causal == 0, window_left == window_right == -1 (the only
- * case the page defines).  Anything else returns ATTN_UNSUPPORTED.
+ * head_dim == 160.  Anything else returns ATTN_UNSUPPORTED; causal outside
+ * {0, 1} or a window bound below -1 returns ATTN_INVALID_ARG.
  *
  * Tensors.  Every activation tensor is a strided view [tokens, heads, 160]
  * with a contiguous feature axis (feature stride 1) and caller-chosen token
@@ -117,9 +126,9 @@ typedef struct {
   const int32_t* cu_k;         /* device int32 [B+1] */
   const float* alibi_slopes;   /* device float32 [B, hq], row stride slopes_stride */
   int64_t slopes_stride;       /* elements between consecutive sequences (>= hq) */
-  int32_t causal;              /* must be 0 */
-  int32_t window_left;         /* must be -1 */
-  int32_t window_right;        /* must be -1 */
+  int32_t causal;              /* 0 or 1 (1: window_right is taken as 0) */
+  int32_t window_left;         /* keys kept down to centre - window_left; -1 = all */
+  int32_t window_right;        /* keys kept up to centre + window_right; -1 = all */
   float softcap;               /* c > 0 caps logits at c*tanh(x/c); 0 = no cap */
   float scale_multiplier;      /* logit scale = scale_multiplier / sqrt(head_dim) */
   int32_t flags;               /* attn_flag bits; 0 for the default behaviour */

@@ -111,10 +111,11 @@ attn_status check_problem(const attn_problem* p) {
   if (p->head_dim != HEAD_DIM)
     return fail(ATTN_UNSUPPORTED, "head_dim %d != 160", p->head_dim);
   if (p->hkv != 1) return fail(ATTN_UNSUPPORTED, "hkv %d != 1", p->hkv);
-  if (p->causal != 0) return fail(ATTN_UNSUPPORTED, "causal masking is not supported");
-  if (p->window_left != -1 || p->window_right != -1)
-    return fail(ATTN_UNSUPPORTED, "sliding windows are not supported (got %d, %d)",
-                p->window_left, p->window_right);
+  if (p->causal != 0 && p->causal != 1)
+    return fail(ATTN_INVALID_ARG, "causal must be 0 or 1 (got %d)", p->causal);
+  if (p->window_left < -1 || p->window_right < -1)
+    return fail(ATTN_INVALID_ARG, "window bounds must be >= -1 (got %d, %d)", p->window_left,
+                p->window_right);
   if (p->batch < 0) return fail(ATTN_INVALID_ARG, "batch %d < 0", p->batch);
   if (p->hq < 1 || p->hq > 1024) return fail(ATTN_INVALID_ARG, "hq %d outside 1..1024", p->hq);
   if (p->total_q < 0 || p->total_k < 0)
@@ -258,6 +259,8 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.fwd_slots = (int)L.row_tiles;
   a.fwd_slots = (int)L.row_tiles;
   pa.kv_wgs = (int)L.kv_wgs;
+  a.win_left = p->window_left;
+  a.win_right = p->causal ? 0 : p->window_right;
   pa.seg_items = KV_SEGMENT_ITEMS;
   a.kv_wgs = (int)L.kv_wgs;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);

@@ -107,7 +107,7 @@ __device__ __forceinline__ int tile_mask_next(TileMask& m, const KvUnit& u, int 
 }
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
-template <class T, bool CAP, int ROLE, bool LATE>
+template <class T, bool CAP, int ROLE, bool LATE, bool WIN>
 __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const KvUnit& u,
                                           int wave, int lane) {
   const int l32 = lane & 31, g = lane >> 5;
@@ -285,8 +285,18 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
   // P and dS of accumulator register r (row rbase + 8 (r/4) + r%4)
-  auto pointwise = [&](int buf, int r, f32x16 (&S)[KB], f32x16 (&dP)[KB]) {
+  auto pointwise = [&](int buf, int r, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB]) {
     const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
+    // WIN: the row keeps keys [wlo, whi] around its unclamped centre
+    float wlo = -3.0e38f, whi = 3.0e38f;
+    if (WIN) {
+      int tok, hd;
+      unfold_row(r0 + rbase + (r >> 2) * 8 + (r & 3), u.lq, (uint32_t)u.lqmul,
+                 (uint32_t)u.lqshift, tok, hd);
+      const int c = tok + u.Lk - u.lq;
+      if (a.win_left >= 0) wlo = (float)(c - a.win_left);
+      if (a.win_right >= 0) whi = (float)(c + a.win_right);
+    }
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
@@ -299,6 +309,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
         p = fast_exp2(__builtin_fmaf(S[kb][r], a.lc.s_lin, bias));
         w = 1.0f;
       }
+      if (WIN) p = keyf[kb] >= wlo && keyf[kb] <= whi ? p : 0.0f;
       S[kb][r] = p;
       dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
     }
@@ -326,7 +337,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   auto pointwise_publish = [&](int buf, int slot, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB],
                                u32x4 (&own)[KB][2]) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) pointwise(buf, r, S, dP);
+    for (int r = 0; r < 16; ++r) pointwise(buf, r, r0, S, dP);
     publish(slot, r0, S, dP, own);
   };
 
@@ -466,7 +477,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 
 }  // namespace
 
-template <class T, bool CAP>
+template <class T, bool CAP, bool WIN>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) KvShared sm;
 
@@ -519,11 +530,11 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
     // waves w and w + 4 share a SIMD
     if (wave < 4) {
-      if (wave & 1) dkdv_wave<T, CAP, 1, false>(a, sm, u, wave, lane);
-      else dkdv_wave<T, CAP, 0, false>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, CAP, 1, false, WIN>(a, sm, u, wave, lane);
+      else dkdv_wave<T, CAP, 0, false, WIN>(a, sm, u, wave, lane);
     } else {
-      if (wave & 1) dkdv_wave<T, CAP, 1, true>(a, sm, u, wave, lane);
-      else dkdv_wave<T, CAP, 0, true>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, CAP, 1, true, WIN>(a, sm, u, wave, lane);
+      else dkdv_wave<T, CAP, 0, true, WIN>(a, sm, u, wave, lane);
     }
     w = vs + l;
     __syncthreads();   // the next segment reuses the LDS buffers
@@ -532,8 +543,14 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
 
 template <class T>
 static hipError_t launch_dkdv_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
-  if (cap) hipLaunchKernelGGL((dkdv_kernel<T, true>), grid, KV_THREADS, 0, s, a);
-  else hipLaunchKernelGGL((dkdv_kernel<T, false>), grid, KV_THREADS, 0, s, a);
+  const bool win = a.win_left >= 0 || a.win_right >= 0;
+  if (cap) {
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, true, true>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, true, false>), grid, KV_THREADS, 0, s, a);
+  } else {
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, false, true>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, false, false>), grid, KV_THREADS, 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -238,7 +238,7 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
 
 }  // namespace
 
-template <class T, bool CAP>
+template <class T, bool CAP, bool WIN>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) union {
     DqShared r;
@@ -295,6 +295,10 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const float cb0 = info[1] - (float)(4 * g);
   const float boff = info[2];
   const float dl = info[3];
+  // window (WIN): the row keeps keys [wlo, whi) around its unclamped centre
+  const int wc = ti + Lk - sq[SQ_LQ];
+  const int wlo = WIN && a.win_left >= 0 ? wc - a.win_left : 0;
+  const int whi = WIN && a.win_right >= 0 ? min(Lk, wc + a.win_right + 1) : Lk;
 
   f32x16 dQ[DBLK];
 #pragma unroll
@@ -327,7 +331,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     const uint16_t* Kb = sm.r.k[buf];
     const uint16_t* Vb = sm.r.v[buf];
     const float cb = cb0 - (float)kbase;
-    const int kleft = Lk - kbase - 4 * g;
+    const int kleft = whi - kbase - 4 * g;
+    const int kfrom = wlo - kbase - 4 * g;
 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
@@ -353,7 +358,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
           p = fast_exp2(__builtin_fmaf(S[r], a.lc.s_lin, bias));
           w = 1.0f;
         }
-        if (decltype(masked)::value) p = jl < kleft ? p : 0.0f;
+        if (WIN) p = jl >= kfrom && jl < kleft ? p : 0.0f;
+        else if (decltype(masked)::value) p = jl < kleft ? p : 0.0f;
         S[r] = p * (dP[r] - dl) * w;
       }
       u32x4 sb[2];
@@ -401,8 +407,14 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
 
 template <class T>
 static hipError_t launch_dq_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
-  if (cap) hipLaunchKernelGGL((dq_kernel<T, true>), grid, ROW_THREADS, 0, s, a);
-  else hipLaunchKernelGGL((dq_kernel<T, false>), grid, ROW_THREADS, 0, s, a);
+  const bool win = a.win_left >= 0 || a.win_right >= 0;
+  if (cap) {
+    if (win) hipLaunchKernelGGL((dq_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a);
+  } else {
+    if (win) hipLaunchKernelGGL((dq_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a);
+  }
   return hipGetLastError();
 }
 

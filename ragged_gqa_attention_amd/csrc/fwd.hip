@@ -71,7 +71,7 @@ static_assert(sizeof(PlanShared) <= sizeof(FwdShared), "the planner fits the til
 // beside them on one compute unit.
 // One 256-row tile of the forward: sequence b (extents q0, Lq, k0, Lk), tile
 // `tile` of its folded rows, key steps [klo, khi).
-template <class T, bool CAP, bool DELTA>
+template <class T, bool CAP, bool DELTA, bool WIN>
 __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const int b,
                                          const int tile, const int q0, const int Lq,
                                          const int k0, const int Lk, const int klo,
@@ -117,6 +117,11 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   // kbase + 32 kb + 8 (r/4) + 4 g + r%4; cb0 - (kbase + 32 kb + 8 (r/4) + r%4)
   // is then j's signed distance from the clamped centre max(i + Lk - Lq, 0)
   const float cb0 = (float)(max(ti + Lk - Lq, 0) - 4 * g);
+  // window (WIN): the row keeps keys [wlo, whi), bounds around its unclamped
+  // centre i + Lk - Lq; a row keeping none ends with l = 0 (out 0, L = -inf)
+  const int wc = ti + Lk - Lq;
+  const int wlo = WIN && a.win_left >= 0 ? wc - a.win_left : 0;
+  const int whi = WIN && a.win_right >= 0 ? min(Lk, wc + a.win_right + 1) : Lk;
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - ti);
   float m = CAP ? 0.0f : -__builtin_inff();       // log2 units, relative to moff
   float lsum = 0.0f;     // exact sum of P
@@ -159,7 +164,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   // the compare and select cost a VALU pair per logit)
   auto logits = [&](int kb, int kbase, auto masked) {
     const float cb = cb0 - (float)kbase;
-    const int kleft = Lk - kbase - 4 * g;          // keys of this lane group still in range
+    const int kleft = whi - kbase - 4 * g;         // keys of this lane group still in range
+    const int kfrom = wlo - kbase - 4 * g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
@@ -169,7 +175,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
                            -slope2 * __builtin_fabsf(cb - (float)jl));
       else
         x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
-      if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
+      if (WIN) x = jl >= kfrom && jl < kleft ? x : -__builtin_inff();
+      else if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
       S[kb][r] = x;
     }
   };
@@ -293,7 +300,9 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
         for (int r = 0; r < 16; ++r) tmax = __builtin_fmaxf(tmax, S[kb][r]);
       tmax = __builtin_fmaxf(tmax, swap_half(tmax));
       const float mnew = __builtin_fmaxf(m, tmax);
-      const float alpha = fast_exp2(m - mnew);
+      // a windowed row may see only masked keys so far: subtract 0, not -inf
+      const float msub = WIN && mnew == -__builtin_inff() ? 0.0f : mnew;
+      const float alpha = fast_exp2(m - msub);
       m = mnew;
       lsum *= alpha;
       lsum_r *= alpha;
@@ -302,7 +311,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[kb][r] -= mnew;
+        for (int r = 0; r < 16; ++r) S[kb][r] -= msub;
       probs(0);
       probs(1);
       pv(0, sm.v[buf]);
@@ -632,7 +641,7 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
 // the shortest next.  The row tiles never wait for the planner: a workgroup
 // finds each tile and its key-step range from cu_q / cu_k itself (the order
 // table, tile_key_range), so the planner runs beside them.
-template <class T, bool CAP, bool DELTA>
+template <class T, bool CAP, bool DELTA, bool WIN>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) FwdShared sm;
   __shared__ FwdOrder ord;
@@ -666,7 +675,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   const int nlist = nlist_s;
   if (nlist >= 0) {
     for (int i = 0; i < nlist; ++i) {
-      fwd_tile<T, CAP, DELTA>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3], list[i][4],
+      fwd_tile<T, CAP, DELTA, WIN>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3], list[i][4],
                               list[i][5], list[i][6], list[i][7]);
       __syncthreads();   // the next tile reuses the LDS buffers
     }
@@ -711,26 +720,26 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     __syncthreads();
     const int b = tinfo[0];
     if (b < 0) break;
-    fwd_tile<T, CAP, DELTA>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5], tinfo[6],
+    fwd_tile<T, CAP, DELTA, WIN>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5], tinfo[6],
                             tinfo[7]);
     __syncthreads();   // the next tile reuses tinfo and the LDS buffers
   }
 }
 
 
-template <class T>
+template <class T, bool WIN>
 static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
                                int grid, hipStream_t s) {
   if (cap) {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, true, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, true, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
   } else {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, false, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, false, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
   }
   return hipGetLastError();
 }
@@ -740,8 +749,11 @@ hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap
   // the planner plus one persistent workgroup per remaining compute unit
   const int grid = 1 + max(1, a.kv_wgs - 1);
   if (a.batch <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_fwd_t<BF16>(a, pa, cap, with_delta, grid, s)
-                          : launch_fwd_t<F16>(a, pa, cap, with_delta, grid, s);
+  if (a.win_left >= 0 || a.win_right >= 0)
+    return dtype == DT_BF16 ? launch_fwd_t<BF16, true>(a, pa, cap, with_delta, grid, s)
+                            : launch_fwd_t<F16, true>(a, pa, cap, with_delta, grid, s);
+  return dtype == DT_BF16 ? launch_fwd_t<BF16, false>(a, pa, cap, with_delta, grid, s)
+                          : launch_fwd_t<F16, false>(a, pa, cap, with_delta, grid, s);
 }
 
 }  // namespace rga

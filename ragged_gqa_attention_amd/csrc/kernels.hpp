@@ -69,6 +69,11 @@ struct AttnArgs {
   int kv_wgs;           // dK/dV workgroups (each takes an equal share of the visits)
   LogitConsts lc;
   Plan plan;
+  // Key window of row i (local positions): keys j with
+  // i + Lk - Lq - win_left <= j <= i + Lk - Lq + win_right are kept, a negative
+  // bound being no bound (causal: win_right = 0); both negative = no mask.
+  int win_left;
+  int win_right;
 };
 
 struct PlanArgs {

@@ -62,9 +62,9 @@ def _call_fwd(prob, q=None, k=None, v=None, out=None, ws_bytes=1 << 30, ws=0x400
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(causal=1), _lib.ATTN_UNSUPPORTED),
-    (dict(window_left=128), _lib.ATTN_UNSUPPORTED),
-    (dict(window_right=0), _lib.ATTN_UNSUPPORTED),
+    (dict(causal=2), _lib.ATTN_INVALID_ARG),
+    (dict(window_left=-2), _lib.ATTN_INVALID_ARG),
+    (dict(window_right=-7), _lib.ATTN_INVALID_ARG),
     (dict(head_dim=128), _lib.ATTN_UNSUPPORTED),
     (dict(hkv=2), _lib.ATTN_UNSUPPORTED),
     (dict(dtype=7), _lib.ATTN_UNSUPPORTED),

@@ -184,11 +184,9 @@ def test_invalid_seqlens_are_flagged():
 def test_python_argument_errors():
     need_gpu()
     g = W.make_workload(0).to("cuda")
-    with pytest.raises(NotImplementedError):
-        rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, causal=True)
-    with pytest.raises(NotImplementedError):
+    with pytest.raises(ValueError):
         rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout,
-                                 window_left=16)
+                                 window_left=-3)
     with pytest.raises(ValueError):
         rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes.double(), g.dout)
     with pytest.raises(ValueError):
