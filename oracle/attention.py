@@ -17,10 +17,10 @@ What is computed (sources are the pages' own words, restated):
   sequence, and normalised by a softmax over that sequence's keys.  The page's
   cases are all noncausal with no window; its signature still carries
   ``causal``, ``window_left`` and ``window_right``.
-* Same page, section "Hard Constraints": the cap is applied to the scaled dot
-  product before ALiBi and before any masking; the K/V gradients are summed
-  over every query head that shares the K/V head; the function returns
-  (out, dq, dk, dv) in the inputs' packed layouts.
+* Same page, section "Hard Constraints": order of the logit steps is tanh
+  cap first, then the ALiBi bias, then the mask; dK and dV collect the
+  contributions of all query heads mapped to their K/V head; the results are
+  (out, dq, dk, dv), shaped and typed like the packed inputs.
 * Page "python-20261012-ragged-flash-attention-gradient-recompute", section
   "Root causes addressed": the stored row statistic is L = m + log l
   (natural log); a row with no keys has L = -inf, output 0 and gradient 0.

@@ -502,3 +502,63 @@ def test_window_mirror_symmetry():
     b = _vjp_w(rev, False, 4, 1)
     for key in ("out", "lse", "dq", "dk", "dv"):
         np.testing.assert_allclose(a[key], b[key][::-1], rtol=0, atol=1e-13, err_msg=key)
+
+
+# ---------------------------------------------------------------- row chunking
+def test_row_chunks_do_not_change_the_result():
+    """sequence_vjp splits a head's query rows into chunks to bound memory; every
+    chunk size gives the same result (each row's softmax spans all keys), which
+    exercises the chunk boundaries that long sequences reach."""
+    rng = np.random.default_rng(25)
+    case = _rand_case(rng, [7], [6], hq=3, D=5, scale=2.0)
+    args = (case["q"], case["k"], case["v"], case["dout"], case["alibi_slopes"][0], 3.0, 0.75)
+    whole = oracle.sequence_vjp(*args, row_chunk=4096)
+    for chunk in (1, 2, 3, 6):
+        part = oracle.sequence_vjp(*args, row_chunk=chunk)
+        for name in ("out", "lse", "dq", "delta", "dk", "dv"):
+            np.testing.assert_allclose(part[name], whole[name], rtol=1e-15, atol=1e-15,
+                                       err_msg=f"chunk {chunk} {name}")
+    for chunk in (2, 5):
+        a = oracle.sequence_vjp(*args, row_chunk=chunk, window=(1, 2))
+        b = oracle.sequence_vjp(*args, window=(1, 2))
+        for name in ("out", "lse", "dq", "dk", "dv"):
+            np.testing.assert_allclose(a[name], b[name], rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("causal,wl,wr", [(True, -1, -1), (False, 2, 1), (False, -1, 0)])
+def test_rows_vjp_matches_sequence_with_mask(causal, wl, wr):
+    rng = np.random.default_rng(26)
+    case = _rand_case(rng, [9], [5], hq=3, D=5, scale=2.0)
+    full = oracle.sequence_vjp(case["q"], case["k"], case["v"], case["dout"],
+                               case["alibi_slopes"][0], 3.0, 0.75,
+                               window=oracle.window_bounds(causal, wl, wr))
+    toks = np.array([0, 8, 3, 1, 5, 6])
+    heads = np.array([2, 0, 1, 0, 2, 1])
+    part = oracle.rows_vjp(case["q"], case["k"], case["v"], case["dout"],
+                           case["alibi_slopes"][0], 3.0, 0.75, toks, heads, causal=causal,
+                           window_left=wl, window_right=wr)
+    for name in ("out", "dq", "lse", "delta"):
+        np.testing.assert_array_equal(np.isneginf(part[name]), np.isneginf(full[name][toks, heads]))
+        fin = np.isfinite(full[name][toks, heads])
+        np.testing.assert_allclose(part[name][fin], full[name][toks, heads][fin],
+                                   rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- negative slopes
+@pytest.mark.parametrize("lq,lk", [(3, 7), (7, 3), (5, 5)])
+def test_alibi_closed_form_negative_slope(lq, lk):
+    """A negative slope rewards distance: with q = 0 the weights are r^|c - j|
+    with r = e^{-mu} > 1, and the same geometric sums give L and P."""
+    D = max(lk, 2)
+    mu = -0.45
+    case = dict(q=np.zeros((lq, 1, D)), k=np.ones((lk, 1, D)),
+                v=np.eye(lk, D)[:, None, :], cu_q=[0, lq], cu_k=[0, lk],
+                alibi_slopes=[[mu]], softcap=3.0, scale_multiplier=0.75)
+    out, lse = _fwd(case)
+    r = math.exp(-mu)
+    for i in range(lq):
+        c = i + lk - lq
+        Z = _alibi_Z(r, c, lk)
+        assert abs(lse[i, 0] - math.log(Z)) <= 1e-13 * max(1.0, abs(math.log(Z)))
+        for j in range(lk):
+            assert abs(out[i, 0, j] - r ** abs(c - j) / Z) <= 1e-14
