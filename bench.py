@@ -134,7 +134,7 @@ def main():
     wl = make_workload(args.config, args.trial)
     g = wl.to(dev)
     call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
-                       scale_multiplier=g.scale_multiplier)
+                       scale_multiplier=g.scale_multiplier, store_ds=True)
     nph = len(_lib.PHASES)
 
     for _ in range(args.warmup):

@@ -50,6 +50,9 @@ def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_rig
         raise ValueError("cu_q and cu_k must both hold batch + 1 offsets")
     batch = cu_q.numel() - 1
     hq = q.shape[1]
+    for name, w in (("window_left", window_left), ("window_right", window_right)):
+        if not -1 <= int(w) <= 2**31 - 1:
+            raise ValueError(f"{name} must lie in [-1, 2**31 - 1] (got {w})")
     if (alibi_slopes.dtype != torch.float32 or alibi_slopes.device.type != "cuda"
             or alibi_slopes.dim() != 2 or tuple(alibi_slopes.shape) != (batch, hq)
             or (batch > 0 and alibi_slopes.stride(1) != 1)):
@@ -91,9 +94,10 @@ DS_DEFAULT_BUDGET = 8 << 30
 
 
 def _bwd_workspace_size(problem, entry, cu_q, cu_k, store_ds) -> int:
-    """store_ds: True (room for every sequence's dS, up to DS_DEFAULT_BUDGET
-    bytes), False (minimum workspace) or a number of extra bytes beyond the
-    minimum."""
+    """store_ds: False (the default everywhere: the minimum workspace, linear
+    in tokens, sized from host-known shapes only), True (room for every
+    sequence's dS up to DS_DEFAULT_BUDGET bytes; reads cu_q / cu_k back to the
+    host, which synchronises) or a number of extra bytes beyond the minimum."""
     base = workspace_size(problem, entry)
     if store_ds is True:
         return min(workspace_size(problem, entry, cu_q, cu_k), base + DS_DEFAULT_BUDGET)
@@ -150,7 +154,7 @@ def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multip
 
 def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3.0,
                     scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1, *,
-                    dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=True,
+                    dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=False,
                     all_keys=False):
     """Backward from a saved forward: returns (dq, dk, dv).  ``store_ds``: see
     _bwd_workspace_size (ignored when ``workspace`` is given: its size decides)."""
@@ -188,13 +192,14 @@ class FullVJP:
 
     Binding once and calling many times keeps the timed region to the library
     call itself.  Outputs are dense [Tq,Hq,160] / [Tk,1,160] tensors.
-    ``store_ds`` sizes the workspace (see _bwd_workspace_size); True reads
-    cu_q / cu_k back to the host once, here.
+    ``store_ds`` sizes the workspace (see _bwd_workspace_size); the default
+    is the minimum workspace, and True reads cu_q / cu_k back to the host
+    once, here, to give every sequence's dS a place.
     """
 
     def __init__(self, q, k, v, cu_q, cu_k, alibi_slopes, dout, causal=False, window_left=-1,
                  window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False,
-                 store_ds=True, all_keys=False):
+                 store_ds=False, all_keys=False):
         self.prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left,
                                  window_right, softcap, scale_multiplier, all_keys)
         dt, dev = q.dtype, q.device
@@ -241,8 +246,10 @@ class FullVJP:
 
 def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
                          scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1,
-                         *, want_lse=False, check=False, store_ds=True, all_keys=False):
-    """Forward + full VJP: returns (out, dq, dk, dv[, lse])."""
+                         *, want_lse=False, check=False, store_ds=False, all_keys=False):
+    """Forward + full VJP: returns (out, dq, dk, dv[, lse]).  With the default
+    store_ds=False nothing synchronises the host: the workspace size depends
+    only on the tensors' shapes and dQ recomputes dS."""
     call = FullVJP(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
                    softcap, scale_multiplier, want_lse=want_lse, store_ds=store_ds,
                    all_keys=all_keys)
@@ -270,7 +277,10 @@ def key_steps(problem: _lib.AttnProblem, entry: int, ws: torch.Tensor, cu_q) -> 
 
 def attention_varlen_feature_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal,
                                       window_left, window_right, softcap, scale_multiplier):
-    """The page's entry point: returns (out, dq, dk, dv), dense, in the inputs' dtype."""
+    """The page's entry point: returns (out, dq, dk, dv), dense, in the inputs'
+    dtype.  It never synchronises the host (minimum workspace, see
+    attn_varlen_full_vjp); callers that want dQ from stored dS bind a FullVJP
+    with store_ds=True."""
     return attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=softcap,
                                 scale_multiplier=scale_multiplier, causal=causal,
                                 window_left=window_left, window_right=window_right)

@@ -13,6 +13,7 @@
 #include <string>
 
 #include "attn_varlen.h"
+#include "entry.hpp"
 #include "kernels.hpp"
 
 using namespace rga;
@@ -21,14 +22,19 @@ namespace {
 
 thread_local std::string g_last_error;
 
+attn_status vfail(attn_status st, const char* fmt, va_list ap) {
+  char buf[512];
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  g_last_error = buf;
+  return st;
+}
+
 attn_status fail(attn_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 attn_status fail(attn_status st, const char* fmt, ...) {
-  char buf[512];
   va_list ap;
   va_start(ap, fmt);
-  vsnprintf(buf, sizeof(buf), fmt, ap);
+  vfail(st, fmt, ap);
   va_end(ap);
-  g_last_error = buf;
   return st;
 }
 
@@ -120,7 +126,7 @@ attn_status check_problem(const attn_problem* p) {
   if (p->hq < 1 || p->hq > 1024) return fail(ATTN_INVALID_ARG, "hq %d outside 1..1024", p->hq);
   if (p->total_q < 0 || p->total_k < 0)
     return fail(ATTN_INVALID_ARG, "negative token count");
-  if (p->total_q > INT32_MAX || p->total_k > INT32_MAX ||
+  if (p->total_q + p->total_k > INT32_MAX ||
       p->total_q * (int64_t)p->hq > (int64_t)INT32_MAX - 4 * ROW_TILE)
     return fail(ATTN_INVALID_ARG, "too many tokens for 32-bit row indices");
   if (!p->cu_q || !p->cu_k) return fail(ATTN_INVALID_ARG, "cu_q / cu_k is NULL");
@@ -259,8 +265,16 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.fwd_slots = (int)L.row_tiles;
   a.fwd_slots = (int)L.row_tiles;
   pa.kv_wgs = (int)L.kv_wgs;
-  a.win_left = p->window_left;
-  a.win_right = p->causal ? 0 : p->window_right;
+  // A left bound of total_k or more keeps every key of every row (a row's
+  // centre i + Lk - Lq is at most Lk - 1 < total_k), and so does a right bound
+  // of total_q or more (the centre is at least Lk - Lq, so centre + total_q >=
+  // Lk); clamping there keeps the kernels' bound arithmetic (centre -/+ bound)
+  // inside int32, given total_q + total_k <= INT32_MAX.
+  a.win_left = p->window_left < 0 ? -1 : (int)std::min<int64_t>(p->window_left, p->total_k);
+  a.win_right = p->causal ? 0
+                          : (p->window_right < 0 ? -1
+                                                 : (int)std::min<int64_t>(p->window_right,
+                                                                          p->total_q));
   pa.seg_items = KV_SEGMENT_ITEMS;
   a.kv_wgs = (int)L.kv_wgs;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
@@ -307,6 +321,70 @@ attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layo
 }
 
 }  // namespace
+
+namespace rga {
+
+attn_status set_error(attn_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vfail(st, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+attn_status full_vjp_impl(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
+                          const attn_tensor* v, const attn_tensor* dout, const attn_tensor* out,
+                          const attn_tensor* dq, const attn_tensor* dk, const attn_tensor* dv,
+                          float* lse, void* workspace, size_t workspace_bytes, hipStream_t s,
+                          const hipEvent_t* ev) {
+  RGA_TRY(check_problem(p));
+  RGA_TRY(check_inputs(p, q, k, v));
+  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
+  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
+  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  AttnArgs a;
+  Layout L;
+  PlanArgs pa;
+  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, a, L, pa));
+  set_view(q, &a.q, &a.q_ts, &a.q_hs);
+  set_view(k, &a.k, &a.k_ts, nullptr);
+  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
+  set_view(out, &a.out, &a.o_ts, &a.o_hs);
+  set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
+  set_view(dk, &a.dk, &a.dk_ts, nullptr);
+  set_view(dv, &a.dv, &a.dv_ts, nullptr);
+  a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
+  // the planner runs inside the forward's grid (the plan phase is empty); an
+  // empty batch runs the planner alone
+  if (p->batch == 0) {
+    RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
+    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+  } else {
+    RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
+    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, s),
+                       "forward launch"));
+  }
+  RGA_TRY(launch_backward(p, a, L, s, ev));
+  if (p->batch == 0) {
+    RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
+    RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
+  }
+  return record(ev, ATTN_PHASES, s);
+}
+
+attn_status min_workspace(const attn_problem* p, int entry, size_t* bytes) {
+  RGA_TRY(check_problem(p));
+  *bytes = make_layout(p, entry, device_cus()).total;
+  return ATTN_OK;
+}
+
+}  // namespace rga
 
 extern "C" {
 
@@ -416,49 +494,13 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p, const attn_tensor*
                                        size_t workspace_bytes, attn_stream_t stream,
                                        void* const* events) {
   g_last_error.clear();
-  RGA_TRY(check_problem(p));
-  RGA_TRY(check_inputs(p, q, k, v));
-  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
-  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
-  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
   if (events) {
     for (int i = 0; i <= ATTN_PHASES; ++i)
       if (!events[i]) return fail(ATTN_INVALID_ARG, "events[%d] is NULL", i);
   }
-  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  AttnArgs a;
-  Layout L;
-  PlanArgs pa;
-  RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, a, L, pa));
-  set_view(q, &a.q, &a.q_ts, &a.q_hs);
-  set_view(k, &a.k, &a.k_ts, nullptr);
-  set_view(v, &a.v, &a.v_ts, nullptr);
-  set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
-  set_view(out, &a.out, &a.o_ts, &a.o_hs);
-  set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
-  set_view(dk, &a.dk, &a.dk_ts, nullptr);
-  set_view(dv, &a.dv, &a.dv_ts, nullptr);
-  a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
-  // the planner runs inside the forward's grid (the plan phase is empty); an
-  // empty batch runs the planner alone
-  if (p->batch == 0) {
-    RGA_TRY(launch_prep_phase(pa, a, L, s, ev));
-    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
-  } else {
-    RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
-    RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
-    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, s),
-                       "forward launch"));
-  }
-  RGA_TRY(launch_backward(p, a, L, s, ev));
-  if (p->batch == 0) {
-    RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
-    RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
-  }
-  return record(ev, ATTN_PHASES, s);
+  return full_vjp_impl(p, q, k, v, dout, out, dq, dk, dv, lse, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream),
+                       reinterpret_cast<const hipEvent_t*>(events));
 }
 
 attn_status attn_varlen_full_vjp(const attn_problem* p, const attn_tensor* q,

@@ -123,7 +123,20 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   const int wlo = WIN && a.win_left >= 0 ? wc - a.win_left : 0;
   const int whi = WIN && a.win_right >= 0 ? min(Lk, wc + a.win_right + 1) : Lk;
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - ti);
-  float m = CAP ? 0.0f : -__builtin_inff();       // log2 units, relative to moff
+  // log2 units, relative to moff.  With a cap, the largest exponent a kept key
+  // can reach: 0 for slope >= 0 (the nearest kept key is the clamped centre
+  // itself), and -slope2 times the largest distance from the clamped centre to
+  // a kept key for a negative slope, which favours far keys.
+  float m = -__builtin_inff();
+  if (CAP) {
+    m = 0.0f;
+    if (slope2 < 0.0f) {
+      const int cc = max(ti + Lk - Lq, 0);
+      const int jlo = max(wlo, 0), jhi = max(whi, jlo + 1);
+      m = -slope2 * (float)max(abs(cc - jlo), abs(cc - (jhi - 1)));
+    }
+  }
+  const float negm = CAP ? -m : 0.0f;
   float lsum = 0.0f;     // exact sum of P
   float lsum_r = 0.0f;   // sum of P rounded to the input dtype
   f32x16 O[DBLK];
@@ -172,7 +185,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
       float x;
       if (CAP)
         x = __builtin_fmaf(a.lc.t_mul, cap_r(S[kb][r], a.lc),
-                           -slope2 * __builtin_fabsf(cb - (float)jl));
+                           __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), negm));
       else
         x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
       if (WIN) x = jl >= kfrom && jl < kleft ? x : -__builtin_inff();

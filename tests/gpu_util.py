@@ -97,3 +97,42 @@ def check_full(wl, label, modes=(True, False)):
         assert_lse(to_np(got["lse"]), ref["lse"], lab)
         results.append(got)
     return results, ref
+
+
+def oracle_sequence_heads(q, k, v, dout, slopes, softcap, scale_multiplier, window=(-1, -1),
+                          workers=4, chunk=4, label=""):
+    """oracle.sequence_vjp of one sequence, run over chunks of query heads in a
+    thread pool (NumPy releases the GIL) with a progress line per chunk.  dk
+    and dv are the sums of the chunks' contributions: every query head adds its
+    own term to its K/V head's gradient (the head-sum invariant pinned in
+    tests/test_oracle.py)."""
+    from concurrent.futures import ThreadPoolExecutor
+    hq = q.shape[1]
+    group = hq // k.shape[1]
+    starts = list(range(0, hq, chunk))
+
+    def run(h0):
+        h1 = min(hq, h0 + chunk)
+        g0 = h0 // group
+        assert (h1 - 1) // group == g0, "a chunk must stay inside one K/V head group"
+        part = oracle.sequence_vjp(q[:, h0:h1], k[:, g0:g0 + 1], v[:, g0:g0 + 1],
+                                   None if dout is None else dout[:, h0:h1], slopes[h0:h1],
+                                   softcap, scale_multiplier, window=window)
+        say(f"  {label} oracle heads {h0}..{h1 - 1} done")
+        return h0, h1, g0, part
+
+    Lq, _, D = q.shape
+    Lk, hkv = k.shape[0], k.shape[1]
+    res = {"out": np.zeros((Lq, hq, D)), "lse": np.full((Lq, hq), -np.inf),
+           "dq": np.zeros((Lq, hq, D)), "dk": np.zeros((Lk, hkv, D)), "dv": np.zeros((Lk, hkv, D))}
+    with ThreadPoolExecutor(max_workers=workers) as ex:
+        for h0, h1, g0, part in ex.map(run, starts):
+            for name in ("out", "lse", "dq"):
+                res[name][:, h0:h1] = part[name]
+            res["dk"][:, g0] += part["dk"][:, 0]
+            res["dv"][:, g0] += part["dv"][:, 0]
+    return res
+
+
+def f64(t):
+    return t.detach().to("cpu").to(torch.float64).numpy()

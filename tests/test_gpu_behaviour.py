@@ -25,8 +25,8 @@ def _bind(g, store_ds=True):
                        scale_multiplier=g.scale_multiplier, want_lse=True, store_ds=store_ds)
 
 
-@pytest.mark.parametrize("cfg,store_ds", [(0, True), (1, True), (3, True), (1, False),
-                                          (3, False)])
+@pytest.mark.parametrize("cfg,store_ds", [(0, True), (1, True), (2, True), (3, True), (4, True),
+                                          (1, False), (2, False), (3, False)])
 def test_bitwise_repeatable(cfg, store_ds):
     """Three calls, outputs pre-filled with different garbage, give identical bits."""
     need_gpu()
@@ -207,3 +207,117 @@ def test_page_entry_point_signature():
     for name, t in zip(("out", "dq", "dk", "dv"), res):
         assert t.dtype == g.q.dtype
         assert_close(name, to_np(t), ref[name], TOL[wl.dtype], "entry")
+
+
+def _negative_slope_workload(dtype, softcap, seed):
+    """Every sequence has a few heads with a negative slope, steep enough that
+    slope * log2(e) * Lk passes 128 (exp2 of that would overflow FP32 if the
+    softmax offset assumed slopes >= 0)."""
+    lq, lk = [19, 70, 3, 40], [700, 260, 1, 1500]
+    hq = 48
+    rng = np.random.default_rng([3000, seed])
+    slopes = W.draw_slopes(rng, len(lq), hq)
+    for b in range(len(lq)):
+        heads = rng.choice(hq, size=3, replace=False)
+        slopes[b, heads] = -rng.uniform(0.05, 0.3, size=3).astype(np.float32)
+    slopes[0, 0] = -0.25
+    width = 192 if dtype == "bf16" else 176
+    return W.custom_workload(lq=lq, lk=lk, hq=hq, dtype=dtype, width=width, step=2, seed=seed,
+                             softcap=softcap, slopes=slopes)
+
+
+@pytest.mark.parametrize("dtype,softcap,causal,wl_,wr", [
+    ("bf16", 3.0, False, -1, -1), ("f16", 3.0, False, -1, -1), ("bf16", 0.0, False, -1, -1),
+    ("bf16", 3.0, False, 40, 3), ("f16", 3.0, True, -1, -1), ("f16", 0.0, False, 9, 30)])
+def test_negative_slopes(dtype, softcap, causal, wl_, wr):
+    """Negative ALiBi slopes favour far keys; the pages give slopes as FP32
+    values without a sign constraint, so the definition is used as it stands."""
+    need_gpu()
+    wl = _negative_slope_workload(dtype, softcap, seed=7)
+    g = wl.to("cuda")
+    inp = W.oracle_inputs(wl)
+    ref = oracle.vjp(inp["q"], inp["k"], inp["v"], inp["cu_q"], inp["cu_k"],
+                     inp["alibi_slopes"], inp["dout"], inp["softcap"], inp["scale_multiplier"],
+                     causal=causal, window_left=wl_, window_right=wr)
+    tol = TOL[wl.dtype]
+    for store_ds in (True, False):
+        lab = f"negative slopes {dtype} softcap={softcap} window=({causal},{wl_},{wr}) ds={store_ds}"
+        say(f"[{lab}]")
+        out, dq, dk, dv, lse = rga.attn_varlen_full_vjp(
+            g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
+            scale_multiplier=g.scale_multiplier, causal=causal, window_left=wl_,
+            window_right=wr, want_lse=True, check=True, store_ds=store_ds)
+        torch.cuda.synchronize()
+        for name, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+            assert_close(name, to_np(t), ref[name], tol, lab)
+        assert_lse(to_np(lse), ref["lse"], lab)
+    # the separate entries too (the backward rebuilds its offsets from L)
+    out, lse = rga.attn_varlen_fwd(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.softcap,
+                                   g.scale_multiplier, causal=causal, window_left=wl_,
+                                   window_right=wr, check=True)
+    dq, dk, dv = rga.attn_varlen_bwd(g.q, g.k, g.v, out, lse, g.dout, g.cu_q, g.cu_k, g.slopes,
+                                     g.softcap, g.scale_multiplier, causal=causal,
+                                     window_left=wl_, window_right=wr, check=True)
+    torch.cuda.synchronize()
+    for name, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_np(t), ref[name], tol, "negative slopes separate entries")
+
+
+@pytest.mark.parametrize("causal,wl_,wr", [(False, 2**31 - 1, 2**31 - 1), (False, 2**31 - 1, -1),
+                                           (False, -1, 2**31 - 1), (True, 2**31 - 1, -1)])
+def test_widest_windows_keep_every_key(causal, wl_, wr):
+    """Window bounds up to 2^31 - 1 keep every key they allow, bit for bit the
+    same as no bound on that side (the library clamps them to the token
+    counts, which already keep every key)."""
+    need_gpu()
+    wl = W.custom_workload(lq=[37, 150, 9, 64], lk=[300, 90, 200, 64], hq=48, dtype="bf16",
+                           width=192, step=1, seed=45)
+    g = wl.to("cuda")
+    want = rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout,
+                                    softcap=g.softcap, scale_multiplier=g.scale_multiplier,
+                                    causal=causal, window_left=-1, window_right=-1,
+                                    want_lse=True)
+    got = rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout,
+                                   softcap=g.softcap, scale_multiplier=g.scale_multiplier,
+                                   causal=causal, window_left=wl_, window_right=wr, want_lse=True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("out", "dq", "dk", "dv", "lse"), want, got):
+        assert torch.equal(a, b), (name, causal, wl_, wr)
+    with pytest.raises(ValueError):
+        rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout,
+                                 window_left=2**32)
+
+
+def test_page_entry_point_never_syncs():
+    """The page's entry point with its default (minimum) workspace enqueues
+    everything on the current stream: it can be captured into a HIP graph,
+    which fails on any host synchronisation or device-to-host copy.  Every
+    replay, with eager work and synchronisations between replays, matches the
+    eager call bitwise."""
+    need_gpu()
+    wl = W.make_workload(0)
+    g = wl.to("cuda")
+    args = (g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, False, -1, -1, g.softcap,
+            g.scale_multiplier)
+    eager = [t.clone() for t in rga.attention_varlen_feature_full_vjp(*args)]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        rga.attention_varlen_feature_full_vjp(*args)   # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = rga.attention_varlen_feature_full_vjp(*args)
+    for rep in range(3):
+        for t in captured:
+            t.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("out", "dq", "dk", "dv"), eager, captured):
+            assert torch.equal(a, b), (rep, name)
+        again = rga.attention_varlen_feature_full_vjp(*args)   # eager work between replays
+        torch.cuda.synchronize()
+        for a, b in zip(eager, again):
+            assert torch.equal(a, b)
