@@ -209,6 +209,29 @@ attn_status attn_varlen_full_vjp_timed(const attn_problem* p,
                                        void* workspace, size_t workspace_bytes,
                                        attn_stream_t stream, void* const* events);
 
+/* Bytes of the static scratch array of attn_varlen_full_vjp_noalloc (256 MiB
+ * per GPU, 0.09 % of an MI355X's 288 GB). */
+#define ATTN_NOALLOC_SCRATCH_BYTES (256u << 20)
+
+/* attn_varlen_full_vjp for callers that cannot allocate device memory (code
+ * under graph capture, tight serving loops, harnesses that forbid allocation):
+ * it takes no workspace and allocates nothing.  Its workspace is a static
+ * device array of ATTN_NOALLOC_SCRATCH_BYTES bytes that each GPU the library
+ * runs on holds until the process ends; results are those of
+ * attn_varlen_full_vjp with a workspace of that size (dS images in what the
+ * minimum layout leaves free).  The caller still passes every input and
+ * output.  Errors: those of attn_varlen_full_vjp, and ATTN_WORKSPACE_TOO_SMALL
+ * when the problem's minimum workspace (attn_varlen_workspace_size) exceeds
+ * the array.  All calls on one GPU share that GPU's array: calls that overlap
+ * on one GPU (several streams or threads) race and must be ordered by the
+ * caller; the device-side cu_q / cu_k check has no workspace to read back. */
+attn_status attn_varlen_full_vjp_noalloc(const attn_problem* p,
+                                         const attn_tensor* q, const attn_tensor* k,
+                                         const attn_tensor* v, const attn_tensor* dout,
+                                         const attn_tensor* out, const attn_tensor* dq,
+                                         const attn_tensor* dk, const attn_tensor* dv,
+                                         float* lse, attn_stream_t stream);
+
 /* Synchronises `stream` and reports the device-side cu_q / cu_k check of the
  * last call that used `workspace`: ATTN_OK or ATTN_BAD_SEQLENS. */
 attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream);

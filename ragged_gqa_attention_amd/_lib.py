@@ -24,6 +24,8 @@ ATTN_BF16 = 1
 
 ATTN_FLAG_ALL_KEYS = 1   # evaluate every key, also where P is exactly 0
 
+NOALLOC_SCRATCH_BYTES = 256 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
+
 ENTRY_FWD = 0
 ENTRY_BWD = 1
 ENTRY_FULL_VJP = 2
@@ -38,6 +40,7 @@ EXPORTED = (
     "attn_varlen_bwd",
     "attn_varlen_full_vjp",
     "attn_varlen_full_vjp_timed",
+    "attn_varlen_full_vjp_noalloc",
     "attn_varlen_check_plan",
     "attn_varlen_key_steps",
     "attn_status_string",
@@ -110,6 +113,8 @@ def load() -> ctypes.CDLL:
                                              vp, sz, vp]
         lib.attn_varlen_full_vjp_timed.argtypes = lib.attn_varlen_full_vjp.argtypes + [
             P(ctypes.c_void_p)]
+        lib.attn_varlen_full_vjp_noalloc.argtypes = [P(AttnProblem), T, T, T, T, T, T, T, T, fp,
+                                                     vp]
         lib.attn_varlen_check_plan.argtypes = [vp, vp]
         lib.attn_varlen_key_steps.argtypes = [P(AttnProblem), ctypes.c_int, vp, i32p,
                                               ctypes.c_int64, vp]
@@ -120,6 +125,7 @@ def load() -> ctypes.CDLL:
         for name in ("attn_varlen_workspace_size", "attn_varlen_workspace_size_ds",
                      "attn_varlen_fwd", "attn_varlen_bwd",
                      "attn_varlen_full_vjp", "attn_varlen_full_vjp_timed",
+                     "attn_varlen_full_vjp_noalloc",
                      "attn_varlen_check_plan", "attn_varlen_key_steps"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib

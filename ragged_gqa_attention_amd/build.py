@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libragged_gqa_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.cpp", "plan.hip", "fwd.hip", "dkdv.hip", "dq.hip"]
+SOURCES = ["api.cpp", "plan.hip", "fwd.hip", "dkdv.hip", "dq.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

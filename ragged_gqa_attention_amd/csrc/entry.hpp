@@ -1,5 +1,6 @@
 // Internal entry points of the library shared between its translation units
-// (api.cpp holds the C ABI and defines them).
+// (api.cpp holds the C ABI and defines them; noalloc.hip, the call with a
+// static scratch, uses them).
 #pragma once
 
 #include <hip/hip_runtime.h>
