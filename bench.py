@@ -37,7 +37,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+full-VJP TFLOP/s (% MFMA peak) and ms/call, ragged GQA Hq=64 D=160"
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense FP16/BF16 matrix peak
-HEAD_DIM = 160
 # credited flops per score element and head-dim unit, by phase (14 in total)
 PHASE_FLOPS = {"fwd": 4, "dkdv": 8, "dq": 2, "plan": 0}
 
@@ -89,7 +88,7 @@ def cpu_baseline(wl, seconds: float):
         n += 1
         if spent >= seconds:
             break
-    flops = 14.0 * elems * HEAD_DIM
+    flops = 14.0 * elems * wl.head_dim
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"first {n} of {wl.batch} sequences of {wl.name} "
@@ -184,16 +183,18 @@ def main():
     ks = call.key_steps().astype(np.int64)
     evaluated = 0
     tile = 0
+    group = wl.hq // wl.hkv   # rows of one K/V head's query heads fold together
     for lq, lk in zip(wl.lq, wl.lk):
-        rows = int(lq) * wl.hq
-        for t0 in range(0, rows, 256):
-            lo, hi = ks[tile]
-            tile += 1
-            evaluated += min(256, rows - t0) * max(0, min(int(hi) * 64, int(lk)) - int(lo) * 64)
+        rows = int(lq) * group
+        for _ in range(wl.hkv):
+            for t0 in range(0, rows, 256):
+                lo, hi = ks[tile]
+                tile += 1
+                evaluated += min(256, rows - t0) * max(0, min(int(hi) * 64, int(lk)) - int(lo) * 64)
     frac = evaluated / elems if elems else 1.0
     value = flops / (ms_per_step * 1e-3) / 1e12
     dom = max(("fwd", "dkdv", "dq"), key=lambda p: phase_ms[p])
-    achieved = PHASE_FLOPS[dom] * elems * HEAD_DIM / (phase_ms[dom] * 1e-3) / 1e12
+    achieved = PHASE_FLOPS[dom] * elems * wl.head_dim / (phase_ms[dom] * 1e-3) / 1e12
     kernel_names = {"fwd": "fwd_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel"}
     traffic = measured_traffic(kernel_names[dom], wl.name)
     line = {
@@ -211,7 +212,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": wl.name, "seed": [args.config, args.trial], "batch": wl.batch,
-            "hq": wl.hq, "hkv": 1, "head_dim": HEAD_DIM, "total_q": wl.total_q,
+            "hq": wl.hq, "hkv": wl.hkv, "head_dim": wl.head_dim, "total_q": wl.total_q,
             "total_k": wl.total_k, "sum_lq_lk": int((wl.lq * wl.lk).sum()),
             "view": f"feature width {wl.width}, token step {wl.step}",
             "softcap": wl.softcap, "scale_multiplier": wl.scale_multiplier,

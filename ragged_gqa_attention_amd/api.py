@@ -15,19 +15,19 @@ import torch
 
 from . import _lib
 
-HEAD_DIM = 160
+HEAD_DIMS = (64, 128, 160)
 _DTYPES = {torch.float16: _lib.ATTN_F16, torch.bfloat16: _lib.ATTN_BF16}
 
 
-def _view(t: torch.Tensor, name: str, dtype, heads=None) -> _lib.AttnTensor:
+def _view(t: torch.Tensor, name: str, dtype, heads=None, dim=None) -> _lib.AttnTensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.device.type != "cuda":
         raise ValueError(f"{name} must live on the GPU")
     if t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if t.dim() != 3 or t.shape[2] != HEAD_DIM:
-        raise ValueError(f"{name} must be [tokens, heads, {HEAD_DIM}], got {tuple(t.shape)}")
+    if t.dim() != 3 or (dim is not None and t.shape[2] != dim):
+        raise ValueError(f"{name} must be [tokens, heads, {dim}], got {tuple(t.shape)}")
     if heads is not None and t.shape[1] != heads:
         raise ValueError(f"{name} has {t.shape[1]} heads, expected {heads}")
     if t.shape[0] > 0 and t.stride(2) != 1:
@@ -41,6 +41,8 @@ def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_rig
     zero (the library skips those by default; results are bitwise the same)."""
     if q.dtype not in _DTYPES:
         raise NotImplementedError(f"dtype {q.dtype} is not supported (FP16 / BF16 only)")
+    if q.dim() != 3 or k.dim() != 3 or k.shape[2] != q.shape[2]:
+        raise ValueError("q [Tq, Hq, D] and k [Tk, Hkv, D] must share D")
     for name, cu in (("cu_q", cu_q), ("cu_k", cu_k)):
         if cu.dtype != torch.int32 or cu.dim() != 1 or cu.device.type != "cuda":
             raise ValueError(f"{name} must be an int32 GPU vector")
@@ -132,15 +134,16 @@ def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multip
     """Forward only: returns (out [Tq,Hq,160] like q, lse float32 [Tq,Hq])."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
                         softcap, scale_multiplier, all_keys)
-    tq, tk = _view(q, "q", q.dtype), _view(k, "k", q.dtype)
-    tv = _view(v, "v", q.dtype, heads=k.shape[1])
+    d = q.shape[2]
+    tq, tk = _view(q, "q", q.dtype, dim=d), _view(k, "k", q.dtype, dim=d)
+    tv = _view(v, "v", q.dtype, heads=k.shape[1], dim=d)
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     if lse is None:
         lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [Tq, Hq] tensor")
-    to = _view(out, "out", q.dtype, heads=q.shape[1])
+    to = _view(out, "out", q.dtype, heads=q.shape[1], dim=d)
     ws = _workspace(workspace_size(prob, _lib.ENTRY_FWD), q.device, workspace)
     st = _lib.load().attn_varlen_fwd(ctypes.byref(prob), ctypes.byref(tq), ctypes.byref(tk),
                                      ctypes.byref(tv), ctypes.byref(to), _fptr(lse),
@@ -160,18 +163,19 @@ def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3
     _bwd_workspace_size (ignored when ``workspace`` is given: its size decides)."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
                         softcap, scale_multiplier, all_keys)
-    dt = q.dtype
-    tq, tk, tv = _view(q, "q", dt), _view(k, "k", dt), _view(v, "v", dt, heads=k.shape[1])
-    to = _view(out, "out", dt, heads=q.shape[1])
-    tdo = _view(dout, "dout", dt, heads=q.shape[1])
+    dt, d = q.dtype, q.shape[2]
+    tq, tk = _view(q, "q", dt, dim=d), _view(k, "k", dt, dim=d)
+    tv = _view(v, "v", dt, heads=k.shape[1], dim=d)
+    to = _view(out, "out", dt, heads=q.shape[1], dim=d)
+    tdo = _view(dout, "dout", dt, heads=q.shape[1], dim=d)
     if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:2]) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [Tq, Hq] tensor")
     dq = torch.empty(q.shape, dtype=dt, device=q.device) if dq is None else dq
     dk = torch.empty(k.shape, dtype=dt, device=q.device) if dk is None else dk
     dv = torch.empty(v.shape, dtype=dt, device=q.device) if dv is None else dv
-    tdq = _view(dq, "dq", dt, heads=q.shape[1])
-    tdk = _view(dk, "dk", dt, heads=k.shape[1])
-    tdv = _view(dv, "dv", dt, heads=k.shape[1])
+    tdq = _view(dq, "dq", dt, heads=q.shape[1], dim=d)
+    tdk = _view(dk, "dk", dt, heads=k.shape[1], dim=d)
+    tdv = _view(dv, "dv", dt, heads=k.shape[1], dim=d)
     if workspace is None:
         ws = _workspace(_bwd_workspace_size(prob, _lib.ENTRY_BWD, cu_q, cu_k, store_ds), q.device)
     else:
@@ -209,10 +213,12 @@ class FullVJP:
         self.dk = torch.empty(k.shape, dtype=dt, device=dev)
         self.dv = torch.empty(v.shape, dtype=dt, device=dev)
         self.lse = torch.empty(q.shape[:2], dtype=torch.float32, device=dev) if want_lse else None
-        self.views = [_view(q, "q", dt), _view(k, "k", dt), _view(v, "v", dt, heads=k.shape[1]),
-                      _view(dout, "dout", dt, heads=q.shape[1]),
-                      _view(self.out, "out", dt), _view(self.dq, "dq", dt),
-                      _view(self.dk, "dk", dt), _view(self.dv, "dv", dt)]
+        d = q.shape[2]
+        self.views = [_view(q, "q", dt, dim=d), _view(k, "k", dt, dim=d),
+                      _view(v, "v", dt, heads=k.shape[1], dim=d),
+                      _view(dout, "dout", dt, heads=q.shape[1], dim=d),
+                      _view(self.out, "out", dt, dim=d), _view(self.dq, "dq", dt, dim=d),
+                      _view(self.dk, "dk", dt, dim=d), _view(self.dv, "dv", dt, dim=d)]
         self.ws = _workspace(_bwd_workspace_size(self.prob, _lib.ENTRY_FULL_VJP, cu_q, cu_k,
                                                  store_ds), dev)
         self.device = dev
@@ -261,12 +267,14 @@ def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
 
 def key_steps(problem: _lib.AttnProblem, entry: int, ws: torch.Tensor, cu_q) -> "np.ndarray":
     """int32 [n_tiles, 2]: per 256-row tile of folded rows (row h * Lq + i of a
-    sequence, tiles in batch order) the first and one past the last 64-key step
-    the last call of ``entry`` on workspace ``ws`` visited.  Synchronises."""
+    sequence's group of hq / hkv heads sharing a K/V head; tiles in batch order,
+    the K/V heads of a sequence in turn) the first and one past the last 64-key
+    step the last call of ``entry`` on workspace ``ws`` visited.  Synchronises."""
     import numpy as np
     cq = cu_q.detach().to("cpu", torch.int64)
     lq = (cq[1:] - cq[:-1]).numpy()
-    n = int(((lq * problem.hq + 255) // 256).sum()) if lq.size else 0
+    group = problem.hq // problem.hkv
+    n = int(((lq * group + 255) // 256).sum()) * problem.hkv if lq.size else 0
     out = np.zeros((n, 2), dtype=np.int32)
     st = _lib.load().attn_varlen_key_steps(
         ctypes.byref(problem), entry, ctypes.c_void_p(ws.data_ptr()),

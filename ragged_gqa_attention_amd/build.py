@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_NAME = "libragged_gqa_attn.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["api.cpp", "plan.hip", "fwd.hip", "dkdv.hip", "dq.hip", "noalloc.hip"]
+SOURCES = (["api.cpp", "plan.hip", "noalloc.hip"] +
+           [f"{k}_d{d}.hip" for k in ("fwd", "dkdv", "dq") for d in (64, 128, 160)])
 ARCH = "gfx950"
 
 
@@ -55,7 +56,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
             print("\n".join(noise), file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 8)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
     tmp = LIB_PATH + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -77,10 +77,11 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 Layout make_layout(const attn_problem* p, int entry, int cus) {
   Layout L{};
-  const int64_t B = p->batch;
+  // plan sequences: one per (packed sequence, K/V head)
+  const int64_t B = (int64_t)p->batch * p->hkv;
   const int64_t rows = p->total_q * p->hq;
   L.row_tiles = ceil_div(rows, ROW_TILE) + B;
-  L.kv_tiles = ceil_div(p->total_k, KEY_TILE) + B;
+  L.kv_tiles = ceil_div(p->total_k * p->hkv, KEY_TILE) + B;
   L.kv_wgs = cus;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -96,13 +97,13 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.wg_first = take(sizeof(int) * (size_t)L.kv_wgs);
   L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
-  L.head_hw = take(sizeof(int) * (size_t)B * p->hq);
+  L.head_hw = take(sizeof(int) * (size_t)p->batch * p->hq);
   L.lse = L.rowinfo = L.part_dk = L.part_dv = 0;
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
     L.rowinfo = take(sizeof(float) * 4 * rows);
     // FP32 partial dK / dV: two key tiles per workgroup (its first and last)
-    const size_t part = sizeof(float) * 2 * (size_t)L.kv_wgs * KEY_TILE * HEAD_DIM;
+    const size_t part = sizeof(float) * 2 * (size_t)L.kv_wgs * KEY_TILE * p->head_dim;
     L.part_dk = take(part);
     L.part_dv = take(part);
   }
@@ -114,9 +115,8 @@ attn_status check_problem(const attn_problem* p) {
   if (!p) return fail(ATTN_INVALID_ARG, "problem is NULL");
   if (p->dtype != ATTN_F16 && p->dtype != ATTN_BF16)
     return fail(ATTN_UNSUPPORTED, "dtype %d is neither F16 nor BF16", p->dtype);
-  if (p->head_dim != HEAD_DIM)
-    return fail(ATTN_UNSUPPORTED, "head_dim %d != 160", p->head_dim);
-  if (p->hkv != 1) return fail(ATTN_UNSUPPORTED, "hkv %d != 1", p->hkv);
+  if (p->head_dim != 64 && p->head_dim != 128 && p->head_dim != 160)
+    return fail(ATTN_UNSUPPORTED, "head_dim %d is not 64, 128 or 160", p->head_dim);
   if (p->causal != 0 && p->causal != 1)
     return fail(ATTN_INVALID_ARG, "causal must be 0 or 1 (got %d)", p->causal);
   if (p->window_left < -1 || p->window_right < -1)
@@ -124,6 +124,11 @@ attn_status check_problem(const attn_problem* p) {
                 p->window_right);
   if (p->batch < 0) return fail(ATTN_INVALID_ARG, "batch %d < 0", p->batch);
   if (p->hq < 1 || p->hq > 1024) return fail(ATTN_INVALID_ARG, "hq %d outside 1..1024", p->hq);
+  if (p->hkv < 1 || p->hq % p->hkv != 0)
+    return fail(ATTN_INVALID_ARG, "hkv %d must be >= 1 and divide hq %d", p->hkv, p->hq);
+  if ((int64_t)p->batch * p->hkv > (1 << 24))
+    return fail(ATTN_INVALID_ARG, "batch x hkv %lld exceeds 2^24",
+                (long long)p->batch * p->hkv);
   if (p->total_q < 0 || p->total_k < 0)
     return fail(ATTN_INVALID_ARG, "negative token count");
   if (p->total_q + p->total_k > INT32_MAX ||
@@ -142,15 +147,16 @@ attn_status check_problem(const attn_problem* p) {
   return ATTN_OK;
 }
 
-attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens, int heads) {
+attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens, int heads,
+                         int dim) {
   if (!t) return fail(ATTN_INVALID_ARG, "%s is NULL", name);
   if (tokens > 0 && !t->data) return fail(ATTN_INVALID_ARG, "%s.data is NULL", name);
   if (t->tok_stride < 0 || t->head_stride < 0)
     return fail(ATTN_INVALID_ARG, "%s has a negative stride", name);
-  if (tokens > 1 && t->tok_stride < HEAD_DIM)
+  if (tokens > 1 && t->tok_stride < dim)
     return fail(ATTN_INVALID_ARG, "%s token stride %lld overlaps rows", name,
                 (long long)t->tok_stride);
-  if (heads > 1 && t->head_stride < HEAD_DIM)
+  if (heads > 1 && t->head_stride < dim)
     return fail(ATTN_INVALID_ARG, "%s head stride %lld overlaps rows", name,
                 (long long)t->head_stride);
   if (t->tok_stride > INT32_MAX || t->head_stride > INT32_MAX)
@@ -163,7 +169,7 @@ attn_status check_tensor(const char* name, const attn_tensor* t, int64_t tokens,
 
 LogitConsts logit_consts(const attn_problem* p) {
   LogitConsts lc;
-  const double sigma = (double)p->scale_multiplier / std::sqrt((double)HEAD_DIM);
+  const double sigma = (double)p->scale_multiplier / std::sqrt((double)p->head_dim);
   const double l2e = 1.4426950408889634;
   const double c = p->softcap;
   lc.sigma = (float)sigma;
@@ -233,7 +239,9 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.slopes = p->alibi_slopes;
   a.slopes_stride = p->slopes_stride;
   a.hq = p->hq;
-  a.batch = p->batch;
+  a.hkv = p->hkv;
+  a.group = p->hq / p->hkv;
+  a.batch = p->batch * p->hkv;   // plan sequences
   a.total_q = p->total_q;
   a.total_k = p->total_k;
   a.lc = logit_consts(p);
@@ -258,8 +266,9 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   pa.skip_log2 = a.skip_log2;
   pa.ksteps = a.ksteps;
   pa.head_hw = reinterpret_cast<int*>(base + L.head_hw);
-  pa.batch = p->batch;
-  pa.hq = p->hq;
+  pa.batch = p->batch * p->hkv;
+  pa.hq = p->hq / p->hkv;
+  pa.hkv = p->hkv;
   pa.total_q = p->total_q;
   pa.total_k = p->total_k;
   pa.fwd_slots = (int)L.row_tiles;
@@ -298,9 +307,9 @@ attn_status launch_prep_phase(const PlanArgs& pa, const AttnArgs& a, const Layou
 
 attn_status check_inputs(const attn_problem* p, const attn_tensor* q, const attn_tensor* k,
                          const attn_tensor* v) {
-  RGA_TRY(check_tensor("q", q, p->total_q, p->hq));
-  RGA_TRY(check_tensor("k", k, p->total_k, 1));
-  RGA_TRY(check_tensor("v", v, p->total_k, 1));
+  RGA_TRY(check_tensor("q", q, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("k", k, p->total_k, p->hkv, p->head_dim));
+  RGA_TRY(check_tensor("v", v, p->total_k, p->hkv, p->head_dim));
   return ATTN_OK;
 }
 
@@ -311,11 +320,13 @@ attn_status launch_backward(const attn_problem* p, const AttnArgs& a, const Layo
   const bool cap = p->softcap > 0.0f;
   if (p->batch > 0) {
     RGA_TRY(record(ev, ATTN_PHASE_DKDV, s));
-    RGA_TRY(hip_status(launch_dkdv(a, p->dtype, cap, (int)L.kv_wgs, s), "dK/dV launch"));
+    RGA_TRY(hip_status(launch_dkdv(a, p->dtype, p->head_dim, cap, (int)L.kv_wgs, s),
+                       "dK/dV launch"));
     RGA_TRY(record(ev, ATTN_PHASE_DQ, s));
     // row tiles, then one partial-sum workgroup per compute unit
-    RGA_TRY(hip_status(launch_dq(a, p->dtype, cap, (int)L.row_tiles + device_cus(), s),
-                       "dQ launch"));
+    RGA_TRY(hip_status(
+        launch_dq(a, p->dtype, p->head_dim, cap, (int)L.row_tiles + device_cus(), s),
+        "dQ launch"));
   }
   return ATTN_OK;
 }
@@ -341,23 +352,23 @@ attn_status full_vjp_impl(const attn_problem* p, const attn_tensor* q, const att
                           const hipEvent_t* ev) {
   RGA_TRY(check_problem(p));
   RGA_TRY(check_inputs(p, q, k, v));
-  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
-  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
-  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("dk", dk, p->total_k, p->hkv, p->head_dim));
+  RGA_TRY(check_tensor("dv", dv, p->total_k, p->hkv, p->head_dim));
   AttnArgs a;
   Layout L;
   PlanArgs pa;
   RGA_TRY(prologue(p, ATTN_ENTRY_FULL_VJP, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
-  set_view(k, &a.k, &a.k_ts, nullptr);
-  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(k, &a.k, &a.k_ts, &a.k_hs);
+  set_view(v, &a.v, &a.v_ts, &a.v_hs);
   set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
   set_view(out, &a.out, &a.o_ts, &a.o_hs);
   set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
-  set_view(dk, &a.dk, &a.dk_ts, nullptr);
-  set_view(dv, &a.dv, &a.dv_ts, nullptr);
+  set_view(dk, &a.dk, &a.dk_ts, &a.dk_hs);
+  set_view(dv, &a.dv, &a.dv_ts, &a.dv_hs);
   a.lse = lse ? lse : reinterpret_cast<float*>(static_cast<char*>(workspace) + L.lse);
   // the planner runs inside the forward's grid (the plan phase is empty); an
   // empty batch runs the planner alone
@@ -367,7 +378,7 @@ attn_status full_vjp_impl(const attn_problem* p, const attn_tensor* q, const att
   } else {
     RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
     RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
-    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, true, s),
+    RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->head_dim, p->softcap > 0.0f, true, s),
                        "forward launch"));
   }
   RGA_TRY(launch_backward(p, a, L, s, ev));
@@ -417,7 +428,8 @@ attn_status attn_varlen_workspace_size_ds(const attn_problem* p, int entry,
     const int64_t lk = (int64_t)cu_k_host[b + 1] - cu_k_host[b];
     if (lq < 0 || lk < 0) return fail(ATTN_BAD_SEQLENS, "cu_q / cu_k decrease at %d", b);
     if (lq > 0 && lk > 0)
-      images += (size_t)ceil_div(lq * p->hq, ROW_TILE) * (size_t)ceil_div(lk, TILE_ROWS);
+      images += (size_t)p->hkv * (size_t)ceil_div(lq * (p->hq / p->hkv), ROW_TILE) *
+                (size_t)ceil_div(lk, TILE_ROWS);
   }
   *bytes = make_layout(p, entry, device_cus()).total;
   if (entry != ATTN_ENTRY_FWD) *bytes += images * DS_IMAGE_BYTES;
@@ -430,7 +442,7 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   g_last_error.clear();
   RGA_TRY(check_problem(p));
   RGA_TRY(check_inputs(p, q, k, v));
-  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq, p->head_dim));
   if (p->total_q > 0 && !lse) return fail(ATTN_INVALID_ARG, "lse is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
@@ -438,13 +450,13 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   PlanArgs pa;
   RGA_TRY(prologue(p, ATTN_ENTRY_FWD, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
-  set_view(k, &a.k, &a.k_ts, nullptr);
-  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(k, &a.k, &a.k_ts, &a.k_hs);
+  set_view(v, &a.v, &a.v_ts, &a.v_hs);
   set_view(out, &a.out, &a.o_ts, &a.o_hs);
   a.lse = lse;
   // an empty batch still runs the planner (it records the cu_q / cu_k check)
   if (p->batch == 0) return launch_prep_phase(pa, a, L, s);
-  return hip_status(launch_fwd(a, pa, p->dtype, p->softcap > 0.0f, false, s),
+  return hip_status(launch_fwd(a, pa, p->dtype, p->head_dim, p->softcap > 0.0f, false, s),
                     "forward launch");
 }
 
@@ -456,11 +468,11 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   g_last_error.clear();
   RGA_TRY(check_problem(p));
   RGA_TRY(check_inputs(p, q, k, v));
-  RGA_TRY(check_tensor("out", out, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq));
-  RGA_TRY(check_tensor("dk", dk, p->total_k, 1));
-  RGA_TRY(check_tensor("dv", dv, p->total_k, 1));
+  RGA_TRY(check_tensor("out", out, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("dout", dout, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("dq", dq, p->total_q, p->hq, p->head_dim));
+  RGA_TRY(check_tensor("dk", dk, p->total_k, p->hkv, p->head_dim));
+  RGA_TRY(check_tensor("dv", dv, p->total_k, p->hkv, p->head_dim));
   if (p->total_q > 0 && !lse) return fail(ATTN_INVALID_ARG, "lse is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   AttnArgs a;
@@ -468,19 +480,19 @@ attn_status attn_varlen_bwd(const attn_problem* p, const attn_tensor* q, const a
   PlanArgs pa;
   RGA_TRY(prologue(p, ATTN_ENTRY_BWD, workspace, workspace_bytes, a, L, pa));
   set_view(q, &a.q, &a.q_ts, &a.q_hs);
-  set_view(k, &a.k, &a.k_ts, nullptr);
-  set_view(v, &a.v, &a.v_ts, nullptr);
+  set_view(k, &a.k, &a.k_ts, &a.k_hs);
+  set_view(v, &a.v, &a.v_ts, &a.v_hs);
   a.out = static_cast<uint16_t*>(out->data);
   a.o_ts = out->tok_stride;
   a.o_hs = out->head_stride;
   set_view(dout, &a.dout, &a.do_ts, &a.do_hs);
   set_view(dq, &a.dq, &a.dq_ts, &a.dq_hs);
-  set_view(dk, &a.dk, &a.dk_ts, nullptr);
-  set_view(dv, &a.dv, &a.dv_ts, nullptr);
+  set_view(dk, &a.dk, &a.dk_ts, &a.dk_hs);
+  set_view(dv, &a.dv, &a.dv_ts, &a.dv_hs);
   a.lse = const_cast<float*>(lse);
   RGA_TRY(launch_prep_phase(pa, a, L, s));
   if (p->batch == 0) return ATTN_OK;
-  RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->softcap > 0.0f, s), "row-record launch"));
+  RGA_TRY(hip_status(launch_rowinfo(a, p->dtype, p->head_dim, p->softcap > 0.0f, s), "row-record launch"));
   RGA_TRY(hip_status(launch_ksteps(a, (int)L.row_tiles, s), "key-step launch"));
   RGA_TRY(hip_status(launch_units(pa, s), "unit-plan launch"));
   return launch_backward(p, a, L, s);

@@ -6,8 +6,8 @@
 //   A: lane holds A[l32][8g .. 8g+7]      (row l32, eight consecutive k)
 //   B: lane holds B[8g .. 8g+7][l32]      (column l32, eight consecutive k)
 //   D: lane holds D[8(r/4) + 4g + r%4][l32] in accumulator register r = 0..15
-// The feature axis (160) is exactly ten k-steps of 16, so no padding of the
-// head dimension is needed.
+// A head dimension D of 64, 128 or 160 is D / 16 k-steps of 16 (ten for 160),
+// so no padding of the feature axis is needed.
 //
 // When a result tile D is reused as a B operand of the next product (P or dS
 // feeding PV / dQ / dK / dV), the sixteen k-values a lane owns are not the
@@ -21,10 +21,15 @@
 
 namespace rga {
 
-constexpr int HEAD_DIM = 160;
-constexpr int KSTEPS = HEAD_DIM / 16;      // k-steps of the QK^T / dO V^T products
-constexpr int DBLK = HEAD_DIM / 32;        // 32-wide feature blocks of O, dQ, dK, dV
-constexpr int CHUNKS = HEAD_DIM / 8;       // 16-byte chunks per 160-element row
+// Feature-axis geometry of head dimension D (64, 128 or 160).
+template <int D>
+struct Geo {
+  static_assert(D == 64 || D == 128 || D == 160, "head dimension 64, 128 or 160");
+  static constexpr int KSTEPS = D / 16;     // k-steps of the QK^T / dO V^T products
+  static constexpr int DBLK = D / 32;       // 32-wide feature blocks of O, dQ, dK, dV
+  static constexpr int CHUNKS = D / 8;      // 16-byte chunks per row
+  static constexpr int BLK_COLS = CHUNKS / 4;   // 4-chunk blocks across a row (tiles.hpp)
+};
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -121,7 +126,10 @@ struct LogitConsts {
   float sigma;    // scale_multiplier / sqrt(head_dim)
 };
 
-// Per-sequence facts written by the planner (int32 each, SEQ_FIELDS per sequence).
+// Per-sequence facts written by the planner (int32 each, SEQ_FIELDS per
+// sequence).  A "sequence" of the plan is one (packed sequence b, K/V head g)
+// pair, v = b * hkv + g: the rows of the group = hq / hkv query heads that share
+// K/V head g fold into its M dimension (row R = h * Lq + i, h local to the group).
 enum SeqField {
   SQ_Q0 = 0, SQ_LQ, SQ_K0, SQ_LK, SQ_ROWS,
   SQ_KTILES,  // 128-key tiles of the sequence (dK/dV)
@@ -130,6 +138,8 @@ enum SeqField {
   SQ_LQMUL,   // fast_div constants of Lq (folded rows are head-major, see unfold_row)
   SQ_LQSHIFT,
   SQ_RTOFF,   // first 256-row tile of the sequence in batch order (prefix of row tiles)
+  SQ_HB,      // first query head of the sequence's head group (g * group)
+  SQ_G,       // its K/V head g
   SEQ_FIELDS
 };
 
@@ -143,7 +153,8 @@ enum KvField {
   KV_V,        // 64-row steps of the row tiles that visit the key tile
   KV_S,        // first of its items in the work list (see plan_units)
   KV_Q0, KV_K0, KV_LK, KV_ROWS, KV_RTOFF, KV_DSOFF, KV_LQ, KV_LQMUL, KV_LQSHIFT,
-  KV_PAD0, KV_PAD1, KV_PAD2,
+  KV_HB, KV_G,   // first query head of the group, K/V head
+  KV_PAD0,
   KV_FIELDS
 };
 

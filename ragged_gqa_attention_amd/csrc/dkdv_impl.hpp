@@ -1,8 +1,9 @@
 // dK / dV kernel: recompute P from the stored row record, then
 //   dP = dO V^T,  dS = P * (dP - Delta) * (1 - tanh^2(s / c)),
 //   dV = sum_rows P^T dO,  dK = sigma sum_rows dS^T Q,
-// summed over every folded (head, token) row of the sequence, i.e. over all
-// query heads that share the K/V head.
+// summed over every folded (head, token) row of the plan sequence, i.e. over
+// all query heads that share the K/V head.  Templated on the head dimension D
+// (64, 128, 160); one translation unit per D.
 //
 // Page "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "Hard
 // Constraints": the K/V gradients reduce over every query head sharing the K/V
@@ -39,23 +40,25 @@
 // row_key_steps) miss the workgroup's 128 keys has P == 0 exactly on all of
 // them, so its row steps are passed over; the steps a workgroup does visit
 // therefore cover every dS image the dQ kernel later reads.
+#pragma once
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
-namespace {
+namespace kvd {
 
 constexpr int KV_NBUF = 3;
 constexpr int KV_WAVES = KV_THREADS / 64;
 constexpr int PAIR_KEYS = KEY_TILE / (KV_WAVES / 2);  // keys of one wave pair
 constexpr int KB = PAIR_KEYS / 32;                    // 32-key blocks per wave
-constexpr int LOADS_PER_WAVE = CHUNKS / 4;          // 4-chunk blocks of a 16-row group (5)
 static_assert(KV_WAVES == 8 && KB == 1, "eight waves: wave w copies tensor w / 4, row group w % 4");
 static_assert(KV_ROW_STEP == TILE_ROWS, "a step is one row tile (see blk_off)");
 
+template <int D>
 struct KvShared {
-  uint16_t qd[KV_NBUF][2][TILE_ELEMS];   // Q and dO rows of a step (blocked)
+  uint16_t qd[KV_NBUF][2][tile_elems<D>()];   // Q and dO rows of a step (blocked)
   f32x4 rinfo[KV_NBUF][KV_ROW_STEP];     // row records of a step
   u32x4 xch[2][KV_WAVES][KB * 2][64];     // [slot][writer wave][kb * 2 + s][lane]
 };
@@ -66,6 +69,8 @@ struct KvShared {
 // last, which comes last.
 struct KvUnit {
   int q0, k0, Lk, rows, key0;
+  int hb, kvh;              // first query head of the group, K/V head
+  int64_t rbase;            // first row record of the plan sequence (q0 hq + hb Lq)
   int lq, lqmul, lqshift;   // unfold_row constants of the sequence
   int first, last;
   int part;  // FP32 partial slot of the segment, -1 when it stores dK / dV directly
@@ -107,11 +112,12 @@ __device__ __forceinline__ int tile_mask_next(TileMask& m, const KvUnit& u, int 
 }
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
-template <class T, bool CAP, int ROLE, bool LATE, bool WIN>
-__device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const KvUnit& u,
+template <class T, int D, bool CAP, int ROLE, bool LATE, bool WIN>
+__device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, const KvUnit& u,
                                           int wave, int lane) {
+  constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, CHUNKS = Geo<D>::CHUNKS;
+  constexpr int LOADS_PER_WAVE = CHUNKS / 4;   // 4-chunk blocks of a 16-row group
   const int l32 = lane & 31, g = lane >> 5;
-  const int hq = a.hq;
 
   // whether row tile t visits the key tile (its key-step range meets the
   // key tile's two steps); the first 64 are requested before the K / V rows
@@ -132,8 +138,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     const int key = u.key0 + kb * 32 + l32;
     keyf[kb] = (float)key;
     const bool ok = key < u.Lk;
-    const uint16_t* kr = a.k + (int64_t)(u.k0 + (ok ? key : 0)) * a.k_ts + g * 8;
-    const uint16_t* vr = a.v + (int64_t)(u.k0 + (ok ? key : 0)) * a.v_ts + g * 8;
+    const uint16_t* kr =
+        a.k + (int64_t)(u.k0 + (ok ? key : 0)) * a.k_ts + (int64_t)u.kvh * a.k_hs + g * 8;
+    const uint16_t* vr =
+        a.v + (int64_t)(u.k0 + (ok ? key : 0)) * a.v_ts + (int64_t)u.kvh * a.v_hs + g * 8;
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
       const u32x4 kx = load16(kr + ks * 16), vx = load16(vr + ks * 16);
@@ -194,7 +202,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     const int lchunk = (ln & 3) ^ ((ln >> 4) & 3);
     if (wave == 0) {
       const int R = r0 + lane;
-      const float* src = a.rowinfo + ((int64_t)u.q0 * hq + min(R, re - 1)) * 4;
+      const float* src = a.rowinfo + (u.rbase + min(R, re - 1)) * 4;
       load_lds16_unseen(R < re ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
     }
     const int R = r0 + lrow;
@@ -204,7 +212,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
     unfold_row(Rc, __builtin_amdgcn_readfirstlane(u.lq),
                (uint32_t)__builtin_amdgcn_readfirstlane(u.lqmul),
                (uint32_t)__builtin_amdgcn_readfirstlane(u.lqshift), tok_, h_);
-    const uint32_t tok = (uint32_t)tok_, h = (uint32_t)h_;
+    const uint32_t tok = (uint32_t)tok_, h = (uint32_t)(h_ + u.hb);
     const uint32_t t_abs = (uint32_t)u.q0 + tok;
     const bool ok = R < re;
     const uint16_t* base = ltensor ? a.dout : a.q;
@@ -220,7 +228,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // row ROLE * 32 + l32, chunk 2 ks + g; ks / 2 selects the block column and
   // ks % 2 the XOR pattern.
   const int arow = ROLE * 32 + l32;
-  const int roff[2] = {blk_off(arow, g), blk_off(arow, 2 + g)};
+  const int roff[2] = {blk_off<D>(arow, g), blk_off<D>(arow, 2 + g)};
   // Transposing reads (see read_tr): lane (i, G) reads row 4 (G/2) + i/4
   // (+ 8) of the 16-row k-step t, features 16 (G%2) + 4 (i%4) of the
   // 32-feature block db, which is chunk 4 db + 2 (G%2) + (i%4)/2; each (t, db)
@@ -228,8 +236,8 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   const int ti = lane & 15, tG = lane >> 4;
   const int trow0 = 4 * (tG >> 1) + (ti >> 2);
   const int tcl = 2 * (tG & 1) + ((ti & 3) >> 1);
-  const int toff_lo = blk_off(trow0, tcl) + 4 * (ti & 1);
-  const int toff_hi = blk_off(trow0 + 8, tcl) + 4 * (ti & 1);
+  const int toff_lo = blk_off<D>(trow0, tcl) + 4 * (ti & 1);
+  const int toff_hi = blk_off<D>(trow0 + 8, tcl) + 4 * (ti & 1);
   // row records of the lane's rows 8 (r/4) + 4 g + r%4 of the wave's half
   const int rbase = ROLE * 32 + g * 4;
 
@@ -439,7 +447,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   // lane owns key key0 + 32 kb + l32, features 32 db + 8 (r/4) + 4 g + r%4
   const float scale = ROLE ? (CAP ? 4.0f * a.lc.sigma : a.lc.sigma) : 1.0f;
   if (u.part < 0) {
-    uint16_t* base = ROLE ? a.dk : a.dv;
+    uint16_t* base = (ROLE ? a.dk : a.dv) + (int64_t)u.kvh * (ROLE ? a.dk_hs : a.dv_hs);
     const int64_t ts = ROLE ? a.dk_ts : a.dv_ts;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
@@ -461,7 +469,7 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
       const int64_t slot = (int64_t)u.part * KEY_TILE + (u.key0 % KEY_TILE) + kb * 32 + l32;
-      float* dst = base + slot * HEAD_DIM + g * 4;
+      float* dst = base + slot * D + g * 4;
 #pragma unroll
       for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -475,11 +483,12 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared& sm, const
   }
 }
 
-}  // namespace
+}  // namespace kvd
 
-template <class T, bool CAP, bool WIN>
+template <class T, int D, bool CAP, bool WIN>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) KvShared sm;
+  using namespace kvd;
+  __shared__ __attribute__((aligned(16))) KvShared<D> sm;
 
   // items [w0, w1) of the work list
   const long long W = a.plan.kv_head[0];
@@ -517,6 +526,9 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.lq = e[KV_LQ];
     u.lqmul = e[KV_LQMUL];
     u.lqshift = e[KV_LQSHIFT];
+    u.hb = e[KV_HB];
+    u.kvh = e[KV_G];
+    u.rbase = (int64_t)u.q0 * a.hq + (int64_t)u.hb * u.lq;
     u.first = (int)f;
     u.last = (int)l;
     // a key tile split over shares: partial slot 2 sh for the share's first
@@ -530,34 +542,35 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
     // waves w and w + 4 share a SIMD
     if (wave < 4) {
-      if (wave & 1) dkdv_wave<T, CAP, 1, false, WIN>(a, sm, u, wave, lane);
-      else dkdv_wave<T, CAP, 0, false, WIN>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, D, CAP, 1, false, WIN>(a, sm, u, wave, lane);
+      else dkdv_wave<T, D, CAP, 0, false, WIN>(a, sm, u, wave, lane);
     } else {
-      if (wave & 1) dkdv_wave<T, CAP, 1, true, WIN>(a, sm, u, wave, lane);
-      else dkdv_wave<T, CAP, 0, true, WIN>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, D, CAP, 1, true, WIN>(a, sm, u, wave, lane);
+      else dkdv_wave<T, D, CAP, 0, true, WIN>(a, sm, u, wave, lane);
     }
     w = vs + l;
     __syncthreads();   // the next segment reuses the LDS buffers
   }
 }
 
-template <class T>
+template <class T, int D>
 static hipError_t launch_dkdv_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
   const bool win = a.win_left >= 0 || a.win_right >= 0;
   if (cap) {
-    if (win) hipLaunchKernelGGL((dkdv_kernel<T, true, true>), grid, KV_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<T, true, false>), grid, KV_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, true, true>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, D, true, false>), grid, KV_THREADS, 0, s, a);
   } else {
-    if (win) hipLaunchKernelGGL((dkdv_kernel<T, false, true>), grid, KV_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<T, false, false>), grid, KV_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, false, true>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, D, false, false>), grid, KV_THREADS, 0, s, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
+template <int D>
+hipError_t launch_dkdv_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_dkdv_t<BF16>(a, cap, grid, s)
-                          : launch_dkdv_t<F16>(a, cap, grid, s);
+  return dtype == DT_BF16 ? launch_dkdv_t<BF16, D>(a, cap, grid, s)
+                          : launch_dkdv_t<F16, D>(a, cap, grid, s);
 }
 
 }  // namespace rga

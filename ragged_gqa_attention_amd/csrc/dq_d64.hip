@@ -1,0 +1,6 @@
+// dQ kernels for head dimension 64 (see dq_impl.hpp).
+#include "dq_impl.hpp"
+
+namespace rga {
+template hipError_t launch_dq_d<64>(const AttnArgs&, int, bool, int, hipStream_t);
+}  // namespace rga

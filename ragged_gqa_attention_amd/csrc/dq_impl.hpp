@@ -13,7 +13,8 @@
 // P is rebuilt exactly as the forward formed it: distances from the clamped
 // centre max(i + Lk - Lq, 0), the large per-row offset kept analytic, and only
 // the small residual log2 l subtracted (see fwd.hip), so no two large numbers
-// are ever subtracted.
+// are ever subtracted.  Templated on the head dimension D (64, 128, 160); one
+// translation unit per D.
 //
 // A workgroup owns 256 folded rows (like the forward) and walks the keys in
 // steps of 64, copied to LDS with direct loads (double-buffered): K and V as
@@ -21,17 +22,20 @@
 // MFMA, dQ^T its K^T operand with two transposing reads of the K rows.  It visits only the key
 // steps the forward recorded for the tile (a.ksteps): outside them every P,
 // and so every dS, is exactly zero.
+#pragma once
+
 #include "kernels.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
-namespace {
+namespace dqd {
 
 // LDS of one key step: K and V rows (row tiles, blk_off), double-buffered.
+template <int D>
 struct DqShared {
-  uint16_t k[2][TILE_ELEMS];
-  uint16_t v[2][TILE_ELEMS];
+  uint16_t k[2][tile_elems<D>()];
+  uint16_t v[2][tile_elems<D>()];
 };
 
 // dK / dV of the 128-key tiles part, part + parts, ... (batch order): key
@@ -42,9 +46,9 @@ struct DqShared {
 // dK/dV kernel has finished (same stream), so its partials are complete.  A
 // tile is 128 x 40 groups of 4 features, ten per thread, whose sums are
 // formed side by side (ten loads per tensor in flight).
-template <class T>
+template <class T, int D>
 __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int parts) {
-  constexpr int QUADS = HEAD_DIM / 4;
+  constexpr int QUADS = D / 4;
   constexpr int PER_THREAD = KEY_TILE * QUADS / ROW_THREADS;
   static_assert(PER_THREAD * ROW_THREADS == KEY_TILE * QUADS, "whole tiles per pass");
   const long long W = a.plan.kv_head[0];
@@ -67,6 +71,8 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
     }
     const int k0 = e[KV_K0] + e[KV_KTILE] * KEY_TILE;
     const int nkeys = min(KEY_TILE, e[KV_LK] - e[KV_KTILE] * KEY_TILE);
+    uint16_t* dkb = a.dk + (int64_t)e[KV_G] * a.dk_hs;
+    uint16_t* dvb = a.dv + (int64_t)e[KV_G] * a.dv_hs;
     f32x4 sk[PER_THREAD], sv[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
@@ -77,8 +83,8 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
       const long long p0 = (long long)p * W / G, p1 = (long long)(p + 1) * W / G;
       if (p0 >= p1) continue;   // an empty share wrote nothing
       const int64_t slot = 2 * (int64_t)p + (S <= p0 ? 0 : 1);
-      const float* pk = a.part_dk + slot * KEY_TILE * HEAD_DIM;
-      const float* pv = a.part_dv + slot * KEY_TILE * HEAD_DIM;
+      const float* pk = a.part_dk + slot * KEY_TILE * D;
+      const float* pv = a.part_dv + slot * KEY_TILE * D;
 #pragma unroll
       for (int j = 0; j < PER_THREAD; ++j) {
         const int i = threadIdx.x + j * ROW_THREADS;   // key i / 40, features 4 (i % 40)
@@ -92,9 +98,9 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
       const int key = i / QUADS, c4 = i - key * QUADS;
       if (key >= nkeys) continue;
       const int64_t t = k0 + key;
-      *reinterpret_cast<u32x2*>(a.dk + t * a.dk_ts + c4 * 4) =
+      *reinterpret_cast<u32x2*>(dkb + t * a.dk_ts + c4 * 4) =
           u32x2{pack2<T>(sk[j][0], sk[j][1]), pack2<T>(sk[j][2], sk[j][3])};
-      *reinterpret_cast<u32x2*>(a.dv + t * a.dv_ts + c4 * 4) =
+      *reinterpret_cast<u32x2*>(dvb + t * a.dv_ts + c4 * 4) =
           u32x2{pack2<T>(sv[j][0], sv[j][1]), pack2<T>(sv[j][2], sv[j][3])};
     }
   }
@@ -105,12 +111,14 @@ __device__ __forceinline__ void reduce_kv_tiles(const AttnArgs& a, int part, int
 // barrier) so that each global store writes 64-byte pieces of rows: lanes
 // 4q .. 4q + 3 of wave w take row 32 w + 16 h + q, chunks (lane % 4) + 4 i.
 // lrow: the tile-local row the lane's accumulator column belongs to.
-template <class T>
+template <class T, int D>
 __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage,
-                                              const f32x16 (&dQ)[DBLK], float scale, int lrow,
-                                              int tile, const int* sq, int wave, int lane) {
+                                              const f32x16 (&dQ)[Geo<D>::DBLK], float scale,
+                                              int lrow, int tile, const int* sq, int wave,
+                                              int lane) {
+  constexpr int DBLK = Geo<D>::DBLK, CHUNKS = Geo<D>::CHUNKS;
   const int q0 = sq[SQ_Q0], rows = sq[SQ_ROWS];
-  constexpr int PITCH = HEAD_DIM + 8;
+  constexpr int PITCH = D + 8;
   const int g = lane >> 5;
   __syncthreads();   // every wave is done with the tile buffers
 #pragma unroll
@@ -128,7 +136,7 @@ __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage
     if (rg >= rows) continue;
     int tk, hd;
     unfold_row(rg, sq, tk, hd);
-    uint16_t* drow = a.dq + (int64_t)(q0 + tk) * a.dq_ts + (int64_t)hd * a.dq_hs;
+    uint16_t* drow = a.dq + (int64_t)(q0 + tk) * a.dq_ts + (int64_t)(sq[SQ_HB] + hd) * a.dq_hs;
 #pragma unroll
     for (int i = 0; i < CHUNKS / 4; ++i) {
       const int c = (lane & 3) + 4 * i;
@@ -140,11 +148,12 @@ __device__ __forceinline__ void store_dq_tile(const AttnArgs& a, uint16_t* stage
 // LDS of the stored-dS path: the dS image (64 keys x 256 rows, ds_off) and
 // the K rows (blk_off) of a key step, three buffers (two steps in flight).
 constexpr int DQS_NBUF = 3;
+template <int D>
 struct DqStoredShared {
   uint16_t ds[DQS_NBUF][DS_IMAGE_ELEMS];
-  uint16_t k[DQS_NBUF][TILE_ELEMS];
+  uint16_t k[DQS_NBUF][tile_elems<D>()];
 };
-static_assert(ROW_TILE * (HEAD_DIM + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ staging fits");
+static_assert(ROW_TILE * (160 + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ staging fits");
 
 // dQ of row tile `tile` from the dS images the dK/dV kernel stored:
 // dQ^T[d][row] += K^T[d][keys] dS^T[keys][row], nothing recomputed.  Both
@@ -153,9 +162,10 @@ static_assert(ROW_TILE * (HEAD_DIM + 8) <= DQS_NBUF * DS_IMAGE_ELEMS, "dQ stagin
 // order of the K^T read).  Limited by the HBM reads of the images.
 // The first two steps' copies are issued before the workgroup's slice of
 // the dK / dV partial sums, so they land while it runs.
-template <class T, bool CAP>
-__device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm, const int* sq,
+template <class T, int D, bool CAP>
+__device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared<D>& sm, const int* sq,
                                           int tile, int klo, int khi) {
+  constexpr int DBLK = Geo<D>::DBLK, BLK_COLS = Geo<D>::BLK_COLS;
   const int q0 = sq[SQ_Q0], Lk = sq[SQ_LK], rows = sq[SQ_ROWS];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -163,10 +173,11 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   const int nks = (Lk + TILE_ROWS - 1) / TILE_ROWS;
   const uint16_t* img0 = a.ds + ((int64_t)sq[SQ_DSOFF] + (int64_t)tile * nks) * DS_IMAGE_ELEMS;
   const int k0 = sq[SQ_K0];
+  const uint16_t* kbase = a.k + (int64_t)sq[SQ_G] * a.k_hs;
   // copies of key step kt: each wave four 1 KB blocks of the image, waves 0-3
-  // also a 16-row group of the K rows (five loads: 9 or 4 per wave)
+  // also a 16-row group of the K rows (D / 32 loads: 4 + D / 32 or 4 per wave)
   constexpr int IMG_LOADS = DS_IMAGE_ELEMS / BLK_ELEMS / ROW_WAVES;
-  static_assert(IMG_LOADS == 4 && BLK_COLS == 5, "waits below count 4 + 5 or 4 loads per step");
+  static_assert(IMG_LOADS == 4, "waits below count 4 image loads per wave and step");
   // (issued unseen by the compiler, which would otherwise hold each step's
   // transposing reads until the copies of the two steps ahead had landed;
   // the waits below order the buffers)
@@ -178,8 +189,8 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
       load_lds16_unseen(img + blk * BLK_ELEMS + lane * 8, sm.ds[buf] + blk * BLK_ELEMS);
     }
     if (wave < 4)
-      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
-                          a.zero, wave, lane);
+      load_row_tile<D, true>(sm.k[buf], kbase + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
+                             a.zero, wave, lane);
   };
 
   // transposing reads (see read_tr): lane (i, G) addresses key rows
@@ -194,8 +205,8 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   // (lane (i, G): key rows 4 (G/2) + i/4 and + 8 of the k-step, chunk
   // 2 (G%2) + (i%4)/2 of the feature block, half i % 2)
   const int kcl = 2 * (tG & 1) + ((ti & 3) >> 1);
-  const int koff_lo = blk_off(krow, kcl) + 4 * (ti & 1);
-  const int koff_hi = blk_off(krow + 8, kcl) + 4 * (ti & 1);
+  const int koff_lo = blk_off<D>(krow, kcl) + 4 * (ti & 1);
+  const int koff_hi = blk_off<D>(krow + 8, kcl) + 4 * (ti & 1);
 
   f32x16 dQ[DBLK];
 #pragma unroll
@@ -207,19 +218,19 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
     // step kt has landed (step kt + 1 may still be in flight) for every wave,
     // and every wave is done with step kt - 1, whose buffer step kt + 2 takes
     if (kt + 1 < khi) {
-      if (wave < 4) wait_vm_le<9>();
-      else wait_vm_le<4>();
+      if (wave < 4) wait_vm_le<IMG_LOADS + BLK_COLS>();
+      else wait_vm_le<IMG_LOADS>();
     } else {
       wait_vm();
     }
     __syncthreads();
     if (kt + 2 < khi) issue(kt + 2, (kt + 2) % DQS_NBUF);
-    const uint16_t* D = sm.ds[buf];
+    const uint16_t* Ds = sm.ds[buf];
     const uint16_t* Kb = sm.k[buf];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const u32x2 lo = read_tr(D + dlo + t * KSTEP_ELEMS);
-      const u32x2 hi = read_tr(D + dhi + t * KSTEP_ELEMS);
+      const u32x2 lo = read_tr(Ds + dlo + t * KSTEP_ELEMS);
+      const u32x2 hi = read_tr(Ds + dhi + t * KSTEP_ELEMS);
       const u32x4 bt = u32x4{lo[0], lo[1], hi[0], hi[1]};
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
@@ -232,18 +243,23 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared& sm,
   }
 
   // lane l32 holds row 32 w + tt_key_pos(l32) of the tile
-  store_dq_tile<T>(a, sm.ds[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma,
-                   wave * 32 + tt_key_pos(l32), tile, sq, wave, lane);
+  store_dq_tile<T, D>(a, sm.ds[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma,
+                      wave * 32 + tt_key_pos(l32), tile, sq, wave, lane);
 }
 
-}  // namespace
+template <int D>
+union DqSmem {
+  DqShared<D> r;
+  DqStoredShared<D> d;
+};
 
-template <class T, bool CAP, bool WIN>
+}  // namespace dqd
+
+template <class T, int D, bool CAP, bool WIN>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) union {
-    DqShared r;
-    DqStoredShared d;
-  } sm;
+  using namespace dqd;
+  constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, BLK_COLS = Geo<D>::BLK_COLS;
+  __shared__ __attribute__((aligned(16))) DqSmem<D> sm;
 
   // The grid holds the row-tile slots plus R workgroups that sum the split
   // dK / dV partials, a slice each; those come right after the first round
@@ -253,7 +269,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int nrt = a.batch > 0 ? a.plan.kv_head[2] : 0;   // row tiles
   const int at = min(nrt, a.kv_wgs);
   if ((int)blockIdx.x >= at && (int)blockIdx.x < at + R) {
-    if (a.total_k > 0) reduce_kv_tiles<T>(a, blockIdx.x - at, R);
+    if (a.total_k > 0) reduce_kv_tiles<T, D>(a, blockIdx.x - at, R);
     return;
   }
   const int slot = (int)blockIdx.x < at ? (int)blockIdx.x : (int)blockIdx.x - R;
@@ -264,7 +280,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
   const int klo = ks[0], khi = ks[1];
   if (a.ds && sq[SQ_DSOFF] >= 0) {
-    dq_stored<T, CAP>(a, sm.d, sq, tile, klo, khi);
+    dq_stored<T, D, CAP>(a, sm.d, sq, tile, klo, khi);
     return;
   }
   const int q0 = sq[SQ_Q0], k0 = sq[SQ_K0], Lk = sq[SQ_LK];
@@ -278,10 +294,15 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const int rr = row_ok ? row : rows - 1;
   int ti, hh;
   unfold_row(rr, sq, ti, hh);
-  const int64_t ri = (int64_t)q0 * a.hq + rr;   // folded row record
+  const int hb = sq[SQ_HB];
+  // folded row record (rows of the group's heads follow q0 hq + hb Lq)
+  const int64_t ri = (int64_t)q0 * a.hq + (int64_t)hb * sq[SQ_LQ] + rr;
 
-  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
-  const uint16_t* dorow = a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)hh * a.do_hs + g * 8;
+  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)(hb + hh) * a.q_hs + g * 8;
+  const uint16_t* dorow =
+      a.dout + (int64_t)(q0 + ti) * a.do_ts + (int64_t)(hb + hh) * a.do_hs + g * 8;
+  const uint16_t* kbase = a.k + (int64_t)sq[SQ_G] * a.k_hs;
+  const uint16_t* vbase = a.v + (int64_t)sq[SQ_G] * a.v_hs;
   u32x4 qf[KSTEPS], df[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -310,21 +331,21 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   // buffers before the transposing reads of K)
   auto issue = [&](int kt, int buf) {
     if (wave < 4)
-      load_row_tile<true>(sm.r.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
-                          a.zero, wave, lane);
+      load_row_tile<D, true>(sm.r.k[buf], kbase + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS,
+                             Lk, a.zero, wave, lane);
     else
-      load_row_tile<true>(sm.r.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
-                          a.zero, wave - 4, lane);
+      load_row_tile<D, true>(sm.r.v[buf], vbase + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS,
+                             Lk, a.zero, wave - 4, lane);
   };
 
   // lane-constant LDS offsets: K / V row reads (row kb * 32 + l32, chunk
   // 2 ks + g) and transposing K reads for the K^T operand (lane (i, G): key
   // rows 4 (G/2) + i/4 and + 8 of a k-step, chunk 2 (G%2) + (i%4)/2, half i % 2)
-  const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
+  const int koff[2] = {blk_off<D>(l32, g), blk_off<D>(l32, 2 + g)};
   const int vi = lane & 15, vG = lane >> 4;
   const int trow = 4 * (vG >> 1) + (vi >> 2), tcl = 2 * (vG & 1) + ((vi & 3) >> 1);
-  const int toff_lo = blk_off(trow, tcl) + 4 * (vi & 1);
-  const int toff_hi = blk_off(trow + 8, tcl) + 4 * (vi & 1);
+  const int toff_lo = blk_off<D>(trow, tcl) + 4 * (vi & 1);
+  const int toff_hi = blk_off<D>(trow + 8, tcl) + 4 * (vi & 1);
 
   // one key step on the tiles in LDS buffer buf; masked: keys past Lk get P = 0
   auto step = [&](int buf, int kbase, auto masked) {
@@ -401,27 +422,28 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     step(nfull & 1, nfull * TILE_ROWS, Flag<true>{});
   }
 
-  store_dq_tile<T>(a, sm.r.k[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma, wave * 32 + l32,
-                   tile, sq, wave, lane);
+  store_dq_tile<T, D>(a, sm.r.k[0], dQ, CAP ? 4.0f * a.lc.sigma : a.lc.sigma, wave * 32 + l32,
+                      tile, sq, wave, lane);
 }
 
-template <class T>
+template <class T, int D>
 static hipError_t launch_dq_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
   const bool win = a.win_left >= 0 || a.win_right >= 0;
   if (cap) {
-    if (win) hipLaunchKernelGGL((dq_kernel<T, true, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<T, true, false>), grid, ROW_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dq_kernel<T, D, true, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, D, true, false>), grid, ROW_THREADS, 0, s, a);
   } else {
-    if (win) hipLaunchKernelGGL((dq_kernel<T, false, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<T, false, false>), grid, ROW_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dq_kernel<T, D, false, true>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, D, false, false>), grid, ROW_THREADS, 0, s, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
+template <int D>
+hipError_t launch_dq_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_dq_t<BF16>(a, cap, grid, s)
-                          : launch_dq_t<F16>(a, cap, grid, s);
+  return dtype == DT_BF16 ? launch_dq_t<BF16, D>(a, cap, grid, s)
+                          : launch_dq_t<F16, D>(a, cap, grid, s);
 }
 
 }  // namespace rga

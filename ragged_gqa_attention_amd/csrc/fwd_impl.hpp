@@ -7,9 +7,12 @@
 // recompute", section "Root causes addressed": stream over key tiles and store
 // only O and L = m + log l.
 //
-// Every query head shares the one K/V head, so the Lq x Hq rows of a sequence
-// are folded into one M dimension (row = head * Lq + token): a workgroup's 256
-// rows reuse each staged K/V tile 256 times.  Each wave owns 32 rows and forms
+// The query heads of a group share one K/V head, so the Lq x group rows of a
+// plan sequence (a packed sequence and one K/V head) are folded into one M
+// dimension (row = head * Lq + token): a workgroup's 256 rows reuse each
+// staged K/V tile 256 times.  The kernels are templated on the head dimension
+// D (64, 128 or 160: D / 16 k-steps of the 32x32x16 MFMA); one translation
+// unit instantiates each D.  Each wave owns 32 rows and forms
 // S^T = K Q^T (keys x rows, Q in registers), so an accumulator lane owns one row
 // and O^T = V^T P^T keeps the row scale per lane.  Key steps of 64 are copied
 // to LDS with direct loads (three buffers), K and V as row tiles: S^T reads
@@ -37,32 +40,26 @@
 // only the key steps [lo, hi) that hold a key some row of its tile keeps (the
 // planner records that range per tile).  In the full-VJP call one more
 // workgroup plans the dK/dV units meanwhile.
+#pragma once
+
 #include "kernels.hpp"
 #include "planner.hpp"
 #include "tiles.hpp"
 
 namespace rga {
 
-namespace {
-
 // LDS of a key step: the K and V rows (row tiles, blk_off), three buffers
 // (one step in flight, one being read, and the previous one still read by the
 // deferred half of the lag waves).
 constexpr int FWD_NBUF = 3;
+template <int D>
 struct FwdShared {
-  uint16_t k[FWD_NBUF][TILE_ELEMS];
-  uint16_t v[FWD_NBUF][TILE_ELEMS];
+  uint16_t k[FWD_NBUF][tile_elems<D>()];
+  uint16_t v[FWD_NBUF][tile_elems<D>()];
 };
-// After the key loop the same LDS holds the normalised O rows (pitch of 168
+// After the key loop the same LDS holds the normalised O rows (pitch of D + 8
 // elements) and each row's record.
-constexpr int O_PITCH = HEAD_DIM + 8;
-static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared),
-              "O staging fits the key-tile buffers");
-
-}  // namespace
-
-static_assert(sizeof(UnitsShared) <= sizeof(FwdShared), "the unit planner fits the tile buffers");
-static_assert(sizeof(PlanShared) <= sizeof(FwdShared), "the planner fits the tile buffers");
+template <int D> constexpr int o_pitch() { return D + 8; }
 
 // Grid: workgroup 0 runs the planner (then, in the full-VJP call, the dK/dV
 // unit plan), workgroups 1 .. a.fwd_slots the row tiles.  The row tiles do
@@ -71,15 +68,23 @@ static_assert(sizeof(PlanShared) <= sizeof(FwdShared), "the planner fits the til
 // beside them on one compute unit.
 // One 256-row tile of the forward: sequence b (extents q0, Lq, k0, Lk), tile
 // `tile` of its folded rows, key steps [klo, khi).
-template <class T, bool CAP, bool DELTA, bool WIN>
-__device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const int b,
+template <class T, int D, bool CAP, bool DELTA, bool WIN>
+__device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, const int b,
                                          const int tile, const int q0, const int Lq,
                                          const int k0, const int Lk, const int klo,
                                          const int khi) {
+  constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, CHUNKS = Geo<D>::CHUNKS;
+  constexpr int BLK_COLS = Geo<D>::BLK_COLS, O_PITCH = o_pitch<D>();
+  static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared<D>),
+                "O staging fits the key-tile buffers");
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int rows = Lq * a.hq;
+  const int rows = Lq * a.group;
+  // plan sequence b = packed sequence bp, K/V head kvh (query heads hb ..)
+  const int bp = b / a.hkv, kvh = b - bp * a.hkv, hb = kvh * a.group;
+  const uint16_t* kbase = a.k + (int64_t)kvh * a.k_hs;
+  const uint16_t* vbase = a.v + (int64_t)kvh * a.v_hs;
 
   // copies of key step kt: waves 0-3 the K rows, waves 4-7 the V rows (one
   // 16-row group each).  Rows past Lk repeat row Lk - 1 (the tile runs before
@@ -88,15 +93,15 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   // Issued unseen by the compiler (it would hold the step's transposing reads
   // until the next step's copies had landed); advance() orders the buffers.
   // The first step's copies go out before the Q rows are requested.
-  const uint16_t* klast = a.k + (int64_t)(k0 + max(Lk, 1) - 1) * a.k_ts;
-  const uint16_t* vlast = a.v + (int64_t)(k0 + max(Lk, 1) - 1) * a.v_ts;
+  const uint16_t* klast = kbase + (int64_t)(k0 + max(Lk, 1) - 1) * a.k_ts;
+  const uint16_t* vlast = vbase + (int64_t)(k0 + max(Lk, 1) - 1) * a.v_ts;
   auto issue = [&](int kt, int buf) {
     if (wave < 4)
-      load_row_tile<true>(sm.k[buf], a.k + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS, Lk,
-                          klast, wave, lane);
+      load_row_tile<D, true>(sm.k[buf], kbase + (int64_t)k0 * a.k_ts, a.k_ts, kt * TILE_ROWS,
+                             Lk, klast, wave, lane);
     else
-      load_row_tile<true>(sm.v[buf], a.v + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS, Lk,
-                          vlast, wave - 4, lane);
+      load_row_tile<D, true>(sm.v[buf], vbase + (int64_t)k0 * a.v_ts, a.v_ts, kt * TILE_ROWS,
+                             Lk, vlast, wave - 4, lane);
   };
   if (klo < khi) issue(klo, klo % FWD_NBUF);
 
@@ -107,12 +112,12 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   const int hh = rr / Lq, ti = rr - hh * Lq;
 
   // Q row as B operand: k-step ks covers features 16ks + 8g .. +7
-  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)hh * a.q_hs + g * 8;
+  const uint16_t* qrow = a.q + (int64_t)(q0 + ti) * a.q_ts + (int64_t)(hb + hh) * a.q_hs + g * 8;
   u32x4 qf[KSTEPS];
 #pragma unroll
   for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = load16(qrow + ks * 16);
 
-  const float slope2 = a.slopes[(int64_t)b * a.slopes_stride + hh] * LOG2E;
+  const float slope2 = a.slopes[(int64_t)bp * a.slopes_stride + hb + hh] * LOG2E;
   // key j of accumulator register r in block kb of the tile at kbase is
   // kbase + 32 kb + 8 (r/4) + 4 g + r%4; cb0 - (kbase + 32 kb + 8 (r/4) + r%4)
   // is then j's signed distance from the clamped centre max(i + Lk - Lq, 0)
@@ -149,12 +154,12 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   // and transposing V reads (see read_tr): lane (i, G) addresses key rows
   // 4 (G/2) + i/4 and + 8 of a 16-key k-step, chunk 2 (G%2) + (i%4)/2 of a
   // 32-feature block, the low or high half of its 16 bytes by i % 2
-  const int koff[2] = {blk_off(l32, g), blk_off(l32, 2 + g)};
+  const int koff[2] = {blk_off<D>(l32, g), blk_off<D>(l32, 2 + g)};
   const int vi = lane & 15, vG = lane >> 4;
   const int vrow = 4 * (vG >> 1) + (vi >> 2);
   const int vcl = 2 * (vG & 1) + ((vi & 3) >> 1);
-  const int voff_lo = blk_off(vrow, vcl) + 4 * (vi & 1);
-  const int voff_hi = blk_off(vrow + 8, vcl) + 4 * (vi & 1);
+  const int voff_lo = blk_off<D>(vrow, vcl) + 4 * (vi & 1);
+  const int voff_hi = blk_off<D>(vrow + 8, vcl) + 4 * (vi & 1);
 
   // S^T[key][row] = K Q^T (lane = row) for key block kb of the K tile Kb
   // (LDS operands are read two k-steps ahead of the MFMA that uses them)
@@ -358,9 +363,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
     eok[h] = rg < rows;
     const int rc = eok[h] ? rg : rows - 1;
     const int hd = rc / Lq, tk = rc - hd * Lq;
-    eout[h] = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)hd * a.o_hs;
+    eout[h] = a.out + (int64_t)(q0 + tk) * a.o_ts + (int64_t)(hb + hd) * a.o_hs;
     if (DELTA) {
-      const uint16_t* drow = a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)hd * a.do_hs;
+      const uint16_t* drow =
+          a.dout + (int64_t)(q0 + tk) * a.do_ts + (int64_t)(hb + hd) * a.do_hs;
 #pragma unroll
       for (int i = 0; i < CHUNKS / 4; ++i) dpre[h][i] = load16(drow + ((lane & 3) + 4 * i) * 8);
     }
@@ -383,7 +389,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
   if (g == 0) {
     sinfo[lrow] = f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f, 0.0f};
     if (row_ok)
-      a.lse[(int64_t)(q0 + ti) * a.hq + hh] = lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
+      a.lse[(int64_t)(q0 + ti) * a.hq + hb + hh] =
+          lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
   }
   __syncthreads();
 #pragma unroll
@@ -411,13 +418,14 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared& sm, const
     if (ok && (lane & 3) == 0 && a.rowinfo) {
       f32x4 rec = sinfo[r];
       rec[3] = DELTA ? dpart : 0.0f;
-      *reinterpret_cast<f32x4*>(a.rowinfo + ((int64_t)q0 * a.hq + rg) * 4) = rec;
+      *reinterpret_cast<f32x4*>(a.rowinfo + ((int64_t)q0 * a.hq + (int64_t)hb * Lq + rg) * 4) =
+          rec;
     }
   }
 }
 
-// The forward's row tiles in a fixed order: sequences by key length, longest
-// first (ties by index), for up to 64 sequences, else batch order; each
+// The forward's row tiles in a fixed order: plan sequences by key length,
+// longest first (ties by index), for up to 64 of them, else batch order; each
 // workgroup builds the table of that order once (from cu_q / cu_k alone).
 constexpr int FWD_ORDER_MAX = 512;
 struct FwdOrder {
@@ -432,20 +440,15 @@ struct FwdOrder {
 template <int NT>
 __device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& ord) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = pa.batch, hq = pa.hq;
+  const int B = pa.batch, hq = pa.hq;   // plan sequences, rows folded per sequence
   if (B <= 64) {
     if (wave == 0) {
       const int b = lane;
       const bool live = b < B;
-      const int bl = min(b, B - 1);   // B >= 1: the forward is not launched otherwise
-      int cq = pa.cu_q[bl], nq = pa.cu_q[bl + 1];
-      int ck = pa.cu_k[bl], nk = pa.cu_k[bl + 1];
-      bool bad = live && (cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
-                          (int64_t)nk > pa.total_k);
-      if (b == 0) bad |= cq != 0 || ck != 0;
-      if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
-      const bool any_bad = __any(bad);
-      const int lq = live ? nq - cq : 0, lk = live ? nk - ck : 0;
+      // B >= 1: the forward is not launched otherwise
+      const SeqExt e = seq_extents(pa, min(b, B - 1));
+      const bool any_bad = __any(live && e.bad);
+      const int lq = live ? e.nq - e.cq : 0, lk = live ? e.nk - e.ck : 0;
       const int n = live ? (lq * hq + ROW_TILE - 1) / ROW_TILE : 0;
       int start = 0, rank = 0;   // over the sequences ranked before b
       for (int j = 0; j < B; ++j) {
@@ -460,9 +463,9 @@ __device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& or
       if (live) {
         ord.start[rank] = start;
         ord.seq[rank] = b;
-        ord.q0[rank] = cq;
+        ord.q0[rank] = e.cq;
         ord.lq[rank] = lq;
-        ord.k0[rank] = ck;
+        ord.k0[rank] = e.ck;
         ord.lk[rank] = lk;
       }
       if (lane == 0) {
@@ -475,16 +478,13 @@ __device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& or
   } else if (B <= FWD_ORDER_MAX) {
     bool bad = false;
     for (int b = tid; b < B; b += NT) {
-      const int cq = pa.cu_q[b], nq = pa.cu_q[b + 1], ck = pa.cu_k[b], nk = pa.cu_k[b + 1];
-      bad |= cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
-             (int64_t)nk > pa.total_k;
-      if (b == 0) bad |= cq != 0 || ck != 0;
-      if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
+      const SeqExt e = seq_extents(pa, b);
+      bad |= e.bad;
       ord.seq[b] = b;
-      ord.q0[b] = cq;
-      ord.lq[b] = max(nq - cq, 0);
-      ord.k0[b] = ck;
-      ord.lk[b] = max(nk - ck, 0);
+      ord.q0[b] = e.cq;
+      ord.lq[b] = max(e.nq - e.cq, 0);
+      ord.k0[b] = e.ck;
+      ord.lk[b] = max(e.nk - e.ck, 0);
     }
     const bool any_bad = __syncthreads_or(bad);
     block_exclusive_scan<NT>(B, [&](int b) { return (ord.lq[b] * hq + ROW_TILE - 1) / ROW_TILE; },
@@ -540,7 +540,7 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
 #pragma unroll
     for (int i = 0; i < SPER; ++i) {
       if (i * NT < B * hq)   // uniform
-        sv[i] = pa.slopes[(int64_t)ord.seq[min(k, B - 1)] * pa.slopes_stride + h];
+        sv[i] = pa.slopes[slope_base(ord.seq[min(k, B - 1)], pa.hkv, hq, pa.slopes_stride) + h];
       k += dk;
       h += dh;
       if (h >= hq) { h -= hq; ++k; }
@@ -654,18 +654,29 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
 // the shortest next.  The row tiles never wait for the planner: a workgroup
 // finds each tile and its key-step range from cu_q / cu_k itself (the order
 // table, tile_key_range), so the planner runs beside them.
-template <class T, bool CAP, bool DELTA, bool WIN>
+// LDS of the forward grid: the key-step buffers of the row tiles, or the
+// planner's tables (workgroup 0), or the longest-first ranking scratch that a
+// row-tile workgroup uses before its first tile.
+template <int D>
+union FwdSmem {
+  FwdShared<D> f;
+  PlanShared p;
+  UnitsShared u;
+  LptScratch l;
+};
+
+template <class T, int D, bool CAP, bool DELTA, bool WIN>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
-  __shared__ __attribute__((aligned(16))) FwdShared sm;
+  __shared__ __attribute__((aligned(16))) FwdSmem<D> smu;
   __shared__ FwdOrder ord;
   __shared__ int tinfo[8];
-  static_assert(sizeof(LptScratch) <= sizeof(FwdShared), "the ranking fits the tile buffers");
+  FwdShared<D>& sm = smu.f;
 
   if (blockIdx.x == 0) {
-    plan_block<ROW_THREADS>(pa, *reinterpret_cast<PlanShared*>(&sm));
+    plan_block<ROW_THREADS>(pa, smu.p);
     if (DELTA) {   // the full-VJP call: the dK/dV units, from the planner's ranges
       __syncthreads();
-      plan_units<ROW_THREADS>(pa, a.plan.seq, *reinterpret_cast<UnitsShared*>(&sm));
+      plan_units<ROW_THREADS>(pa, a.plan.seq, smu.u);
     }
     return;
   }
@@ -679,7 +690,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   __shared__ int list[FWD_LIST_MAX][8];
   __shared__ int nlist_s;
   if (status == 1) {
-    const int n = lpt_list<ROW_THREADS>(pa, ord, *reinterpret_cast<LptScratch*>(&sm), list, w, P);
+    const int n = lpt_list<ROW_THREADS>(pa, ord, smu.l, list, w, P);
     if (threadIdx.x == 0) nlist_s = n;
   } else if (threadIdx.x == 0) {
     nlist_s = -1;
@@ -688,8 +699,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   const int nlist = nlist_s;
   if (nlist >= 0) {
     for (int i = 0; i < nlist; ++i) {
-      fwd_tile<T, CAP, DELTA, WIN>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3], list[i][4],
-                              list[i][5], list[i][6], list[i][7]);
+      fwd_tile<T, D, CAP, DELTA, WIN>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3],
+                                      list[i][4], list[i][5], list[i][6], list[i][7]);
       __syncthreads();   // the next tile reuses the LDS buffers
     }
     return;
@@ -733,40 +744,41 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     __syncthreads();
     const int b = tinfo[0];
     if (b < 0) break;
-    fwd_tile<T, CAP, DELTA, WIN>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5], tinfo[6],
-                            tinfo[7]);
+    fwd_tile<T, D, CAP, DELTA, WIN>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5],
+                                    tinfo[6], tinfo[7]);
     __syncthreads();   // the next tile reuses tinfo and the LDS buffers
   }
 }
 
 
-template <class T, bool WIN>
+template <class T, int D, bool WIN>
 static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
                                int grid, hipStream_t s) {
   if (cap) {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, true, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, true, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
   } else {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, false, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, false, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
-                      bool with_delta, hipStream_t s) {
+template <int D>
+hipError_t launch_fwd_d(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
+                        bool with_delta, hipStream_t s) {
   // the planner plus one persistent workgroup per remaining compute unit
   const int grid = 1 + max(1, a.kv_wgs - 1);
   if (a.batch <= 0) return hipSuccess;
   if (a.win_left >= 0 || a.win_right >= 0)
-    return dtype == DT_BF16 ? launch_fwd_t<BF16, true>(a, pa, cap, with_delta, grid, s)
-                            : launch_fwd_t<F16, true>(a, pa, cap, with_delta, grid, s);
-  return dtype == DT_BF16 ? launch_fwd_t<BF16, false>(a, pa, cap, with_delta, grid, s)
-                          : launch_fwd_t<F16, false>(a, pa, cap, with_delta, grid, s);
+    return dtype == DT_BF16 ? launch_fwd_t<BF16, D, true>(a, pa, cap, with_delta, grid, s)
+                            : launch_fwd_t<F16, D, true>(a, pa, cap, with_delta, grid, s);
+  return dtype == DT_BF16 ? launch_fwd_t<BF16, D, false>(a, pa, cap, with_delta, grid, s)
+                          : launch_fwd_t<F16, D, false>(a, pa, cap, with_delta, grid, s);
 }
 
 }  // namespace rga

@@ -19,7 +19,8 @@ constexpr int KEY_TILE = 128;
 // Rows or keys of one LDS row tile (see tiles.hpp): the key step of the
 // row-tile kernels and the row step of dK/dV.
 constexpr int TILE_ROWS = 64;
-constexpr int TILE_ELEMS = TILE_ROWS * HEAD_DIM;
+// 16-bit elements of one row tile of head dimension D
+template <int D> constexpr int tile_elems() { return TILE_ROWS * D; }
 // Folded rows staged per step of the dK/dV kernel (each wave of a pair forms
 // P and dS for half of them).
 constexpr int KV_ROW_STEP = TILE_ROWS;
@@ -45,7 +46,7 @@ struct AttnArgs {
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;
   const uint16_t* zero; // 512 zero bytes: source of the loads of rows past a tile's end
-  float* part_dk;       // [units][KEY_TILE][HEAD_DIM] FP32 partials (split sequences)
+  float* part_dk;       // [units][KEY_TILE][D] FP32 partials (split sequences)
   float* part_dv;
   // dS images written by dK/dV and read by dQ for the sequences the planner
   // gave a slot (SQ_DSOFF >= 0); sequence images are row-tile major:
@@ -61,8 +62,11 @@ struct AttnArgs {
   // slope * log2(e) * |c_i - j| exceeds it are dropped (the planner's ranges).
   float skip_log2;
   const float* slopes;  int64_t slopes_stride;
-  int hq;
-  int batch;
+  int64_t k_hs, v_hs, dk_hs, dv_hs;   // K/V head strides (hkv > 1)
+  int hq;               // query heads (row stride of lse and of the row records)
+  int group;            // query heads per K/V head: the rows folded per plan sequence
+  int hkv;
+  int batch;            // plan sequences: packed sequences x hkv
   int64_t total_q;
   int64_t total_k;
   int fwd_slots;        // entries of plan.fwd_map; the dQ grid has more (partial sums)
@@ -80,8 +84,9 @@ struct PlanArgs {
   const int* cu_q;
   const int* cu_k;
   const float* slopes;  int64_t slopes_stride;
-  int batch;
-  int hq;
+  int batch;            // plan sequences (packed sequences x hkv)
+  int hq;               // query heads per plan sequence (the group)
+  int hkv;              // K/V heads: plan sequence v is packed sequence v / hkv
   int64_t total_q;
   int64_t total_k;
   // Skip bound of the key-step ranges the planner records (log2 units, 0 =
@@ -151,19 +156,67 @@ __device__ __forceinline__ void row_key_steps(bool exists, float slope2, int cen
   key_steps_of(centre, key_half_width(slope2, Lk, thr), Lk, lo, hi);
 }
 
+// Offset of plan sequence v's first slope: packed sequence v / hkv, query
+// heads from (v % hkv) * group (the slopes are [batch, hq], row stride given).
+__device__ __forceinline__ int64_t slope_base(int v, int hkv, int group, int64_t stride) {
+  const int b = v / hkv;
+  return (int64_t)b * stride + (int64_t)(v - b * hkv) * group;
+}
+
 // Planner (one workgroup), for the calls whose forward grid does not hold it.
 hipError_t launch_prep(const PlanArgs& pa, hipStream_t s);
 // Forward over the a.fwd_slots row-tile slots, with the planner (pa) in an
 // extra workgroup beside them; with_delta (the full-VJP call) also plans the
-// dK/dV units there and writes the row records.
-hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
-                      bool with_delta, hipStream_t s);
-hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s);
+// dK/dV units there and writes the row records.  One instantiation per head
+// dimension D (fwd_d<D>.hip and so on); the dispatchers below pick it.
+template <int D>
+hipError_t launch_fwd_d(const AttnArgs& a, const PlanArgs& pa, int dtype, bool cap,
+                        bool with_delta, hipStream_t s);
+template <int D>
+hipError_t launch_dkdv_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
+template <int D>
+hipError_t launch_dq_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
+extern template hipError_t launch_fwd_d<64>(const AttnArgs&, const PlanArgs&, int, bool, bool,
+                                            hipStream_t);
+extern template hipError_t launch_fwd_d<128>(const AttnArgs&, const PlanArgs&, int, bool, bool,
+                                             hipStream_t);
+extern template hipError_t launch_fwd_d<160>(const AttnArgs&, const PlanArgs&, int, bool, bool,
+                                             hipStream_t);
+extern template hipError_t launch_dkdv_d<64>(const AttnArgs&, int, bool, int, hipStream_t);
+extern template hipError_t launch_dkdv_d<128>(const AttnArgs&, int, bool, int, hipStream_t);
+extern template hipError_t launch_dkdv_d<160>(const AttnArgs&, int, bool, int, hipStream_t);
+extern template hipError_t launch_dq_d<64>(const AttnArgs&, int, bool, int, hipStream_t);
+extern template hipError_t launch_dq_d<128>(const AttnArgs&, int, bool, int, hipStream_t);
+extern template hipError_t launch_dq_d<160>(const AttnArgs&, int, bool, int, hipStream_t);
+
+inline hipError_t launch_fwd(const AttnArgs& a, const PlanArgs& pa, int dtype, int d, bool cap,
+                             bool with_delta, hipStream_t s) {
+  switch (d) {
+    case 64: return launch_fwd_d<64>(a, pa, dtype, cap, with_delta, s);
+    case 128: return launch_fwd_d<128>(a, pa, dtype, cap, with_delta, s);
+    default: return launch_fwd_d<160>(a, pa, dtype, cap, with_delta, s);
+  }
+}
+inline hipError_t launch_dkdv(const AttnArgs& a, int dtype, int d, bool cap, int grid,
+                              hipStream_t s) {
+  switch (d) {
+    case 64: return launch_dkdv_d<64>(a, dtype, cap, grid, s);
+    case 128: return launch_dkdv_d<128>(a, dtype, cap, grid, s);
+    default: return launch_dkdv_d<160>(a, dtype, cap, grid, s);
+  }
+}
+inline hipError_t launch_dq(const AttnArgs& a, int dtype, int d, bool cap, int grid,
+                            hipStream_t s) {
+  switch (d) {
+    case 64: return launch_dq_d<64>(a, dtype, cap, grid, s);
+    case 128: return launch_dq_d<128>(a, dtype, cap, grid, s);
+    default: return launch_dq_d<160>(a, dtype, cap, grid, s);
+  }
+}
+hipError_t launch_rowinfo(const AttnArgs& a, int dtype, int d, bool cap, hipStream_t s);
 // Key-step ranges of the standalone backward, from the row records, and its
 // dK/dV units planned from them.
 hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s);
 hipError_t launch_units(const PlanArgs& pa, hipStream_t s);
-hipError_t launch_dkdv(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
-hipError_t launch_dq(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s);
 
 }  // namespace rga

@@ -39,8 +39,9 @@ hipError_t launch_prep(const PlanArgs& pa, hipStream_t s) {
 // slope in base-2 units, the clamped ALiBi centre and the base-2 residual of
 // the stored natural-log L relative to the row offset the forward used (see
 // fwd.hip).  Eight lanes share a row; each reads 16-byte chunks.
-template <class T, bool CAP>
+template <class T, int D, bool CAP>
 __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
+  constexpr int CHUNKS = Geo<D>::CHUNKS;
   const int64_t gid = (int64_t)blockIdx.x * WG_THREADS + threadIdx.x;
   const int64_t r = gid >> 3;
   const int sub = (int)(gid & 7);
@@ -63,17 +64,21 @@ __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   acc += __shfl_xor(acc, 2, 64);
   acc += __shfl_xor(acc, 4, 64);
   if (!ok || sub != 0) return;
-  // sequence of token t: the last b with q0(b) <= t (never an empty one)
+  // packed sequence of token t: the last b with q0(b) <= t (never an empty
+  // one), searched over the plan records of its first K/V head (v = b hkv)
   const int* seq = a.plan.seq;
-  int lo = 0, hi = a.batch - 1;
+  const int nb = a.batch / a.hkv;
+  int lo = 0, hi = nb - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (seq[mid * SEQ_FIELDS + SQ_Q0] <= t) lo = mid; else hi = mid - 1;
+    if (seq[mid * a.hkv * SEQ_FIELDS + SQ_Q0] <= t) lo = mid; else hi = mid - 1;
   }
-  const int* s = seq + lo * SEQ_FIELDS;
+  const int* s = seq + lo * a.hkv * SEQ_FIELDS;
   const int i = (int)(t - s[SQ_Q0]);
   const int Lq = s[SQ_LQ], Lk = s[SQ_LK];
-  const int64_t fr = (int64_t)s[SQ_Q0] * a.hq + (int64_t)h * Lq + i;   // folded row record
+  // folded row record: head-major over the packed sequence's hq heads, so the
+  // rows of the group of K/V head g start at q0 hq + g group Lq
+  const int64_t fr = (int64_t)s[SQ_Q0] * a.hq + (int64_t)h * Lq + i;
   const float slope2 = a.slopes[(int64_t)lo * a.slopes_stride + h] * LOG2E;
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - i);
   const float L = a.lse[r];
@@ -100,8 +105,8 @@ __global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
   float slope2 = 0.0f, thr = 0.0f;
   int centre = 0;
   if (ok && Lk > 0) {
-    const f32x4 info =
-        *reinterpret_cast<const f32x4*>(a.rowinfo + ((int64_t)sq[SQ_Q0] * a.hq + R) * 4);
+    const f32x4 info = *reinterpret_cast<const f32x4*>(
+        a.rowinfo + ((int64_t)sq[SQ_Q0] * a.hq + (int64_t)sq[SQ_HB] * sq[SQ_LQ] + R) * 4);
     slope2 = info[0];
     centre = (int)info[1];
     const float radd = info[2];   // added to every exponent of the row
@@ -150,18 +155,28 @@ hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_rowinfo(const AttnArgs& a, int dtype, bool cap, hipStream_t s) {
+template <int D>
+static hipError_t launch_rowinfo_t(const AttnArgs& a, int dtype, bool cap, int grid,
+                                   hipStream_t s) {
+  if (dtype == DT_BF16) {
+    if (cap) hipLaunchKernelGGL((rowinfo_kernel<BF16, D, true>), grid, WG_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((rowinfo_kernel<BF16, D, false>), grid, WG_THREADS, 0, s, a);
+  } else {
+    if (cap) hipLaunchKernelGGL((rowinfo_kernel<F16, D, true>), grid, WG_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((rowinfo_kernel<F16, D, false>), grid, WG_THREADS, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rowinfo(const AttnArgs& a, int dtype, int d, bool cap, hipStream_t s) {
   const int64_t n = a.total_q * a.hq * 8;
   if (n <= 0) return hipSuccess;
   const int grid = (int)((n + WG_THREADS - 1) / WG_THREADS);
-  if (dtype == DT_BF16) {
-    if (cap) hipLaunchKernelGGL((rowinfo_kernel<BF16, true>), grid, WG_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((rowinfo_kernel<BF16, false>), grid, WG_THREADS, 0, s, a);
-  } else {
-    if (cap) hipLaunchKernelGGL((rowinfo_kernel<F16, true>), grid, WG_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((rowinfo_kernel<F16, false>), grid, WG_THREADS, 0, s, a);
+  switch (d) {
+    case 64: return launch_rowinfo_t<64>(a, dtype, cap, grid, s);
+    case 128: return launch_rowinfo_t<128>(a, dtype, cap, grid, s);
+    default: return launch_rowinfo_t<160>(a, dtype, cap, grid, s);
   }
-  return hipGetLastError();
 }
 
 }  // namespace rga

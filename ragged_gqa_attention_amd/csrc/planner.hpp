@@ -7,6 +7,26 @@
 
 namespace rga {
 
+// Extents of plan sequence v (packed sequence v / hkv) from cu_q / cu_k, and
+// whether they fail the planner's checks (see plan_block).
+struct SeqExt {
+  int cq, nq, ck, nk;
+  bool bad;
+};
+__device__ __forceinline__ SeqExt seq_extents(const PlanArgs& pa, int v) {
+  const int b = v / pa.hkv, nb = pa.batch / pa.hkv;
+  SeqExt e;
+  e.cq = pa.cu_q[b];
+  e.nq = pa.cu_q[b + 1];
+  e.ck = pa.cu_k[b];
+  e.nk = pa.cu_k[b + 1];
+  e.bad = e.cq < 0 || e.nq < e.cq || (int64_t)e.nq > pa.total_q || e.ck < 0 || e.nk < e.ck ||
+          (int64_t)e.nk > pa.total_k;
+  if (b == 0) e.bad |= e.cq != 0 || e.ck != 0;
+  if (b == nb - 1) e.bad |= (int64_t)e.nq != pa.total_q || (int64_t)e.nk != pa.total_k;
+  return e;
+}
+
 // Block-wide helpers of the planners, for workgroups of NT threads (NT / 64
 // waves); `red` / `part` are LDS arrays of one entry per wave.
 
@@ -209,7 +229,7 @@ __device__ __forceinline__ void plan_units(const PlanArgs& a, const int* seq, Un
     e[KV_Q0] = s[SQ_Q0]; e[KV_K0] = s[SQ_K0]; e[KV_LK] = s[SQ_LK]; e[KV_ROWS] = s[SQ_ROWS];
     e[KV_RTOFF] = s[SQ_RTOFF]; e[KV_DSOFF] = s[SQ_DSOFF]; e[KV_LQ] = s[SQ_LQ];
     e[KV_LQMUL] = s[SQ_LQMUL]; e[KV_LQSHIFT] = s[SQ_LQSHIFT];
-    e[KV_PAD0] = 0; e[KV_PAD1] = 0; e[KV_PAD2] = 0;
+    e[KV_HB] = s[SQ_HB]; e[KV_G] = s[SQ_G]; e[KV_PAD0] = 0;
   }, part);
   __threadfence_block();
   __syncthreads();
@@ -258,16 +278,17 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
     int b = sb0, h = sh0;
 #pragma unroll
     for (int k = 0; k < SPER; ++k) {
-      sv[k] = a.slopes[(int64_t)min(b, B - 1) * a.slopes_stride + h];
+      sv[k] = a.slopes[slope_base(min(b, B - 1), a.hkv, hq, a.slopes_stride) + h];
       b += sdb;
       h += sdh;
       if (h >= hq) { h -= hq; ++b; }
     }
   }
-  // checks of cu_q / cu_k and the per-sequence extents in one pass; an
-  // invalid batch is then planned with every sequence empty
-  auto extents = [&](int b, int q0, int lq, int k0, int lk) {
-    int* s = seq + b * SEQ_FIELDS;
+  // checks of cu_q / cu_k and the per-sequence extents in one pass (plan
+  // sequence v = packed sequence v / hkv, K/V head v % hkv); an invalid batch
+  // is then planned with every sequence empty
+  auto extents = [&](int v, int q0, int lq, int k0, int lk) {
+    int* s = seq + v * SEQ_FIELDS;
     s[SQ_Q0] = q0; s[SQ_LQ] = lq; s[SQ_K0] = k0; s[SQ_LK] = lk;
     s[SQ_ROWS] = lq * a.hq;
     s[SQ_KTILES] = (lk + KEY_TILE - 1) / KEY_TILE;
@@ -275,21 +296,19 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
     fast_div_consts(lq, mul, sh);
     s[SQ_LQSHIFT] = (int)sh;
     s[SQ_LQMUL] = (int)mul;
+    const int g = v - (v / a.hkv) * a.hkv;
+    s[SQ_HB] = g * a.hq;
+    s[SQ_G] = g;
   };
-  bool bad = false;
-  for (int b = tid; b <= B; b += NT) {
-    const int cq = a.cu_q[b], ck = a.cu_k[b];
-    const int nq = b < B ? a.cu_q[b + 1] : cq, nk = b < B ? a.cu_k[b + 1] : ck;
-    bool fail = cq < 0 || (int64_t)cq > a.total_q || ck < 0 || (int64_t)ck > a.total_k;
-    if (b == 0) fail |= (cq != 0) || (ck != 0);
-    if (b == B) fail |= ((int64_t)cq != a.total_q) || ((int64_t)ck != a.total_k);
-    if (b < B) fail |= (nq < cq) || (nk < ck);
-    bad |= fail;
+  // an empty batch still has cu[0], which must be 0 = total
+  bool bad = B == 0 && tid == 0 &&
+             (a.cu_q[0] != 0 || a.cu_k[0] != 0 || a.total_q != 0 || a.total_k != 0);
+  for (int v = tid; v < B; v += NT) {
+    const SeqExt e = seq_extents(a, v);
+    bad |= e.bad;
     // (a failed check leaves this sequence empty, so no length is negative)
-    if (b < B) {
-      if (fail) extents(b, 0, 0, 0, 0);
-      else extents(b, cq, nq - cq, ck, nk - ck);
-    }
+    if (e.bad) extents(v, 0, 0, 0, 0);
+    else extents(v, e.cq, e.nq - e.cq, e.ck, e.nk - e.ck);
   }
   const bool ok = __syncthreads_or(bad) == 0;
   if (tid == 0) a.plan.flag[0] = ok ? 0 : 1;
@@ -334,7 +353,8 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
       for (int k = 0; k < PER; ++k) {
         const int i = i0 + k * NT + tid;
         const int b = i / hq;
-        v[k] = i < B * hq ? a.slopes[(int64_t)b * a.slopes_stride + (i - b * hq)] : 0.0f;
+        v[k] = i < B * hq ? a.slopes[slope_base(b, a.hkv, hq, a.slopes_stride) + (i - b * hq)]
+                          : 0.0f;
       }
 #pragma unroll
       for (int k = 0; k < PER; ++k) {
@@ -416,7 +436,7 @@ struct RowTile {
 };
 
 // false past the last tile, or when cu_q / cu_k are invalid (the planner
-// flags that case and plans nothing)
+// flags that case and plans nothing).  b is a plan sequence (see SeqField).
 __device__ __forceinline__ bool find_row_tile(const PlanArgs& pa, int slot, RowTile& t) {
   const int lane = threadIdx.x & 63;
   const int B = pa.batch, hq = pa.hq;
@@ -426,16 +446,10 @@ __device__ __forceinline__ bool find_row_tile(const PlanArgs& pa, int slot, RowT
     const bool live = b < B;
     // unconditional loads (lanes past B - 1 repeat the last sequence), so
     // the four requests are in flight together
-    const int bl = min(b, B - 1);
-    int cq = pa.cu_q[bl], nq = pa.cu_q[bl + 1];
-    int ck = pa.cu_k[bl], nk = pa.cu_k[bl + 1];
-    if (!live) cq = nq = ck = nk = 0;
-    bool bad = live && (cq < 0 || nq < cq || (int64_t)nq > pa.total_q || ck < 0 || nk < ck ||
-                        (int64_t)nk > pa.total_k);
-    if (b == 0 && live) bad |= cq != 0 || ck != 0;
-    if (b == B - 1) bad |= (int64_t)nq != pa.total_q || (int64_t)nk != pa.total_k;
-    if (__any(bad)) return false;
-    const int lq = nq - cq, lk = nk - ck;
+    SeqExt e = seq_extents(pa, min(b, B - 1));
+    if (!live) e.cq = e.nq = e.ck = e.nk = 0;
+    if (__any(live && e.bad)) return false;
+    const int lq = e.nq - e.cq, lk = e.nk - e.ck;
     const int n = live ? (lq * hq + ROW_TILE - 1) / ROW_TILE : 0;
     // first tile of sequence b: the tiles of the sequences ranked before it
     int start = 0;
@@ -448,28 +462,22 @@ __device__ __forceinline__ bool find_row_tile(const PlanArgs& pa, int slot, RowT
     const int ob = __ffsll((long long)own) - 1;
     t.b = ob;
     t.tile = slot - __builtin_amdgcn_readlane(start, ob);
-    t.q0 = __builtin_amdgcn_readlane(cq, ob);
+    t.q0 = __builtin_amdgcn_readlane(e.cq, ob);
     t.lq = __builtin_amdgcn_readlane(lq, ob);
-    t.k0 = __builtin_amdgcn_readlane(ck, ob);
+    t.k0 = __builtin_amdgcn_readlane(e.ck, ob);
     t.lk = __builtin_amdgcn_readlane(lk, ob);
     return true;
   }
-  // batch order: lane l owns sequences [l seg, l seg + seg)
+  // batch order: lane l owns plan sequences [l seg, l seg + seg)
   const int seg = (B + 63) / 64;
   const int lo = min(B, lane * seg), hi = min(B, lo + seg);
   bool bad = false;
   int count = 0;
-  int pq = pa.cu_q[lo], pk = pa.cu_k[lo];
-  if (lo == 0) bad |= pq != 0 || pk != 0;
-  bad |= pq < 0 || pk < 0;
   for (int b = lo; b < hi; ++b) {
-    const int nq = pa.cu_q[b + 1], nk = pa.cu_k[b + 1];
-    bad |= nq < pq || nk < pk || (int64_t)nq > pa.total_q || (int64_t)nk > pa.total_k;
-    count += ((nq - pq) * hq + ROW_TILE - 1) / ROW_TILE;
-    pq = nq;
-    pk = nk;
+    const SeqExt e = seq_extents(pa, b);
+    bad |= e.bad;
+    count += ((e.nq - e.cq) * hq + ROW_TILE - 1) / ROW_TILE;
   }
-  if (lo < hi && hi == B) bad |= (int64_t)pq != pa.total_q || (int64_t)pk != pa.total_k;
   if (__any(bad)) return false;
   int x = count;   // inclusive scan over lanes
 #pragma unroll
@@ -484,15 +492,15 @@ __device__ __forceinline__ bool find_row_tile(const PlanArgs& pa, int slot, RowT
   if (lane == ol) {
     int run = run0;
     for (int b = lo; b < hi; ++b) {
-      const int q = pa.cu_q[b], nq = pa.cu_q[b + 1];
-      const int n = ((nq - q) * hq + ROW_TILE - 1) / ROW_TILE;
+      const SeqExt e = seq_extents(pa, b);
+      const int n = ((e.nq - e.cq) * hq + ROW_TILE - 1) / ROW_TILE;
       if (slot < run + n) {
         t.b = b;
         t.tile = slot - run;
-        t.q0 = q;
-        t.lq = nq - q;
-        t.k0 = pa.cu_k[b];
-        t.lk = pa.cu_k[b + 1] - t.k0;
+        t.q0 = e.cq;
+        t.lq = e.nq - e.cq;
+        t.k0 = e.ck;
+        t.lk = e.nk - e.ck;
         break;
       }
       run += n;
@@ -521,7 +529,7 @@ __device__ __forceinline__ void tile_key_range(const PlanArgs& pa, const RowTile
   for (int h0 = hfirst; h0 <= hlast; h0 += 64) {
     const int h = h0 + lane;
     if (h <= hlast) {
-      const float slope = pa.slopes[(int64_t)t.b * pa.slopes_stride + h];
+      const float slope = pa.slopes[slope_base(t.b, pa.hkv, pa.hq, pa.slopes_stride) + h];
       const int hw = key_half_width(slope * LOG2E, t.lk, pa.skip_log2);
       const int ia = h == hfirst ? R0 - h * t.lq : 0;
       const int ib = h == hlast ? R1 - 1 - h * t.lq : t.lq - 1;

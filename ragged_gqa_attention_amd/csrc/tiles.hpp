@@ -8,8 +8,9 @@
 // slots of 16 bytes (measured on gfx950: odd row strides in 16-byte units are
 // conflict-free, a 320-byte stride is 4-way).
 //
-//  * Row tile: 64 rows (keys or folded query rows) x 160 features = 20 chunks
-//    of 16 bytes per row, stored in blocks of 16 rows x 4 chunks (blk_off).
+//  * Row tile: 64 rows (keys or folded query rows) x D features = D / 8 chunks
+//    of 16 bytes per row (20 for D = 160), stored in blocks of 16 rows x 4
+//    chunks (blk_off).
 //    Read one chunk per lane ("row read", the A/B operand of a product that
 //    contracts over features) or with the transposing read (the operand of a
 //    product that contracts over rows).
@@ -33,7 +34,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void gbl_void_t;
 
 constexpr int BLK_ELEMS = 64 * 8;                     // one 16-row x 4-chunk block
-constexpr int BLK_COLS = CHUNKS / 4;                  // blocks across a row (5)
 
 __device__ __forceinline__ u32x4 load16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -55,9 +55,12 @@ __device__ __forceinline__ u32x2 read_tr(const uint16_t* p) {
 // XOR-ed with (r / 4) % 4.  One wave load fills one block, reading 64
 // contiguous bytes from each of 16 rows; a row read (16 lanes = 16
 // consecutive rows of one chunk) and a transposing read (4 rows x 2 adjacent
-// chunks) both touch 16 distinct bank slots.
+// chunks) both touch 16 distinct bank slots.  A row spans Geo<D>::BLK_COLS
+// blocks (D / 32).
+template <int D>
 __device__ __forceinline__ int blk_off(int r, int c) {
-  return (((r >> 4) * BLK_COLS + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
+  constexpr int BC = Geo<D>::BLK_COLS;
+  return (((r >> 4) * BC + (c >> 2)) * 64 + (r & 15) * 4 + ((c & 3) ^ ((r >> 2) & 3))) * 8;
 }
 
 // Key order of the accumulator layout reused as a B operand: the middle two
@@ -115,22 +118,23 @@ __device__ __forceinline__ void wait_vm_le() {
 }
 
 // Copies the blocked row tile of rows [row0, row0 + 64) of a strided
-// [tokens, 160] view (rows past `nrows` read `zero`) with four waves: wave
+// [tokens, D] view (rows past `nrows` read `zero`) with four waves: wave
 // group w (0..3) copies rows 16 w .. 16 w + 15, lane l holding row
-// 16 w + l / 4 for all five of its loads.  UNSEEN: issue them as
+// 16 w + l / 4 for all D / 32 of its loads.  UNSEEN: issue them as
 // load_lds16_unseen.
-template <bool UNSEEN = false>
+template <int D, bool UNSEEN = false>
 __device__ __forceinline__ void load_row_tile(uint16_t* tile, const uint16_t* src, int64_t ts,
                                               int row0, int nrows, const uint16_t* zero,
                                               int w, int lane) {
+  constexpr int BC = Geo<D>::BLK_COLS;
   const int r = 16 * w + (lane >> 2);
   const int c = (lane & 3) ^ ((lane >> 4) & 3);
   const bool ok = row0 + r < nrows;
   const uint16_t* p = (ok ? src + (int64_t)(row0 + r) * ts : zero) + c * 8;
 #pragma unroll
-  for (int b = 0; b < BLK_COLS; ++b) {
-    if (UNSEEN) load_lds16_unseen(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
-    else load_lds16(p + b * 32, tile + (w * BLK_COLS + b) * BLK_ELEMS);
+  for (int b = 0; b < BC; ++b) {
+    if (UNSEEN) load_lds16_unseen(p + b * 32, tile + (w * BC + b) * BLK_ELEMS);
+    else load_lds16(p + b * 32, tile + (w * BC + b) * BLK_ELEMS);
   }
 }
 

@@ -65,8 +65,10 @@ def _call_fwd(prob, q=None, k=None, v=None, out=None, ws_bytes=1 << 30, ws=0x400
     (dict(causal=2), _lib.ATTN_INVALID_ARG),
     (dict(window_left=-2), _lib.ATTN_INVALID_ARG),
     (dict(window_right=-7), _lib.ATTN_INVALID_ARG),
-    (dict(head_dim=128), _lib.ATTN_UNSUPPORTED),
-    (dict(hkv=2), _lib.ATTN_UNSUPPORTED),
+    (dict(head_dim=96), _lib.ATTN_UNSUPPORTED),
+    (dict(head_dim=256), _lib.ATTN_UNSUPPORTED),
+    (dict(hkv=3), _lib.ATTN_INVALID_ARG),
+    (dict(hkv=0), _lib.ATTN_INVALID_ARG),
     (dict(dtype=7), _lib.ATTN_UNSUPPORTED),
     (dict(hq=0), _lib.ATTN_INVALID_ARG),
     (dict(batch=-1), _lib.ATTN_INVALID_ARG),

@@ -75,13 +75,13 @@ def draw_slopes(rng: np.random.Generator, B: int, hq: int) -> np.ndarray:
     return (base[None, :] * u).astype(np.float32)
 
 
-def _poisoned_view(rng, T, H, width, step, dtype, scale, chunk_tokens=8192):
-    """NaN-filled buffer [T*step, H, width]; the view [::step, :, :160] holds N(0,1)*scale."""
+def _poisoned_view(rng, T, H, width, step, dtype, scale, head_dim=HEAD_DIM, chunk_tokens=8192):
+    """NaN-filled buffer [T*step, H, width]; the view [::step, :, :head_dim] holds N(0,1)*scale."""
     buf = torch.full((max(T * step, 1), H, width), float("nan"), dtype=dtype)
-    view = buf[::step, :, :HEAD_DIM][:T]
+    view = buf[::step, :, :head_dim][:T]
     for t0 in range(0, T, chunk_tokens):
         t1 = min(T, t0 + chunk_tokens)
-        x = rng.standard_normal(size=(t1 - t0, H, HEAD_DIM), dtype=np.float32)
+        x = rng.standard_normal(size=(t1 - t0, H, head_dim), dtype=np.float32)
         if scale != 1.0:
             x *= np.float32(scale)
         view[t0:t1].copy_(torch.from_numpy(x))   # float32 -> 16-bit, nearest-even
@@ -104,6 +104,7 @@ class Workload:
     bufs: dict                  # name -> padded backing buffer
     softcap: float = 3.0
     scale_multiplier: float = 0.75
+    head_dim: int = HEAD_DIM
 
     @property
     def batch(self):
@@ -119,7 +120,7 @@ class Workload:
 
     def view(self, name):
         T = self.total_q if name in ("q", "dout") else self.total_k
-        return self.bufs[name][::self.step, :, :HEAD_DIM][:T]
+        return self.bufs[name][::self.step, :, :self.head_dim][:T]
 
     @property
     def q(self):
@@ -150,43 +151,98 @@ class Workload:
 
     def flops(self) -> float:
         """Credited work of forward + full VJP: 14 * sum_b Lq_b Lk_b * Hq * D."""
-        return 14.0 * self.score_elements() * HEAD_DIM
+        return 14.0 * self.score_elements() * self.head_dim
 
     def min_hbm_bytes(self) -> int:
         """Read q, dout, k, v once; write out, dq, dk, dv once; FP32 lse and delta."""
         e = 2
         tq = self.total_q * self.hq
         tk = self.total_k * self.hkv
-        return 4 * tq * HEAD_DIM * e + 4 * tk * HEAD_DIM * e + 2 * tq * 4
+        return 4 * tq * self.head_dim * e + 4 * tk * self.head_dim * e + 2 * tq * 4
 
 
 def _build(name, lq, lk, hq, dtype_name, width, step, scale, rng, softcap=3.0,
-           scale_multiplier=0.75, slopes=None):
+           scale_multiplier=0.75, slopes=None, hkv=1, head_dim=HEAD_DIM):
     lq = np.asarray(lq, np.int64)
     lk = np.asarray(lk, np.int64)
     B = len(lq)
+    if hq % hkv != 0:
+        raise ValueError("hkv must divide hq")
+    if width < head_dim:
+        raise ValueError("buffer width below the head dimension")
     if slopes is None:
         slopes = draw_slopes(rng, B, hq)
     dtype = TORCH_DTYPES[dtype_name]
     Tq, Tk = int(lq.sum()), int(lk.sum())
     bufs = {}
-    for nm, T, H in (("q", Tq, hq), ("k", Tk, 1), ("v", Tk, 1), ("dout", Tq, hq)):
-        bufs[nm], _ = _poisoned_view(rng, T, H, width, step, dtype, scale)
+    for nm, T, H in (("q", Tq, hq), ("k", Tk, hkv), ("v", Tk, hkv), ("dout", Tq, hq)):
+        bufs[nm], _ = _poisoned_view(rng, T, H, width, step, dtype, scale, head_dim)
     cu_q = torch.tensor(np.concatenate([[0], np.cumsum(lq)]), dtype=torch.int32)
     cu_k = torch.tensor(np.concatenate([[0], np.cumsum(lk)]), dtype=torch.int32)
-    return Workload(name=name, dtype=dtype, hq=hq, hkv=1, width=width, step=step,
+    return Workload(name=name, dtype=dtype, hq=hq, hkv=hkv, width=width, step=step,
                     lq=lq, lk=lk, cu_q=cu_q, cu_k=cu_k,
                     slopes=torch.from_numpy(np.ascontiguousarray(slopes)), bufs=bufs,
-                    softcap=softcap, scale_multiplier=scale_multiplier)
+                    softcap=softcap, scale_multiplier=scale_multiplier, head_dim=head_dim)
 
 
 def make_workload(cfg: int, trial: int = 0) -> Workload:
-    """One of the five named configurations; ``trial`` reseeds the draw."""
+    """One of the five named configurations (or a GQA_VARIANTS index);
+    ``trial`` reseeds the draw."""
+    if cfg in GQA_VARIANTS:
+        return make_gqa_variant(cfg, trial)
     c = CONFIGS[cfg]
     rng = np.random.default_rng([cfg, trial])
     lq, lk = draw_lengths(cfg, rng)
     return _build(f"cfg{cfg}_{c['name']}", lq, lk, c["hq"], c["dtype"], c["width"],
                   c["step"], c["scale"], rng)
+
+
+# Grouped-query variants of the Q-short/K-long draw (same lengths and
+# slopes recipe, several K/V heads, head dimensions 128 and 64), used to
+# measure the general GQA paths; they are not among the page-derived configs.
+GQA_VARIANTS = {
+    5: dict(name="q_short_k_long_hkv8_d128", base=1, hkv=8, head_dim=128, width=128, step=2),
+    6: dict(name="q_short_k_long_hkv4_d64", base=1, hkv=4, head_dim=64, width=64, step=2),
+}
+
+
+def make_gqa_variant(index: int, trial: int = 0) -> Workload:
+    c = GQA_VARIANTS[index]
+    b = CONFIGS[c["base"]]
+    rng = np.random.default_rng([c["base"], trial])
+    lq, lk = draw_lengths(c["base"], rng)
+    return _build(f"cfg{index}_{c['name']}", lq, lk, b["hq"], b["dtype"], c["width"], c["step"],
+                  b["scale"], rng, hkv=c["hkv"], head_dim=c["head_dim"])
+
+
+def fuzz_gqa_workload(seed: int, max_batch: int = 5, max_len: int = 260,
+                      budget: int = 2_000_000) -> Workload:
+    """Small random case over K/V head counts (hkv divides hq) and head
+    dimensions 64 / 128 / 160, with the fuzz lengths of fuzz_workload."""
+    rng = np.random.default_rng([1100, seed])
+    hq = int(rng.choice([8, 16, 48, 64]))
+    hkv = int(rng.choice([h for h in (1, 2, 4, 8) if hq % h == 0]))
+    head_dim = int(rng.choice([64, 128, 160]))
+    dtype_name = str(rng.choice(["f16", "bf16"]))
+    step = int(rng.integers(1, 4))
+    width = head_dim + int(rng.choice([0, 16, 32]))
+    B = int(rng.integers(1, max_batch + 1))
+
+    def one():
+        if rng.uniform() < 0.5:
+            return int(rng.choice(_EDGE_LENGTHS))
+        return int(rng.integers(0, max_len + 1))
+
+    lq = np.array([one() for _ in range(B)], np.int64)
+    lk = np.array([one() for _ in range(B)], np.int64)
+    while int((lq * lk).sum()) * hq > budget:
+        i = int(np.argmax(lq * lk))
+        lq[i] //= 2
+        lk[i] //= 2
+    scale = float(rng.choice([1.0, 1.5, 3.0]))
+    softcap = 3.0 if rng.uniform() < 0.85 else 0.0
+    return _build(f"fuzz_gqa{seed}", lq, lk, hq, dtype_name, width, step, scale, rng,
+                  softcap=softcap, hkv=hkv, head_dim=head_dim)
 
 
 # Lengths that sit on and around the 32/64/128 tile edges used on the device.
@@ -223,11 +279,12 @@ def fuzz_workload(seed: int, max_batch: int = 6, max_len: int = 300,
 
 
 def custom_workload(lq, lk, hq=48, dtype="f16", width=176, step=2, scale=1.0, seed=0,
-                    softcap=3.0, scale_multiplier=0.75, slopes=None) -> Workload:
-    """Explicit lengths, for edge-case tests."""
+                    softcap=3.0, scale_multiplier=0.75, slopes=None, hkv=1,
+                    head_dim=HEAD_DIM) -> Workload:
+    """Explicit lengths (and K/V heads, head dimension), for edge-case tests."""
     rng = np.random.default_rng([2000, seed])
     return _build("custom", lq, lk, hq, dtype, width, step, scale, rng, softcap=softcap,
-                  scale_multiplier=scale_multiplier, slopes=slopes)
+                  scale_multiplier=scale_multiplier, slopes=slopes, hkv=hkv, head_dim=head_dim)
 
 
 def oracle_inputs(wl: Workload):
