@@ -1,5 +1,5 @@
 /*
- * attn_varlen.h -- C ABI of the MI355X (gfx950) ragged extreme-GQA attention
+ * attn_varlen.h -- C ABI of the MI355X (gfx950) ragged grouped-query attention
  * library: forward pass and full vector-Jacobian product.
  *
  * The operation (page "Noncausal Global Extreme-GQA Ragged Attention Full
@@ -7,7 +7,8 @@
  *
  *   For every sequence b of a packed ragged batch (query tokens
  *   [cu_q[b], cu_q[b+1]), key tokens [cu_k[b], cu_k[b+1])), every query head
- *   h and its K/V head g, with local positions i (query) and j (key),
+ *   h and its K/V head g = h / (hq / hkv), with local positions i (query)
+ *   and j (key),
  *   Lq = cu_q[b+1]-cu_q[b], Lk = cu_k[b+1]-cu_k[b], D = head_dim:
  *
  *     s_ij = (scale_multiplier / sqrt(D)) * <q_ih, k_jg>
@@ -32,11 +33,15 @@
  * cap and ALiBi of kept keys are unchanged; a row that keeps no key is a row
  * with no keys (out = 0, dq = 0, lse = -inf).
  *
- * Supported: dtype F16 or BF16 (one dtype for every 16-bit tensor), hkv == 1,
- * head_dim == 160.  Anything else returns ATTN_UNSUPPORTED; causal outside
- * {0, 1} or a window bound below -1 returns ATTN_INVALID_ARG.
+ * Supported: dtype F16 or BF16 (one dtype for every 16-bit tensor), any hkv
+ * dividing hq (grouped key/value heads), head_dim 64, 128 or 160 (page
+ * "Pairwise-Gated Attention Engine", section "The task", names head sizes 64
+ * and 128 and grouped K/V heads; the first page's cases are 160 over one K/V
+ * head).  Another dtype or head_dim returns ATTN_UNSUPPORTED; hkv not
+ * dividing hq, causal outside {0, 1} or a window bound below -1 returns
+ * ATTN_INVALID_ARG.
  *
- * Tensors.  Every activation tensor is a strided view [tokens, heads, 160]
+ * Tensors.  Every activation tensor is a strided view [tokens, heads, head_dim]
  * with a contiguous feature axis (feature stride 1) and caller-chosen token
  * and head strides, in elements.  Device pointers and both strides must be
  * multiples of 16 bytes / 8 elements (ATTN_MISALIGNED otherwise).  Offsets are
@@ -84,7 +89,7 @@ extern "C" {
 typedef enum {
   ATTN_OK = 0,
   ATTN_INVALID_ARG = -1,          /* null pointer, bad size, feature stride != 1 */
-  ATTN_UNSUPPORTED = -2,          /* causal/window/head_dim/hkv/dtype outside the supported set */
+  ATTN_UNSUPPORTED = -2,          /* head_dim or dtype outside the supported set */
   ATTN_MISALIGNED = -3,           /* pointer or stride not a multiple of 16 B */
   ATTN_WORKSPACE_TOO_SMALL = -4,
   ATTN_HIP_ERROR = -5,            /* a HIP runtime call or launch failed */
@@ -107,7 +112,8 @@ typedef enum {
 /* A hipStream_t; NULL is the default stream. */
 typedef void* attn_stream_t;
 
-/* Strided view [tokens, heads, head_dim] of 16-bit elements, feature stride 1. */
+/* Strided view [tokens, heads, head_dim] of 16-bit elements, feature stride 1
+ * (q, dout, out, dq: hq heads; k, v, dk, dv: hkv heads). */
 typedef struct {
   void* data;            /* device pointer to element [0, 0, 0] */
   int64_t tok_stride;    /* elements between consecutive tokens */
@@ -118,8 +124,8 @@ typedef struct {
   int32_t dtype;               /* attn_dtype */
   int32_t batch;               /* B >= 0 sequences */
   int32_t hq;                  /* query heads, 1..1024 */
-  int32_t hkv;                 /* K/V heads; must be 1 */
-  int32_t head_dim;            /* must be 160 */
+  int32_t hkv;                 /* K/V heads, dividing hq; query head h reads head h / (hq / hkv) */
+  int32_t head_dim;            /* 64, 128 or 160 */
   int64_t total_q;             /* tokens in the q / dout / out / dq views (= cu_q[B]) */
   int64_t total_k;             /* tokens in the k / v / dk / dv views (= cu_k[B]) */
   const int32_t* cu_q;         /* device int32 [B+1], cu_q[0] = 0, nondecreasing */
@@ -146,7 +152,8 @@ attn_status attn_varlen_workspace_size(const attn_problem* p, int entry, size_t*
  * one product dS K instead of a second recomputation of S, P and dP (page
  * "Noncausal Global Extreme-GQA Ragged Attention Full VJP", section "Hard
  * Constraints": the cap derivative multiplies dP - Delta).  A sequence needs
- * ceil(Lq * hq / 256) * ceil(Lk / 64) images of 32 KiB; sequences get room in
+ * hkv * ceil(Lq * (hq / hkv) / 256) * ceil(Lk / 64) images of 32 KiB; sequences
+ * (each K/V head in turn) get room in
  * batch order while it lasts and the rest recompute, so every workspace size
  * from the minimum up gives the same results to within rounding (the stored
  * and the recomputed dS round the same value; a sequence's dQ is bitwise
@@ -237,12 +244,14 @@ attn_status attn_varlen_full_vjp_noalloc(const attn_problem* p,
 attn_status attn_varlen_check_plan(void* workspace, attn_stream_t stream);
 
 /* Diagnostics: the key steps the last call of `entry` on `workspace` (same
- * problem sizes) evaluated.  The folded rows of sequence b (row h * Lq + i for
- * head h, token i) form ceil(Lq * hq / 256) tiles of 256; for each tile, in
- * batch order, host_out receives two int32: the first and one past the last
- * 64-key step of the sequence that the tile's rows visit (see "Far keys"
- * above; 0 and ceil(Lk / 64) when nothing is skipped).  n_tiles is the number
- * of such tiles (sum over b); host_out holds 2 * n_tiles values.  Synchronises
+ * problem sizes) evaluated.  The folded rows of sequence b and K/V head g (row
+ * h * Lq + i for local head h of g's group, token i) form
+ * ceil(Lq * (hq / hkv) / 256) tiles of 256; for each tile, in batch order and
+ * K/V head order inside a sequence, host_out receives two int32: the first
+ * and one past the last 64-key step of the sequence that the tile's rows
+ * visit (see "Far keys" above; 0 and ceil(Lk / 64) when nothing is skipped).
+ * n_tiles is the number of such tiles (sum over b and g); host_out holds
+ * 2 * n_tiles values.  Synchronises
  * `stream`.  Errors: ATTN_INVALID_ARG for a NULL pointer or n_tiles outside
  * 0 .. the bound the workspace layout allows; ATTN_HIP_ERROR if the copy
  * fails. */
