@@ -35,6 +35,12 @@ Readings taken where the pages are silent (each is listed in the design doc):
         dS = dA * (1 - tanh^2(S / c)),  dQ = sigma dS K,
         dK = sigma sum_h dS^T Q,  dV = sum_h P^T dO.
 
+  - dropout (page "python-20261012-ragged-flash-attention-gradient-
+    recompute", section "Root causes addressed"): the keep mask M and the
+    scale 1 / (1 - p) come from oracle/dropout.py; with D = M / (1 - p) per
+    row, out = (P * D) V, the statistic L is that of P (before dropout), and
+    the chain rule gives dV = sum_h (P * D)^T dO, dP = (dO V^T) * D,
+    Delta = rowsum(P * dP) = rowsum(dO * out), then dA, dS, dQ, dK as below.
   - masks (the pages name the arguments but never define them): key j of
     query row i is kept iff i + Lk - Lq - window_left <= j <= i + Lk - Lq +
     window_right, a negative bound meaning no limit on that side; ``causal``
@@ -53,6 +59,8 @@ import math
 
 import numpy as np
 
+from . import dropout as _dropout
+
 __all__ = ["sequence_vjp", "forward", "vjp", "rows_vjp", "window_bounds"]
 
 
@@ -67,12 +75,15 @@ def _as_f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv, window=(-1, -1)):
+def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv, window=(-1, -1),
+               drop=None):
     """Forward and VJP for one head of one sequence, rows at query positions ``i_pos``.
 
     Qh [n, D], dOh [n, D] (or None), K/V [Lk, D]; ``i_pos`` are the local
-    query positions of those n rows.  Returns out, lse, and, when dOh is
-    given, dq, delta and (if ``want_kv``) this head's dK/dV contributions.
+    query positions of those n rows.  ``drop``: None, or the dropout factors
+    [n, Lk] (1 / (1 - p) where a key is kept, 0 where it is dropped).  Returns
+    out, lse, and, when dOh is given, dq, delta and (if ``want_kv``) this
+    head's dK/dV contributions.
     """
     n, D = Qh.shape
     out = np.zeros((n, D))
@@ -117,12 +128,16 @@ def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv, win
     E = np.exp(A - m)
     l = E.sum(axis=1, keepdims=True)
     P = E / np.where(l > 0.0, l, 1.0)
-    res["out"] = P @ V
+    # dropout acts on the normalised weights; L keeps the undropped statistic
+    Pd = P if drop is None else P * drop
+    res["out"] = Pd @ V
     res["lse"] = np.where(has, (m + np.log(np.where(l > 0.0, l, 1.0)))[:, 0], -np.inf)
     if dOh is None:
         return res
 
     dP = dOh @ V.T                                           # [n, Lk]
+    if drop is not None:
+        dP = dP * drop                                       # d out / d P of the dropped weights
     delta = (P * dP).sum(axis=1)                             # = rowsum(dO * O)
     dA = P * (dP - delta[:, None])
     dS = dA * (1.0 - U * U) if U is not None else dA
@@ -130,16 +145,19 @@ def _head_rows(Qh, K, V, dOh, i_pos, Lq, Lk, slope, softcap, sigma, want_kv, win
     res["delta"] = delta
     if want_kv:
         res["dk"] = sigma * (dS.T @ Qh)
-        res["dv"] = P.T @ dOh
+        res["dv"] = Pd.T @ dOh
     return res
 
 
-def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096, window=(-1, -1)):
+def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096, window=(-1, -1),
+                 dropout=None):
     """Forward and full VJP of one sequence.
 
     Q, dO: [Lq, Hq, D]; K, V: [Lk, Hkv, D]; slopes: [Hq].  ``dO`` may be None
-    (forward only).  Returns a dict with out [Lq,Hq,D], lse [Lq,Hq] and, with
-    dO, dq [Lq,Hq,D], delta [Lq,Hq], dk/dv [Lk,Hkv,D].
+    (forward only).  ``dropout``: None or (seed, b, rates) with b the
+    sequence's index in the batch and rates float32 [Lq, Hq] (see
+    oracle/dropout.py).  Returns a dict with out [Lq,Hq,D], lse [Lq,Hq] and,
+    with dO, dq [Lq,Hq,D], delta [Lq,Hq], dk/dv [Lk,Hkv,D].
     """
     Q = _as_f64(Q)
     K = _as_f64(K)
@@ -160,10 +178,14 @@ def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096,
         g = h // group
         for r0 in range(0, Lq, row_chunk):
             r1 = min(Lq, r0 + row_chunk)
+            drop = None
+            if dropout is not None:
+                seed, b, rates = dropout
+                drop = _dropout.keep_scale(seed, b, h, np.arange(r0, r1), Lk, rates[r0:r1, h])
             part = _head_rows(Q[r0:r1, h], K[:, g], V[:, g],
                               None if dO is None else dO[r0:r1, h],
                               np.arange(r0, r1), Lq, Lk, float(slopes[h]),
-                              softcap, sigma, want_kv=True, window=window)
+                              softcap, sigma, want_kv=True, window=window, drop=drop)
             out[r0:r1, h] = part["out"]
             lse[r0:r1, h] = part["lse"]
             if dO is not None:
@@ -176,7 +198,20 @@ def sequence_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, row_chunk=4096,
     return res
 
 
-def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, window=(-1, -1)):
+def _rates(dropout_p, Tq, Hq):
+    """Per-row float32 rates [Tq, Hq] from a scalar or an array, or None when
+    there is no dropout (a scalar 0)."""
+    if np.ndim(dropout_p) == 0:
+        if float(dropout_p) == 0.0:
+            return None
+        return np.full((Tq, Hq), dropout_p, dtype=np.float32)
+    r = np.asarray(dropout_p, dtype=np.float32)
+    assert r.shape == (Tq, Hq), "per-row dropout rates must be [total_q, hq]"
+    return r
+
+
+def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, window=(-1, -1),
+         dropout_p=0.0, dropout_seed=0):
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
@@ -187,6 +222,7 @@ def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, win
     Tk, Hkv, _ = k.shape
     B = len(cu_q) - 1
     assert len(cu_k) == B + 1 and slopes.shape == (B, Hq)
+    rates = _rates(dropout_p, Tq, Hq)
     res = {"out": np.zeros((Tq, Hq, D)), "lse": np.full((Tq, Hq), -np.inf)}
     if dout is not None:
         dout = _as_f64(dout)
@@ -197,7 +233,8 @@ def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, win
         k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
         part = sequence_vjp(q[q0:q1], k[k0:k1], v[k0:k1],
                             None if dout is None else dout[q0:q1],
-                            slopes[b], softcap, scale_multiplier, window=window)
+                            slopes[b], softcap, scale_multiplier, window=window,
+                            dropout=None if rates is None else (dropout_seed, b, rates[q0:q1]))
         res["out"][q0:q1] = part["out"]
         res["lse"][q0:q1] = part["lse"]
         if dout is not None:
@@ -209,28 +246,30 @@ def _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, win
 
 
 def forward(q, k, v, cu_q, cu_k, alibi_slopes, softcap, scale_multiplier, causal=False,
-            window_left=-1, window_right=-1):
-    """out [Tq,Hq,D] and lse [Tq,Hq] (natural log) for a packed ragged batch."""
+            window_left=-1, window_right=-1, dropout_p=0.0, dropout_seed=0):
+    """out [Tq,Hq,D] and lse [Tq,Hq] (natural log) for a packed ragged batch.
+    dropout_p: a float32 rate in [0, 1) or per-row rates [Tq, Hq]."""
     res = _run(q, k, v, cu_q, cu_k, alibi_slopes, None, softcap, scale_multiplier,
-               window_bounds(causal, window_left, window_right))
+               window_bounds(causal, window_left, window_right), dropout_p, dropout_seed)
     return res["out"], res["lse"]
 
 
 def vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier, causal=False,
-        window_left=-1, window_right=-1):
+        window_left=-1, window_right=-1, dropout_p=0.0, dropout_seed=0):
     """Forward plus full VJP; dict with out, dq, dk, dv, lse, delta (float64)."""
     return _run(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap, scale_multiplier,
-                window_bounds(causal, window_left, window_right))
+                window_bounds(causal, window_left, window_right), dropout_p, dropout_seed)
 
 
 def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads, causal=False,
-             window_left=-1, window_right=-1):
+             window_left=-1, window_right=-1, dropout=None):
     """out, lse, dq, delta for selected rows of one sequence.
 
     Each row's result depends only on its own q/dout row and the sequence's
     K/V, so a sample of rows can be checked at any sequence length.  ``tokens``
     and ``heads`` are equal-length integer arrays of local query positions and
-    head indices.  Returns arrays shaped [n, D] / [n].
+    head indices.  ``dropout`` as in sequence_vjp.  Returns arrays shaped
+    [n, D] / [n].
     """
     Q = _as_f64(Q)
     K = _as_f64(K)
@@ -248,10 +287,14 @@ def rows_vjp(Q, K, V, dO, slopes, softcap, scale_multiplier, tokens, heads, caus
     for h in np.unique(heads):
         sel = np.nonzero(heads == h)[0]
         g = int(h) // group
+        drop = None
+        if dropout is not None:
+            seed, b, rates = dropout
+            drop = _dropout.keep_scale(seed, b, int(h), tokens[sel], Lk, rates[tokens[sel], h])
         part = _head_rows(Q[tokens[sel], h], K[:, g], V[:, g], dO[tokens[sel], h],
                           tokens[sel], Lq, Lk, float(slopes[h]), softcap, sigma,
                           want_kv=False,
-                          window=window_bounds(causal, window_left, window_right))
+                          window=window_bounds(causal, window_left, window_right), drop=drop)
         for key in res:
             res[key][sel] = part[key]
     return res
