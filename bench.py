@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--trial", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dropout-p", type=float, default=0.0,
+                    help="counter-based dropout rate (0 = none, the configurations' setting)")
+    ap.add_argument("--dropout-seed", type=int, default=1234)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -133,7 +136,8 @@ def main():
     wl = make_workload(args.config, args.trial)
     g = wl.to(dev)
     call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
-                       scale_multiplier=g.scale_multiplier, store_ds=True)
+                       scale_multiplier=g.scale_multiplier, store_ds=True,
+                       dropout_p=args.dropout_p, dropout_seed=args.dropout_seed)
     nph = len(_lib.PHASES)
 
     for _ in range(args.warmup):
@@ -216,6 +220,7 @@ def main():
             "total_k": wl.total_k, "sum_lq_lk": int((wl.lq * wl.lk).sum()),
             "view": f"feature width {wl.width}, token step {wl.step}",
             "softcap": wl.softcap, "scale_multiplier": wl.scale_multiplier,
+            "dropout_p": args.dropout_p,
         },
         "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 3),
         "ms_per_call_median": round(float(np.median(per_call)), 4),

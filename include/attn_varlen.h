@@ -33,6 +33,19 @@
  * cap and ALiBi of kept keys are unchanged; a row that keeps no key is a row
  * with no keys (out = 0, dq = 0, lse = -inf).
  *
+ * Dropout.  Page "python-20261012-ragged-flash-attention-gradient-recompute",
+ * section "Root causes addressed": a counter-based splitmix64 hash of (seed,
+ * b, h, row, col), so the backward rebuilds the forward's mask whatever the
+ * tiling; one rate or one per row.  Reading taken: the (sequence b, query
+ * head h) stream state is output b * 2^16 + h + 1 of splitmix64 (Steele, Lea
+ * and Flood 2014) started at dropout_seed; the word of local row i and local
+ * key j is output i * 2^32 + j + 1 of that stream; key j is kept iff the
+ * word's top 32 bits reach floor(p * 2^32), and kept weights P_ij are scaled
+ * by 1 / (1 - p).  Dropout acts after the softmax: lse is that of the
+ * undropped weights, out = (P * mask / (1 - p)) V, and the backward is its
+ * exact VJP.  Dropout is on when dropout_p > 0 or dropout_rates is not NULL;
+ * per-row rates are read on the device and clamped to [0, 1 - 2^-24].
+ *
  * Supported: dtype F16 or BF16 (one dtype for every 16-bit tensor), any hkv
  * dividing hq (grouped key/value heads), head_dim 64, 128 or 160 (page
  * "Pairwise-Gated Attention Engine", section "The task", names head sizes 64
@@ -138,6 +151,10 @@ typedef struct {
   float softcap;               /* c > 0 caps logits at c*tanh(x/c); 0 = no cap */
   float scale_multiplier;      /* logit scale = scale_multiplier / sqrt(head_dim) */
   int32_t flags;               /* attn_flag bits; 0 for the default behaviour */
+  float dropout_p;             /* dropout rate in [0, 1); 0 = none (see "Dropout") */
+  uint64_t dropout_seed;       /* seed of the counter-based dropout hash */
+  const float* dropout_rates;  /* NULL, or device float32 [total_q, hq] contiguous per-row
+                                  rates in [0, 1) that replace dropout_p */
 } attn_problem;
 
 /* Bytes of workspace that `entry` (attn_entry) needs for problem `p`.

@@ -71,7 +71,10 @@ class AttnProblem(ctypes.Structure):
                 ("window_right", ctypes.c_int32),
                 ("softcap", ctypes.c_float),
                 ("scale_multiplier", ctypes.c_float),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32),
+                ("dropout_p", ctypes.c_float),
+                ("dropout_seed", ctypes.c_uint64),
+                ("dropout_rates", ctypes.c_void_p)]
 
 
 class AttnError(RuntimeError):

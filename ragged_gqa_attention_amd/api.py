@@ -36,9 +36,13 @@ def _view(t: torch.Tensor, name: str, dtype, heads=None, dim=None) -> _lib.AttnT
 
 
 def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                 softcap, scale_multiplier, all_keys=False) -> _lib.AttnProblem:
+                 softcap, scale_multiplier, all_keys=False, dropout_p=0.0, dropout_seed=0,
+                 dropout_rates=None) -> _lib.AttnProblem:
     """``all_keys``: evaluate every key, also the far ones whose P is exactly
-    zero (the library skips those by default; results are bitwise the same)."""
+    zero (the library skips those by default; results are bitwise the same).
+    Dropout: a rate ``dropout_p`` in [0, 1) or per-row rates ``dropout_rates``
+    (float32 GPU tensor [Tq, Hq], contiguous) with ``dropout_seed`` (see the
+    header's "Dropout")."""
     if q.dtype not in _DTYPES:
         raise NotImplementedError(f"dtype {q.dtype} is not supported (FP16 / BF16 only)")
     if q.dim() != 3 or k.dim() != 3 or k.shape[2] != q.shape[2]:
@@ -60,7 +64,17 @@ def make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_rig
             or (batch > 0 and alibi_slopes.stride(1) != 1)):
         raise ValueError(f"alibi_slopes must be a float32 GPU tensor [{batch}, {hq}] "
                          "with contiguous rows")
+    if dropout_rates is not None:
+        if (dropout_rates.dtype != torch.float32 or dropout_rates.device.type != "cuda"
+                or tuple(dropout_rates.shape) != (q.shape[0], hq)
+                or not dropout_rates.is_contiguous()):
+            raise ValueError(f"dropout_rates must be a contiguous float32 GPU tensor "
+                             f"[{q.shape[0]}, {hq}]")
+    if not 0.0 <= float(dropout_p) < 1.0:
+        raise ValueError("dropout_p must lie in [0, 1)")
     return _lib.AttnProblem(
+        dropout_p=float(dropout_p), dropout_seed=int(dropout_seed) & (2**64 - 1),
+        dropout_rates=dropout_rates.data_ptr() if dropout_rates is not None else None,
         dtype=_DTYPES[q.dtype], batch=batch, hq=hq, hkv=k.shape[1], head_dim=q.shape[2],
         total_q=q.shape[0], total_k=k.shape[0],
         cu_q=cu_q.data_ptr(), cu_k=cu_k.data_ptr(),
@@ -130,10 +144,12 @@ def _check_plan(ws, device):
 
 def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multiplier=0.75,
                     causal=False, window_left=-1, window_right=-1, *, out=None, lse=None,
-                    workspace=None, check=False, all_keys=False):
-    """Forward only: returns (out [Tq,Hq,160] like q, lse float32 [Tq,Hq])."""
+                    workspace=None, check=False, all_keys=False, dropout_p=0.0, dropout_seed=0,
+                    dropout_rates=None):
+    """Forward only: returns (out [Tq,Hq,D] like q, lse float32 [Tq,Hq])."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                        softcap, scale_multiplier, all_keys)
+                        softcap, scale_multiplier, all_keys, dropout_p, dropout_seed,
+                        dropout_rates)
     d = q.shape[2]
     tq, tk = _view(q, "q", q.dtype, dim=d), _view(k, "k", q.dtype, dim=d)
     tv = _view(v, "v", q.dtype, heads=k.shape[1], dim=d)
@@ -158,11 +174,13 @@ def attn_varlen_fwd(q, k, v, cu_q, cu_k, alibi_slopes, softcap=3.0, scale_multip
 def attn_varlen_bwd(q, k, v, out, lse, dout, cu_q, cu_k, alibi_slopes, softcap=3.0,
                     scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1, *,
                     dq=None, dk=None, dv=None, workspace=None, check=False, store_ds=False,
-                    all_keys=False):
+                    all_keys=False, dropout_p=0.0, dropout_seed=0, dropout_rates=None):
     """Backward from a saved forward: returns (dq, dk, dv).  ``store_ds``: see
-    _bwd_workspace_size (ignored when ``workspace`` is given: its size decides)."""
+    _bwd_workspace_size (ignored when ``workspace`` is given: its size decides).
+    The dropout arguments must be those of the forward."""
     prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left, window_right,
-                        softcap, scale_multiplier, all_keys)
+                        softcap, scale_multiplier, all_keys, dropout_p, dropout_seed,
+                        dropout_rates)
     dt, d = q.dtype, q.shape[2]
     tq, tk = _view(q, "q", dt, dim=d), _view(k, "k", dt, dim=d)
     tv = _view(v, "v", dt, heads=k.shape[1], dim=d)
@@ -203,11 +221,13 @@ class FullVJP:
 
     def __init__(self, q, k, v, cu_q, cu_k, alibi_slopes, dout, causal=False, window_left=-1,
                  window_right=-1, softcap=3.0, scale_multiplier=0.75, *, want_lse=False,
-                 store_ds=False, all_keys=False):
+                 store_ds=False, all_keys=False, dropout_p=0.0, dropout_seed=0,
+                 dropout_rates=None):
         self.prob = make_problem(q, k, cu_q, cu_k, alibi_slopes, causal, window_left,
-                                 window_right, softcap, scale_multiplier, all_keys)
+                                 window_right, softcap, scale_multiplier, all_keys, dropout_p,
+                                 dropout_seed, dropout_rates)
         dt, dev = q.dtype, q.device
-        self.inputs = (q, k, v, dout, cu_q, cu_k, alibi_slopes)   # keep alive
+        self.inputs = (q, k, v, dout, cu_q, cu_k, alibi_slopes, dropout_rates)   # keep alive
         self.out = torch.empty(q.shape, dtype=dt, device=dev)
         self.dq = torch.empty(q.shape, dtype=dt, device=dev)
         self.dk = torch.empty(k.shape, dtype=dt, device=dev)
@@ -252,13 +272,15 @@ class FullVJP:
 
 def attn_varlen_full_vjp(q, k, v, cu_q, cu_k, alibi_slopes, dout, softcap=3.0,
                          scale_multiplier=0.75, causal=False, window_left=-1, window_right=-1,
-                         *, want_lse=False, check=False, store_ds=False, all_keys=False):
+                         *, want_lse=False, check=False, store_ds=False, all_keys=False,
+                         dropout_p=0.0, dropout_seed=0, dropout_rates=None):
     """Forward + full VJP: returns (out, dq, dk, dv[, lse]).  With the default
     store_ds=False nothing synchronises the host: the workspace size depends
     only on the tensors' shapes and dQ recomputes dS."""
     call = FullVJP(q, k, v, cu_q, cu_k, alibi_slopes, dout, causal, window_left, window_right,
                    softcap, scale_multiplier, want_lse=want_lse, store_ds=store_ds,
-                   all_keys=all_keys)
+                   all_keys=all_keys, dropout_p=dropout_p, dropout_seed=dropout_seed,
+                   dropout_rates=dropout_rates)
     res = call()
     if check:
         call.check_plan()

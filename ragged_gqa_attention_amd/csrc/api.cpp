@@ -66,7 +66,7 @@ int device_cus() {
 
 struct Layout {
   size_t seq, flag, zero, fwd_map, ktab, wg_first, kv_head, ksteps, head_hw;
-  size_t lse, rowinfo, part_dk, part_dv;
+  size_t lse, rowinfo, droprec, part_dk, part_dv;
   size_t total;
   int64_t kv_wgs;       // dK/dV workgroups (one per compute unit)
   int64_t row_tiles;
@@ -74,6 +74,8 @@ struct Layout {
 };
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool dropout_on(const attn_problem* p) { return p->dropout_p > 0.0f || p->dropout_rates; }
 
 Layout make_layout(const attn_problem* p, int entry, int cus) {
   Layout L{};
@@ -98,10 +100,11 @@ Layout make_layout(const attn_problem* p, int entry, int cus) {
   L.kv_head = take(sizeof(int) * 4);
   L.ksteps = take(sizeof(int) * 2 * (size_t)L.row_tiles);
   L.head_hw = take(sizeof(int) * (size_t)p->batch * p->hq);
-  L.lse = L.rowinfo = L.part_dk = L.part_dv = 0;
+  L.lse = L.rowinfo = L.droprec = L.part_dk = L.part_dv = 0;
   if (entry == ATTN_ENTRY_FULL_VJP) L.lse = take(sizeof(float) * rows);
   if (entry != ATTN_ENTRY_FWD) {
     L.rowinfo = take(sizeof(float) * 4 * rows);
+    if (dropout_on(p)) L.droprec = take(sizeof(uint32_t) * 4 * rows);
     // FP32 partial dK / dV: two key tiles per workgroup (its first and last)
     const size_t part = sizeof(float) * 2 * (size_t)L.kv_wgs * KEY_TILE * p->head_dim;
     L.part_dk = take(part);
@@ -144,6 +147,8 @@ attn_status check_problem(const attn_problem* p) {
     return fail(ATTN_INVALID_ARG, "scale_multiplier must be finite");
   if ((p->flags & ~ATTN_FLAG_ALL_KEYS) != 0)
     return fail(ATTN_INVALID_ARG, "unknown flags 0x%x", (unsigned)p->flags);
+  if (!(p->dropout_p >= 0.0f && p->dropout_p < 1.0f))
+    return fail(ATTN_INVALID_ARG, "dropout_p must lie in [0, 1)");
   return ATTN_OK;
 }
 
@@ -254,6 +259,14 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
   a.ksteps = reinterpret_cast<int*>(base + L.ksteps);
   a.zero = reinterpret_cast<const uint16_t*>(base + L.zero);
   if (L.rowinfo) a.rowinfo = reinterpret_cast<float*>(base + L.rowinfo);
+  // dropout: the scalar rate's threshold floor(p 2^32) and scale, exact /
+  // correctly rounded in double (the device derives per-row rates the same way)
+  a.drop_on = dropout_on(p) ? 1 : 0;
+  a.drop_seed = p->dropout_seed;
+  a.drop_thr = (uint32_t)std::floor((double)p->dropout_p * 4294967296.0);
+  a.drop_scale = (float)(1.0 / (1.0 - (double)p->dropout_p));
+  a.drop_rates = p->dropout_rates;
+  if (L.droprec) a.droprec = reinterpret_cast<u32x4*>(base + L.droprec);
   if (L.part_dk) {
     a.part_dk = reinterpret_cast<float*>(base + L.part_dk);
     a.part_dv = reinterpret_cast<float*>(base + L.part_dv);

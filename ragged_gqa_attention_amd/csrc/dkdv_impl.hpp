@@ -42,6 +42,7 @@
 // therefore cover every dS image the dQ kernel later reads.
 #pragma once
 
+#include "dropout.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -56,11 +57,12 @@ constexpr int KB = PAIR_KEYS / 32;                    // 32-key blocks per wave
 static_assert(KV_WAVES == 8 && KB == 1, "eight waves: wave w copies tensor w / 4, row group w % 4");
 static_assert(KV_ROW_STEP == TILE_ROWS, "a step is one row tile (see blk_off)");
 
-template <int D>
+template <int D, bool DROP>
 struct KvShared {
   uint16_t qd[KV_NBUF][2][tile_elems<D>()];   // Q and dO rows of a step (blocked)
   f32x4 rinfo[KV_NBUF][KV_ROW_STEP];     // row records of a step
   u32x4 xch[2][KV_WAVES][KB * 2][64];     // [slot][writer wave][kb * 2 + s][lane]
+  u32x4 drec[DROP ? KV_NBUF : 1][DROP ? KV_ROW_STEP : 1];   // dropout records of a step
 };
 
 // What a segment works on: visiting 64-row steps number first .. last - 1 (in
@@ -112,9 +114,9 @@ __device__ __forceinline__ int tile_mask_next(TileMask& m, const KvUnit& u, int 
 }
 
 // The work of one wave; ROLE 0 accumulates dV, ROLE 1 dK.
-template <class T, int D, bool CAP, int ROLE, bool LATE, bool WIN>
-__device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, const KvUnit& u,
-                                          int wave, int lane) {
+template <class T, int D, bool CAP, int ROLE, bool LATE, bool WIN, bool DROP>
+__device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D, DROP>& sm,
+                                          const KvUnit& u, int wave, int lane) {
   constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, CHUNKS = Geo<D>::CHUNKS;
   constexpr int LOADS_PER_WAVE = CHUNKS / 4;   // 4-chunk blocks of a 16-row group
   const int l32 = lane & 31, g = lane >> 5;
@@ -205,6 +207,11 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, co
       const float* src = a.rowinfo + (u.rbase + min(R, re - 1)) * 4;
       load_lds16_unseen(R < re ? (const void*)src : (const void*)a.zero, &sm.rinfo[buf][0]);
     }
+    if (DROP && wave == 1) {
+      const int R = r0 + lane;
+      const u32x4* src = a.droprec + u.rbase + min(R, re - 1);
+      load_lds16_unseen(R < re ? (const void*)src : (const void*)a.zero, &sm.drec[buf][0]);
+    }
     const int R = r0 + lrow;
     const int Rc = min(R, re - 1);
     int tok_, h_;
@@ -290,11 +297,20 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, co
     *reinterpret_cast<u32x4*>(img + (ds_lane ^ (16 * s))) = ds_key_ok ? v : u32x4{0u, 0u, 0u, 0u};
   };
 
+  // dropout: gamma times the lane's key (the word of row i and key j is the
+  // output function at the row's counter base plus gamma j)
+  uint64_t gkey[KB];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) gkey[kb] = SM_GAMMA * (uint64_t)(u.key0 + kb * 32 + l32);
+
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
-  // P and dS of accumulator register r (row rbase + 8 (r/4) + r%4)
+  // P and dS of accumulator register r (row rbase + 8 (r/4) + r%4); with
+  // dropout P is the kept, scaled weight (dV's operand) and dP is scaled or 0
   auto pointwise = [&](int buf, int r, int r0, f32x16 (&S)[KB], f32x16 (&dP)[KB]) {
     const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
+    u32x4 dr = u32x4{0u, 0u, 0u, 0u};
+    if (DROP) dr = sm.drec[buf][rbase + (r >> 2) * 8 + (r & 3)];
     // WIN: the row keeps keys [wlo, whi] around its unclamped centre
     float wlo = -3.0e38f, whi = 3.0e38f;
     if (WIN) {
@@ -318,8 +334,16 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, co
         w = 1.0f;
       }
       if (WIN) p = keyf[kb] >= wlo && keyf[kb] <= whi ? p : 0.0f;
-      S[kb][r] = p;
-      dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
+      if (DROP) {
+        const bool keep = sm_word_hi(drop_base(dr) + gkey[kb]) >= dr[2];
+        const float sc = drop_scale_of(dr);
+        const float dpe = keep ? dP[kb][r] * sc : 0.0f;
+        dP[kb][r] = p * (dpe - ri[3]) * w;
+        S[kb][r] = keep ? p * sc : 0.0f;
+      } else {
+        S[kb][r] = p;
+        dP[kb][r] = p * (dP[kb][r] - ri[3]) * w;
+      }
     }
   };
   // packs P and dS; the own product's half goes to `own`, the other to the
@@ -485,10 +509,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D>& sm, co
 
 }  // namespace kvd
 
-template <class T, int D, bool CAP, bool WIN>
+template <class T, int D, bool CAP, bool WIN, bool DROP>
 __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   using namespace kvd;
-  __shared__ __attribute__((aligned(16))) KvShared<D> sm;
+  __shared__ __attribute__((aligned(16))) KvShared<D, DROP> sm;
 
   // items [w0, w1) of the work list
   const long long W = a.plan.kv_head[0];
@@ -542,26 +566,26 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     u.step_lo = ktile * (KEY_TILE / TILE_ROWS);
     // waves w and w + 4 share a SIMD
     if (wave < 4) {
-      if (wave & 1) dkdv_wave<T, D, CAP, 1, false, WIN>(a, sm, u, wave, lane);
-      else dkdv_wave<T, D, CAP, 0, false, WIN>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, D, CAP, 1, false, WIN, DROP>(a, sm, u, wave, lane);
+      else dkdv_wave<T, D, CAP, 0, false, WIN, DROP>(a, sm, u, wave, lane);
     } else {
-      if (wave & 1) dkdv_wave<T, D, CAP, 1, true, WIN>(a, sm, u, wave, lane);
-      else dkdv_wave<T, D, CAP, 0, true, WIN>(a, sm, u, wave, lane);
+      if (wave & 1) dkdv_wave<T, D, CAP, 1, true, WIN, DROP>(a, sm, u, wave, lane);
+      else dkdv_wave<T, D, CAP, 0, true, WIN, DROP>(a, sm, u, wave, lane);
     }
     w = vs + l;
     __syncthreads();   // the next segment reuses the LDS buffers
   }
 }
 
-template <class T, int D>
+template <class T, int D, bool DROP>
 static hipError_t launch_dkdv_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
   const bool win = a.win_left >= 0 || a.win_right >= 0;
   if (cap) {
-    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, true, true>), grid, KV_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<T, D, true, false>), grid, KV_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, true, true, DROP>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, D, true, false, DROP>), grid, KV_THREADS, 0, s, a);
   } else {
-    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, false, true>), grid, KV_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dkdv_kernel<T, D, false, false>), grid, KV_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dkdv_kernel<T, D, false, true, DROP>), grid, KV_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dkdv_kernel<T, D, false, false, DROP>), grid, KV_THREADS, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -569,8 +593,11 @@ static hipError_t launch_dkdv_t(const AttnArgs& a, bool cap, int grid, hipStream
 template <int D>
 hipError_t launch_dkdv_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_dkdv_t<BF16, D>(a, cap, grid, s)
-                          : launch_dkdv_t<F16, D>(a, cap, grid, s);
+  if (a.drop_on)
+    return dtype == DT_BF16 ? launch_dkdv_t<BF16, D, true>(a, cap, grid, s)
+                            : launch_dkdv_t<F16, D, true>(a, cap, grid, s);
+  return dtype == DT_BF16 ? launch_dkdv_t<BF16, D, false>(a, cap, grid, s)
+                          : launch_dkdv_t<F16, D, false>(a, cap, grid, s);
 }
 
 }  // namespace rga

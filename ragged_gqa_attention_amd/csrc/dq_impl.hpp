@@ -24,6 +24,7 @@
 // and so every dS, is exactly zero.
 #pragma once
 
+#include "dropout.hpp"
 #include "kernels.hpp"
 #include "tiles.hpp"
 
@@ -255,7 +256,7 @@ union DqSmem {
 
 }  // namespace dqd
 
-template <class T, int D, bool CAP, bool WIN>
+template <class T, int D, bool CAP, bool WIN, bool DROP>
 __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   using namespace dqd;
   constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, BLK_COLS = Geo<D>::BLK_COLS;
@@ -316,6 +317,14 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
   const float cb0 = info[1] - (float)(4 * g);
   const float boff = info[2];
   const float dl = info[3];
+  // dropout record of the row: counter base (plus this lane's key offset
+  // 4 g), threshold, scale; dP of a dropped key is 0, of a kept one scaled
+  u32x4 drec = u32x4{0u, 0u, 0u, 0u};
+  uint64_t dbase = 0;
+  if (DROP) {
+    drec = Lk > 0 && row_ok ? a.droprec[ri] : u32x4{0u, 0u, 0u, 0u};
+    dbase = drop_base(drec) + SM_GAMMA * (uint64_t)(4 * g);
+  }
   // window (WIN): the row keeps keys [wlo, whi) around its unclamped centre
   const int wc = ti + Lk - sq[SQ_LQ];
   const int wlo = WIN && a.win_left >= 0 ? wc - a.win_left : 0;
@@ -381,7 +390,13 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
         }
         if (WIN) p = jl >= kfrom && jl < kleft ? p : 0.0f;
         else if (decltype(masked)::value) p = jl < kleft ? p : 0.0f;
-        S[r] = p * (dP[r] - dl) * w;
+        if (DROP) {
+          const bool keep = drop_keep(dbase + SM_GAMMA * (uint64_t)kbase, (uint32_t)jl, drec[2]);
+          const float dpe = keep ? dP[r] * drop_scale_of(drec) : 0.0f;
+          S[r] = p * (dpe - dl) * w;
+        } else {
+          S[r] = p * (dP[r] - dl) * w;
+        }
       }
       u32x4 sb[2];
 #pragma unroll
@@ -426,15 +441,15 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
                       tile, sq, wave, lane);
 }
 
-template <class T, int D>
+template <class T, int D, bool DROP>
 static hipError_t launch_dq_t(const AttnArgs& a, bool cap, int grid, hipStream_t s) {
   const bool win = a.win_left >= 0 || a.win_right >= 0;
   if (cap) {
-    if (win) hipLaunchKernelGGL((dq_kernel<T, D, true, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<T, D, true, false>), grid, ROW_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dq_kernel<T, D, true, true, DROP>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, D, true, false, DROP>), grid, ROW_THREADS, 0, s, a);
   } else {
-    if (win) hipLaunchKernelGGL((dq_kernel<T, D, false, true>), grid, ROW_THREADS, 0, s, a);
-    else hipLaunchKernelGGL((dq_kernel<T, D, false, false>), grid, ROW_THREADS, 0, s, a);
+    if (win) hipLaunchKernelGGL((dq_kernel<T, D, false, true, DROP>), grid, ROW_THREADS, 0, s, a);
+    else hipLaunchKernelGGL((dq_kernel<T, D, false, false, DROP>), grid, ROW_THREADS, 0, s, a);
   }
   return hipGetLastError();
 }
@@ -442,8 +457,11 @@ static hipError_t launch_dq_t(const AttnArgs& a, bool cap, int grid, hipStream_t
 template <int D>
 hipError_t launch_dq_d(const AttnArgs& a, int dtype, bool cap, int grid, hipStream_t s) {
   if (grid <= 0) return hipSuccess;
-  return dtype == DT_BF16 ? launch_dq_t<BF16, D>(a, cap, grid, s)
-                          : launch_dq_t<F16, D>(a, cap, grid, s);
+  if (a.drop_on)
+    return dtype == DT_BF16 ? launch_dq_t<BF16, D, true>(a, cap, grid, s)
+                            : launch_dq_t<F16, D, true>(a, cap, grid, s);
+  return dtype == DT_BF16 ? launch_dq_t<BF16, D, false>(a, cap, grid, s)
+                          : launch_dq_t<F16, D, false>(a, cap, grid, s);
 }
 
 }  // namespace rga

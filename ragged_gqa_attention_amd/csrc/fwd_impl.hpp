@@ -42,6 +42,7 @@
 // workgroup plans the dK/dV units meanwhile.
 #pragma once
 
+#include "dropout.hpp"
 #include "kernels.hpp"
 #include "planner.hpp"
 #include "tiles.hpp"
@@ -68,7 +69,7 @@ template <int D> constexpr int o_pitch() { return D + 8; }
 // beside them on one compute unit.
 // One 256-row tile of the forward: sequence b (extents q0, Lq, k0, Lk), tile
 // `tile` of its folded rows, key steps [klo, khi).
-template <class T, int D, bool CAP, bool DELTA, bool WIN>
+template <class T, int D, bool CAP, bool DELTA, bool WIN, bool DROP>
 __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, const int b,
                                          const int tile, const int q0, const int Lq,
                                          const int k0, const int Lk, const int klo,
@@ -202,22 +203,44 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   // the sum of those same rounded values (lsum_r), so O is an exact convex
   // combination of V rows: a single-key row reproduces v_0 and delta = dO.O
   // matches dP.  L and the backward's residual use the exact FP32 sum.
+  // Dropout: the row's record (counter base, threshold, scale); the sums l
+  // and lsum_r stay those of the undropped weights, the PV operand holds the
+  // kept ones and the scale multiplies O at the end.
+  u32x4 drec = u32x4{0u, 0u, 0u, 0u};
+  uint64_t dbase = 0;
+  if (DROP) {
+    drec = drop_row(a, bp, hb + hh, ti, (int64_t)(q0 + ti));
+    dbase = drop_base(drec) + SM_GAMMA * (uint64_t)(4 * g);   // this lane's key offset 4 g
+  }
   u32x4 pb[2][2];
-  auto probs = [&](int kb) {
+  auto probs = [&](int kb, int kbase) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const float p = fast_exp2(S[kb][r]);
       lsum += p;
       S[kb][r] = p;
     }
+    auto pack = [&]() {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
-                        pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
-                        pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
-                        pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
+      for (int s = 0; s < 2; ++s)
+        pb[kb][s] = u32x4{pack2<T>(S[kb][8 * s + 0], S[kb][8 * s + 1]),
+                          pack2<T>(S[kb][8 * s + 2], S[kb][8 * s + 3]),
+                          pack2<T>(S[kb][8 * s + 4], S[kb][8 * s + 5]),
+                          pack2<T>(S[kb][8 * s + 6], S[kb][8 * s + 7])};
+    };
+    pack();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
 #pragma unroll
       for (int w = 0; w < 4; ++w) lsum_r = add_pair<T>(pb[kb][s][w], lsum_r);
+    if (DROP) {
+      const uint64_t zs = dbase + SM_GAMMA * (uint64_t)kbase;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+        if (!drop_keep(zs, jl, drec[2])) S[kb][r] = 0.0f;
+      }
+      pack();
     }
   };
   // O^T[d][row] += V^T[d][keys] P^T[keys][row] for key block kb of the V row
@@ -271,17 +294,17 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
         const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
         if (LAG && kt > klo) {   // the previous step is a full one
           logits(1, kbase - TILE_ROWS, unmasked);
-          probs(1);
+          probs(1, kbase - TILE_ROWS);
           pv(1, sm.v[(kt - 1) % FWD_NBUF]);
         }
         scores(0, sm.k[buf]);
         scores(1, sm.k[buf]);
         logits(0, kbase, mk);
-        probs(0);
+        probs(0, kbase);
         pv(0, sm.v[buf]);
         if (!LAG) {
           logits(1, kbase, mk);
-          probs(1);
+          probs(1, kbase);
           pv(1, sm.v[buf]);
         }
       };
@@ -297,7 +320,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
         const int kt = khi - 1;
         if (partial) logits(1, kt * TILE_ROWS, masked);
         else logits(1, kt * TILE_ROWS, unmasked);
-        probs(1);
+        probs(1, kt * TILE_ROWS);
         pv(1, sm.v[kt % FWD_NBUF]);
       }
     };
@@ -330,8 +353,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) S[kb][r] -= msub;
-      probs(0);
-      probs(1);
+      probs(0, kbase);
+      probs(1, kbase);
       pv(0, sm.v[buf]);
       pv(1, sm.v[buf]);
     };
@@ -349,7 +372,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   // the dO loads of Delta) move whole 64-byte pieces of rows: in the
   // accumulator layout a lane holds 8-byte pieces of one row, which would
   // touch a new row every lane.  Delta = dO . O uses the rounded O, as the
-  // standalone backward does from the stored output.
+  // standalone backward does from the stored output (plus, with dropout, the
+  // rounding residual, see below).
   // lanes 4q .. 4q + 3 of wave w later take row 32 w + 16 h + q (h = 0, 1),
   // chunks (lane % 4) + 4 i; their dO pieces are requested first
   int erow[2];
@@ -373,7 +397,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   }
   lsum += swap_half(lsum);
   lsum_r += swap_half(lsum_r);
-  const float inv = lsum_r > 0.0f ? 1.0f / lsum_r : 0.0f;
+  const float inv = lsum_r > 0.0f ? (DROP ? drop_scale_of(drec) : 1.0f) / lsum_r
+                                  : 0.0f;
   const float res = m + fast_log2(lsum);
   __syncthreads();   // every wave is done with the key tiles
   uint16_t* obuf = reinterpret_cast<uint16_t*>(&sm);
@@ -388,17 +413,19 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
                 pack2<T>(O[db][rq * 4 + 2] * inv, O[db][rq * 4 + 3] * inv)};
   if (g == 0) {
     sinfo[lrow] = f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f, 0.0f};
+    // the backward's dropout record of this row
+    if (DELTA && DROP && row_ok)
+      a.droprec[(int64_t)q0 * a.hq + (int64_t)hb * Lq + row] = drec;
     if (row_ok)
       a.lse[(int64_t)(q0 + ti) * a.hq + hb + hh] =
           lsum > 0.0f ? (moff + res) * LN2 : -__builtin_inff();
   }
   __syncthreads();
+  float dpart[2] = {0.0f, 0.0f};
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int r = wave * 32 + 16 * h + (lane >> 2);
-    const int rg = erow[h];
     const bool ok = eok[h];
-    float dpart = 0.0f;
 #pragma unroll
     for (int i = 0; i < CHUNKS / 4; ++i) {
       const int c = (lane & 3) + 4 * i;
@@ -408,16 +435,56 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
         const u32x4 d = dpre[h][i];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          dpart += lo_f<T>(o[e]) * lo_f<T>(d[e]) + hi_f<T>(o[e]) * hi_f<T>(d[e]);
+          dpart[h] += lo_f<T>(o[e]) * lo_f<T>(d[e]) + hi_f<T>(o[e]) * hi_f<T>(d[e]);
       }
     }
+  }
+  if (DELTA && DROP) {
+    // With dropout, O carries the scale 1 / (1 - p), so the rounded output no
+    // longer reproduces the FP32 dP of a row with a single kept key exactly:
+    // Delta adds dO . (O - round(O)), the residual staged through the same
+    // LDS rows, which brings it to the FP32 O.
+    __syncthreads();   // every wave has read its rounded rows
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float o = O[db][rq * 4 + e] * inv;
+          const uint32_t w = pack2<T>(o, 0.0f);
+          x[e] = o - lo_f<T>(w);
+        }
+        *reinterpret_cast<u32x2*>(obuf + lrow * O_PITCH + db * 32 + rq * 8 + g * 4) =
+            u32x2{pack2<T>(x[0], x[1]), pack2<T>(x[2], x[3])};
+      }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = wave * 32 + 16 * h + (lane >> 2);
+#pragma unroll
+      for (int i = 0; i < CHUNKS / 4; ++i) {
+        const u32x4 o = load16(obuf + r * O_PITCH + ((lane & 3) + 4 * i) * 8);
+        const u32x4 d = dpre[h][i];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          dpart[h] += lo_f<T>(o[e]) * lo_f<T>(d[e]) + hi_f<T>(o[e]) * hi_f<T>(d[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = wave * 32 + 16 * h + (lane >> 2);
+    const int rg = erow[h];
+    const bool ok = eok[h];
     if (DELTA) {
-      dpart += __shfl_xor(dpart, 1, 64);
-      dpart += __shfl_xor(dpart, 2, 64);
+      dpart[h] += __shfl_xor(dpart[h], 1, 64);
+      dpart[h] += __shfl_xor(dpart[h], 2, 64);
     }
     if (ok && (lane & 3) == 0 && a.rowinfo) {
       f32x4 rec = sinfo[r];
-      rec[3] = DELTA ? dpart : 0.0f;
+      rec[3] = DELTA ? dpart[h] : 0.0f;
       *reinterpret_cast<f32x4*>(a.rowinfo + ((int64_t)q0 * a.hq + (int64_t)hb * Lq + rg) * 4) =
           rec;
     }
@@ -665,7 +732,7 @@ union FwdSmem {
   LptScratch l;
 };
 
-template <class T, int D, bool CAP, bool DELTA, bool WIN>
+template <class T, int D, bool CAP, bool DELTA, bool WIN, bool DROP>
 __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, const PlanArgs pa) {
   __shared__ __attribute__((aligned(16))) FwdSmem<D> smu;
   __shared__ FwdOrder ord;
@@ -699,7 +766,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   const int nlist = nlist_s;
   if (nlist >= 0) {
     for (int i = 0; i < nlist; ++i) {
-      fwd_tile<T, D, CAP, DELTA, WIN>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3],
+      fwd_tile<T, D, CAP, DELTA, WIN, DROP>(a, sm, list[i][0], list[i][1], list[i][2], list[i][3],
                                       list[i][4], list[i][5], list[i][6], list[i][7]);
       __syncthreads();   // the next tile reuses the LDS buffers
     }
@@ -744,28 +811,43 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     __syncthreads();
     const int b = tinfo[0];
     if (b < 0) break;
-    fwd_tile<T, D, CAP, DELTA, WIN>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5],
+    fwd_tile<T, D, CAP, DELTA, WIN, DROP>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5],
                                     tinfo[6], tinfo[7]);
     __syncthreads();   // the next tile reuses tinfo and the LDS buffers
   }
 }
 
 
-template <class T, int D, bool WIN>
+template <class T, int D, bool WIN, bool DROP>
 static hipError_t launch_fwd_t(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
                                int grid, hipStream_t s) {
   if (cap) {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, D, true, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, true, WIN, DROP>), grid, ROW_THREADS, 0, s, a,
+                         pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, true, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, true, false, WIN, DROP>), grid, ROW_THREADS, 0, s, a,
+                         pa);
   } else {
     if (with_delta)
-      hipLaunchKernelGGL((fwd_kernel<T, D, false, true, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, true, WIN, DROP>), grid, ROW_THREADS, 0, s, a,
+                         pa);
     else
-      hipLaunchKernelGGL((fwd_kernel<T, D, false, false, WIN>), grid, ROW_THREADS, 0, s, a, pa);
+      hipLaunchKernelGGL((fwd_kernel<T, D, false, false, WIN, DROP>), grid, ROW_THREADS, 0, s, a,
+                         pa);
   }
   return hipGetLastError();
+}
+
+template <class T, int D>
+static hipError_t launch_fwd_td(const AttnArgs& a, const PlanArgs& pa, bool cap, bool with_delta,
+                                int grid, hipStream_t s) {
+  const bool win = a.win_left >= 0 || a.win_right >= 0;
+  if (a.drop_on)
+    return win ? launch_fwd_t<T, D, true, true>(a, pa, cap, with_delta, grid, s)
+               : launch_fwd_t<T, D, false, true>(a, pa, cap, with_delta, grid, s);
+  return win ? launch_fwd_t<T, D, true, false>(a, pa, cap, with_delta, grid, s)
+             : launch_fwd_t<T, D, false, false>(a, pa, cap, with_delta, grid, s);
 }
 
 template <int D>
@@ -774,11 +856,8 @@ hipError_t launch_fwd_d(const AttnArgs& a, const PlanArgs& pa, int dtype, bool c
   // the planner plus one persistent workgroup per remaining compute unit
   const int grid = 1 + max(1, a.kv_wgs - 1);
   if (a.batch <= 0) return hipSuccess;
-  if (a.win_left >= 0 || a.win_right >= 0)
-    return dtype == DT_BF16 ? launch_fwd_t<BF16, D, true>(a, pa, cap, with_delta, grid, s)
-                            : launch_fwd_t<F16, D, true>(a, pa, cap, with_delta, grid, s);
-  return dtype == DT_BF16 ? launch_fwd_t<BF16, D, false>(a, pa, cap, with_delta, grid, s)
-                          : launch_fwd_t<F16, D, false>(a, pa, cap, with_delta, grid, s);
+  return dtype == DT_BF16 ? launch_fwd_td<BF16, D>(a, pa, cap, with_delta, grid, s)
+                          : launch_fwd_td<F16, D>(a, pa, cap, with_delta, grid, s);
 }
 
 }  // namespace rga

@@ -78,6 +78,15 @@ struct AttnArgs {
   // bound being no bound (causal: win_right = 0); both negative = no mask.
   int win_left;
   int win_right;
+  // Dropout (see dropout.hpp): the seed, the scalar rate's threshold and
+  // scale, optional per-row rates [total_q, hq] (NULL: the scalar rate), and
+  // the per-row records [total_q * hq] the backward reads (row record index).
+  int drop_on;          // dropout with the fields below
+  uint64_t drop_seed;
+  uint32_t drop_thr;
+  float drop_scale;
+  const float* drop_rates;
+  u32x4* droprec;
 };
 
 struct PlanArgs {

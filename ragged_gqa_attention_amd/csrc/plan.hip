@@ -12,6 +12,7 @@
 //     near-equal length, sized so that the units fill whole rounds of the
 //     compute units.
 // Each workgroup finds its item in a map with one load.
+#include "dropout.hpp"
 #include "kernels.hpp"
 #include "planner.hpp"
 #include "tiles.hpp"
@@ -85,6 +86,7 @@ __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   const float negres = Lk > 0 ? moff - L * LOG2E : 0.0f;
   *reinterpret_cast<f32x4*>(a.rowinfo + fr * 4) =
       f32x4{slope2, (float)max(i + Lk - Lq, 0), negres, acc};
+  if (a.drop_on) a.droprec[fr] = drop_row(a, lo, h, i, t);
 }
 
 // Key-step ranges of the standalone backward (the full-VJP call takes the
