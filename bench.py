@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--trial", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--causal", action="store_true", help="bottom-right causal mask")
+    ap.add_argument("--window", type=int, nargs=2, default=(-1, -1), metavar=("LEFT", "RIGHT"),
+                    help="sliding window bounds (-1 = none)")
     ap.add_argument("--dropout-p", type=float, default=0.0,
                     help="counter-based dropout rate (0 = none, the configurations' setting)")
     ap.add_argument("--dropout-seed", type=int, default=1234)
@@ -137,6 +140,8 @@ def main():
     g = wl.to(dev)
     call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
                        scale_multiplier=g.scale_multiplier, store_ds=True,
+                       causal=args.causal, window_left=args.window[0],
+                       window_right=args.window[1],
                        dropout_p=args.dropout_p, dropout_seed=args.dropout_seed)
     nph = len(_lib.PHASES)
 
@@ -182,7 +187,18 @@ def main():
         torch.cuda.synchronize()
 
     elems = wl.score_elements()
-    flops = wl.flops()
+    if args.causal or args.window[0] >= 0 or args.window[1] >= 0:
+        # a mask removes pairs from the work: credit only the kept ones
+        wr_ = 0 if args.causal else args.window[1]
+        wl_ = args.window[0]
+        kept = 0
+        for lq, lk in zip(wl.lq, wl.lk):
+            c = np.arange(int(lq)) + int(lk) - int(lq)
+            lo = np.maximum(0, c - wl_) if wl_ >= 0 else np.zeros_like(c)
+            hi = np.minimum(int(lk) - 1, c + wr_) if wr_ >= 0 else np.full_like(c, int(lk) - 1)
+            kept += int(np.maximum(hi - lo + 1, 0).sum())
+        elems = kept * wl.hq
+    flops = 14.0 * elems * wl.head_dim
     # share of the credited (row, key) pairs inside the recorded key-step ranges
     ks = call.key_steps().astype(np.int64)
     evaluated = 0
@@ -220,7 +236,7 @@ def main():
             "total_k": wl.total_k, "sum_lq_lk": int((wl.lq * wl.lk).sum()),
             "view": f"feature width {wl.width}, token step {wl.step}",
             "softcap": wl.softcap, "scale_multiplier": wl.scale_multiplier,
-            "dropout_p": args.dropout_p,
+            "dropout_p": args.dropout_p, "causal": args.causal, "window": list(args.window),
         },
         "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 3),
         "ms_per_call_median": round(float(np.median(per_call)), 4),

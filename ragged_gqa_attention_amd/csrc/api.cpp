@@ -298,6 +298,8 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
                                                  : (int)std::min<int64_t>(p->window_right,
                                                                           p->total_q));
   pa.seg_items = KV_SEGMENT_ITEMS;
+  pa.win_left = a.win_left;
+  pa.win_right = a.win_right;
   a.kv_wgs = (int)L.kv_wgs;
   pa.zero = reinterpret_cast<uint16_t*>(base + L.zero);
   pa.plan = a.plan;

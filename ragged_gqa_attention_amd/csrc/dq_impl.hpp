@@ -212,6 +212,7 @@ __device__ __forceinline__ void dq_stored(const AttnArgs& a, DqStoredShared<D>& 
   f32x16 dQ[DBLK];
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) dQ[db] = f32x16{};
+  // (klo <= khi: every range leaves the planner through finish_range)
   if (klo < khi) issue(klo, klo % DQS_NBUF);
   if (klo + 1 < khi) issue(klo + 1, (klo + 1) % DQS_NBUF);
   for (int kt = klo; kt < khi; ++kt) {

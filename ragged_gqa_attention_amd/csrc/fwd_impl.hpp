@@ -639,13 +639,15 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
       const int ia = h == hfirst ? R0 - h * lq : 0;
       const int ib = h == hlast ? R1 - 1 - h * lq : lq - 1;
       const int hw = sc.hw[k * hq + h];
-      int l0, u0, l1, u1;
-      key_steps_of(max(ia + lk - lq, 0), hw, lk, l0, u0);
-      key_steps_of(max(ib + lk - lq, 0), hw, lk, l1, u1);
-      lo = min(lo, l0);
-      hi = max(hi, u1);
+      int l, u;
+      token_range_steps(ia, ib, lq, lk, hw, pa.win_left, pa.win_right, l, u);
+      if (l < u) {
+        lo = min(lo, l);
+        hi = max(hi, u);
+      }
     }
-    const int c = LPT_CLASSES - 1 - min(hi - lo, LPT_CLASSES - 1);
+    finish_range(lo, hi);
+    const int c = LPT_CLASSES - 1 - min(max(hi - lo, 0), LPT_CLASSES - 1);
     sc.cls[t] = c;
     sc.ks[t][0] = lo;
     sc.ks[t][1] = hi;

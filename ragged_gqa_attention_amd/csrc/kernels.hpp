@@ -103,6 +103,8 @@ struct PlanArgs {
   float skip_log2;
   int* ksteps;          // [row tiles * 2] ranges the planner writes (AttnArgs::ksteps)
   int* head_hw;         // [B * hq] key half-widths, when they do not fit the planner's LDS
+  int win_left;         // key window (AttnArgs::win_left / win_right): the ranges
+  int win_right;        //   keep only the steps that hold some row's window keys
   long long ds_images;  // dS images that fit the workspace (0: no stored dS)
   int fwd_slots;        // entries of plan.fwd_map (the row-tile launches' grid)
   int kv_wgs;           // dK/dV workgroups (the dK/dV launch's grid)
@@ -154,6 +156,45 @@ __device__ __forceinline__ void key_steps_of(int centre, int ds, int Lk, int& lo
   } else {
     lo = max(0, centre - ds) / TILE_ROWS;
     hi = min(Lk - 1, centre + ds) / TILE_ROWS + 1;
+  }
+}
+
+// A tile's final key-step range: (0, 0) when its rows keep no key (the
+// per-row neutral element (INT_MAX, 0) never leaves a range computation), so
+// every consumer sees lo <= hi and hi - lo >= 0.
+__device__ __forceinline__ void finish_range(int& lo, int& hi) {
+  if (lo >= hi) {
+    lo = 0;
+    hi = 0;
+  }
+}
+
+// Key steps of query tokens [ia, ib] of a sequence: those of the ALiBi rule
+// for the head's half-width ds (key_steps_of at the tokens' clamped centres,
+// both bounds grow with the token), intersected with the key steps that hold
+// some token's window keys [i + Lk - Lq - wl, i + Lk - Lq + wr] (a negative
+// bound is no bound).  An empty result is lo >= hi.
+__device__ __forceinline__ void token_range_steps(int ia, int ib, int Lq, int Lk, int ds, int wl,
+                                                  int wr, int& lo, int& hi) {
+  int l0, u0, l1, u1;
+  key_steps_of(max(ia + Lk - Lq, 0), ds, Lk, l0, u0);
+  key_steps_of(max(ib + Lk - Lq, 0), ds, Lk, l1, u1);
+  lo = l0;
+  hi = u1;
+  if (wl >= 0 || wr >= 0) {
+    const int klo = wl >= 0 ? max(0, ia + Lk - Lq - wl) : 0;
+    const int khi = wr >= 0 ? min(Lk - 1, ib + Lk - Lq + wr) : Lk - 1;
+    if (klo > khi) {
+      lo = 0x7fffffff;
+      hi = 0;
+      return;
+    }
+    lo = max(lo, klo / TILE_ROWS);
+    hi = min(hi, khi / TILE_ROWS + 1);
+    if (lo >= hi) {
+      lo = 0x7fffffff;
+      hi = 0;
+    }
   }
 }
 

@@ -117,6 +117,19 @@ __global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
   }
   int lo, hi;
   row_key_steps(ok, slope2, centre, Lk, thr, lo, hi);
+  if (ok && Lk > 0 && (a.win_left >= 0 || a.win_right >= 0)) {
+    // only the steps that hold the row's window keys
+    int i, h;
+    unfold_row(R, sq, i, h);
+    int wlo, whi;
+    token_range_steps(i, i, sq[SQ_LQ], Lk, -1, a.win_left, a.win_right, wlo, whi);
+    lo = max(lo, wlo);
+    hi = min(hi, whi);
+    if (lo >= hi) {
+      lo = 0x7fffffff;
+      hi = 0;
+    }
+  }
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -133,6 +146,7 @@ __global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
       lo = min(lo, span[0][w]);
       hi = max(hi, span[1][w]);
     }
+    finish_range(lo, hi);
     int* ks = a.ksteps + 2 * (sq[SQ_RTOFF] + tile);
     ks[0] = lo;
     ks[1] = hi;

@@ -83,8 +83,8 @@ constexpr int PLAN_LDS_KT = 2048;
 // row_key_steps over its rows.  For one head both bounds grow with the token
 // (the centre does), so each head the tile spans contributes its first and
 // its last row.
-__device__ __forceinline__ void tile_key_steps(const int* s, int t, const int* hw, int& lo,
-                                               int& hi) {
+__device__ __forceinline__ void tile_key_steps(const int* s, int t, const int* hw, int wl, int wr,
+                                               int& lo, int& hi) {
   const int Lq = s[SQ_LQ], Lk = s[SQ_LK], rows = s[SQ_ROWS];
   const int R0 = t * ROW_TILE, R1 = min(rows, R0 + ROW_TILE);
   const int hfirst = R0 / Lq, hlast = (R1 - 1) / Lq;
@@ -93,12 +93,14 @@ __device__ __forceinline__ void tile_key_steps(const int* s, int t, const int* h
   for (int h = hfirst; h <= hlast; ++h) {
     const int ia = h == hfirst ? R0 - h * Lq : 0;
     const int ib = h == hlast ? R1 - 1 - h * Lq : Lq - 1;
-    int l0, u0, l1, u1;
-    key_steps_of(max(ia + Lk - Lq, 0), hw[h], Lk, l0, u0);
-    key_steps_of(max(ib + Lk - Lq, 0), hw[h], Lk, l1, u1);
-    lo = min(lo, l0);
-    hi = max(hi, u1);
+    int l, u;
+    token_range_steps(ia, ib, Lq, Lk, hw[h], wl, wr, l, u);
+    if (l < u) {
+      lo = min(lo, l);
+      hi = max(hi, u);
+    }
   }
+  finish_range(lo, hi);
 }
 
 // Last index r in [0, n) with key(r) <= x (key nondecreasing, key(0) <= x).
@@ -375,11 +377,11 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
     const int b = seq_of_tile(g);
     const int* s = seq + b * SEQ_FIELDS;
     int lo, hi;
-    tile_key_steps(s, g - s[SQ_RTOFF], hw + b * hq, lo, hi);
+    tile_key_steps(s, g - s[SQ_RTOFF], hw + b * hq, a.win_left, a.win_right, lo, hi);
     a.ksteps[2 * g] = lo;
     a.ksteps[2 * g + 1] = hi;
     // class 0 holds the longest tiles
-    atomicAdd(&l_class[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+    atomicAdd(&l_class[PLAN_COST_CLASSES - 1 - min(max(hi - lo, 0), PLAN_COST_CLASSES - 1)], 1);
   }
   __syncthreads();
   // workgroup -> row tile, longest first; entries past the last tile get
@@ -389,7 +391,8 @@ __device__ __forceinline__ void plan_block(const PlanArgs& a, PlanShared& sh) {
                                      part);
   for (int g = tid; g < nrt; g += NT) {
     const int lo = a.ksteps[2 * g], hi = a.ksteps[2 * g + 1];
-    const int pos = atomicAdd(&l_foff_c[PLAN_COST_CLASSES - 1 - min(hi - lo, PLAN_COST_CLASSES - 1)], 1);
+    const int pos =
+        atomicAdd(&l_foff_c[PLAN_COST_CLASSES - 1 - min(max(hi - lo, 0), PLAN_COST_CLASSES - 1)], 1);
     const int b = seq_of_tile(g);
     a.plan.fwd_map[2 * pos] = b;
     a.plan.fwd_map[2 * pos + 1] = g - seq[b * SEQ_FIELDS + SQ_RTOFF];
@@ -533,11 +536,12 @@ __device__ __forceinline__ void tile_key_range(const PlanArgs& pa, const RowTile
       const int hw = key_half_width(slope * LOG2E, t.lk, pa.skip_log2);
       const int ia = h == hfirst ? R0 - h * t.lq : 0;
       const int ib = h == hlast ? R1 - 1 - h * t.lq : t.lq - 1;
-      int l0, u0, l1, u1;
-      key_steps_of(max(ia + t.lk - t.lq, 0), hw, t.lk, l0, u0);
-      key_steps_of(max(ib + t.lk - t.lq, 0), hw, t.lk, l1, u1);
-      lo = min(lo, l0);
-      hi = max(hi, u1);
+      int l, u;
+      token_range_steps(ia, ib, t.lq, t.lk, hw, pa.win_left, pa.win_right, l, u);
+      if (l < u) {
+        lo = min(lo, l);
+        hi = max(hi, u);
+      }
     }
   }
 #pragma unroll
@@ -545,6 +549,7 @@ __device__ __forceinline__ void tile_key_range(const PlanArgs& pa, const RowTile
     lo = min(lo, __shfl_xor(lo, o, 64));
     hi = max(hi, __shfl_xor(hi, o, 64));
   }
+  finish_range(lo, hi);
   lo = __builtin_amdgcn_readfirstlane(lo);
   hi = __builtin_amdgcn_readfirstlane(hi);
 }

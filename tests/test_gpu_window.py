@@ -109,3 +109,110 @@ def test_causal_empty_rows_and_separate_entries():
         torch.cuda.synchronize()
         for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
             assert_close(name, to_np(t), ref[name], tol, f"bwd entry store_ds={store_ds}")
+
+
+def _window_ranges_host(wl, wl_, wr, thr):
+    """The library's range rule on the host: per head of a 256-row tile, the
+    ALiBi steps of its first and last token (FP32 half-width) intersected with
+    the steps holding its tokens' window keys; the union over the tile's heads."""
+    LOG2E = 1.4426950408889634
+    slopes = wl.slopes.numpy().astype(np.float32)
+    out = []
+    for b in range(wl.batch):
+        Lq, Lk = int(wl.lq[b]), int(wl.lk[b])
+        rows = Lq * wl.hq
+        for R0 in range(0, rows, 256):
+            R1 = min(rows, R0 + 256)
+            lo, hi = 2**31 - 1, 0
+            for h in range(R0 // Lq, (R1 - 1) // Lq + 1):
+                ia = R0 - h * Lq if h == R0 // Lq else 0
+                ib = R1 - 1 - h * Lq if h == (R1 - 1) // Lq else Lq - 1
+                slope2 = slopes[b, h] * np.float32(LOG2E)
+                span = np.float32(thr) / slope2 if slope2 > 0 else np.inf
+                nks = (Lk + 63) // 64
+                if slope2 > 0 and span < np.float32(Lk):
+                    ds = int(span)
+                    l0 = max(0, max(ia + Lk - Lq, 0) - ds) // 64
+                    u1 = min(Lk - 1, max(ib + Lk - Lq, 0) + ds) // 64 + 1
+                else:
+                    l0, u1 = 0, nks
+                klo = max(0, ia + Lk - Lq - wl_) if wl_ >= 0 else 0
+                khi = min(Lk - 1, ib + Lk - Lq + wr) if wr >= 0 else Lk - 1
+                if klo > khi:
+                    continue
+                l, u = max(l0, klo // 64), min(u1, khi // 64 + 1)
+                if l < u:
+                    lo, hi = min(lo, l), max(hi, u)
+            out.append((lo, hi) if lo < hi else (0, 0))   # rows that keep nothing
+    return np.array(out, np.int64).reshape(-1, 2)
+
+
+@pytest.mark.parametrize("causal,wl_,wr", [(True, -1, -1), (False, 100, 0), (False, 64, 64),
+                                           (False, -1, 5)])
+def test_window_key_steps(causal, wl_, wr):
+    """The row tiles visit only the key steps that hold some row's window
+    keys (intersected with the far-key rule): the recorded ranges equal the
+    host rule (tiles whose rows keep nothing get the empty range (0, 0)),
+    cover every kept key of every row, the outputs match the oracle, and a
+    causal call on equal lengths visits at most 80 % of the steps (a 256-row
+    tile spans 256 consecutive tokens of one head, so its causal range is a
+    prefix of the keys)."""
+    need_gpu()
+    wl = W.custom_workload(lq=[700, 37, 300, 1000], lk=[700, 900, 40, 1000], hq=16,
+                           dtype="bf16", width=160, step=1, seed=46)
+    g = wl.to("cuda")
+    call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, causal=causal,
+                       window_left=wl_, window_right=wr, softcap=g.softcap,
+                       scale_multiplier=g.scale_multiplier, store_ds=True)
+    out, dq, dk, dv = call()
+    torch.cuda.synchronize()
+    got = call.key_steps().astype(np.int64)
+    ewr = 0 if causal else wr
+    ref = _oracle(wl, causal, wl_, wr)
+    for name, t in (("out", out), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(name, to_np(t), ref[name], TOL[wl.dtype], f"window ranges {causal} {wl_} {wr}")
+    want = _window_ranges_host(wl, wl_, ewr, 160.0 + 2.0 * wl.softcap * 1.4426950408889634)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want)
+    # every key a row keeps (inside its window and within the ALiBi rule's
+    # half-width of its clamped centre) lies inside its tile's range
+    thr = np.float32(160.0 + 2.0 * wl.softcap * 1.4426950408889634)
+    slopes = wl.slopes.numpy().astype(np.float32)
+    t = 0
+    for b in range(wl.batch):
+        Lq, Lk = int(wl.lq[b]), int(wl.lk[b])
+        rows = Lq * wl.hq
+        R = np.arange(rows)
+        i, h = R % Lq, R // Lq
+        c = i + Lk - Lq
+        cc = np.maximum(c, 0)
+        slope2 = slopes[b, h] * np.float32(1.4426950408889634)
+        with np.errstate(divide="ignore", over="ignore"):
+            span = np.where(slope2 > 0, thr / slope2, np.inf)
+        ds = np.where(span < Lk, np.floor(np.minimum(span, 2.0**30)), 2**30).astype(np.int64)
+        klo = np.maximum(cc - ds, 0)
+        khi = np.minimum(cc + ds, Lk - 1)
+        if wl_ >= 0:
+            klo = np.maximum(klo, c - wl_)
+        if ewr >= 0:
+            khi = np.minimum(khi, c + ewr)
+        for R0 in range(0, rows, 256):
+            lo, hi = got[t]
+            t += 1
+            sel = slice(R0, min(rows, R0 + 256))
+            kept = klo[sel] <= khi[sel]
+            if kept.any():
+                assert lo < hi
+                assert np.all(klo[sel][kept] >= 64 * lo) and np.all(khi[sel][kept] < 64 * hi)
+    if causal:
+        full = sum(((int(lk) + 63) // 64) * ((int(lq) * wl.hq + 255) // 256)
+                   for lq, lk in zip(wl.lq, wl.lk) if lq == lk)
+        vis = 0
+        t = 0
+        for lq, lk in zip(wl.lq, wl.lk):
+            n = (int(lq) * wl.hq + 255) // 256
+            if lq == lk:
+                vis += int(np.maximum(got[t:t + n, 1] - got[t:t + n, 0], 0).sum())
+            t += n
+        say(f"  causal, equal lengths: {vis} of {full} key steps visited")
+        assert vis < 0.8 * full
