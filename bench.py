@@ -69,11 +69,26 @@ def cpu_baseline(wl, seconds: float):
     until about `seconds` of CPU time."""
     import oracle
     from workloads import oracle_inputs
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        blas = [{"api": i.get("internal_api"), "version": i.get("version"),
+                 "threads": i.get("num_threads"), "arch": i.get("architecture")}
+                for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:  # pragma: no cover - threadpoolctl is optional
-        threads = os.cpu_count() or 1
+        pass
+    # NumPy's elementwise steps run on one thread; its matrix products use the
+    # BLAS pool, so the pool's size is the most threads the oracle can use
+    threads = max([b["threads"] or 1 for b in blas] + [1])
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    cpu_model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     inp = oracle_inputs(wl)
     cu_q, cu_k = inp["cu_q"], inp["cu_k"]
     spent, elems, n = 0.0, 0, 0
@@ -90,7 +105,8 @@ def cpu_baseline(wl, seconds: float):
             break
     flops = 14.0 * elems * wl.head_dim
     return {"value": round(flops / spent / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "os_cpu_count": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "blas": blas,
             "sample": f"first {n} of {wl.batch} sequences of {wl.name} "
                       f"(sum Lq*Lk*Hq = {elems}), float64 NumPy forward + VJP, "
                       f"{spent:.1f} s"}

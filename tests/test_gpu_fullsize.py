@@ -61,17 +61,17 @@ def test_balanced_long_shortest_sequence_in_full():
     g = wl.to("cuda")
     res = {}
     for mode in (True, False):
-        say(f"[cfg4] GPU call store_ds={mode}")
+        say(f"[balanced_long] GPU call store_ds={mode}")
         res[mode] = gpu_full(g, store_ds=mode)
     for name in ("out", "lse", "dk", "dv"):
         assert torch.equal(res[True][name], res[False][name]), name
-    _compare_sequence(wl, res[True], b, "cfg4 store_ds=True", workers=6)
+    _compare_sequence(wl, res[True], b, "balanced_long store_ds=True", workers=6)
     q0, q1, _, _ = _seq(wl, b)
     ref_dq = res[True]["dq"][q0:q1].float()
     other = res[False]["dq"][q0:q1].float()
     # stored and recomputed dS round the same value: dq agrees to the tolerance
     err = (ref_dq - other).abs().max().item() / ref_dq.abs().max().item()
-    say(f"  cfg4 dq stored vs recomputed dS: {err:.2e}")
+    say(f"  balanced_long dq stored vs recomputed dS: {err:.2e}")
     assert err <= TOL[wl.dtype]
 
 
@@ -84,7 +84,7 @@ def test_mixed_extreme_long_sequence_dkdv():
     b = 4
     assert wl.lq[b] >= 1000 and wl.lk[b] >= 1000
     got = gpu_full(wl.to("cuda"))
-    _compare_sequence(wl, got, b, "cfg3 trial3", workers=6)
+    _compare_sequence(wl, got, b, "mixed_extreme trial 3", workers=6)
 
 
 def _long_keys(dtype, softcap, seed):

@@ -24,9 +24,9 @@ from tests.gpu_util import (TOL, assert_close, assert_lse, check_full, gpu_full,
 pytestmark = pytest.mark.gpu
 
 
-def test_config0_tiny_full_parity():
+def test_tiny_ragged_gqa_full_parity():
     need_gpu()
-    check_full(W.make_workload(0), "cfg0")
+    check_full(W.make_workload(0), "tiny_ragged_gqa")
 
 
 @pytest.mark.parametrize("seed", range(30))
@@ -35,11 +35,11 @@ def test_fuzz_parity(seed):
     check_full(W.fuzz_workload(seed), f"fuzz{seed}")
 
 
-def test_config1_full_parity():
+def test_q_short_k_long_full_parity():
     """The benchmarked Hq=64 Q-short/K-long configuration, every element, with
     dQ from stored dS and with dQ recomputing dS."""
     need_gpu()
-    (stored, recomputed), _ = check_full(W.make_workload(1), "cfg1")
+    (stored, recomputed), _ = check_full(W.make_workload(1), "q_short_k_long")
     # storing dS changes nothing before dQ
     for name in ("out", "lse", "dk", "dv"):
         assert torch.equal(stored[name], recomputed[name]), name
@@ -57,7 +57,7 @@ def test_partial_ds_capacity():
     base = rga.workspace_size(prob, 2)
     assert full > base
     # room for about 40 % of the images, plus a few bytes that fit no image
-    (part,), ref = check_full(wl, "cfg1 partial", modes=((full - base) * 2 // 5 + 1000,))
+    (part,), ref = check_full(wl, "q_short_k_long partial", modes=((full - base) * 2 // 5 + 1000,))
     stored = gpu_full(g, store_ds=True)
     for name in ("out", "lse", "dk", "dv"):
         assert torch.equal(part[name], stored[name]), name
@@ -104,8 +104,8 @@ def test_large_config_sampled_parity(cfg):
             got_rows[name].append(to_np(sel))
     for name in ("out", "dq"):
         assert_close(name, np.concatenate(got_rows[name]), np.concatenate(ref_rows[name]), tol,
-                     f"cfg{cfg} sampled rows")
-    assert_lse(np.concatenate(got_rows["lse"]), np.concatenate(ref_rows["lse"]), f"cfg{cfg}")
+                     f"{wl.name} sampled rows")
+    assert_lse(np.concatenate(got_rows["lse"]), np.concatenate(ref_rows["lse"]), f"{wl.name}")
 
     # full dk / dv of the cheapest sequences with more than one key and query
     cost = wl.lq * wl.lk
@@ -120,7 +120,7 @@ def test_large_config_sampled_parity(cfg):
                                   wl.softcap, wl.scale_multiplier)
         for name in ("dk", "dv", "out", "dq"):
             sl = slice(k0, k1) if name in ("dk", "dv") else slice(q0, q1)
-            assert_close(name, to_np(g[name][sl]), ref[name], tol, f"cfg{cfg} seq{b}")
+            assert_close(name, to_np(g[name][sl]), ref[name], tol, f"{wl.name} seq{b}")
 
     # sum_j dv_j = sum over the sequence's rows of dout, for every sequence
     dv = to_np(g["dv"])
@@ -131,6 +131,6 @@ def test_large_config_sampled_parity(cfg):
         lhs = dv[k0:k1, 0].sum(0)
         rhs = _f64(wl.dout[q0:q1]).sum((0, 1)) if q1 > q0 else np.zeros(160)
         scale = np.abs(dv[k0:k1, 0]).sum(0).max() + np.abs(rhs).max() + 1e-30
-        assert np.abs(lhs - rhs).max() <= tol * scale, f"cfg{cfg} seq{b}: sum dv identity"
+        assert np.abs(lhs - rhs).max() <= tol * scale, f"{wl.name} seq{b}: sum dv identity"
     for name in ("out", "dq", "dk", "dv"):
-        assert torch.isfinite(g[name]).all(), f"cfg{cfg} {name} non-finite"
+        assert torch.isfinite(g[name]).all(), f"{wl.name} {name} non-finite"

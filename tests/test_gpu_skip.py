@@ -40,9 +40,9 @@ def _long_key_workload():
 
 
 WORKLOADS = {
-    "cfg0": lambda: W.make_workload(0),
-    "cfg1": lambda: W.make_workload(1),
-    "cfg3": lambda: W.make_workload(3),
+    "tiny_ragged_gqa": lambda: W.make_workload(0),
+    "q_short_k_long": lambda: W.make_workload(1),
+    "mixed_extreme": lambda: W.make_workload(3),
     "long_keys": _long_key_workload,
 }
 
@@ -121,11 +121,11 @@ def test_skip_is_bitwise_exact(name):
         assert np.array_equal(full[:, 0], np.zeros_like(nks)) and np.array_equal(full[:, 1], nks)
         kept = float((part[:, 1] - part[:, 0]).sum()) / max(1, int(nks.sum()))
         say(f"  key steps visited: {kept:.3f} of all")
-        if name in ("cfg1", "long_keys"):
+        if name in ("q_short_k_long", "long_keys"):
             assert kept < 0.95, "the workload should exercise the skipping"
 
 
-@pytest.mark.parametrize("name", ["cfg1", "long_keys"])
+@pytest.mark.parametrize("name", ["q_short_k_long", "long_keys"])
 def test_key_steps_follow_the_rule(name):
     need_gpu()
     wl = WORKLOADS[name]()

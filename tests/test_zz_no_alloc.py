@@ -62,7 +62,7 @@ def _with_workspace(g):
 def test_noalloc_matches_workspace_entry():
     need_gpu()
     names = ("out", "dq", "dk", "dv", "lse")
-    for label, wl in (("cfg1", W.make_workload(1)), ("cfg0", W.make_workload(0))):
+    for label, wl in (("q_short_k_long", W.make_workload(1)), ("tiny_ragged_gqa", W.make_workload(0))):
         say(f"[noalloc] {label} Tq={wl.total_q} Tk={wl.total_k} hq={wl.hq}")
         g = wl.to("cuda")
         got = _noalloc(g)

@@ -193,7 +193,7 @@ def make_workload(cfg: int, trial: int = 0) -> Workload:
     c = CONFIGS[cfg]
     rng = np.random.default_rng([cfg, trial])
     lq, lk = draw_lengths(cfg, rng)
-    return _build(f"cfg{cfg}_{c['name']}", lq, lk, c["hq"], c["dtype"], c["width"],
+    return _build(c["name"], lq, lk, c["hq"], c["dtype"], c["width"],
                   c["step"], c["scale"], rng)
 
 
@@ -211,7 +211,7 @@ def make_gqa_variant(index: int, trial: int = 0) -> Workload:
     b = CONFIGS[c["base"]]
     rng = np.random.default_rng([c["base"], trial])
     lq, lk = draw_lengths(c["base"], rng)
-    return _build(f"cfg{index}_{c['name']}", lq, lk, b["hq"], b["dtype"], c["width"], c["step"],
+    return _build(c["name"], lq, lk, b["hq"], b["dtype"], c["width"], c["step"],
                   b["scale"], rng, hkv=c["hkv"], head_dim=c["head_dim"])
 
 
