@@ -181,19 +181,43 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   // capped and biased logits (log2 units) of key block kb of the step at
   // kbase; masked: keys past Lk get -inf (only a partial last step needs it,
   // the compare and select cost a VALU pair per logit)
-  auto logits = [&](int kb, int kbase, auto masked) {
+  // near: the step holds keys on both sides of some row's centre; otherwise
+  // (every key at or before every centre of the wave) the distance is
+  // cb - jl >= 0 and the bias slope2 jl - slope2 cb + negm takes one FMA
+  // per logit instead of a subtraction and an FMA.  The two forms differ by
+  // the rounding of slope2 cb, below 2^-23 (150 + 64 slope2) for any logit
+  // whose weight does not underflow.
+  auto logits = [&](int kb, int kbase, auto masked, auto near) {
     const float cb = cb0 - (float)kbase;
+    const float cl = __builtin_fmaf(-slope2, cb, negm);
     const int kleft = whi - kbase - 4 * g;         // keys of this lane group still in range
     const int kfrom = wlo - kbase - 4 * g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+      // (the order of the two only steers the register allocator: cap first
+      // spills least in the dropout instances, bias first runs fastest in
+      // the others)
+      float rc = 0.0f, bias;
+      auto bias_of = [&]() {
+        return decltype(near)::value
+                   ? __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), negm)
+                   : __builtin_fmaf(slope2, (float)jl, cl);
+      };
+      if (DROP) {
+        if (CAP) rc = cap_r(S[kb][r], a.lc);
+        bias = bias_of();
+      } else {
+        bias = bias_of();
+        if (CAP) rc = cap_r(S[kb][r], a.lc);
+      }
       float x;
       if (CAP)
-        x = __builtin_fmaf(a.lc.t_mul, cap_r(S[kb][r], a.lc),
-                           __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), negm));
-      else
+        x = __builtin_fmaf(a.lc.t_mul, rc, bias);
+      else if (decltype(near)::value)
         x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
+      else
+        x = __builtin_fmaf(S[kb][r], a.lc.s_lin, bias);
       if (WIN) x = jl >= kfrom && jl < kleft ? x : -__builtin_inff();
       else if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
       S[kb][r] = x;
@@ -278,48 +302,110 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   const int kfull = min(khi, nfull);
   constexpr Flag<false> unmasked{};
   constexpr Flag<true> masked{};
+  // far steps [klo, kfar): every key lies at or before every clamped centre
+  // of the wave's rows (see logits); they come first, then the near ones.
+  // (With dropout every step takes the general form: the dropout variant is
+  // already short of registers and a second loop body pushes it to spill.)
+  int kfar = klo;
+  if (!DROP) {
+    int cmin = max(ti + Lk - Lq, 0);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) cmin = min(cmin, __shfl_xor(cmin, o, 64));
+    kfar = min(kfull, (__builtin_amdgcn_readfirstlane(cmin) + 1) / TILE_ROWS);
+  }
 
   if (CAP) {
     // The offset is fixed, so the two 32-key blocks of a step are independent.
     // Waves w and w + 4 share a SIMD; if both ran the same order they would
     // want the matrix core and the VALU at the same moments.  Wave w (lead)
     // takes a step as S0 S1 | logits/P 0 | PV0 | logits/P 1 | PV1; wave w + 4
-    // (lag) defers block 1 of each step into the next one: (logits/P 1 | PV1
-    // of the previous step) S0 S1 | logits/P 0 | PV0, so its VALU work falls on
-    // the lead wave's products and the other way round.  A deferred block reads
-    // the previous step's V tile, hence three LDS buffers.
+    // (lag) defers block 1 of each step into the next one: logits/P 1 of the
+    // previous step | S0 S1 | PV1 of the previous step | logits/P 0 | PV0, so
+    // its VALU work falls on the lead wave's products and the other way round.
+    // A deferred block reads the previous step's V tile, hence three LDS
+    // buffers.
     auto run = [&](auto lag) {
       constexpr bool LAG = decltype(lag)::value;
-      auto step = [&](int kt, auto mk) {
+      // DEF: the step opens with block 1 of the previous (full) step
+      // NEAR: the general distance form (see logits); a far step's deferred
+      // block belongs to an earlier, also far, step
+      auto step = [&](int kt, auto mk, auto def, auto nr) {
+        constexpr bool DEF = decltype(def)::value;
         const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
-        if (LAG && kt > klo) {   // the previous step is a full one
-          logits(1, kbase - TILE_ROWS, unmasked);
+        if (DEF) {
+          logits(1, kbase - TILE_ROWS, unmasked, nr);
           probs(1, kbase - TILE_ROWS);
-          pv(1, sm.v[(kt - 1) % FWD_NBUF]);
         }
         scores(0, sm.k[buf]);
         scores(1, sm.k[buf]);
-        logits(0, kbase, mk);
+        if (DEF) pv(1, sm.v[(kt - 1) % FWD_NBUF]);
+        logits(0, kbase, mk, nr);
         probs(0, kbase);
         pv(0, sm.v[buf]);
         if (!LAG) {
-          logits(1, kbase, mk);
+          logits(1, kbase, mk, nr);
           probs(1, kbase);
           pv(1, sm.v[buf]);
         }
       };
-      for (int kt = klo; kt < kfull; ++kt) {
-        advance(kt);
-        step(kt, unmasked);
+      // block 1 of step kt - 1, on its own
+      auto deferred = [&](int kt) {
+        logits(1, (kt - 1) * TILE_ROWS, unmasked, Flag<true>{});
+        probs(1, (kt - 1) * TILE_ROWS);
+        pv(1, sm.v[(kt - 1) % FWD_NBUF]);
+      };
+      int kt = klo;
+      if (DROP) {   // one loop body (this variant is short of registers)
+        auto step1 = [&](int kt, auto mk) {
+          const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
+          if (LAG && kt > klo) {   // the previous step is a full one
+            logits(1, kbase - TILE_ROWS, unmasked, Flag<true>{});
+            probs(1, kbase - TILE_ROWS);
+            pv(1, sm.v[(kt - 1) % FWD_NBUF]);
+          }
+          scores(0, sm.k[buf]);
+          scores(1, sm.k[buf]);
+          logits(0, kbase, mk, Flag<true>{});
+          probs(0, kbase);
+          pv(0, sm.v[buf]);
+          if (!LAG) {
+            logits(1, kbase, mk, Flag<true>{});
+            probs(1, kbase);
+            pv(1, sm.v[buf]);
+          }
+        };
+        for (; kt < kfull; ++kt) {
+          advance(kt);
+          step1(kt, unmasked);
+        }
+        if (partial) {
+          advance(nfull);
+          step1(nfull, masked);
+        }
+      } else {
+        if (LAG && kt < kfull) {   // the first step defers nothing yet
+          advance(kt);
+          step(kt, unmasked, Flag<false>{}, Flag<true>{});
+          ++kt;
+        }
+        for (; kt < kfar; ++kt) {
+          advance(kt);
+          step(kt, unmasked, Flag<LAG>{}, Flag<false>{});
+        }
+        for (; kt < kfull; ++kt) {
+          advance(kt);
+          step(kt, unmasked, Flag<LAG>{}, Flag<true>{});
+        }
       }
-      if (partial) {
+      if (!DROP && partial) {
         advance(nfull);
-        step(nfull, masked);
+        if (LAG && nfull > klo) deferred(nfull);
+        step(nfull, masked, Flag<false>{}, Flag<true>{});
       }
       if (LAG && klo < khi) {   // block 1 of the last step
         const int kt = khi - 1;
-        if (partial) logits(1, kt * TILE_ROWS, masked);
-        else logits(1, kt * TILE_ROWS, unmasked);
+        if (partial) logits(1, kt * TILE_ROWS, masked, Flag<true>{});
+        else logits(1, kt * TILE_ROWS, unmasked, Flag<true>{});
         probs(1, kt * TILE_ROWS);
         pv(1, sm.v[kt % FWD_NBUF]);
       }
@@ -328,12 +414,12 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
     else run(Flag<true>{});
   } else {
     // running maximum over both blocks of a step, then rescale
-    auto step = [&](int kt, auto mk) {
+    auto step = [&](int kt, auto mk, auto nr) {
       const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
       scores(0, sm.k[buf]);
       scores(1, sm.k[buf]);
-      logits(0, kbase, mk);
-      logits(1, kbase, mk);
+      logits(0, kbase, mk, nr);
+      logits(1, kbase, mk, nr);
       float tmax = -__builtin_inff();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -358,13 +444,19 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
       pv(0, sm.v[buf]);
       pv(1, sm.v[buf]);
     };
-    for (int kt = klo; kt < kfull; ++kt) {
+    int kt = klo;
+    if (!DROP)
+      for (; kt < kfar; ++kt) {
+        advance(kt);
+        step(kt, unmasked, Flag<false>{});
+      }
+    for (; kt < kfull; ++kt) {
       advance(kt);
-      step(kt, unmasked);
+      step(kt, unmasked, Flag<true>{});
     }
     if (partial) {
       advance(nfull);
-      step(nfull, masked);
+      step(nfull, masked, Flag<true>{});
     }
   }
 
@@ -715,12 +807,24 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
   return n;   // valid in wave 0; the caller broadcasts it
 }
 
+// Seat of worker workgroup j (1 <= j < G) at the snake's table: the workers
+// of XCD 0 first, then those of XCD 1, and so on.  Workgroup j runs on XCD
+// j % 8 (the dispatcher deals workgroups round robin), so the consecutive
+// ranks of a round (the row tiles of one sequence sit next to each other in
+// the ranking) go to one XCD and share its L2 for their K and V rows.
+__device__ __forceinline__ int worker_seat(int j, int G) {
+  const int x = j & 7;
+  int before = 0;   // workers j' >= 1 with j' % 8 < x
+  for (int y = 0; y < x; ++y) before += (y < G ? (G - y + 7) / 8 : 0) - (y == 0 ? 1 : 0);
+  return before + (j >> 3) - (x == 0 ? 1 : 0);
+}
+
 // Grid: workgroup 0 runs the planner (then, in the full-VJP call, the dK/dV
 // unit plan); workgroups 1 .. P (one per remaining compute unit) are
 // persistent and deal the row tiles among themselves like cards in a snake:
-// in round r workgroup w takes rank r P + w (r even) or r P + P - 1 - w (r
-// odd), so a workgroup whose first tile was among the longest takes one of
-// the shortest next.  The row tiles never wait for the planner: a workgroup
+// in round r the worker at seat w (worker_seat) takes rank r P + w (r even)
+// or r P + P - 1 - w (r odd), so a workgroup whose first tile was among the
+// longest takes one of the shortest next.  The row tiles never wait for the planner: a workgroup
 // finds each tile and its key-step range from cu_q / cu_k itself (the order
 // table, tile_key_range), so the planner runs beside them.
 // LDS of the forward grid: the key-step buffers of the row tiles, or the
@@ -749,7 +853,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     }
     return;
   }
-  const int w = (int)blockIdx.x - 1, P = (int)gridDim.x - 1;
+  const int w = worker_seat((int)blockIdx.x, (int)gridDim.x), P = (int)gridDim.x - 1;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   build_fwd_order<ROW_THREADS>(pa, ord);

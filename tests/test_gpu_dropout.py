@@ -121,7 +121,10 @@ def test_dropout_with_masks_and_no_cap(causal, wl_, wr, softcap):
 
 def test_per_row_rates():
     """Per-row rates [Tq, Hq] (zero on every third row), against the oracle;
-    rows with rate 0 equal the undropped call bitwise in out and lse."""
+    rows with rate 0 match the undropped call to rounding: the undropped
+    forward forms the ALiBi bias of key steps wholly before every centre of
+    a wave as slope2 j + const, the dropout forward always as
+    -slope2 |c - j| (the same value up to one rounding of slope2 c)."""
     need_gpu()
     wl = W.custom_workload(lq=[37, 130], lk=[300, 90], hq=16, dtype="f16", width=176, step=2,
                            seed=13)
@@ -138,8 +141,14 @@ def test_per_row_rates():
             assert_close(name, to_np(got[name]), ref[name], tol, f"rates ds={store_ds}")
         assert_lse(to_np(got["lse"]), ref["lse"], "rates")
     plain = _call(g, 0.0, 0)
-    assert torch.equal(got["out"][::3], plain["out"][::3])
-    assert torch.equal(got["lse"], plain["lse"])
+    x, y = got["out"][::3].float(), plain["out"][::3].float()
+    ulp = torch.finfo(plain["out"].dtype).eps
+    assert ((x - y).abs() <= 2 * ulp * y.abs() + 2.0 ** -24).all()
+    # L is that of the undropped weights on every row
+    lx, ly = got["lse"].float(), plain["lse"].float()
+    fin = torch.isfinite(ly)
+    assert torch.equal(torch.isfinite(lx), fin)
+    assert ((lx - ly)[fin].abs() <= 1e-5 * (1.0 + ly[fin].abs())).all()
 
 
 def test_same_mask_whatever_the_schedule():
