@@ -64,6 +64,25 @@ def measured_traffic(kernel: str, workload: str):
     return float(m.group(1))
 
 
+def measured_busy(kernel: str, workload: str):
+    """Per-unit busy fractions of a kernel (MFMA, VALU, their co-issue, LDS)
+    from the committed SQ counter summary, or None when it is missing or the
+    kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"sq_counters_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    d = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m = re.search(rf"busy {kernel}: mfma=([0-9.]+) valu=([0-9.]+) coissue=([0-9.]+) lds=([0-9.]+)"
+                  rf" clock_mhz=([0-9.]+)", text)
+    if not m or not d or d.group(1) != kernel_source_digest():
+        return None
+    keys = ("mfma", "valu", "coissue", "lds")
+    out = {k: float(v) for k, v in zip(keys, m.groups()[:4])}
+    out["clock_mhz"] = float(m.group(5))
+    return out
+
+
 def cpu_baseline(wl, seconds: float):
     """The float64 oracle, unchanged, on the first sequences of the workload
     until about `seconds` of CPU time."""
@@ -233,6 +252,12 @@ def main():
     achieved = PHASE_FLOPS[dom] * elems * wl.head_dim / (phase_ms[dom] * 1e-3) / 1e12
     kernel_names = {"fwd": "fwd_kernel", "dkdv": "dkdv_kernel", "dq": "dq_kernel"}
     traffic = measured_traffic(kernel_names[dom], wl.name)
+    busy = measured_busy(kernel_names[dom], wl.name)
+    # what holds the kernel below the MFMA roof, from its SQ counters: the
+    # unit with the larger busy share (the two overlap only by `coissue`)
+    limiter = None
+    if busy is not None:
+        limiter = "valu" if busy["valu"] > busy["mfma"] else "mfma"
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -268,6 +293,8 @@ def main():
             "frac": round(achieved / MFMA_PEAK_TFLOPS, 5),
             "achieved_executed": round(achieved * frac, 3),
             "traffic": traffic,
+            "limiter": limiter,
+            "busy": busy,
         },
     }
     if not args.no_cpu_baseline:
