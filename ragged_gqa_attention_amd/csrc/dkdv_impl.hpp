@@ -526,9 +526,18 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
   const int sh = G % 8 == 0 ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
   const long long w0 = (long long)sh * W / G;
   const long long w1 = (long long)(sh + 1) * W / G;
-  int gt = a.plan.wg_first[sh];
-  if (w0 >= w1 || gt < 0) return;
-  for (long long w = w0; w < w1 && gt < nkt; ++gt) {
+  const int gt0 = a.plan.wg_first[sh];
+  if (w0 >= w1 || gt0 < 0) return;
+  // Segments in three passes over the share's key tiles: its whole key tiles,
+  // then the head of its last one, then the tail of its first one.  Every
+  // share thus starts at the first row of a key tile, and since the shares of
+  // an XCD hold neighbouring key tiles of the same sequences, its workgroups
+  // walk the same Q / dO rows at about the same time and read them through
+  // the XCD's L2 (a share that opened with the tail of a key tile would sit
+  // at an arbitrary row).  Which segment lands in which partial slot does not
+  // change, so neither does any result.
+  for (int pass = 0; pass < 3; ++pass)
+  for (long long w = w0, gt = gt0; w < w1 && gt < nkt; ++gt) {
     // lane and wave are re-derived per segment behind an empty asm, so the
     // compiler cannot keep the segment's lane-constant offsets live across
     // segments (that pushes the pipeline into scratch)
@@ -541,6 +550,8 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
     if (V == 0 || vs + V <= w) continue;       // nothing of this key tile left
     const long long f = max(w, vs) - vs, l = min(w1, vs + V) - vs;
     if (f >= l) break;   // the share ends among the key tile's segment items
+    w = vs + l;
+    if ((f > 0 ? 2 : (l < V ? 1 : 0)) != pass) continue;   // whole, head, tail
     const int ktile = e[KV_KTILE];
     KvUnit u;
     u.q0 = e[KV_Q0];
@@ -572,7 +583,6 @@ __global__ __launch_bounds__(KV_THREADS, 1) void dkdv_kernel(const AttnArgs a) {
       if (wave & 1) dkdv_wave<T, D, CAP, 1, true, WIN, DROP>(a, sm, u, wave, lane);
       else dkdv_wave<T, D, CAP, 0, true, WIN, DROP>(a, sm, u, wave, lane);
     }
-    w = vs + l;
     __syncthreads();   // the next segment reuses the LDS buffers
   }
 }
