@@ -593,6 +593,7 @@ struct FwdOrder {
   int start[FWD_ORDER_MAX + 1];   // first rank of entry k; start[n] = nrt
   int seq[FWD_ORDER_MAX], q0[FWD_ORDER_MAX], lq[FWD_ORDER_MAX], k0[FWD_ORDER_MAX],
       lk[FWD_ORDER_MAX];
+  int lqv[64], lkv[64];   // query / key lengths by plan sequence (up to 64 of them)
   int part[16];   // block scan partials
 };
 
@@ -626,6 +627,8 @@ __device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& or
         ord.lq[rank] = lq;
         ord.k0[rank] = e.ck;
         ord.lk[rank] = lk;
+        ord.lqv[b] = lq;
+        ord.lkv[b] = lk;
       }
       if (lane == 0) {
         ord.start[B] = total;
@@ -669,8 +672,11 @@ constexpr int LPT_MAX_HEADS = 4096;
 constexpr int LPT_MAX_TILES = 2048;
 constexpr int LPT_CLASSES = 1024;   // key steps (longer tiles share class 0)
 constexpr int FWD_LIST_MAX = 16;    // tiles one workgroup resolves in advance
+constexpr int LPT_SPER = LPT_MAX_HEADS / ROW_THREADS;   // slopes per thread
 struct LptScratch {
-  int hw[LPT_MAX_HEADS];          // key half-width of (table entry, head)
+  int hlo[LPT_MAX_HEADS];         // key-step range of every token of (plan sequence, head)
+  int hhi[LPT_MAX_HEADS];
+  int hw[LPT_MAX_HEADS];          // key half-width of (plan sequence, head)
   int cls[LPT_MAX_TILES];         // class of tile t (t: rank in table order)
   int ks[LPT_MAX_TILES][2];       // key-step range of tile t
   int hist[LPT_CLASSES];
@@ -680,37 +686,52 @@ struct LptScratch {
 // Fills list[i] = {b, tile, q0, lq, k0, lk, klo, khi} for the workgroup's
 // ranks r < nrt (round i of the snake); returns their count, or -1 when the
 // batch does not qualify (the caller then finds each tile itself).
+// Whether lpt_list ranks this batch (its scratch holds every (plan sequence,
+// head) and every tile), and its slopes, requested by the caller before the
+// sequence table so that the two loads overlap: thread tid holds (plan
+// sequence, head) pairs tid, tid + NT, ... in plan-sequence order.
+__device__ __forceinline__ bool lpt_fits(const PlanArgs& pa) {
+  return pa.batch <= 64 && pa.batch * pa.hq <= LPT_MAX_HEADS;
+}
+template <int NT>
+__device__ __forceinline__ void lpt_load_slopes(const PlanArgs& pa, float (&sv)[LPT_SPER]) {
+  const int hq = pa.hq, n = pa.batch * hq;
+#pragma unroll
+  for (int i = 0; i < LPT_SPER; ++i) {
+    const int p = (int)threadIdx.x + i * NT;
+    sv[i] = 0.0f;
+    if (i * NT < n && p < n) {
+      const int v = p / hq;
+      sv[i] = pa.slopes[slope_base(v, pa.hkv, hq, pa.slopes_stride) + (p - v * hq)];
+    }
+  }
+}
+
 template <int NT>
 __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord, LptScratch& sc,
-                                        int (*list)[8], int w, int P) {
+                                        int (*list)[8], int w, int P,
+                                        const float (&sv)[LPT_SPER]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int B = pa.batch, hq = pa.hq, nrt = ord.nrt;
-  if (B > 64 || B * hq > LPT_MAX_HEADS || nrt > LPT_MAX_TILES) return -1;
+  if (!lpt_fits(pa) || nrt > LPT_MAX_TILES) return -1;
   // rounds of the snake; a workgroup's ranks grow from round to round, so it
   // stops at its first rank past the last tile
   const int rounds = (nrt + P - 1) / P;
   if (rounds > FWD_LIST_MAX) return -1;
-  // half-widths of every (table entry k, head h), all slope loads in flight
-  constexpr int SPER = LPT_MAX_HEADS / NT;
-  float sv[SPER];
-  {
-    int k = tid / hq, h = tid - (tid / hq) * hq;
-    const int dk = NT / hq, dh = NT - (NT / hq) * hq;
-#pragma unroll
-    for (int i = 0; i < SPER; ++i) {
-      if (i * NT < B * hq)   // uniform
-        sv[i] = pa.slopes[slope_base(ord.seq[min(k, B - 1)], pa.hkv, hq, pa.slopes_stride) + h];
-      k += dk;
-      h += dh;
-      if (h >= hq) { h -= hq; ++k; }
-    }
-  }
+  // half-width and whole-head key-step range of every (plan sequence, head)
   for (int c = tid; c < LPT_CLASSES; c += NT) sc.hist[c] = 0;
 #pragma unroll
-  for (int i = 0; i < SPER; ++i) {
+  for (int i = 0; i < LPT_SPER; ++i) {
     const int p = tid + i * NT;
-    if (i * NT < B * hq && p < B * hq)
-      sc.hw[p] = key_half_width(sv[i] * LOG2E, ord.lk[p / hq], pa.skip_log2);
+    if (i * NT < B * hq && p < B * hq) {
+      const int v = p / hq, lq = ord.lqv[v], lk = ord.lkv[v];
+      const int hw = key_half_width(sv[i] * LOG2E, lk, pa.skip_log2);
+      sc.hw[p] = hw;
+      int l = 0x7fffffff, u = 0;
+      if (lq > 0) token_range_steps(0, lq - 1, lq, lk, hw, pa.win_left, pa.win_right, l, u);
+      sc.hlo[p] = l;
+      sc.hhi[p] = u;
+    }
   }
   __syncthreads();
   auto entry_of = [&](int t) {   // last table entry whose first rank is <= t
@@ -724,15 +745,22 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
   for (int t = tid; t < nrt; t += NT) {   // tile_key_steps of every tile
     const int k = entry_of(t);
     const int lq = ord.lq[k], lk = ord.lk[k];
+    const int hbase = ord.seq[k] * hq;
     const int R0 = (t - ord.start[k]) * ROW_TILE, R1 = min(lq * hq, R0 + ROW_TILE);
     const int hfirst = R0 / lq, hlast = (R1 - 1) / lq;
     int lo = 0x7fffffff, hi = 0;
+    // the first and last heads may hold part of their tokens; the ones
+    // between hold all of them (the whole-head range)
     for (int h = hfirst; h <= hlast; ++h) {
-      const int ia = h == hfirst ? R0 - h * lq : 0;
-      const int ib = h == hlast ? R1 - 1 - h * lq : lq - 1;
-      const int hw = sc.hw[k * hq + h];
       int l, u;
-      token_range_steps(ia, ib, lq, lk, hw, pa.win_left, pa.win_right, l, u);
+      if (h == hfirst || h == hlast) {
+        const int ia = h == hfirst ? R0 - h * lq : 0;
+        const int ib = h == hlast ? R1 - 1 - h * lq : lq - 1;
+        token_range_steps(ia, ib, lq, lk, sc.hw[hbase + h], pa.win_left, pa.win_right, l, u);
+      } else {
+        l = sc.hlo[hbase + h];
+        u = sc.hhi[hbase + h];
+      }
       if (l < u) {
         lo = min(lo, l);
         hi = max(hi, u);
@@ -765,46 +793,47 @@ __device__ __forceinline__ int lpt_list(const PlanArgs& pa, const FwdOrder& ord,
     if (lane == 63) sc.off[LPT_CLASSES] = run;
   }
   __syncthreads();
-  // wave 0 resolves the workgroup's ranks: class c of rank r (last class with
-  // off <= r), then the (r - off[c])-th tile of class c in table order
-  int n = 0;
-  if (wave == 0) {
-    for (int round = 0; round < rounds; ++round) {
-      const int r = round * P + ((round & 1) ? P - 1 - w : w);
-      if (r >= nrt) break;
-      int lo = 0, hi = LPT_CLASSES - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sc.off[mid] <= r) lo = mid; else hi = mid - 1;
+  // each wave resolves some of the workgroup's ranks (round i falls to wave
+  // i % 8): the class c of rank r is the last class with off <= r (a search
+  // over 64 and then 16 offsets, each one ballot), then the tile is the
+  // (r - off[c])-th of class c in table order
+  int n = 0;   // rounds whose rank lies below nrt (a prefix: ranks grow)
+  for (int round = 0; round < rounds; ++round)
+    if (round * P + ((round & 1) ? P - 1 - w : w) < nrt) n = round + 1;
+  for (int round = wave; round < n; round += NT / 64) {
+    const int r = round * P + ((round & 1) ? P - 1 - w : w);
+    constexpr int CPL = LPT_CLASSES / 64;
+    const uint64_t b1 = __ballot(sc.off[lane * CPL] <= r);   // lane 0's offset is 0
+    const int L = 63 - __builtin_clzll(b1);
+    const uint64_t b2 = __ballot(lane < CPL && sc.off[L * CPL + min(lane, CPL - 1)] <= r);
+    const int c = L * CPL + (63 - __builtin_clzll(b2));
+    int want = r - sc.off[c], t = -1;
+    for (int base = 0; base < nrt && t < 0; base += 64) {
+      const uint64_t m = __ballot(base + lane < nrt && sc.cls[base + lane] == c);
+      const int cnt = __popcll(m);
+      if (want < cnt) {
+        uint64_t mm = m;
+        for (int i = 0; i < want; ++i) mm &= mm - 1;   // drop the lowest want bits
+        t = base + __builtin_ctzll(mm);
+      } else {
+        want -= cnt;
       }
-      const int c = lo;
-      int want = r - sc.off[c], t = -1;
-      for (int base = 0; base < nrt && t < 0; base += 64) {
-        const uint64_t m = __ballot(base + lane < nrt && sc.cls[base + lane] == c);
-        const int cnt = __popcll(m);
-        if (want < cnt) {
-          uint64_t mm = m;
-          for (int i = 0; i < want; ++i) mm &= mm - 1;   // drop the lowest want bits
-          t = base + __builtin_ctzll(mm);
-        } else {
-          want -= cnt;
-        }
-      }
-      const int k = entry_of(t);
-      if (lane == 0) {
-        list[n][0] = ord.seq[k];
-        list[n][1] = t - ord.start[k];
-        list[n][2] = ord.q0[k];
-        list[n][3] = ord.lq[k];
-        list[n][4] = ord.k0[k];
-        list[n][5] = ord.lk[k];
-        list[n][6] = sc.ks[t][0];
-        list[n][7] = sc.ks[t][1];
-      }
-      ++n;
+    }
+    // table entry of tile t: the last with start <= t
+    const uint64_t be = __ballot(lane < B && ord.start[min(lane, B - 1)] <= t);
+    const int k = 63 - __builtin_clzll(be);
+    if (lane == 0) {
+      list[round][0] = ord.seq[k];
+      list[round][1] = t - ord.start[k];
+      list[round][2] = ord.q0[k];
+      list[round][3] = ord.lq[k];
+      list[round][4] = ord.k0[k];
+      list[round][5] = ord.lk[k];
+      list[round][6] = sc.ks[t][0];
+      list[round][7] = sc.ks[t][1];
     }
   }
-  return n;   // valid in wave 0; the caller broadcasts it
+  return n;   // the same in every thread; list[] is complete after a barrier
 }
 
 // Seat of worker workgroup j (1 <= j < G) at the snake's table: the workers
@@ -856,6 +885,8 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   const int w = worker_seat((int)blockIdx.x, (int)gridDim.x), P = (int)gridDim.x - 1;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  float sv[LPT_SPER];
+  if (lpt_fits(pa)) lpt_load_slopes<ROW_THREADS>(pa, sv);
   build_fwd_order<ROW_THREADS>(pa, ord);
   const int status = ord.status;
   if (status == 0) return;
@@ -863,7 +894,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   __shared__ int list[FWD_LIST_MAX][8];
   __shared__ int nlist_s;
   if (status == 1) {
-    const int n = lpt_list<ROW_THREADS>(pa, ord, smu.l, list, w, P);
+    const int n = lpt_list<ROW_THREADS>(pa, ord, smu.l, list, w, P, sv);
     if (threadIdx.x == 0) nlist_s = n;
   } else if (threadIdx.x == 0) {
     nlist_s = -1;
