@@ -149,6 +149,8 @@ def main():
     ap.add_argument("--dropout-p", type=float, default=0.0,
                     help="counter-based dropout rate (0 = none, the configurations' setting)")
     ap.add_argument("--dropout-seed", type=int, default=1234)
+    ap.add_argument("--recompute-ds", action="store_true",
+                    help="dQ rebuilds dS instead of reading the dK/dV kernel's stored images")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     args = ap.parse_args()
@@ -174,7 +176,7 @@ def main():
     wl = make_workload(args.config, args.trial)
     g = wl.to(dev)
     call = rga.FullVJP(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout, softcap=g.softcap,
-                       scale_multiplier=g.scale_multiplier, store_ds=True,
+                       scale_multiplier=g.scale_multiplier, store_ds=not args.recompute_ds,
                        causal=args.causal, window_left=args.window[0],
                        window_right=args.window[1],
                        dropout_p=args.dropout_p, dropout_seed=args.dropout_seed)
@@ -278,6 +280,7 @@ def main():
             "view": f"feature width {wl.width}, token step {wl.step}",
             "softcap": wl.softcap, "scale_multiplier": wl.scale_multiplier,
             "dropout_p": args.dropout_p, "causal": args.causal, "window": list(args.window),
+            "stored_ds": not args.recompute_ds,
         },
         "pct_mfma_peak": round(100.0 * value / MFMA_PEAK_TFLOPS, 3),
         "ms_per_call_median": round(float(np.median(per_call)), 4),
