@@ -50,8 +50,9 @@
 namespace rga {
 
 // LDS of a key step: the K and V rows (row tiles, blk_off), three buffers
-// (one step in flight, one being read, and the previous one still read by the
-// deferred half of the lag waves).
+// (one step in flight, one being read, and, with dropout, the previous one
+// still read by the deferred half of waves 4-7; the O staging of the
+// epilogue needs their room in any case).
 constexpr int FWD_NBUF = 3;
 template <int D>
 struct FwdShared {
@@ -315,92 +316,52 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   }
 
   if (CAP) {
-    // The offset is fixed, so the two 32-key blocks of a step are independent.
-    // Waves w and w + 4 share a SIMD; if both ran the same order they would
-    // want the matrix core and the VALU at the same moments.  Wave w (lead)
-    // takes a step as S0 S1 | logits/P 0 | PV0 | logits/P 1 | PV1; wave w + 4
-    // (lag) defers block 1 of each step into the next one: logits/P 1 of the
-    // previous step | S0 S1 | PV1 of the previous step | logits/P 0 | PV0, so
-    // its VALU work falls on the lead wave's products and the other way round.
-    // A deferred block reads the previous step's V tile, hence three LDS
-    // buffers.
-    auto run = [&](auto lag) {
+    // The offset is fixed, so the two 32-key blocks of a step are
+    // independent: every wave takes a step as S0 S1 | logits/P 0 | PV0 |
+    // logits/P 1 | PV1.  (Offsetting the two waves of a SIMD, one of them
+    // deferring block 1 of each step into the next, measured 1.5 % slower.)
+    auto step = [&](int kt, auto mk, auto nr) {
+      const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
+      scores(0, sm.k[buf]);
+      scores(1, sm.k[buf]);
+      logits(0, kbase, mk, nr);
+      probs(0, kbase);
+      pv(0, sm.v[buf]);
+      logits(1, kbase, mk, nr);
+      probs(1, kbase);
+      pv(1, sm.v[buf]);
+    };
+    // With dropout, waves w and w + 4 (one SIMD) run offset instead: wave
+    // w + 4 defers block 1 of each step into the next (it reads the previous
+    // step's V tile, hence three LDS buffers); under the dropout variant's
+    // register pressure that order spills least.
+    auto run_drop = [&](auto lag) {
       constexpr bool LAG = decltype(lag)::value;
-      // DEF: the step opens with block 1 of the previous (full) step
-      // NEAR: the general distance form (see logits); a far step's deferred
-      // block belongs to an earlier, also far, step
-      auto step = [&](int kt, auto mk, auto def, auto nr) {
-        constexpr bool DEF = decltype(def)::value;
+      auto step1 = [&](int kt, auto mk) {
         const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
-        if (DEF) {
-          logits(1, kbase - TILE_ROWS, unmasked, nr);
+        if (LAG && kt > klo) {   // the previous step is a full one
+          logits(1, kbase - TILE_ROWS, Flag<WIN>{}, Flag<true>{});
           probs(1, kbase - TILE_ROWS);
+          pv(1, sm.v[(kt - 1) % FWD_NBUF]);
         }
         scores(0, sm.k[buf]);
         scores(1, sm.k[buf]);
-        if (DEF) pv(1, sm.v[(kt - 1) % FWD_NBUF]);
-        logits(0, kbase, mk, nr);
+        logits(0, kbase, mk, Flag<true>{});
         probs(0, kbase);
         pv(0, sm.v[buf]);
         if (!LAG) {
-          logits(1, kbase, mk, nr);
+          logits(1, kbase, mk, Flag<true>{});
           probs(1, kbase);
           pv(1, sm.v[buf]);
         }
       };
-      // block 1 of step kt - 1, on its own
-      auto deferred = [&](int kt) {
-        logits(1, (kt - 1) * TILE_ROWS, unmasked, Flag<true>{});
-        probs(1, (kt - 1) * TILE_ROWS);
-        pv(1, sm.v[(kt - 1) % FWD_NBUF]);
-      };
-      int kt = klo;
-      if (DROP) {   // one loop body (this variant is short of registers)
-        auto step1 = [&](int kt, auto mk) {
-          const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
-          if (LAG && kt > klo) {   // the previous step is a full one
-            logits(1, kbase - TILE_ROWS, unmasked, Flag<true>{});
-            probs(1, kbase - TILE_ROWS);
-            pv(1, sm.v[(kt - 1) % FWD_NBUF]);
-          }
-          scores(0, sm.k[buf]);
-          scores(1, sm.k[buf]);
-          logits(0, kbase, mk, Flag<true>{});
-          probs(0, kbase);
-          pv(0, sm.v[buf]);
-          if (!LAG) {
-            logits(1, kbase, mk, Flag<true>{});
-            probs(1, kbase);
-            pv(1, sm.v[buf]);
-          }
-        };
-        for (; kt < kfull; ++kt) {
-          advance(kt);
-          step1(kt, unmasked);
-        }
-        if (partial) {
-          advance(nfull);
-          step1(nfull, masked);
-        }
-      } else {
-        if (LAG && kt < kfull) {   // the first step defers nothing yet
-          advance(kt);
-          step(kt, unmasked, Flag<false>{}, Flag<true>{});
-          ++kt;
-        }
-        for (; kt < kfar; ++kt) {
-          advance(kt);
-          step(kt, unmasked, Flag<LAG>{}, Flag<false>{});
-        }
-        for (; kt < kfull; ++kt) {
-          advance(kt);
-          step(kt, unmasked, Flag<LAG>{}, Flag<true>{});
-        }
+      for (int kt = klo; kt < kfull; ++kt) {
+        advance(kt);
+        step1(kt, unmasked);
       }
-      if (!DROP && partial) {
+      if (partial) {
         advance(nfull);
-        if (LAG && nfull > klo) deferred(nfull);
-        step(nfull, masked, Flag<false>{}, Flag<true>{});
+        step1(nfull, masked);
       }
       if (LAG && klo < khi) {   // block 1 of the last step
         const int kt = khi - 1;
@@ -410,8 +371,24 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
         pv(1, sm.v[kt % FWD_NBUF]);
       }
     };
-    if (wave < 4) run(Flag<false>{});
-    else run(Flag<true>{});
+    if (DROP) {
+      if (wave < 4) run_drop(Flag<false>{});
+      else run_drop(Flag<true>{});
+    } else {
+      int kt = klo;
+      for (; kt < kfar; ++kt) {
+        advance(kt);
+        step(kt, unmasked, Flag<false>{});
+      }
+      for (; kt < kfull; ++kt) {
+        advance(kt);
+        step(kt, unmasked, Flag<true>{});
+      }
+      if (partial) {
+        advance(nfull);
+        step(nfull, masked, Flag<true>{});
+      }
+    }
   } else {
     // running maximum over both blocks of a step, then rescale
     auto step = [&](int kt, auto mk, auto nr) {
