@@ -213,8 +213,8 @@ attn_status attn_varlen_full_vjp(const attn_problem* p,
 typedef enum {
   ATTN_PHASE_PLAN = 0,     /* separate planning launch: only for an empty batch (the
                               planner otherwise runs inside the forward's grid) */
-  ATTN_PHASE_FWD = 1,      /* forward: out, lse, delta = rowsum(dout * out), beside it the
-                              work lists from cu_q / cu_k and the transposed K tiles */
+  ATTN_PHASE_FWD = 1,      /* forward: out, lse, delta = rowsum(dout * out); its first
+                              workgroup plans the work lists from cu_q / cu_k */
   ATTN_PHASE_DKDV = 2,     /* dK, dV over all sharing heads */
   ATTN_PHASE_DQ = 3,       /* dQ, and the fixed-order sum of split dK / dV partials */
   ATTN_PHASES = 4
