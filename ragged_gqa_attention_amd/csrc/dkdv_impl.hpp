@@ -303,6 +303,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D, DROP>& 
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) gkey[kb] = SM_GAMMA * (uint64_t)(u.key0 + kb * 32 + l32);
 
+  // window bounds on j - c (an open side: beyond any distance)
+  const float wdlo = a.win_left >= 0 ? (float)-a.win_left : -3.0e38f;
+  const float wdhi = a.win_right >= 0 ? (float)a.win_right : 3.0e38f;
+
   // P and dS of the wave's half; the own product's half stays in `mine`, the
   // other goes to the partner through LDS slot `slot`.
   // P and dS of accumulator register r (row rbase + 8 (r/4) + r%4); with
@@ -311,19 +315,12 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D, DROP>& 
     const f32x4 ri = sm.rinfo[buf][rbase + (r >> 2) * 8 + (r & 3)];
     u32x4 dr = u32x4{0u, 0u, 0u, 0u};
     if (DROP) dr = sm.drec[buf][rbase + (r >> 2) * 8 + (r & 3)];
-    // WIN: the row keeps keys [wlo, whi] around its unclamped centre
-    float wlo = -3.0e38f, whi = 3.0e38f;
-    if (WIN) {
-      int tok, hd;
-      unfold_row(r0 + rbase + (r >> 2) * 8 + (r & 3), u.lq, (uint32_t)u.lqmul,
-                 (uint32_t)u.lqshift, tok, hd);
-      const int c = tok + u.Lk - u.lq;
-      if (a.win_left >= 0) wlo = (float)(c - a.win_left);
-      if (a.win_right >= 0) whi = (float)(c + a.win_right);
-    }
+    // WIN: the record holds the unclamped centre c (the bias takes the
+    // clamped one) and the row keeps keys j with j - c in [wdlo, wdhi]
+    const float cc = WIN ? __builtin_fmaxf(ri[1], 0.0f) : ri[1];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(ri[1] - keyf[kb]), ri[2]);
+      const float bias = __builtin_fmaf(-ri[0], __builtin_fabsf(cc - keyf[kb]), ri[2]);
       float p, w;
       if (CAP) {
         const float rc = cap_r(S[kb][r], a.lc);
@@ -333,7 +330,10 @@ __device__ __forceinline__ void dkdv_wave(const AttnArgs& a, KvShared<D, DROP>& 
         p = fast_exp2(__builtin_fmaf(S[kb][r], a.lc.s_lin, bias));
         w = 1.0f;
       }
-      if (WIN) p = keyf[kb] >= wlo && keyf[kb] <= whi ? p : 0.0f;
+      if (WIN) {
+        const float dj = keyf[kb] - ri[1];
+        p = dj >= wdlo && dj <= wdhi ? p : 0.0f;
+      }
       if (DROP) {
         const bool keep = sm_word_hi(drop_base(dr) + gkey[kb]) >= dr[2];
         const float sc = drop_scale_of(dr);

@@ -311,11 +311,12 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void dq_kernel(const AttnArgs a) {
     qf[ks] = load16(qrow + ks * 16);
     df[ks] = load16(dorow + ks * 16);
   }
-  // row record: slope * log2(e), clamped centre, -residual, Delta
+  // row record: slope * log2(e), centre (unclamped under a window), -residual,
+  // Delta
   const f32x4 info = Lk > 0 ? *reinterpret_cast<const f32x4*>(a.rowinfo + ri * 4)
                             : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const float slope2 = info[0];
-  const float cb0 = info[1] - (float)(4 * g);
+  const float cb0 = (WIN ? __builtin_fmaxf(info[1], 0.0f) : info[1]) - (float)(4 * g);
   const float boff = info[2];
   const float dl = info[3];
   // dropout record of the row: counter base (plus this lane's key offset

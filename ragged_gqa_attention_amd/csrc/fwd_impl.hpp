@@ -129,6 +129,17 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
   const int wc = ti + Lk - Lq;
   const int wlo = WIN && a.win_left >= 0 ? wc - a.win_left : 0;
   const int whi = WIN && a.win_right >= 0 ? min(Lk, wc + a.win_right + 1) : Lk;
+  // the wave's tightest bounds: blocks inside [wlo_max, whi_min) are unmasked
+  int wlo_max = wlo, whi_min = whi;
+  if (WIN) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      wlo_max = max(wlo_max, __shfl_xor(wlo_max, o, 64));
+      whi_min = min(whi_min, __shfl_xor(whi_min, o, 64));
+    }
+    wlo_max = __builtin_amdgcn_readfirstlane(wlo_max);
+    whi_min = __builtin_amdgcn_readfirstlane(whi_min);
+  }
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - ti);
   // log2 units, relative to moff.  With a cap, the largest exponent a kept key
   // can reach: 0 for slope >= 0 (the nearest kept key is the clamped centre
@@ -219,9 +230,20 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
         x = __builtin_fmaf(-slope2, __builtin_fabsf(cb - (float)jl), S[kb][r] * a.lc.s_lin);
       else
         x = __builtin_fmaf(S[kb][r], a.lc.s_lin, bias);
-      if (WIN) x = jl >= kfrom && jl < kleft ? x : -__builtin_inff();
-      else if (decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
+      if (!WIN && decltype(masked)::value) x = jl < kleft ? x : -__builtin_inff();
       S[kb][r] = x;
+    }
+    // WIN: only a block that some row's window cuts (or that reaches past
+    // Lk, where every window ends) pays for the per-logit test
+    if (WIN) {
+      const int j0 = kbase + kb * 32;
+      if (!(j0 >= wlo_max && j0 + 32 <= whi_min)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int jl = kb * 32 + (r >> 2) * 8 + (r & 3);
+          S[kb][r] = jl >= kfrom && jl < kleft ? S[kb][r] : -__builtin_inff();
+        }
+      }
     }
   };
   // P rounded to the input dtype feeds the PV product, and O is normalised by
@@ -481,7 +503,8 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
           u32x2{pack2<T>(O[db][rq * 4 + 0] * inv, O[db][rq * 4 + 1] * inv),
                 pack2<T>(O[db][rq * 4 + 2] * inv, O[db][rq * 4 + 3] * inv)};
   if (g == 0) {
-    sinfo[lrow] = f32x4{slope2, (float)max(ti + Lk - Lq, 0), lsum > 0.0f ? -res : 0.0f, 0.0f};
+    sinfo[lrow] = f32x4{slope2, (float)(WIN ? ti + Lk - Lq : max(ti + Lk - Lq, 0)),
+                        lsum > 0.0f ? -res : 0.0f, 0.0f};
     // the backward's dropout record of this row
     if (DELTA && DROP && row_ok)
       a.droprec[(int64_t)q0 * a.hq + (int64_t)hb * Lq + row] = drec;

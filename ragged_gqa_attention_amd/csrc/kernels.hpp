@@ -41,7 +41,9 @@ struct AttnArgs {
   float* lse;           // [total_q * hq], natural log
   // [total_q * hq] records of 4 floats, one per folded row (sequence b's rows
   // at q0(b) * hq + R, R = h * Lq + i), read by the backward:
-  //   slope * log2(e), clamped ALiBi centre max(i + Lk - Lq, 0),
+  //   slope * log2(e), the ALiBi centre i + Lk - Lq (clamped at 0, the centre
+  //   the bias measures from, unless a window or causal mask is set: then
+  //   unclamped, for the window test, and each reader clamps it),
   //   minus the base-2 log of the row's softmax sum relative to the row offset
   //   m_i (see fwd.hip), and Delta = rowsum(dout * out).
   float* rowinfo;

@@ -37,7 +37,8 @@ hipError_t launch_prep(const PlanArgs& pa, hipStream_t s) {
 
 // Row records for the backward entry that starts from a saved forward:
 // Delta = sum_d dout[row, d] * out[row, d] over the stored 16-bit output, the
-// slope in base-2 units, the clamped ALiBi centre and the base-2 residual of
+// slope in base-2 units, the ALiBi centre (clamped at 0 unless a window or
+// causal mask is set, whose test needs the unclamped one) and the base-2 residual of
 // the stored natural-log L relative to the row offset the forward used (see
 // fwd.hip).  Eight lanes share a row; each reads 16-byte chunks.
 template <class T, int D, bool CAP>
@@ -84,8 +85,9 @@ __global__ __launch_bounds__(WG_THREADS) void rowinfo_kernel(const AttnArgs a) {
   const float moff = (CAP ? a.lc.t_add : 0.0f) - slope2 * (float)max(0, Lq - Lk - i);
   const float L = a.lse[r];
   const float negres = Lk > 0 ? moff - L * LOG2E : 0.0f;
+  const bool win = a.win_left >= 0 || a.win_right >= 0;
   *reinterpret_cast<f32x4*>(a.rowinfo + fr * 4) =
-      f32x4{slope2, (float)max(i + Lk - Lq, 0), negres, acc};
+      f32x4{slope2, (float)(win ? i + Lk - Lq : max(i + Lk - Lq, 0)), negres, acc};
   if (a.drop_on) a.droprec[fr] = drop_row(a, lo, h, i, t);
 }
 
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(WG_THREADS) void ksteps_kernel(const AttnArgs a) {
     const f32x4 info = *reinterpret_cast<const f32x4*>(
         a.rowinfo + ((int64_t)sq[SQ_Q0] * a.hq + (int64_t)sq[SQ_HB] * sq[SQ_LQ] + R) * 4);
     slope2 = info[0];
-    centre = (int)info[1];
+    centre = max((int)info[1], 0);   // unclamped under a window
     const float radd = info[2];   // added to every exponent of the row
     if (a.skip_log2 > 0.0f && __builtin_isfinite(radd))
       thr = SKIP_UNDERFLOW + __builtin_fmaxf(radd, 0.0f);
