@@ -25,7 +25,7 @@ What is computed (sources are the pages' own words, restated):
   "Root causes addressed": the stored row statistic is L = m + log l
   (natural log); a row with no keys has L = -inf, output 0 and gradient 0.
 
-Readings taken where the pages are silent (each is listed in the design doc):
+Readings taken where the pages are silent:
   - ``softcap == 0`` means no cap (identity); the pages always use 3.
   - head_dim in the scale is the logical feature count D (160), never the
     padded buffer width.

@@ -5,7 +5,7 @@ Page "python-20261012-ragged-flash-attention-gradient-recompute", section
 splitmix64 hash of (seed, b, h, row, col), so the backward rebuilds exactly
 the forward's mask whatever the tiling, with one rate for everything or one
 per row.  The pages fix neither how the five values are combined nor how a
-word becomes a keep decision; the reading taken (also listed in the design doc):
+word becomes a keep decision; the reading taken:
 
 * splitmix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
   generators", 2014): from state x it returns mix64(x + n * gamma) as its
