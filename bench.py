@@ -17,6 +17,9 @@ longest average duration, timed by a loop of K calls (run just before the
 headline loop) with HIP events recorded on the library's stream before each
 phase; its `achieved` is credited FLOPs / duration, and `achieved_executed`
 scales it by the evaluated fraction (the matrix work the kernel really does).
+`kernels` puts each kernel against its own roof: the forward and dK/dV against
+the MFMA peak, dQ (which reads the stored dS images) against HBM, with the
+fabric bytes of the committed traffic summary when it matches the sources.
 `cpu_baseline` times the float64 oracle on a bounded sample of the same workload.
 """
 from __future__ import annotations
@@ -37,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fwd+full-VJP TFLOP/s (% MFMA peak) and ms/call, ragged GQA Hq=64 D=160"
 MFMA_PEAK_TFLOPS = 2500.0     # MI355X dense FP16/BF16 matrix peak
+HBM_PEAK_TBPS = 8.0           # MI355X HBM3E
 # credited flops per score element and head-dim unit, by phase (14 in total)
 PHASE_FLOPS = {"fwd": 4, "dkdv": 8, "dq": 2, "plan": 0}
 
@@ -62,6 +66,21 @@ def measured_traffic(kernel: str, workload: str):
     if not m or not d or d.group(1) != kernel_source_digest():
         return None
     return float(m.group(1))
+
+
+def measured_kernel_bytes(workload: str):
+    """Fabric bytes (read, written) per launch of each kernel from the committed
+    traffic summary, or None when it is missing or the kernels changed."""
+    path = os.path.join(ROOT, "profiles", f"dkdv_kernel_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    d = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    if not d or d.group(1) != kernel_source_digest():
+        return None
+    rows = re.findall(r"^\| `(\w+)<[^`]*>` \| [0-9.]+ \| [0-9.]+ \| ([0-9.]+) \| ([0-9.]+) \|",
+                      text, re.M)
+    return {k: (float(r) * 1e6, float(w) * 1e6) for k, r, w in rows} or None
 
 
 def measured_busy(kernel: str, workload: str):
@@ -260,6 +279,34 @@ def main():
     limiter = None
     if busy is not None:
         limiter = "valu" if busy["valu"] > busy["mfma"] else "mfma"
+    # every kernel against its own roof: the forward and dK/dV do far more
+    # matrix work per byte than the MI355X ridge (2500 TFLOP/s / 8 TB/s), dQ
+    # with stored dS does 2 D flops per 2-byte dS element read, below it
+    kbytes = measured_kernel_bytes(wl.name)
+    kernels = {}
+    for ph in ("fwd", "dkdv", "dq"):
+        name = kernel_names[ph]
+        t = phase_ms[ph] * 1e-3
+        tf = PHASE_FLOPS[ph] * elems * wl.head_dim / t / 1e12
+        e = {"ms": round(phase_ms[ph], 4), "credited_tflops": round(tf, 3),
+             "mfma_frac": round(tf / MFMA_PEAK_TFLOPS, 5)}
+        hbm = ph == "dq" and not args.recompute_ds
+        if kbytes and name in kbytes:
+            rd, wr = kbytes[name]
+            e["fabric_tbps"] = round((rd + wr) / t / 1e12, 3)
+            e["fabric_bytes"] = int(rd + wr)
+        elif hbm:
+            # algorithmic bytes: the dS images read (2 B per evaluated element)
+            # and dQ written
+            byts = 2.0 * elems * frac + 2.0 * wl.total_q * wl.hq * wl.head_dim
+            e["fabric_tbps"] = round(byts / t / 1e12, 3)
+            e["fabric_bytes"] = None
+        e["bound"] = "hbm" if hbm else "mfma"
+        if hbm:
+            e["frac"] = round(e["fabric_tbps"] / HBM_PEAK_TBPS, 5)
+        else:
+            e["frac"] = e["mfma_frac"]
+        kernels[name] = e
     line = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -299,6 +346,7 @@ def main():
             "limiter": limiter,
             "busy": busy,
         },
+        "kernels": kernels,
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
