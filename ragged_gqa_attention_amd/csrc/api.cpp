@@ -297,6 +297,16 @@ attn_status prologue(const attn_problem* p, int entry, void* ws, size_t ws_bytes
                           : (p->window_right < 0 ? -1
                                                  : (int)std::min<int64_t>(p->window_right,
                                                                           p->total_q));
+  // The forward ranks every row tile in LDS when the batch fits its limits
+  // (the row-tile bound L.row_tiles over-counts the tiles, so a batch that
+  // passes here always fits); otherwise it deals the tiles past its first
+  // round by ticket, and the ticket is reset before each forward launch.
+  const int64_t workers = std::max<int64_t>(1, L.kv_wgs - 1);
+  const bool ranked = pa.batch <= LPT_MAX_SEQS &&
+                      (int64_t)pa.batch * pa.hq <= LPT_MAX_HEADS &&
+                      L.row_tiles <= LPT_MAX_TILES &&
+                      ceil_div(L.row_tiles, workers) <= FWD_LIST_MAX;
+  a.fwd_ticket = ranked ? nullptr : a.plan.flag + 2;
   pa.seg_items = KV_SEGMENT_ITEMS;
   pa.win_left = a.win_left;
   pa.win_right = a.win_right;
@@ -393,6 +403,7 @@ attn_status full_vjp_impl(const attn_problem* p, const attn_tensor* q, const att
   } else {
     RGA_TRY(record(ev, ATTN_PHASE_PLAN, s));
     RGA_TRY(record(ev, ATTN_PHASE_FWD, s));
+    if (a.fwd_ticket) RGA_TRY(hip_status(launch_ticket_reset(a.fwd_ticket, s), "ticket reset"));
     RGA_TRY(hip_status(launch_fwd(a, pa, p->dtype, p->head_dim, p->softcap > 0.0f, true, s),
                        "forward launch"));
   }
@@ -471,6 +482,7 @@ attn_status attn_varlen_fwd(const attn_problem* p, const attn_tensor* q, const a
   a.lse = lse;
   // an empty batch still runs the planner (it records the cu_q / cu_k check)
   if (p->batch == 0) return launch_prep_phase(pa, a, L, s);
+  if (a.fwd_ticket) RGA_TRY(hip_status(launch_ticket_reset(a.fwd_ticket, s), "ticket reset"));
   return hip_status(launch_fwd(a, pa, p->dtype, p->head_dim, p->softcap > 0.0f, false, s),
                     "forward launch");
 }

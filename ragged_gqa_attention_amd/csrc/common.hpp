@@ -161,7 +161,8 @@ enum KvField {
 // Work lists built on the device; all arrays live in the caller's workspace.
 struct Plan {
   int* seq;        // [B * SEQ_FIELDS]
-  int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation
+  int* flag;       // [4]    [0] = 1 when cu_q / cu_k failed validation,
+                   //        [2] the forward's tile ticket (AttnArgs::fwd_ticket)
   // Row-tile workgroup i -> (sequence, tile in sequence), longest tiles first,
   // (-1, 0) past the last tile; a workgroup finds its tile with one load.
   int* fwd_map;    // [fwd_slots * 2]

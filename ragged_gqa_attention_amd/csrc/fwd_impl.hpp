@@ -668,10 +668,7 @@ __device__ __forceinline__ void build_fwd_order(const PlanArgs& pa, FwdOrder& or
 // derives the same ranking) and resolves the ranks it deals itself before its
 // first tile; the snake then pairs long tiles with short ones.  The scratch
 // lives in the key-tile buffers, which no tile uses yet.
-constexpr int LPT_MAX_HEADS = 4096;
-constexpr int LPT_MAX_TILES = 2048;
 constexpr int LPT_CLASSES = 1024;   // key steps (longer tiles share class 0)
-constexpr int FWD_LIST_MAX = 16;    // tiles one workgroup resolves in advance
 constexpr int LPT_SPER = LPT_MAX_HEADS / ROW_THREADS;   // slopes per thread
 struct LptScratch {
   int hlo[LPT_MAX_HEADS];         // key-step range of every token of (plan sequence, head)
@@ -691,7 +688,7 @@ struct LptScratch {
 // sequence table so that the two loads overlap: thread tid holds (plan
 // sequence, head) pairs tid, tid + NT, ... in plan-sequence order.
 __device__ __forceinline__ bool lpt_fits(const PlanArgs& pa) {
-  return pa.batch <= 64 && pa.batch * pa.hq <= LPT_MAX_HEADS;
+  return pa.batch <= LPT_MAX_SEQS && pa.batch * pa.hq <= LPT_MAX_HEADS;
 }
 template <int NT>
 __device__ __forceinline__ void lpt_load_slopes(const PlanArgs& pa, float (&sv)[LPT_SPER]) {
@@ -909,15 +906,33 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     }
     return;
   }
+  // Without the ranked list, rank r is the r-th tile of the order table (or
+  // of batch order).  Round 0 deals ranks 0 .. P - 1 by seat; after that a
+  // workgroup that finishes a tile takes the next rank from the ticket
+  // (a.fwd_ticket, reset before the launch), so the tiles of large batches,
+  // whose lengths the snake cannot pair up, go to whichever workgroup is free
+  // first.  Without a ticket the snake continues.  Every rank is taken once
+  // either way, and a tile's result does not depend on who computes it.
+  // (The dropout instances keep the snake: the ticket code pushes their
+  // register allocation into spills.)
+  int* const ticket = DROP ? nullptr : a.fwd_ticket;
   for (int round = 0;; ++round) {
-    const int r = round * P + ((round & 1) ? P - 1 - w : w);
-    if (status == 1 && r >= ord.nrt) break;
+    int r = round * P + ((round & 1) ? P - 1 - w : w);
+    const bool by_ticket = ticket != nullptr && round > 0;
+    if (!by_ticket && status == 1 && r >= ord.nrt) break;
     // wave 0 finds the tile of rank r and its key steps (the planner's
     // range) and hands them over through LDS
     if (wave == 0) {
-      RowTile rt;
+      if (by_ticket) {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(ticket, 1);
+        r = P + __builtin_amdgcn_readfirstlane(t);   // lane 0's ticket
+      }
+      RowTile rt{};
       bool ok = true;
-      if (status == 1) {   // last table entry whose first rank is <= r (a nonempty one)
+      if (status == 1 && r >= ord.nrt) {
+        ok = false;
+      } else if (status == 1) {   // last table entry whose first rank is <= r (a nonempty one)
         int lo = 0, hi = ord.n - 1;
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;

@@ -60,6 +60,10 @@ struct AttnArgs {
   // planner (rewritten by ksteps_kernel in the standalone backward) and read
   // by the forward, dK/dV and dQ kernels.
   int* ksteps;
+  // The forward's tile ticket (plan.flag[2]), reset to 0 by a launch just
+  // before the forward; null when the forward deals every tile in its fixed
+  // snake (the batches whose ranking fits a workgroup).  See fwd_kernel.
+  int* fwd_ticket;
   // Skip bound in log2 units (0 turns skipping off): keys whose ALiBi term
   // slope * log2(e) * |c_i - j| exceeds it are dropped (the planner's ranges).
   float skip_log2;
@@ -215,6 +219,14 @@ __device__ __forceinline__ int64_t slope_base(int v, int hkv, int group, int64_t
   return (int64_t)b * stride + (int64_t)(v - b * hkv) * group;
 }
 
+// Limits of the forward's longest-first list (each workgroup ranks every tile
+// in LDS, fwd_impl.hpp): plan sequences, (plan sequence, head) pairs, row
+// tiles, and rounds of the snake a workgroup resolves in advance.
+constexpr int LPT_MAX_SEQS = 64;
+constexpr int LPT_MAX_HEADS = 4096;
+constexpr int LPT_MAX_TILES = 2048;
+constexpr int FWD_LIST_MAX = 16;
+
 // Planner (one workgroup), for the calls whose forward grid does not hold it.
 hipError_t launch_prep(const PlanArgs& pa, hipStream_t s);
 // Forward over the a.fwd_slots row-tile slots, with the planner (pa) in an
@@ -266,6 +278,8 @@ inline hipError_t launch_dq(const AttnArgs& a, int dtype, int d, bool cap, int g
   }
 }
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, int d, bool cap, hipStream_t s);
+// Sets *ticket = 0 on the stream (a one-thread launch, safe to capture).
+hipError_t launch_ticket_reset(int* ticket, hipStream_t s);
 // Key-step ranges of the standalone backward, from the row records, and its
 // dK/dV units planned from them.
 hipError_t launch_ksteps(const AttnArgs& a, int grid, hipStream_t s);

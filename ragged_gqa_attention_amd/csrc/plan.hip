@@ -186,6 +186,15 @@ static hipError_t launch_rowinfo_t(const AttnArgs& a, int dtype, bool cap, int g
   return hipGetLastError();
 }
 
+__global__ __launch_bounds__(64) void ticket_kernel(int* ticket) {
+  if (threadIdx.x == 0) *ticket = 0;
+}
+
+hipError_t launch_ticket_reset(int* ticket, hipStream_t s) {
+  hipLaunchKernelGGL(ticket_kernel, 1, 64, 0, s, ticket);
+  return hipGetLastError();
+}
+
 hipError_t launch_rowinfo(const AttnArgs& a, int dtype, int d, bool cap, hipStream_t s) {
   const int64_t n = a.total_q * a.hq * 8;
   if (n <= 0) return hipSuccess;
