@@ -74,7 +74,8 @@ template <class T, int D, bool CAP, bool DELTA, bool WIN, bool DROP>
 __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, const int b,
                                          const int tile, const int q0, const int Lq,
                                          const int k0, const int Lk, const int klo,
-                                         const int khi) {
+                                         const int khi, int* const grab = nullptr,
+                                         int* const grabbed = nullptr, const int grab_base = 0) {
   constexpr int KSTEPS = Geo<D>::KSTEPS, DBLK = Geo<D>::DBLK, CHUNKS = Geo<D>::CHUNKS;
   constexpr int BLK_COLS = Geo<D>::BLK_COLS, O_PITCH = o_pitch<D>();
   static_assert(ROW_TILE * O_PITCH * 2 + ROW_TILE * 16 <= (int)sizeof(FwdShared<D>),
@@ -459,6 +460,10 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
     }
   }
 
+  // grab (ticket dealing): the workgroup's next rank is requested here, so the
+  // atomic's round trip overlaps the epilogue, and lands in *grabbed at the end
+  int ticket_got = 0;
+  if (grab != nullptr && threadIdx.x == 0) ticket_got = atomicAdd(grab, 1);
   // Epilogue.  The normalised O goes through LDS so that global stores (and
   // the dO loads of Delta) move whole 64-byte pieces of rows: in the
   // accumulator layout a lane holds 8-byte pieces of one row, which would
@@ -581,6 +586,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
           rec;
     }
   }
+  if (grab != nullptr && threadIdx.x == 0) *grabbed = grab_base + ticket_got;
 }
 
 // The forward's row tiles in a fixed order: plan sequences by key length,
@@ -914,20 +920,19 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
   // first.  Without a ticket the snake continues.  Every rank is taken once
   // either way, and a tile's result does not depend on who computes it.
   // (The dropout instances keep the snake: the ticket code pushes their
-  // register allocation into spills.)
+  // register allocation into spills.)  Each tile requests the next rank
+  // during its epilogue (fwd_tile), so the atomic's round trip stays off the
+  // path.  (One ticket per XCD, keeping a sequence's neighbouring tiles in one
+  // L2, balanced worse and measured slower at three of four such workloads.)
   int* const ticket = DROP ? nullptr : a.fwd_ticket;
+  __shared__ int next_rank;
   for (int round = 0;; ++round) {
-    int r = round * P + ((round & 1) ? P - 1 - w : w);
     const bool by_ticket = ticket != nullptr && round > 0;
+    const int r = by_ticket ? next_rank : round * P + ((round & 1) ? P - 1 - w : w);
     if (!by_ticket && status == 1 && r >= ord.nrt) break;
     // wave 0 finds the tile of rank r and its key steps (the planner's
     // range) and hands them over through LDS
     if (wave == 0) {
-      if (by_ticket) {
-        int t = 0;
-        if (lane == 0) t = atomicAdd(ticket, 1);
-        r = P + __builtin_amdgcn_readfirstlane(t);   // lane 0's ticket
-      }
       RowTile rt{};
       bool ok = true;
       if (status == 1 && r >= ord.nrt) {
@@ -964,7 +969,7 @@ __global__ __launch_bounds__(ROW_THREADS, 1) void fwd_kernel(const AttnArgs a, c
     const int b = tinfo[0];
     if (b < 0) break;
     fwd_tile<T, D, CAP, DELTA, WIN, DROP>(a, sm, b, tinfo[1], tinfo[2], tinfo[3], tinfo[4], tinfo[5],
-                                    tinfo[6], tinfo[7]);
+                                    tinfo[6], tinfo[7], ticket, &next_rank, P);
     __syncthreads();   // the next tile reuses tinfo and the LDS buffers
   }
 }
