@@ -48,6 +48,44 @@ def test_bitwise_repeatable(cfg, store_ds):
                                b.view(torch.uint8) if b.dtype != torch.float32 else b.view(torch.int32))
 
 
+@pytest.mark.parametrize("store_ds", [True, False])
+def test_results_do_not_depend_on_the_schedule(store_ds):
+    """A sequence's out, lse and dQ are the same bits whether it runs inside
+    the whole q_long_k_short batch (28k row tiles: the forward deals its tiles
+    by ticket, so which workgroup takes which tile changes from call to call)
+    or in a batch of three (ranked longest first and dealt in a fixed snake),
+    since every row tile is computed the same way by whichever workgroup
+    takes it, over the same key steps.  dK and dV sum partial segments whose
+    split follows the batch, so they agree to rounding only."""
+    need_gpu()
+    g = W.make_workload(2).to("cuda")
+    whole = rga.attn_varlen_full_vjp(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.dout,
+                                     softcap=g.softcap, scale_multiplier=g.scale_multiplier,
+                                     want_lse=True, check=True, store_ds=store_ds)
+    torch.cuda.synchronize()
+    cu_q = g.cu_q.cpu().tolist()
+    cu_k = g.cu_k.cpu().tolist()
+    for b0 in (0, 17):
+        b1 = b0 + 3
+        q0, q1, k0, k1 = cu_q[b0], cu_q[b1], cu_k[b0], cu_k[b1]
+        cq = (g.cu_q[b0:b1 + 1] - q0).contiguous()
+        ck = (g.cu_k[b0:b1 + 1] - k0).contiguous()
+        part = rga.attn_varlen_full_vjp(g.q[q0:q1], g.k[k0:k1], g.v[k0:k1], cq, ck,
+                                        g.slopes[b0:b1].contiguous(), g.dout[q0:q1],
+                                        softcap=g.softcap, scale_multiplier=g.scale_multiplier,
+                                        want_lse=True, check=True, store_ds=store_ds)
+        torch.cuda.synchronize()
+        out_w, dq_w, dk_w, dv_w, lse_w = whole
+        out_p, dq_p, dk_p, dv_p, lse_p = part
+        label = f"sequences {b0}..{b1 - 1}, stored dS {store_ds}"
+        assert torch.equal(out_p.view(torch.int16), out_w[q0:q1].view(torch.int16)), label
+        assert torch.equal(lse_p.view(torch.int32), lse_w[q0:q1].view(torch.int32)), label
+        assert torch.equal(dq_p.view(torch.int16), dq_w[q0:q1].view(torch.int16)), label
+        for name, x, y in (("dk", dk_p, dk_w[k0:k1]), ("dv", dv_p, dv_w[k0:k1])):
+            assert_close(name, x.float().cpu().numpy(), y.float().cpu().numpy(), TOL[g.dtype],
+                         label)
+
+
 def test_forward_and_backward_entries():
     """attn_varlen_fwd then attn_varlen_bwd match the oracle like the fused call."""
     need_gpu()
