@@ -84,6 +84,14 @@ def test_results_do_not_depend_on_the_schedule(store_ds):
         for name, x, y in (("dk", dk_p, dk_w[k0:k1]), ("dv", dv_p, dv_w[k0:k1])):
             assert_close(name, x.float().cpu().numpy(), y.float().cpu().numpy(), TOL[g.dtype],
                          label)
+    if store_ds:
+        # the forward-only entry deals the same batch by ticket too
+        out_f, lse_f = rga.attn_varlen_fwd(g.q, g.k, g.v, g.cu_q, g.cu_k, g.slopes, g.softcap,
+                                           g.scale_multiplier, check=True)
+        torch.cuda.synchronize()
+        assert_close("out", out_f.float().cpu().numpy(), whole[0].float().cpu().numpy(),
+                     TOL[g.dtype], "forward entry")
+        assert_lse(lse_f.cpu().numpy(), whole[4].cpu().numpy(), "forward entry")
 
 
 def test_forward_and_backward_entries():
