@@ -343,16 +343,20 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
     // independent: every wave takes a step as S0 S1 | logits/P 0 | PV0 |
     // logits/P 1 | PV1.  (Offsetting the two waves of a SIMD, one of them
     // deferring block 1 of each step into the next, measured 1.5 % slower.)
-    auto step = [&](int kt, auto mk, auto nr) {
+    // (b1 false: every key of block 1 lies past Lk, so its weights are
+    // exactly 0 and add nothing to O or l; only a partial last step has it)
+    auto step = [&](int kt, auto mk, auto nr, bool b1 = true) {
       const int buf = kt % FWD_NBUF, kbase = kt * TILE_ROWS;
       scores(0, sm.k[buf]);
-      scores(1, sm.k[buf]);
+      if (b1) scores(1, sm.k[buf]);
       logits(0, kbase, mk, nr);
       probs(0, kbase);
       pv(0, sm.v[buf]);
-      logits(1, kbase, mk, nr);
-      probs(1, kbase);
-      pv(1, sm.v[buf]);
+      if (b1) {
+        logits(1, kbase, mk, nr);
+        probs(1, kbase);
+        pv(1, sm.v[buf]);
+      }
     };
     // With dropout, waves w and w + 4 (one SIMD) run offset instead: wave
     // w + 4 defers block 1 of each step into the next (it reads the previous
@@ -409,7 +413,7 @@ __device__ __forceinline__ void fwd_tile(const AttnArgs& a, FwdShared<D>& sm, co
       }
       if (partial) {
         advance(nfull);
-        step(nfull, masked, Flag<true>{});
+        step(nfull, masked, Flag<true>{}, Lk - nfull * TILE_ROWS > 32);
       }
     }
   } else {
